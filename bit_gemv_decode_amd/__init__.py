@@ -1,0 +1,12 @@
+"""MI355X (gfx950) ternary GEMV: BITCOS / five-trit / 2-bit packed weights, int8 activations.
+
+The compute path is libternary_gemv.so (C ABI in include/ternary_gemv.h; HIP kernels for gfx950);
+this package is its Python binding plus the seeded synthetic-input generator.
+"""
+from .binding import (FMT_2BIT, FMT_5TRIT, FMT_BITCOS, FMT_NAMES, TG_GROUP, TG_MAX_M, DeviceWeights, Packed,
+                      TgError, describe, pack, pack_2bit, pack_5trit, pack_bitcos, ternary_gemv, ternary_gemv_acc,
+                      unpack, validate)
+
+__all__ = ["FMT_BITCOS", "FMT_5TRIT", "FMT_2BIT", "FMT_NAMES", "TG_GROUP", "TG_MAX_M", "DeviceWeights", "Packed",
+           "TgError", "describe", "pack", "pack_bitcos", "pack_5trit", "pack_2bit", "ternary_gemv",
+           "ternary_gemv_acc", "unpack", "validate"]

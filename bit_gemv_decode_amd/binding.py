@@ -1,0 +1,252 @@
+"""Thin Python binding of the C ABI in include/ternary_gemv.h (argument marshalling only).
+
+Every numeric step runs in libternary_gemv.so: the host packers in C++ and the GEMV in HIP kernels
+on the GPU. PyTorch supplies device memory and streams; numpy supplies host arrays. There is no
+fallback: if the library is missing or the GPU path is unavailable the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libternary_gemv.so")
+
+TG_GROUP = 128
+TG_MAX_M = 16
+TG_HEADER_BYTES = 256
+FMT_BITCOS, FMT_5TRIT, FMT_2BIT = 1, 2, 3
+FMT_NAMES = {FMT_BITCOS: "bitcos", FMT_5TRIT: "5trit", FMT_2BIT: "2bit"}
+ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4: "TG_EFORMAT",
+          -5: "TG_ECORRUPT", -6: "TG_ENOSPACE", -7: "TG_EHIP"}
+
+# Every symbol include/ternary_gemv.h declares.
+EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_describe", "tg_validate", "tg_unpack",
+           "ternary_gemv", "ternary_gemv_acc", "tg_strerror", "tg_version"]
+
+
+class TgError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({strerror(code)})")
+
+
+class TgDesc(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("fmt", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("nnz", ctypes.c_uint64),
+                ("off_codes", ctypes.c_uint64), ("bytes_codes", ctypes.c_uint64),
+                ("off_signs", ctypes.c_uint64), ("bytes_signs", ctypes.c_uint64),
+                ("off_index", ctypes.c_uint64), ("bytes_index", ctypes.c_uint64),
+                ("bytes_total", ctypes.c_uint64), ("bytes_payload", ctypes.c_uint64),
+                ("reserved", ctypes.c_uint64 * 2)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libternary_gemv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_gemv_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        for name in ("tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit"):
+            f = getattr(L, name)
+            f.argtypes = [p, i64, i64, p, sz, ctypes.POINTER(sz)]
+            f.restype = ctypes.c_int
+        L.tg_describe.argtypes = [p, sz, ctypes.POINTER(TgDesc)]
+        L.tg_describe.restype = ctypes.c_int
+        L.tg_validate.argtypes = [p, sz]
+        L.tg_validate.restype = ctypes.c_int
+        L.tg_unpack.argtypes = [p, sz, p]
+        L.tg_unpack.restype = ctypes.c_int
+        L.ternary_gemv.argtypes = [ctypes.POINTER(TgDesc), p, p, p, p, ctypes.c_int32, p]
+        L.ternary_gemv.restype = ctypes.c_int
+        L.ternary_gemv_acc.argtypes = [ctypes.POINTER(TgDesc), p, p, p, ctypes.c_int32, p]
+        L.ternary_gemv_acc.restype = ctypes.c_int
+        L.tg_strerror.argtypes = [ctypes.c_int]
+        L.tg_strerror.restype = ctypes.c_char_p
+        L.tg_version.argtypes = []
+        L.tg_version.restype = ctypes.c_uint32
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().tg_strerror(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise TgError(code, what)
+
+
+def _host_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Packed:
+    """A host packed buffer (descriptor + sections) as produced by the library's packers."""
+
+    def __init__(self, buf: np.ndarray):
+        self.buf = buf
+        self.desc = describe(buf)
+
+    fmt = property(lambda self: self.desc.fmt)
+    n = property(lambda self: self.desc.n)
+    k = property(lambda self: self.desc.k)
+    nnz = property(lambda self: self.desc.nnz)
+    payload_bytes = property(lambda self: self.desc.bytes_payload)
+
+    def section(self, name: str) -> np.ndarray:
+        off = getattr(self.desc, "off_" + name)
+        nbytes = getattr(self.desc, "bytes_" + name)
+        return self.buf[off:off + nbytes]
+
+    def sign_bytes(self) -> np.ndarray:
+        return self.section("signs")[: (self.nnz + 7) // 8]
+
+    def rowoff(self) -> np.ndarray:
+        return self.section("index").view(np.uint32)
+
+
+def _pack(fn_name: str, w: np.ndarray) -> Packed:
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    if w.ndim != 2:
+        raise ValueError("weights must be a 2-D [n, k] int8 array")
+    n, k = w.shape
+    fn = getattr(lib(), fn_name)
+    need = ctypes.c_size_t(0)
+    _check(fn(_host_ptr(w), n, k, None, 0, ctypes.byref(need)), fn_name)
+    buf = np.empty(need.value, dtype=np.uint8)
+    got = ctypes.c_size_t(0)
+    _check(fn(_host_ptr(w), n, k, _host_ptr(buf), buf.size, ctypes.byref(got)), fn_name)
+    return Packed(buf)
+
+
+def pack_bitcos(w: np.ndarray) -> Packed:
+    return _pack("tg_pack_bitcos", w)
+
+
+def pack_5trit(w: np.ndarray) -> Packed:
+    return _pack("tg_pack_5trit", w)
+
+
+def pack_2bit(w: np.ndarray) -> Packed:
+    return _pack("tg_pack_2bit", w)
+
+
+PACKERS = {FMT_BITCOS: pack_bitcos, FMT_5TRIT: pack_5trit, FMT_2BIT: pack_2bit}
+
+
+def pack(fmt: int, w: np.ndarray) -> Packed:
+    return PACKERS[fmt](w)
+
+
+def describe(buf: np.ndarray) -> TgDesc:
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    d = TgDesc()
+    _check(lib().tg_describe(_host_ptr(buf), buf.size, ctypes.byref(d)), "tg_describe")
+    return d
+
+
+def validate(buf: np.ndarray) -> None:
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    _check(lib().tg_validate(_host_ptr(buf), buf.size), "tg_validate")
+
+
+def unpack(buf: np.ndarray) -> np.ndarray:
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    d = describe(buf)
+    w = np.empty((d.n, d.k), dtype=np.int8)
+    _check(lib().tg_unpack(_host_ptr(buf), buf.size, _host_ptr(w)), "tg_unpack")
+    return w
+
+
+# ----------------------------------------------------------------------------------------------- GPU
+
+class DeviceWeights:
+    """A packed buffer resident in GPU memory (a torch uint8 tensor) plus its host descriptor."""
+
+    def __init__(self, packed: Packed, device="cuda"):
+        import torch
+
+        self.desc = packed.desc
+        self.tensor = torch.from_numpy(packed.buf).to(device)
+
+    @classmethod
+    def from_tensor(cls, desc: TgDesc, tensor):
+        obj = cls.__new__(cls)
+        obj.desc = desc
+        obj.tensor = tensor
+        return obj
+
+    fmt = property(lambda self: self.desc.fmt)
+    n = property(lambda self: self.desc.n)
+    k = property(lambda self: self.desc.k)
+    payload_bytes = property(lambda self: self.desc.bytes_payload)
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_cuda(t, dtype, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ternary_gemv(w: DeviceWeights, scales, x, y=None, stream=None):
+    """y[m, n] = sum_g scales[n, g] * acc[m, n, g] (see include/ternary_gemv.h). Asynchronous."""
+    import torch
+
+    _require_cuda(w.tensor, torch.uint8, "weights")
+    _require_cuda(scales, torch.float16, "scales")
+    _require_cuda(x, torch.int8, "x")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    m = x.shape[0]
+    if x.shape[1] != w.k or tuple(scales.shape) != (w.n, w.k // TG_GROUP):
+        raise ValueError("shape mismatch between weights, scales and x")
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    _require_cuda(y, torch.float32, "y")
+    if tuple(y.shape) != (m, w.n):
+        raise ValueError("y has the wrong shape")
+    _check(lib().ternary_gemv(ctypes.byref(w.desc), ctypes.c_void_p(w.tensor.data_ptr()),
+                              ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(x.data_ptr()),
+                              ctypes.c_void_p(y.data_ptr()), m, _stream_handle(stream)), "ternary_gemv")
+    return y
+
+
+def ternary_gemv_acc(w: DeviceWeights, x, acc=None, stream=None):
+    """int32 per-group accumulators acc[m, n, k/128] (bit-exact entry point). Asynchronous."""
+    import torch
+
+    _require_cuda(w.tensor, torch.uint8, "weights")
+    _require_cuda(x, torch.int8, "x")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    m = x.shape[0]
+    if x.shape[1] != w.k:
+        raise ValueError("x has the wrong length")
+    if acc is None:
+        acc = torch.empty((m, w.n, w.k // TG_GROUP), dtype=torch.int32, device=x.device)
+    _require_cuda(acc, torch.int32, "acc")
+    _check(lib().ternary_gemv_acc(ctypes.byref(w.desc), ctypes.c_void_p(w.tensor.data_ptr()),
+                                  ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(acc.data_ptr()), m,
+                                  _stream_handle(stream)), "ternary_gemv_acc")
+    return acc

@@ -1,0 +1,150 @@
+/*
+ * ternary_gemv.h -- C ABI of the MI355X (gfx950) ternary GEMV library.
+ *
+ * The operation ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-C, the int8 path after
+ * Fig. 5): int8 activations times a ternary {-1, 0, +1} weight matrix whose groups of 128 consecutive
+ * reduction elements share one 16-bit scale. Dot products accumulate exactly in int32 per group and
+ * the group scale is applied once per group:
+ *
+ *     acc[m][n][g] = sum_{k = 128 g}^{128 g + 127} W[n][k] * x[m][k]              (int32, exact)
+ *     y[m][n]      = sum_g scale[n][g] * acc[m][n][g]                            (fp64 sum, fp32 store)
+ *
+ * W is n rows by k reduction elements (k a multiple of 128), x is m rows of k int8, y is m rows of
+ * n floats. The weights are read straight from one of three packed formats:
+ *
+ *   TG_FMT_BITCOS -- "BITmap and COmpacted Signs" (same paper, Sec. II-A, Fig. 2, Eq. 1): a presence
+ *       bitmap with one bit per weight (set where the weight is non-zero) plus a sign stream with one
+ *       bit per non-zero weight, in the bitmap's storage order (the j-th sign bit belongs to the j-th
+ *       set bit). 2 - z bits per weight at zero density z. Layout here: the bitmap is row-major, bit
+ *       (r*k + c) of the bit stream is weight (r, c), packed LSB-first (the Eq. (2)-(3) example maps
+ *       the first element to the least-significant bit); a sign bit of 1 marks -1. An index of n+1
+ *       unsigned 32-bit sign positions (rowoff[r] = sign-stream position of row r's first non-zero,
+ *       rowoff[n] = nnz) lets a row start decoding without scanning the rows before it.
+ *   TG_FMT_5TRIT -- five ternary digits per byte (same paper, Sec. I; "Sub-Two-Bit Ternary Weight
+ *       Storage with Table-Free Arithmetic Decoding", abstract): 3^5 = 243 <= 256, 26 bytes per
+ *       128-weight group (1.625 bits per weight). Byte b of a group holds weights 5b..5b+4 as base-3
+ *       digits d = w + 1, the first weight least significant; byte 25 holds weights 125..127 and two
+ *       padding digits of value 1. Bytes >= 243 are invalid.
+ *   TG_FMT_2BIT -- two bits per weight (Table I's "2-bit packing"): code c = w + 1, four codes per
+ *       byte, the first weight in the lowest two bits. Code 3 is invalid.
+ *
+ * Scales are IEEE binary16, row-major [n][k/128], and are passed separately from the packed weights.
+ *
+ * Conventions
+ *   - Every buffer is owned by the caller. The library allocates no device memory and keeps no
+ *     mutable global state; all functions are re-entrant.
+ *   - Functions return TG_OK (0) or a negative TG_E* code; tg_strerror() names it. On error nothing
+ *     is written to outputs and nothing is enqueued on the GPU.
+ *   - Host functions (tg_pack_*, tg_describe, tg_validate, tg_unpack) take host pointers and are
+ *     synchronous.
+ *   - ternary_gemv / ternary_gemv_acc take a HOST copy of the packed buffer's descriptor and DEVICE
+ *     pointers for everything else; they enqueue on `stream` (a hipStream_t passed as void*, NULL =
+ *     the default stream) and return without synchronising.
+ */
+#ifndef TERNARY_GEMV_H
+#define TERNARY_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_GROUP 128         /* reduction elements per scale group */
+#define TG_MAX_M 16          /* most activation rows one ternary_gemv call accepts */
+#define TG_MAGIC 0x53444754u /* "TGDS" little-endian: first word of every packed buffer */
+#define TG_VERSION 1u
+#define TG_HEADER_BYTES 256u /* the descriptor occupies the first 256 bytes of a packed buffer */
+
+typedef enum { TG_FMT_BITCOS = 1, TG_FMT_5TRIT = 2, TG_FMT_2BIT = 3 } tg_fmt;
+
+enum {
+    TG_OK = 0,
+    TG_EINVAL = -1,       /* null pointer, bad enum value, m outside [1, TG_MAX_M] */
+    TG_ENOTTERNARY = -2,  /* a weight outside {-1, 0, +1} was given to a packer */
+    TG_ESHAPE = -3,       /* n < 1, k < 1, k not a multiple of 128, or sizes that overflow the format */
+    TG_EFORMAT = -4,      /* the buffer is not a packed buffer of this library/version */
+    TG_ECORRUPT = -5,     /* a packed buffer whose contents contradict its descriptor */
+    TG_ENOSPACE = -6,     /* the output buffer is smaller than required */
+    TG_EHIP = -7          /* the HIP runtime reported an error while enqueuing */
+};
+
+/*
+ * Descriptor stored in the first TG_HEADER_BYTES of every packed buffer (host byte order, i.e.
+ * little-endian). Section offsets are in bytes from the start of the buffer and are 256-aligned.
+ *   BITCOS: codes = bitmap (n*k/8 bytes), signs = sign stream (ceil(nnz/8) bytes followed by zero
+ *           padding up to bytes_signs), index = rowoff (4*(n+1) bytes).
+ *   5TRIT:  codes = n * (k/128) * 26 bytes, row-major by (row, group). No signs or index.
+ *   2BIT:   codes = n * k / 4 bytes, row-major. No signs or index.
+ */
+typedef struct tg_desc {
+    uint32_t magic;      /* TG_MAGIC */
+    uint32_t version;    /* TG_VERSION */
+    int32_t fmt;         /* tg_fmt */
+    int32_t group;       /* TG_GROUP */
+    int64_t n;           /* rows */
+    int64_t k;           /* reduction elements per row */
+    uint64_t nnz;        /* non-zero weights (all formats) */
+    uint64_t off_codes, bytes_codes;
+    uint64_t off_signs, bytes_signs;
+    uint64_t off_index, bytes_index;
+    uint64_t bytes_total; /* whole buffer, header included */
+    uint64_t bytes_payload; /* algorithmic bytes: codes + ceil(nnz/8) sign bytes + index (no padding, no header) */
+    uint64_t reserved[2];
+} tg_desc;
+
+/*
+ * Packers: convert a host int8 matrix W[n][k] (values in {-1, 0, +1}) into a packed buffer
+ * (descriptor + sections). Two-call pattern: with out == NULL only *out_bytes is written (the size
+ * needed); otherwise out must hold out_cap >= that size, and *out_bytes receives the size written.
+ * Errors: TG_EINVAL (w or out_bytes NULL), TG_ESHAPE (n < 1, k < 1, k % 128 != 0, or more than
+ * 2^32 - 1 non-zeros for BITCOS), TG_ENOTTERNARY, TG_ENOSPACE.
+ */
+int tg_pack_bitcos(const int8_t *w, int64_t n, int64_t k, void *out, size_t out_cap, size_t *out_bytes);
+int tg_pack_5trit(const int8_t *w, int64_t n, int64_t k, void *out, size_t out_cap, size_t *out_bytes);
+int tg_pack_2bit(const int8_t *w, int64_t n, int64_t k, void *out, size_t out_cap, size_t *out_bytes);
+
+/* Read and check the descriptor of a host packed buffer of `bytes` bytes (header fields only).
+ * Errors: TG_EINVAL, TG_EFORMAT (magic/version/fmt/group wrong or bytes too small),
+ * TG_ECORRUPT (sections that do not fit the buffer or do not match n, k, nnz). */
+int tg_describe(const void *packed, size_t bytes, tg_desc *out);
+
+/* Full content check of a host packed buffer: the descriptor, then every code (five-trit bytes < 243
+ * with weight-0 padding digits, no 2-bit code 3) and, for BITCOS, rowoff[0] = 0, each row's index
+ * step equal to that row's bitmap popcount, rowoff[n] = nnz. Returns TG_OK or the first error. */
+int tg_validate(const void *packed, size_t bytes);
+
+/* Decode a host packed buffer back to int8 W[n][k] (w_out holds n*k bytes); lossless. Validates
+ * first (same errors as tg_validate). */
+int tg_unpack(const void *packed, size_t bytes, int8_t *w_out);
+
+/*
+ * GPU GEMV (asynchronous). desc: host copy of the descriptor of the packed buffer whose device copy
+ * is W (bytes_total bytes, the same image as the host buffer). scales: device fp16 [n][k/128] bit
+ * patterns. x: device int8 [m][k]. y: device float [m][n]. 1 <= m <= TG_MAX_M.
+ * The kernels trust W's contents as far as its descriptor describes them (validate host buffers
+ * with tg_validate before upload); every device read stays inside the sections the descriptor
+ * names even for corrupt contents, so a corrupt buffer gives wrong numbers, not a fault.
+ * Alignment: W and x 16-byte aligned, y / acc 4-byte aligned, scales 2-byte aligned.
+ * Errors: TG_EINVAL (null or misaligned pointer, m out of range), TG_EFORMAT / TG_ECORRUPT
+ * (descriptor), TG_EHIP (launch failure).
+ */
+int ternary_gemv(const tg_desc *desc, const void *W, const uint16_t *scales, const int8_t *x, float *y,
+                 int32_t m, void *stream);
+
+/* Same contraction, but writes the exact int32 per-group accumulators acc[m][n][k/128] instead of y
+ * (no scales). This is the bit-exact parity entry point. */
+int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_t *acc, int32_t m, void *stream);
+
+/* Static string for a TG_* code ("unknown error" for anything else). */
+const char *tg_strerror(int code);
+
+/* TG_VERSION of the loaded library. */
+uint32_t tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERNARY_GEMV_H */

@@ -1,0 +1,152 @@
+"""C ABI: exported symbols, error codes and corrupt-buffer detection (CPU only, no compute calls)."""
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+import bit_gemv_decode_amd as B
+from bit_gemv_decode_amd import binding, synth
+from tests.conftest import ROOT
+
+
+def _declared_functions():
+    src = open(f"{ROOT}/include/ternary_gemv.h").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(binding.EXPORTS), declared
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert binding.lib().tg_version() == 1
+
+
+def test_strerror_names_every_code():
+    for code in range(0, -8, -1):
+        assert binding.strerror(code) != "unknown error"
+    assert binding.strerror(-99) == "unknown error"
+
+
+def _raw(fn, w, n, k, out=None, cap=0):
+    need = ctypes.c_size_t(0)
+    ptr = None if w is None else w.ctypes.data_as(ctypes.c_void_p)
+    outp = None if out is None else out.ctypes.data_as(ctypes.c_void_p)
+    return fn(ptr, n, k, outp, cap, ctypes.byref(need)), need.value
+
+
+@pytest.mark.parametrize("name", ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit"])
+def test_packer_errors(name):
+    fn = getattr(binding.lib(), name)
+    w = np.zeros((4, 256), np.int8)
+    assert _raw(fn, None, 4, 256)[0] == -1
+    assert _raw(fn, w, 4, 200)[0] == -3  # k % 128
+    assert _raw(fn, w, 0, 256)[0] == -3
+    assert _raw(fn, w, 4, 0)[0] == -3
+    bad = w.copy()
+    bad[2, 100] = 2
+    assert _raw(fn, bad, 4, 256)[0] == -2
+    bad[2, 100] = -128
+    assert _raw(fn, bad, 4, 256)[0] == -2
+    code, need = _raw(fn, w, 4, 256)
+    assert code == 0 and need > 0
+    small = np.zeros(need - 1, np.uint8)
+    assert _raw(fn, w, 4, 256, small, small.size)[0] == -6
+    assert not small.any()  # nothing written on error
+    with pytest.raises(B.TgError):
+        B.pack(1 if "bitcos" in name else 2 if "5trit" in name else 3, bad)
+
+
+def test_describe_rejects_foreign_and_truncated_buffers():
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    p = B.pack_bitcos(w)
+    with pytest.raises(B.TgError) as e:
+        B.describe(p.buf[:100])
+    assert e.value.code == -4
+    bad = p.buf.copy()
+    bad[0] ^= 1  # magic
+    with pytest.raises(B.TgError) as e:
+        B.describe(bad)
+    assert e.value.code == -4
+    with pytest.raises(B.TgError) as e:
+        B.describe(p.buf[: p.desc.bytes_total - 256])  # sections past the end
+    assert e.value.code == -5
+
+
+def _poke_desc(buf, field, value):
+    out = buf.copy()
+    d = binding.TgDesc.from_buffer(out)
+    setattr(d, field, value)
+    return out
+
+
+def test_describe_rejects_inconsistent_descriptors():
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    p = B.pack_bitcos(w)
+    for field, value, code in [("fmt", 9, -4), ("group", 64, -4), ("version", 2, -4), ("k", 200, -5),
+                               ("n", 0, -5), ("nnz", 8 * 256 + 1, -5), ("bytes_codes", 1, -5),
+                               ("off_signs", 300, -5), ("bytes_index", 4, -5), ("bytes_payload", 1, -5)]:
+        with pytest.raises(B.TgError) as e:
+            B.describe(_poke_desc(p.buf, field, value))
+        assert e.value.code == code, field
+    t = B.pack_5trit(w)
+    with pytest.raises(B.TgError) as e:
+        B.describe(_poke_desc(t.buf, "bytes_total", t.desc.off_codes + t.desc.bytes_codes))
+    assert e.value.code == -5
+
+
+def test_validate_detects_corrupt_contents():
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    p = B.pack_bitcos(w)
+    bad = p.buf.copy()
+    bad[p.desc.off_index + 4 * 3] += 1  # rowoff[3] no longer matches the bitmap
+    with pytest.raises(B.TgError) as e:
+        B.validate(bad)
+    assert e.value.code == -5
+    bad = p.buf.copy()
+    bad[p.desc.off_codes] ^= 1  # bitmap popcount of row 0 changes
+    with pytest.raises(B.TgError) as e:
+        B.unpack(bad)
+    assert e.value.code == -5
+    t = B.pack_5trit(w)
+    bad = t.buf.copy()
+    bad[t.desc.off_codes + 7] = 243
+    with pytest.raises(B.TgError):
+        B.validate(bad)
+    bad = t.buf.copy()
+    bad[t.desc.off_codes + 25] = 0  # padding digits must be weight 0
+    with pytest.raises(B.TgError):
+        B.validate(bad)
+    b = B.pack_2bit(w)
+    bad = b.buf.copy()
+    bad[b.desc.off_codes + 3] |= 0xC0  # code 3
+    with pytest.raises(B.TgError):
+        B.validate(bad)
+    bad = b.buf.copy()
+    bad[b.desc.off_codes + 3] ^= 0x01  # still valid codes, but the non-zero count changes
+    with pytest.raises(B.TgError):
+        B.validate(bad)
+
+
+def test_gemv_argument_errors_before_any_gpu_work():
+    L = binding.lib()
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = B.pack_bitcos(w).desc
+    dummy = ctypes.c_void_p(256)
+    # null descriptor / pointers, m out of range, misalignment: rejected on the host
+    assert L.ternary_gemv(None, dummy, dummy, dummy, dummy, 1, None) == -1
+    assert L.ternary_gemv(ctypes.byref(d), None, dummy, dummy, dummy, 1, None) == -1
+    assert L.ternary_gemv(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, None) == -1
+    assert L.ternary_gemv(ctypes.byref(d), dummy, dummy, dummy, dummy, 17, None) == -1
+    assert L.ternary_gemv(ctypes.byref(d), ctypes.c_void_p(264), dummy, dummy, dummy, 1, None) == -1
+    assert L.ternary_gemv(ctypes.byref(d), dummy, None, dummy, dummy, 1, None) == -1
+    assert L.ternary_gemv_acc(ctypes.byref(d), dummy, dummy, None, 1, None) == -1
+    d2 = binding.TgDesc.from_buffer_copy(d)
+    d2.magic = 0
+    assert L.ternary_gemv(ctypes.byref(d2), dummy, dummy, dummy, dummy, 1, None) == -4
+    d2 = binding.TgDesc.from_buffer_copy(d)
+    d2.bytes_signs = 4
+    assert L.ternary_gemv_acc(ctypes.byref(d2), dummy, dummy, dummy, 1, None) == -5

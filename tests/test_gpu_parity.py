@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Int32 per-group accumulators must match bit for bit. fp32 outputs must satisfy, element by element,
+|y - y_ref| <= 1e-5 * max(|y_ref|, sum_g |s * acc| / sqrt(ng)): a 1e-5 relative bound, measured
+against the size of the terms when cancellation makes y_ref itself tiny. Both sides sum exact
+fp64 products (fp16 * int32 needs at most 26 bits), so for the scale ranges used here the fp64 sums
+are exact and y is expected to be bit-identical; the test also reports how many elements differ.
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import bit_gemv_decode_amd as B
+import oracle as O
+from bit_gemv_decode_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+FMTS = [B.FMT_BITCOS, B.FMT_5TRIT, B.FMT_2BIT]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    return torch.device("cuda:0")
+
+
+def y_tolerance_ok(y, y_ref, acc, scales):
+    s = scales.astype(np.float64)[None, :, :]
+    terms = np.abs(s * acc.astype(np.float64)).sum(-1) / np.sqrt(acc.shape[-1])
+    bound = 1e-5 * np.maximum(np.abs(y_ref.astype(np.float64)), terms)
+    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    return bool(np.all(err <= bound)), int((y != y_ref).sum())
+
+
+def run_case(w, x, scales, fmts=FMTS, label=""):
+    dev = _dev()
+    acc_ref = O.gemv_acc(w, x)
+    y_ref = O.combine(acc_ref, scales)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    st = torch.from_numpy(np.ascontiguousarray(scales)).to(dev)
+    for fmt in fmts:
+        _say(f"[gpu] {label} fmt={B.FMT_NAMES[fmt]} n={w.shape[0]} k={w.shape[1]} m={x.shape[0]}")
+        dw = B.DeviceWeights(B.pack(fmt, w), dev)
+        acc = B.ternary_gemv_acc(dw, xt)
+        y = B.ternary_gemv(dw, st, xt)
+        torch.cuda.synchronize()
+        acc_np = acc.cpu().numpy()
+        y_np = y.cpu().numpy()
+        assert np.array_equal(acc_np, acc_ref), f"{label} {B.FMT_NAMES[fmt]}: int32 accumulators differ"
+        ok, ndiff = y_tolerance_ok(y_np, y_ref, acc_ref, scales)
+        assert ok, f"{label} {B.FMT_NAMES[fmt]}: y outside tolerance"
+        assert ndiff == 0, f"{label} {B.FMT_NAMES[fmt]}: {ndiff} y values not bit-identical"
+
+
+SMALL = [(1, 128, 0.42, 1), (3, 256, 0.0, 2), (4, 640, 1.0, 1), (5, 2176, 0.42, 3), (37, 4096, 0.4, 4),
+         (129, 5120, 0.47, 1), (64, 2560, 0.95, 5), (17, 14336, 0.44, 16), (9, 384, 0.3, 7), (130, 1024, 0.515, 2)]
+
+
+@pytest.mark.parametrize("n,k,z,m", SMALL, ids=[f"{n}x{k}_z{z}_m{m}" for n, k, z, m in SMALL])
+def test_small_shapes(n, k, z, m):
+    seed = n * 1000 + k + m
+    w = synth.ternary(n, k, z, seed=seed)
+    x = synth.activations(m, k, seed=seed)
+    s = synth.scales(n, k // 128, seed=seed)
+    run_case(w, x, s, label=f"small {n}x{k}")
+
+
+@pytest.mark.parametrize("k,start", [(128, 60), (256, 124)])
+def test_brute_force_patterns(k, start):
+    pats = np.array(list(itertools.product([-1, 0, 1], repeat=8)), np.int8)
+    w = np.zeros((len(pats), k), np.int8)
+    w[:, start:start + 8] = pats
+    x = np.concatenate([synth.activations(2, k, seed=9), np.full((1, k), -128, np.int8), np.full((1, k), 127, np.int8)])
+    s = synth.scales(len(pats), k // 128, seed=9)
+    run_case(w, x, s, label=f"brute k={k} start={start}")
+
+
+def test_extreme_activations_and_structure():
+    n, k = 70, 2048
+    w = synth.ternary(n, k, 0.4, seed=31)
+    w[0] = 0            # empty row
+    w[1] = 1            # full positive row
+    w[2] = -1           # full negative row
+    w[3, :] = 0
+    w[3, 2047] = -1     # single non-zero at the very end
+    w[4, :64] = 0       # leading empty word
+    x = np.stack([np.full(k, -128, np.int8), np.full(k, 127, np.int8), synth.activations(1, k, seed=31)[0]])
+    s = synth.scales(n, k // 128, seed=31)
+    s[5, 3] = np.float16(0.0)
+    s[6, :] = np.float16(65504.0)
+    s[7, 0] = np.float16(-0.5)
+    run_case(w, x, s, label="extremes")
+
+
+def test_non_default_stream():
+    dev = _dev()
+    n, k = 96, 4096
+    w = synth.ternary(n, k, 0.4, seed=41)
+    x = synth.activations(1, k, seed=41)
+    s = synth.scales(n, k // 128, seed=41)
+    y_ref = O.gemv(w, s, x)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        dw = B.DeviceWeights(B.pack_bitcos(w), dev)
+        y = B.ternary_gemv(dw, torch.from_numpy(s).to(dev), torch.from_numpy(x).to(dev), stream=st)
+    st.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y_ref)
+
+
+# ----- the benchmark workloads at full size ---------------------------------------------------------
+
+LLAMA = {"q": (4096, 4096), "k": (1024, 4096), "v": (1024, 4096), "o": (4096, 4096),
+         "gate": (14336, 4096), "up": (14336, 4096), "down": (4096, 14336)}
+
+
+def test_single_gemv_2560():
+    n = k = 2560
+    w = synth.ternary(n, k, 0.42, seed=0)
+    run_case(w, synth.activations(1, k, seed=0), synth.scales(n, k // 128, seed=0), label="2560x2560")
+
+
+@pytest.mark.parametrize("name", list(LLAMA))
+def test_llama3_8b_layer(name):
+    n, k = LLAMA[name]
+    role = list(LLAMA).index(name)
+    w = synth.ternary(n, k, 0.40, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+    x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
+    s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
+    run_case(w, x, s, label=f"llama3-8b {name}")
+
+
+@pytest.mark.parametrize("z", [0.30, 0.375, 0.42, 0.47, 0.515])
+def test_zero_density_sweep_8192(z):
+    n = k = 8192
+    w = synth.ternary(n, k, z, seed=0)
+    run_case(w, synth.activations(1, k, seed=0), synth.scales(n, k // 128, seed=0), label=f"8192 z={z}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("name", ["gate", "down"])
+def test_thin_batch(name, m):
+    n, k = LLAMA[name]
+    w = synth.ternary(n, k, 0.44, seed=0, tid=synth.tensor_id(0, 1 if name == "gate" else 2, synth.STREAM_W))
+    x = synth.activations(m, k, seed=m)
+    s = synth.scales(n, k // 128, seed=0)
+    run_case(w, x, s, fmts=[B.FMT_BITCOS], label=f"thin {name} m={m}")
+
+
+def test_dead_rows_layer_5120():
+    # Four point seven six percent of FFN neurons identically zero at the same indices in gate and up.
+    n, k = 25600, 5120
+    dead = synth.dead_rows(n, round(0.0476 * n), seed=0)
+    assert dead.size == 1219
+    for role in (4, 5):
+        w = synth.ternary(n, k, 0.47, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+        w[dead] = 0
+        x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
+        s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
+        run_case(w, x, s, fmts=[B.FMT_BITCOS], label=f"dead-rows role={role}")
