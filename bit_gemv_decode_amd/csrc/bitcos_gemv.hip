@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kByteLutEntries = 6561;  // sum over the 256 presence bytes of 2^popcount = 3^8
 
-struct ByteLut {
+struct alignas(16) ByteLut {
     uint64_t ent[kByteLutEntries + 1];  // padded to an even count for 16-byte copies
     uint16_t base[256];
 };
