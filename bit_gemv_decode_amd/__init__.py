@@ -4,9 +4,9 @@ The compute path is libternary_gemv.so (C ABI in include/ternary_gemv.h; HIP ker
 this package is its Python binding plus the seeded synthetic-input generator.
 """
 from .binding import (FMT_2BIT, FMT_5TRIT, FMT_BITCOS, FMT_NAMES, TG_GROUP, TG_MAX_M, DeviceWeights, Packed,
-                      TgError, describe, pack, pack_2bit, pack_5trit, pack_bitcos, ternary_gemv, ternary_gemv_acc,
+                      Plan, TgError, describe, pack, pack_2bit, pack_5trit, pack_bitcos, ternary_gemv, ternary_gemv_acc,
                       unpack, validate)
 
 __all__ = ["FMT_BITCOS", "FMT_5TRIT", "FMT_2BIT", "FMT_NAMES", "TG_GROUP", "TG_MAX_M", "DeviceWeights", "Packed",
-           "TgError", "describe", "pack", "pack_bitcos", "pack_5trit", "pack_2bit", "ternary_gemv",
+           "Plan", "TgError", "describe", "pack", "pack_bitcos", "pack_5trit", "pack_2bit", "ternary_gemv",
            "ternary_gemv_acc", "unpack", "validate"]

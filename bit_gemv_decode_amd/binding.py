@@ -24,7 +24,9 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 
 # Every symbol include/ternary_gemv.h declares.
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_describe", "tg_validate", "tg_unpack",
-           "ternary_gemv", "ternary_gemv_acc", "tg_strerror", "tg_version"]
+           "ternary_gemv", "ternary_gemv_acc", "tg_plan_table_bytes", "tg_plan_init", "ternary_gemv_plan",
+           "tg_strerror", "tg_version"]
+PLAN_MAX_M = 3
 
 
 class TgError(RuntimeError):
@@ -41,6 +43,12 @@ class TgDesc(ctypes.Structure):
                 ("off_index", ctypes.c_uint64), ("bytes_index", ctypes.c_uint64),
                 ("bytes_total", ctypes.c_uint64), ("bytes_payload", ctypes.c_uint64),
                 ("reserved", ctypes.c_uint64 * 2)]
+
+
+class TgPlan(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("fmt", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("count", ctypes.c_int32), ("units", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
+                ("acc_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("table", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,6 +76,13 @@ def lib():
         L.ternary_gemv.restype = ctypes.c_int
         L.ternary_gemv_acc.argtypes = [ctypes.POINTER(TgDesc), p, p, p, ctypes.c_int32, p]
         L.ternary_gemv_acc.restype = ctypes.c_int
+        L.tg_plan_table_bytes.argtypes = [ctypes.c_int32]
+        L.tg_plan_table_bytes.restype = sz
+        L.tg_plan_init.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p, p, p,
+                                   p, ctypes.c_int32]
+        L.tg_plan_init.restype = ctypes.c_int
+        L.ternary_gemv_plan.argtypes = [ctypes.POINTER(TgPlan), p]
+        L.ternary_gemv_plan.restype = ctypes.c_int
         L.tg_strerror.argtypes = [ctypes.c_int]
         L.tg_strerror.restype = ctypes.c_char_p
         L.tg_version.argtypes = []
@@ -250,3 +265,54 @@ def ternary_gemv_acc(w: DeviceWeights, x, acc=None, stream=None):
                                   ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(acc.data_ptr()), m,
                                   _stream_handle(stream)), "ternary_gemv_acc")
     return acc
+
+
+class Plan:
+    """Several GEMVs of one format run as one launch (tg_plan_init / ternary_gemv_plan).
+
+    weights: list of DeviceWeights; xs: int8 [m, k] device tensors; scales and ys (fp16 [n, k/128],
+    float32 [m, n]) for fp32 outputs, or accs (int32 [m, n, k/128]) for accumulator outputs. The plan
+    keeps references to every tensor it names, and its device table, for its lifetime.
+    """
+
+    def __init__(self, weights, xs, scales=None, ys=None, accs=None):
+        import torch
+
+        count = len(weights)
+        if count < 1 or len(xs) != count:
+            raise ValueError("one x per weight matrix is required")
+        acc_mode = accs is not None
+        if acc_mode:
+            if len(accs) != count:
+                raise ValueError("one acc per weight matrix is required")
+        elif scales is None or ys is None or len(scales) != count or len(ys) != count:
+            raise ValueError("scales and ys (one per matrix) are required for fp32 outputs")
+        m = xs[0].shape[0] if xs[0].dim() == 2 else 1
+        for i, w in enumerate(weights):
+            _require_cuda(w.tensor, torch.uint8, "weights")
+            _require_cuda(xs[i], torch.int8, "x")
+            if xs[i].shape[-1] != w.k or (xs[i].shape[0] if xs[i].dim() == 2 else 1) != m:
+                raise ValueError("every x must be [m, k] with the same m")
+            if acc_mode:
+                _require_cuda(accs[i], torch.int32, "acc")
+                if tuple(accs[i].shape) != (m, w.n, w.k // TG_GROUP):
+                    raise ValueError("acc has the wrong shape")
+            else:
+                _require_cuda(scales[i], torch.float16, "scales")
+                _require_cuda(ys[i], torch.float32, "y")
+                if tuple(scales[i].shape) != (w.n, w.k // TG_GROUP) or tuple(ys[i].shape) != (m, w.n):
+                    raise ValueError("scales or y has the wrong shape")
+        L = lib()
+        nbytes = L.tg_plan_table_bytes(count)
+        self.table = torch.empty(nbytes, dtype=torch.uint8, device=xs[0].device)
+        descs = (TgDesc * count)(*[w.desc for w in weights])
+        P = ctypes.c_void_p * count
+        ptr = lambda ts: P(*[t.data_ptr() for t in ts]) if ts is not None else None
+        self.plan = TgPlan()
+        self._keep = (list(weights), list(xs), scales, ys, accs)
+        _check(L.tg_plan_init(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count, descs,
+                              ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(ys), ptr(accs), m),
+               "tg_plan_init")
+
+    def run(self, stream=None):
+        _check(lib().ternary_gemv_plan(ctypes.byref(self.plan), _stream_handle(stream)), "ternary_gemv_plan")

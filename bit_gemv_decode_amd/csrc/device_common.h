@@ -37,8 +37,71 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+
+// v moved across lanes by one DPP pattern. Lanes in rows the mask leaves out receive an undefined
+// value: only use results from lanes whose source is defined.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum of v over each aligned group of `width` lanes (width 1, 2, 4, 8 or 16, wave-uniform); every lane
+// of the group receives it. width 32: lanes 31 and 63 receive their half's sum. width 64: lane 63
+// receives the total. In every case the last lane of each group holds the group's sum. All lanes
+// must be active.
+__device__ __forceinline__ double seg_sum_f64(double v, int width) {
+    if (width >= 2) v += dpp_f64<kDppQuadSwap1>(v);
+    if (width >= 4) v += dpp_f64<kDppQuadSwap2>(v);
+    if (width >= 8) v += dpp_f64<kDppRowHalfMirror>(v);
+    if (width >= 16) v += dpp_f64<kDppRowMirror>(v);
+    if (width >= 32) v += dpp_f64<kDppRowBcast15, 0xA>(v);
+    if (width >= 64) v += dpp_f64<kDppRowBcast31, 0xC>(v);
+    return v;
+}
+
+// Total of v over the wave, returned as a wave-uniform value.
+__device__ __forceinline__ double wave_total_f64(double v) {
+    v = seg_sum_f64(v, 64);
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // IEEE binary16 bit pattern -> float (exact).
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw (untyped) buffer resource over `bytes` bytes at p. Loads through it that fall outside the
+// range return zero instead of faulting. Loads through buffer intrinsics are also never merged
+// across loop iterations by the compiler, which keeps software-pipelined loads where they are
+// written. Ranges are limited to 4 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x3 buf_u32x3(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);

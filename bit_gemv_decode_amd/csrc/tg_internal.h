@@ -13,27 +13,51 @@ constexpr uint64_t kSignPad = 16;     // zero bytes after the sign stream (room 
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-// Arguments every GEMV kernel receives (device pointers into one packed buffer plus the
-// caller's scales, activations and outputs).
-struct GemvArgs {
+// One GEMV as the kernels see it: device pointers into one packed buffer plus the caller's
+// scales, activations and outputs. Filled on the host from a checked descriptor.
+struct Problem {
     const uint8_t *codes;     // bitmap (BITCOS) or code bytes (5-trit, 2-bit)
     const uint32_t *signs;    // BITCOS sign stream as little-endian dwords
     const uint32_t *rowoff;   // BITCOS per-row sign positions, n + 1 entries
-    uint32_t sign_dwords;     // dwords in the sign section (reads are clamped below this)
-    int32_t n, k;             // rows, reduction length (k % 128 == 0)
-    const uint16_t *scales;   // fp16 [n][k/128]
+    const uint16_t *scales;   // fp16 [n][k/128] (value path)
     const int8_t *x;          // int8 [m][k]
     float *y;                 // float [m][n] (value path)
     int32_t *acc;             // int32 [m][n][k/128] (accumulator path)
-    int32_t m;                // activation rows handled by this launch
+    uint32_t codes_bytes;     // bytes of the codes section
+    uint32_t sign_bytes;      // bytes of the sign section
+    int32_t n, k;             // rows, reduction length (k % 128 == 0)
+    int32_t unit_begin;       // index of this GEMV's first work unit within its launch
+    int32_t reserved;
+};
+
+// Arguments of one launch: either a single GEMV passed by value (table == nullptr) or a device
+// table of `count` GEMVs sharing one format and one m, processed by one persistent grid.
+struct GroupArgs {
+    const Problem *table;
+    int32_t count;
+    int32_t units;            // total work units over all GEMVs
+    int32_t m;                // activation rows (1 .. 3 on the vector path)
+    int32_t rows_per_unit;    // rows one wave processes as a unit
+    Problem one;
 };
 
 // Host-side checks of a descriptor; `limit` is the buffer length when known (0 = trust bytes_total).
 int check_desc(const tg_desc *d, uint64_t limit);
 
-// Kernel launchers (asynchronous; return the HIP status of the launch).
-hipError_t launch_bitcos(const GemvArgs &a, bool acc_out, hipStream_t s);
-hipError_t launch_t5(const GemvArgs &a, bool acc_out, hipStream_t s);
-hipError_t launch_b2(const GemvArgs &a, bool acc_out, hipStream_t s);
+// Fill a Problem from a checked descriptor and the caller's pointers.
+Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, const int8_t *x, float *y,
+                     int32_t *acc);
+
+// Rows per work unit the launcher of `fmt` uses for a GEMV of this shape and m.
+int rows_per_unit(int fmt, int64_t n, int64_t k, int m);
+
+// Kernel launchers (asynchronous; return the HIP status of the launch). `g.one` or `g.table` holds
+// the problems; the launchers set grid sizes themselves.
+hipError_t launch_bitcos(const GroupArgs &g, bool acc_out, hipStream_t s);
+hipError_t launch_t5(const GroupArgs &g, bool acc_out, hipStream_t s);
+hipError_t launch_b2(const GroupArgs &g, bool acc_out, hipStream_t s);
+
+// Number of compute units of the current device (cached).
+int device_cus();
 
 }  // namespace tg

@@ -137,6 +137,46 @@ int ternary_gemv(const tg_desc *desc, const void *W, const uint16_t *scales, con
  * (no scales). This is the bit-exact parity entry point. */
 int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_t *acc, int32_t m, void *stream);
 
+/*
+ * Grouped launch: several GEMVs of one format and one activation-row count m (1 <= m <= 3) run as
+ * one persistent kernel. This is the batched form of the same operation (each GEMV is computed
+ * exactly as ternary_gemv / ternary_gemv_acc compute it); it removes the per-launch ramp and lets
+ * the memory pipeline stay full across matrices, e.g. the q/k/v or gate/up projections of a decode
+ * step, or a whole layer stack in a benchmark.
+ *
+ * tg_plan_table_bytes(count): bytes of device memory the table of `count` GEMVs needs.
+ * tg_plan_init: checks every descriptor and pointer (the same rules as ternary_gemv; all formats
+ *   equal), then writes the table into `table` (caller-owned DEVICE memory of at least
+ *   tg_plan_table_bytes(count) bytes, 16-byte aligned) with a synchronous host-to-device copy, and
+ *   fills the host struct *plan. descs, W, scales, x, y, acc are host arrays of `count` entries;
+ *   W/scales/x/y/acc entries are device pointers. Pass acc == NULL for fp32 outputs y (then y and
+ *   scales are required), or acc != NULL for int32 accumulators (y and scales may be NULL).
+ *   Errors: TG_EINVAL (null or misaligned pointer, mixed formats, count < 1, m outside [1, 3],
+ *   table too small), TG_EFORMAT / TG_ECORRUPT (a descriptor), TG_ESHAPE (a section beyond 4 GiB),
+ *   TG_EHIP (the copy failed). The plan stays valid while the table and every buffer it names do.
+ * ternary_gemv_plan: enqueues all GEMVs of the plan on `stream` as one launch (asynchronous).
+ *   Errors: TG_EINVAL (not an initialised plan), TG_EHIP.
+ */
+#define TG_PLAN_MAGIC 0x4E4C5054u /* "TPLN" */
+
+typedef struct tg_plan {
+    uint32_t magic;      /* TG_PLAN_MAGIC once initialised */
+    int32_t fmt;         /* tg_fmt shared by every GEMV */
+    int32_t m;           /* activation rows of every GEMV */
+    int32_t count;       /* GEMVs in the table */
+    int32_t units;       /* work units over all GEMVs */
+    int32_t rows_per_unit;
+    int32_t acc_mode;    /* 1: int32 accumulator outputs */
+    int32_t reserved;
+    void *table;         /* device table written by tg_plan_init */
+} tg_plan;
+
+size_t tg_plan_table_bytes(int32_t count);
+int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                 const void *const *W, const uint16_t *const *scales, const int8_t *const *x, float *const *y,
+                 int32_t *const *acc, int32_t m);
+int ternary_gemv_plan(const tg_plan *plan, void *stream);
+
 /* Static string for a TG_* code ("unknown error" for anything else). */
 const char *tg_strerror(int code);
 

@@ -150,3 +150,40 @@ def test_gemv_argument_errors_before_any_gpu_work():
     d2 = binding.TgDesc.from_buffer_copy(d)
     d2.bytes_signs = 4
     assert L.ternary_gemv_acc(ctypes.byref(d2), dummy, dummy, dummy, 1, None) == -5
+
+
+def test_plan_argument_errors_before_any_gpu_work():
+    L = binding.lib()
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = B.pack_bitcos(w).desc
+    descs = (binding.TgDesc * 1)(d)
+    dummy = ctypes.c_void_p(256)
+    P1 = ctypes.c_void_p * 1
+    ptrs = P1(256)
+    plan = binding.TgPlan()
+    nbytes = L.tg_plan_table_bytes(1)
+    assert nbytes > 0 and L.tg_plan_table_bytes(0) == 0
+    # null plan / table / descriptors, bad count or m, misaligned or short table: TG_EINVAL
+    assert L.tg_plan_init(None, dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), None, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 0, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 4) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), ctypes.c_void_p(264), nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs,
+                          None, 1) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes - 1, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    # value mode without y
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, None, None, 1) == -1
+    # a corrupt descriptor is reported as such
+    bad = (binding.TgDesc * 1)(binding.TgDesc.from_buffer_copy(d))
+    bad[0].magic = 0
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, bad, ptrs, ptrs, ptrs, ptrs, None, 1) == -4
+    # mixed formats
+    d5 = B.pack_5trit(w).desc
+    two = (binding.TgDesc * 2)(d, d5)
+    P2 = ctypes.c_void_p * 2
+    p2 = P2(256, 256)
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, L.tg_plan_table_bytes(2), 2, two, p2, p2, p2, p2, None,
+                          1) == -1
+    # running a plan that was never initialised
+    assert L.ternary_gemv_plan(ctypes.byref(binding.TgPlan()), None) == -1
+    assert L.ternary_gemv_plan(None, None) == -1

@@ -115,6 +115,63 @@ def test_non_default_stream():
     assert np.array_equal(y.cpu().numpy(), y_ref)
 
 
+# ----- grouped launch (one persistent kernel over a table of GEMVs) ------------------------------------
+
+# Shapes cover: full 4096-weight chunks only (4096), full chunks plus power-of-two tails of 2, 4 and 8
+# rows per step (14336, 5120, 25600 -> 32, 16 and 8 lanes per row), tails only (1024, 384: 8 and 6
+# lanes), a non-power-of-two tail (2560: 40 lanes) and single-row and odd-row matrices.
+PLAN_SHAPES = [(96, 4096), (40, 5120), (33, 14336), (7, 2560), (130, 1024), (1, 128), (64, 384), (9, 25600)]
+
+
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: B.FMT_NAMES[f])
+def test_plan_matches_oracle(fmt, m):
+    dev = _dev()
+    _say(f"[gpu] plan fmt={B.FMT_NAMES[fmt]} m={m} shapes={PLAN_SHAPES}")
+    ws, xs, ss, refs, accrefs, dws = [], [], [], [], [], []
+    for i, (n, k) in enumerate(PLAN_SHAPES):
+        w = synth.ternary(n, k, 0.4 + 0.01 * i, seed=100 + i)
+        x = synth.activations(m, k, seed=200 + i)
+        s = synth.scales(n, k // 128, seed=300 + i)
+        acc_ref = O.gemv_acc(w, x)
+        accrefs.append(acc_ref)
+        refs.append(O.combine(acc_ref, s))
+        dws.append(B.DeviceWeights(B.pack(fmt, w), dev))
+        xs.append(torch.from_numpy(x).to(dev))
+        ss.append(torch.from_numpy(s).to(dev))
+    ys = [torch.full((m, w.n), float("nan"), dtype=torch.float32, device=dev) for w in dws]
+    accs = [torch.full((m, w.n, w.k // 128), -7, dtype=torch.int32, device=dev) for w in dws]
+    B.Plan(dws, xs, scales=ss, ys=ys).run()
+    B.Plan(dws, xs, accs=accs).run()
+    torch.cuda.synchronize()
+    for i, (n, k) in enumerate(PLAN_SHAPES):
+        assert np.array_equal(accs[i].cpu().numpy(), accrefs[i]), f"plan acc {n}x{k}"
+        y = ys[i].cpu().numpy()
+        ok, ndiff = y_tolerance_ok(y, refs[i], accrefs[i], ss[i].cpu().numpy())
+        assert ok and ndiff == 0, f"plan y {n}x{k}: within tolerance {ok}, {ndiff} differ"
+
+
+def test_plan_equals_per_call_and_replays():
+    dev = _dev()
+    shapes = [(4096, 4096), (1024, 4096), (512, 14336)]
+    dws, xs, ss, ys1 = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.ternary(n, k, 0.4, seed=7 + i)
+        dws.append(B.DeviceWeights(B.pack_bitcos(w), dev))
+        xs.append(torch.from_numpy(synth.activations(1, k, seed=8 + i)).to(dev))
+        ss.append(torch.from_numpy(synth.scales(n, k // 128, seed=9 + i)).to(dev))
+        ys1.append(B.ternary_gemv(dws[-1], ss[-1], xs[-1]))
+    ys = [torch.empty((1, w.n), dtype=torch.float32, device=dev) for w in dws]
+    plan = B.Plan(dws, xs, scales=ss, ys=ys)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ys1):
+            assert torch.equal(a, b), f"replay {rep}"
+
+
 # ----- the benchmark workloads at full size ---------------------------------------------------------
 
 LLAMA = {"q": (4096, 4096), "k": (1024, 4096), "v": (1024, 4096), "o": (4096, 4096),
