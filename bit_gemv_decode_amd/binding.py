@@ -25,7 +25,7 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 # Every symbol include/ternary_gemv.h declares.
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_describe", "tg_validate", "tg_unpack",
            "ternary_gemv", "ternary_gemv_acc", "tg_plan_table_bytes", "tg_plan_init", "ternary_gemv_plan",
-           "tg_strerror", "tg_version"]
+           "tg_stream_read", "tg_strerror", "tg_version"]
 PLAN_MAX_M = 3
 
 
@@ -48,7 +48,7 @@ class TgDesc(ctypes.Structure):
 class TgPlan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("fmt", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("count", ctypes.c_int32), ("units", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
-                ("acc_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("table", ctypes.c_void_p)]
+                ("acc_mode", ctypes.c_int32), ("waves", ctypes.c_int32), ("table", ctypes.c_void_p)]
 
 
 _lib = None
@@ -83,6 +83,8 @@ def lib():
         L.tg_plan_init.restype = ctypes.c_int
         L.ternary_gemv_plan.argtypes = [ctypes.POINTER(TgPlan), p]
         L.ternary_gemv_plan.restype = ctypes.c_int
+        L.tg_stream_read.argtypes = [p, sz, p, ctypes.c_int32, ctypes.c_int32, p]
+        L.tg_stream_read.restype = ctypes.c_int
         L.tg_strerror.argtypes = [ctypes.c_int]
         L.tg_strerror.restype = ctypes.c_char_p
         L.tg_version.argtypes = []
@@ -316,3 +318,15 @@ class Plan:
 
     def run(self, stream=None):
         _check(lib().ternary_gemv_plan(ctypes.byref(self.plan), _stream_handle(stream)), "ternary_gemv_plan")
+
+
+def stream_read(buf, sink, blocks: int, unroll: int, stream=None):
+    """Bandwidth reference: read all of `buf` (a uint8 device tensor) with the stream-read kernel."""
+    import torch
+
+    _require_cuda(buf, torch.uint8, "buf")
+    _require_cuda(sink, torch.int32, "sink")
+    if sink.numel() < blocks * 4:
+        raise ValueError("sink needs blocks * 4 words")
+    _check(lib().tg_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.c_void_p(sink.data_ptr()),
+                                blocks, unroll, _stream_handle(stream)), "tg_stream_read")

@@ -8,7 +8,7 @@
 
 namespace tg {
 
-int bitcos_rows_per_unit(int64_t n, int64_t k, int m);
+int bitcos_rows_per_unit(int64_t n, int64_t k, int m, bool table);
 
 int device_cus() {
     static int cached = 0;
@@ -43,8 +43,8 @@ Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, co
     return p;
 }
 
-int rows_per_unit(int fmt, int64_t n, int64_t k, int m) {
-    return fmt == TG_FMT_BITCOS ? bitcos_rows_per_unit(n, k, m) : 1;
+int rows_per_unit(int fmt, int64_t n, int64_t k, int m, bool table) {
+    return fmt == TG_FMT_BITCOS ? bitcos_rows_per_unit(n, k, m, table) : 1;
 }
 
 }  // namespace tg
@@ -91,7 +91,7 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
                              acc_out ? acc + (size_t)m0 * n * ng : nullptr);
         g.count = 1;
         g.m = mt;
-        g.rows_per_unit = rows_per_unit(desc->fmt, n, k, mt);
+        g.rows_per_unit = rows_per_unit(desc->fmt, n, k, mt, false);
         g.units = (int32_t)((n + g.rows_per_unit - 1) / g.rows_per_unit);
         g.one.unit_begin = 0;
         if (launch(desc->fmt, g, acc_out, s) != hipSuccess) return TG_EHIP;
@@ -111,8 +111,17 @@ extern "C" int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t
     return gemv_common(desc, W, nullptr, x, nullptr, acc, m, stream, true);
 }
 
+namespace {
+
+// Waves of a persistent BITCOS launch on this device; a plan's per-wave ranges are sized for it.
+int plan_waves() { return device_cus() * kBitcosBlocksPerCu * kBitcosWavesPerBlock; }
+
+size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
+
+}  // namespace
+
 extern "C" size_t tg_plan_table_bytes(int32_t count) {
-    return count > 0 ? (size_t)count * sizeof(Problem) : 0;
+    return count > 0 ? ranges_offset(count) + (size_t)plan_waves() * sizeof(WaveRange) : 0;
 }
 
 extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
@@ -135,21 +144,48 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         if (acc_mode ? (!acc[i] || ((uintptr_t)acc[i] & 3))
                      : (!y[i] || !scales[i] || ((uintptr_t)y[i] & 3) || ((uintptr_t)scales[i] & 1)))
             return TG_EINVAL;
-        rpu = std::max(rpu, rows_per_unit(fmt, d->n, d->k, m));
+        rpu = std::max(rpu, rows_per_unit(fmt, d->n, d->k, m, true));
     }
-    // A table has plenty of work: use the largest batch every GEMV allows.
-    if (fmt == TG_FMT_BITCOS) rpu = m == 1 ? 8 : 4;
     int64_t units = 0;
+    double total_cost = 0;
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr);
         host[i].unit_begin = (int32_t)units;
         units += (d->n + rpu - 1) / rpu;
+        total_cost += (double)d->n * (double)d->k;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
-    if (hipMemcpy(table, host.data(), tg_plan_table_bytes(count), hipMemcpyHostToDevice) != hipSuccess)
-        return TG_EHIP;
+    // Contiguous unit ranges per wave, balanced by cost (rows x k of each unit).
+    const int nw = plan_waves();
+    std::vector<WaveRange> ranges((size_t)nw);
+    {
+        int32_t pi = 0;
+        int64_t u = 0;
+        double done = 0;
+        for (int w = 0; w < nw; ++w) {
+            ranges[w].begin = (int32_t)u;
+            ranges[w].problem = pi;
+            const double target = total_cost * (double)(w + 1) / (double)nw;
+            while (u < units) {
+                while (pi + 1 < count && u >= host[pi + 1].unit_begin) ++pi;
+                const int64_t row0 = (u - host[pi].unit_begin) * rpu;
+                const double cost = (double)std::min<int64_t>(rpu, host[pi].n - row0) * (double)host[pi].k;
+                if (done + 0.5 * cost > target && w + 1 < nw) break;
+                done += cost;
+                ++u;
+            }
+            if (w + 1 == nw) u = units;
+            ranges[w].end = (int32_t)u;
+            ranges[w].reserved = 0;
+            if (ranges[w].begin == ranges[w].end) ranges[w].problem = 0;
+        }
+    }
+    std::vector<uint8_t> img(tg_plan_table_bytes(count), 0);
+    memcpy(img.data(), host.data(), (size_t)count * sizeof(Problem));
+    memcpy(img.data() + ranges_offset(count), ranges.data(), ranges.size() * sizeof(WaveRange));
+    if (hipMemcpy(table, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess) return TG_EHIP;
     memset(plan, 0, sizeof(*plan));
     plan->magic = TG_PLAN_MAGIC;
     plan->fmt = fmt;
@@ -158,6 +194,7 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
     plan->units = (int32_t)units;
     plan->rows_per_unit = rpu;
     plan->acc_mode = acc_mode ? 1 : 0;
+    plan->waves = nw;
     plan->table = table;
     return TG_OK;
 }
@@ -168,9 +205,23 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
+    if (plan->fmt == TG_FMT_BITCOS) {
+        if (plan->waves != plan_waves()) return TG_EINVAL;  // built for another device
+        g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
+        g.waves = plan->waves;
+    }
     g.count = plan->count;
     g.units = plan->units;
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
     return launch(plan->fmt, g, plan->acc_mode != 0, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
+}
+
+extern "C" int tg_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, int32_t unroll,
+                              void *stream) {
+    if (!buf || !sink || blocks < 1 || ((uintptr_t)buf & 15) || bytes == 0 || bytes > 0xFFFFFFFFull || bytes % 16)
+        return TG_EINVAL;
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return TG_EINVAL;
+    return launch_stream_read(buf, (uint32_t)bytes, sink, blocks, unroll, (hipStream_t)stream) == hipSuccess ? TG_OK
+                                                                                                        : TG_EHIP;
 }

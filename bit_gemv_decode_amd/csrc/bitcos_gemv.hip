@@ -72,7 +72,7 @@ constexpr ByteLut make_byte_lut() {
 
 __device__ const ByteLut kByteLut = make_byte_lut();
 
-constexpr int kWaves = 8;
+constexpr int kWaves = kBitcosWavesPerBlock;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kChunkDwords = 128;  // bitmap dwords of one full chunk (64 lanes x 2)
 
@@ -91,26 +91,28 @@ struct Rsrc {
     __amdgpu_buffer_rsrc_t bm, sg, sc, x;
 };
 
+// Out-of-range buffer offset: a load there returns zero and makes no memory request.
+constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
+
 // One lane's share of a step after its bitmap dwords arrived: sign window and scale loads issued.
 struct Staged {
     uint2 bm;
     u32x3 sg;        // sign dwords q, q+1, q+2 of the stream
     uint32_t r0;     // bit of sg.x where the lane's first sign sits
-    uint16_t scale;  // fp16 scale of the lane's group (value path)
+    uint16_t scale;  // fp16 scale bits of the lane's group (value path)
 };
 
-// `o0` is the stream position of the lane's first sign. The window load covers o0 .. o0 + 95
-// (a lane's <= 64 signs start at most 31 bits into the first dword); reads past the section
-// return zero.
+// Sign window for a lane whose first sign is at stream position o0 (the window covers o0 .. o0+95,
+// enough for the <= 64 signs of two bitmap dwords), and the scale of its group.
 template <bool ACC>
-__device__ __forceinline__ Staged issue_signs(const Rsrc &r, uint2 bm, uint32_t o0, uint32_t scale_idx) {
+__device__ __forceinline__ Staged issue_signs(const Rsrc &r, uint2 bm, bool act, uint32_t o0, uint32_t scale_idx) {
     Staged st;
     st.bm = bm;
     st.r0 = o0 & 31;
-    st.sg = buf_u32x3(r.sg, (o0 >> 5) * 4);
-    // unconditional for every lane: a branch around a load makes the compiler wait for every load
-    // in flight (the accumulator path has no scales)
-    st.scale = ACC ? (uint16_t)0 : buf_u16(r.sc, scale_idx * 2);
+    st.sg = buf_u32x3(r.sg, act ? (o0 >> 5) * 4 : kNoLoad);
+    // unconditional for every lane (a branch around a load makes the compiler wait for every load in
+    // flight); inactive lanes read nothing
+    st.scale = ACC ? (uint16_t)0 : buf_u16(r.sc, act ? scale_idx * 2 : kNoLoad);
     return st;
 }
 
@@ -155,176 +157,208 @@ __device__ __forceinline__ void decode_staged(const Staged &st, const LutView &l
     }
 }
 
-// Load the 64 activation bytes of each of the M rows of x that a lane needs, starting at byte k0
-// (zeros for an inactive lane).
-template <int M>
-__device__ __forceinline__ void load_x(const Rsrc &r, int k, int k0, bool active, uint32_t (&xr)[M][16]) {
+// Geometry of one chunk of k (wave-uniform). A full chunk is 4096 weights: one row per step, 64
+// lanes of 2 bitmap dwords. The tail chunk (k % 4096) gives each row L = tail/2 lanes and, when L
+// is a power of two, packs 64/L rows into a step; otherwise one row per step. Lane l sits in step
+// row l >> lg, at segment position l & (2^lg - 1); for a non-power-of-two tail lg = 6 (one
+// segment) and lanes at or past L are idle. All derived by shifts, without branches.
+struct Geo {
+    int dw_base;  // first bitmap dword of the chunk within a row
+    int L;        // lanes per row
+    int lg;       // log2 of the segment width
+    int rps;      // rows per step (1 << (6 - lg))
+    int G;        // 128-groups per row in the chunk (L / 2)
+    bool full;    // L == 64
+};
+
+__device__ __forceinline__ int nchunks_of(const Problem &p) {
+    const int kd = p.k >> 5;
+    return kd / kChunkDwords + ((kd % kChunkDwords) ? 1 : 0);
+}
+
+__device__ __forceinline__ Geo geo_of(const Problem &p, int c) {
+    const int kd = p.k >> 5;
+    const int nfull = kd / kChunkDwords;
+    Geo g;
+    g.full = c < nfull;
+    g.dw_base = (g.full ? c : nfull) * kChunkDwords;
+    g.L = g.full ? 64 : (kd - g.dw_base) >> 1;
+    const bool pow2 = (g.L & (g.L - 1)) == 0;
+    g.lg = pow2 ? 31 - __builtin_clz((unsigned)g.L) : 6;
+    g.rps = 1 << (6 - g.lg);
+    g.G = g.L >> 1;
+    return g;
+}
+
+// Steps of a batch of nrows unit rows: ceil(nrows / rps).
+__device__ __forceinline__ int nsteps_of(const Geo &g, int nrows) {
+    return (nrows + g.rps - 1) >> (6 - g.lg);
+}
+
+// Per-lane view of a chunk geometry.
+struct LaneGeo {
+    int ri;   // row of the lane within a step
+    int seg;  // lane index within its row segment
+    bool ok;  // lane belongs to a row segment
+    int dw0;  // lane's first bitmap dword within the row
+};
+
+__device__ __forceinline__ LaneGeo lane_geo(const Geo &g, int lane) {
+    LaneGeo l;
+    l.ri = lane >> g.lg;
+    l.seg = lane & ((1 << g.lg) - 1);
+    l.ok = l.seg < g.L;
+    l.dw0 = g.dw_base + 2 * l.seg;
+    return l;
+}
+
+// Everything a batch needs before its scans: bitmap dwords of each step, the activation bytes of
+// the lane's 64 weights, and (for a unit's first chunk) the unit rows' sign cursors.
+template <int M, int NB>
+struct Batch {
+    uint32_t xr[M][16];
+    uint2 b[NB];
+    uint32_t rowoff;
+};
+
+// `live` false: issue the same instructions with out-of-range offsets (no memory traffic), so that
+// the caller needs no branch around the loads.
+template <int M, int NB>
+__device__ __forceinline__ void issue_batch(const Problem &p, int u, int c, bool live, Batch<M, NB> &bt) {
+    const int lane = threadIdx.x & 63;
+    const int kd = p.k >> 5;
+    const int row0 = (u - p.unit_begin) * NB;
+    const int nrows = min(NB, p.n - row0);
+    const Geo g = geo_of(p, c);
+    const LaneGeo l = lane_geo(g, lane);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.codes, p.codes_bytes);
+    // x first: a later wait for x then never has to wait for the (HBM) bitmap loads
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
+    for (int mi = 0; mi < M; ++mi)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const u32x4 v = buf_u32x4(r.x, (uint32_t)(mi * k + k0 + 16 * j));
-            xr[mi][4 * j] = active ? v.x : 0u;
-            xr[mi][4 * j + 1] = active ? v.y : 0u;
-            xr[mi][4 * j + 2] = active ? v.z : 0u;
-            xr[mi][4 * j + 3] = active ? v.w : 0u;
+            const u32x4 v = buf_u32x4(rx, (live && l.ok) ? (uint32_t)(mi * p.k + 32 * l.dw0 + 16 * j) : kNoLoad);
+            bt.xr[mi][4 * j] = v.x;
+            bt.xr[mi][4 * j + 1] = v.y;
+            bt.xr[mi][4 * j + 2] = v.z;
+            bt.xr[mi][4 * j + 3] = v.w;
         }
+#pragma unroll
+    for (int st = 0; st < NB; ++st) {
+        const int ur = st * g.rps + l.ri;
+        const bool act = live && l.ok && ur < nrows;
+        const u32x2 v = buf_u32x2(rb, act ? (uint32_t)((row0 + ur) * kd + l.dw0) * 4 : kNoLoad);
+        bt.b[st] = make_uint2(v.x, v.y);
+    }
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
+    bt.rowoff = buf_u32(ri, (live && c == 0 && lane < nrows) ? (uint32_t)(row0 + lane) * 4 : kNoLoad);
+}
+
+// Scan each step's lane popcounts, advance the unit rows' cursors (lane u tracks unit row u) and
+// issue the sign-window and scale loads.
+template <int M, bool ACC, int NB>
+__device__ __forceinline__ void stage_batch(const Problem &p, int u, int c, const Batch<M, NB> &bt, uint32_t &cur_v,
+                                            Staged (&S)[NB]) {
+    const int lane = threadIdx.x & 63;
+    const int ng = p.k >> 7;
+    const int row0 = (u - p.unit_begin) * NB;
+    const int nrows = min(NB, p.n - row0);
+    const Geo g = geo_of(p, c);
+    const LaneGeo l = lane_geo(g, lane);
+    const int gcol = l.dw0 >> 2;
+    Rsrc r;
+    r.sg = make_rsrc(p.signs, p.sign_bytes);
+    r.sc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)ng * 2u);
+    if (c == 0) cur_v = bt.rowoff;
+    const int nsteps = nsteps_of(g, nrows);
+#pragma unroll
+    for (int st = 0; st < NB; ++st) {
+        if (st >= nsteps) break;  // wave-uniform: no row of the unit left for this step
+        const uint2 b = bt.b[st];
+        const uint32_t pc = __builtin_popcount(b.x) + __builtin_popcount(b.y);
+        const uint32_t incl = wave_incl_scan(pc);
+        const int ur = st * g.rps + l.ri;
+        const bool act = l.ok && ur < nrows;
+        uint32_t o0;
+        if (g.full) {
+            const uint32_t rowcur = (uint32_t)__builtin_amdgcn_readlane((int)cur_v, st);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            cur_v += lane == st ? total : 0u;
+            o0 = rowcur + incl - pc;
+        } else {
+            // inclusive sums just before this lane's row segment and at its end (the shuffles run
+            // on every lane: a lane-permute reading from a lane that is switched off returns zero)
+            const int seg_first = l.ri << g.lg;
+            const uint32_t prev = (uint32_t)__shfl((int)incl, max(seg_first - 1, 0), 64);
+            const uint32_t before = seg_first > 0 ? prev : 0u;
+            const uint32_t end = (uint32_t)__shfl((int)incl, min(seg_first + g.L - 1, 63), 64);
+            const uint32_t rowcur = (uint32_t)__shfl((int)cur_v, min(ur, 63), 64);
+            // unit row v = st*rps + i takes the total of step row i (held by lane i*L)
+            const int i = lane - st * g.rps;
+            const bool mine = i >= 0 && i < g.rps;
+            const uint32_t t = (uint32_t)__shfl((int)(end - before), mine ? i * g.L : 0, 64);
+            cur_v += mine ? t : 0u;
+            o0 = rowcur + incl - pc - before;
+        }
+        S[st] = issue_signs<ACC>(r, b, act, o0, (uint32_t)((row0 + ur) * ng + gcol));
     }
 }
 
-// Process one unit: rows [row0, row0 + nrows) of problem p (1 <= nrows <= NB), all k.
-// Each chunk of k is one fully unrolled batch of NB steps. Steps past the unit re-read its last
-// row, change no cursor and write nothing. `red` is the wave's LDS scratch of M * NB * 32 doubles.
+// Decode every step of a batch. Accumulator path: store each group's int32 sum. Value path: the
+// group sums and scale bits go to the wave's LDS scratch; the batch's rows are then summed by 64/NB
+// lanes each (scale * acc in fp64) and added to the row sums held by lane u for unit row u.
 template <int M, bool ACC, int NB>
-__device__ void run_unit(const Problem &p, const Rsrc &r, int row0, int nrows, const LutView &lut, double *red) {
+__device__ __forceinline__ void finish_batch(const Problem &p, int u, int c, const Staged (&S)[NB],
+                                             const uint32_t (&xr)[M][16], const LutView &lut, int32_t *red_acc,
+                                             uint16_t *red_sc, double (&yv)[M]) {
     const int lane = threadIdx.x & 63;
-    const int n = p.n, k = p.k;
-    const int kd = k >> 5;  // bitmap dwords per row
-    const int ng = k >> 7;
-    const int nfull = kd / kChunkDwords;
-    const int tail = kd - nfull * kChunkDwords;  // multiple of 4
-    const int last = nrows - 1;
-
-    // lane u < nrows tracks row row0 + u: its running sign cursor and its output sums
-    uint32_t cur_v = p.rowoff[row0 + min(lane, last)];
-    double yv[M];
+    const int ng = p.k >> 7;
+    const int row0 = (u - p.unit_begin) * NB;
+    const int nrows = min(NB, p.n - row0);
+    const Geo g = geo_of(p, c);
+    const LaneGeo l = lane_geo(g, lane);
+    const int gi = l.seg >> 1;  // lane's group within the chunk
+    const int nsteps = nsteps_of(g, nrows);
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) yv[mi] = 0.0;
-
-    uint32_t xr[M][16];
-
-    // ---------------- full chunks: one row per step, 64 lanes x 2 dwords ----------------
-    for (int c = 0; c < nfull; ++c) {
-        const int dw0 = c * kChunkDwords + 2 * lane;  // lane's first bitmap dword in the row
-        const int g = dw0 >> 2;                       // lane's group
-        load_x<M>(r, k, 32 * dw0, true, xr);
-        uint2 b[NB];
+    for (int st = 0; st < NB; ++st) {
+        if (st >= nsteps) break;  // wave-uniform
+        const int ur = st * g.rps + l.ri;
+        const bool act = l.ok && ur < nrows;
+        int acc[M];
+        decode_staged<M>(S[st], lut, xr, acc);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const u32x2 v = buf_u32x2(r.bm, (uint32_t)((row0 + min(j, last)) * kd + dw0) * 4);
-            b[j] = make_uint2(v.x, v.y);
-        }
-        TG_SCHED_FENCE();
-        Staged S[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int jc = min(j, last);
-            const uint32_t pc = __builtin_popcount(b[j].x) + __builtin_popcount(b[j].y);
-            const uint32_t incl = wave_incl_scan(pc);
-            const uint32_t rowcur = (uint32_t)__builtin_amdgcn_readlane((int)cur_v, jc);
-            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-            cur_v += (lane == j && j < nrows) ? total : 0u;
-            S[j] = issue_signs<ACC>(r, b[j], rowcur + incl - pc, ACC ? 0u : (uint32_t)((row0 + jc) * ng + g));
-        }
-        TG_SCHED_FENCE();
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            int acc[M];
-            decode_staged<M>(S[j], lut, xr, acc);
-#pragma unroll
-            for (int mi = 0; mi < M; ++mi) {
-                const int v = acc[mi] + __builtin_amdgcn_update_dpp(0, acc[mi], kDppQuadSwap1, 0xF, 0xF, false);
+        for (int mi = 0; mi < M; ++mi) {
+            const int v = acc[mi] + __builtin_amdgcn_update_dpp(0, acc[mi], kDppQuadSwap1, 0xF, 0xF, false);
+            if (act && !(lane & 1)) {
                 if (ACC) {
-                    if (!(lane & 1) && j < nrows) p.acc[((size_t)mi * n + row0 + j) * ng + g] = v;
-                } else if (!(lane & 1)) {
-                    red[(mi * NB + j) * 32 + (lane >> 1)] = (double)half_bits_to_float(S[j].scale) * (double)v;
-                }
-            }
-        }
-        if (!ACC) {
-            // Row j's 32 group terms are summed by the 64/NB lanes of segment j.
-            constexpr int LPR = 64 / NB;                  // lanes per row
-            constexpr int EPL = NB >= 2 ? NB / 2 : 1;     // terms per lane
-            const int rj = lane / LPR;
-            const int e0 = (lane % LPR) * EPL;
-#pragma unroll
-            for (int mi = 0; mi < M; ++mi) {
-                double t = 0.0;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    if (NB >= 2 || lane < 32) t += red[(mi * NB + rj) * 32 + e0 + e];
-                t = seg_sum_f64(t, LPR);
-                const double rowsum = __shfl(t, (min(lane, NB - 1) + 1) * LPR - 1, 64);
-                yv[mi] += lane < NB ? rowsum : 0.0;
-            }
-        }
-    }
-
-    // ---------------- tail: the last `tail` dwords of several rows per step ----------------
-    if (tail) {
-        const int L = tail >> 1;                  // lanes per row (even, < 64)
-        const bool pow2 = (L & (L - 1)) == 0;
-        // rows per step: power-of-two segments are reduced inside the segment; other widths take
-        // one row per step and reduce over the whole wave
-        const int rps = pow2 ? 64 / L : 1;
-        const int ri = lane / L;                  // row of this lane within a step
-        const int seg = lane - ri * L;
-        const bool lane_ok = ri < rps;
-        const int dw0 = nfull * kChunkDwords + 2 * seg;
-        const int g = dw0 >> 2;
-        const int seg_first = ri * L;
-        const int seg_last = min(seg_first + L - 1, 63);
-        load_x<M>(r, k, 32 * dw0, lane_ok, xr);
-        const int nsteps = (nrows + rps - 1) / rps;  // <= NB
-        uint2 b[NB];
-#pragma unroll
-        for (int st = 0; st < NB; ++st) {
-            const int u = st * rps + ri;
-            const u32x2 v = buf_u32x2(r.bm, (uint32_t)((row0 + min(u, last)) * kd + (lane_ok ? dw0 : 0)) * 4);
-            b[st] = (lane_ok && u < nrows) ? make_uint2(v.x, v.y) : make_uint2(0, 0);
-        }
-        TG_SCHED_FENCE();
-        Staged S[NB];
-#pragma unroll
-        for (int st = 0; st < NB; ++st) {
-            const int u = st * rps + ri;
-            const bool act = lane_ok && u < nrows;
-            const uint32_t pc = __builtin_popcount(b[st].x) + __builtin_popcount(b[st].y);
-            const uint32_t incl = wave_incl_scan(pc);
-            // inclusive sums just before this lane's row segment and at its end (the shuffles run
-            // on every lane: a lane-permute reading from a lane that is switched off returns zero)
-            const uint32_t prev = (uint32_t)__shfl((int)incl, max(seg_first - 1, 0), 64);
-            const uint32_t before = seg_first > 0 ? prev : 0u;
-            const uint32_t end = (uint32_t)__shfl((int)incl, seg_last, 64);
-            const uint32_t rowcur = (uint32_t)__shfl((int)cur_v, min(u, 63), 64);
-            // unit row v = st*rps + i takes the total of step row i (held by lane i*L)
-            const int i = lane - st * rps;
-            const bool mine = i >= 0 && i < rps && lane < nrows;
-            const uint32_t t = (uint32_t)__shfl((int)(end - before), mine ? i * L : 0, 64);
-            cur_v += mine ? t : 0u;
-            S[st] = issue_signs<ACC>(r, b[st], act ? rowcur + incl - pc - before : 0u,
-                                     (act && !ACC) ? (uint32_t)((row0 + u) * ng + g) : 0u);
-        }
-        TG_SCHED_FENCE();
-#pragma unroll
-        for (int st = 0; st < NB; ++st) {
-            if (st >= nsteps) break;  // wave-uniform
-            int acc[M];
-            decode_staged<M>(S[st], lut, xr, acc);
-            const int u = st * rps + ri;
-            const bool act = lane_ok && u < nrows;
-#pragma unroll
-            for (int mi = 0; mi < M; ++mi) {
-                const int v = acc[mi] + __builtin_amdgcn_update_dpp(0, acc[mi], kDppQuadSwap1, 0xF, 0xF, false);
-                if (ACC) {
-                    if (act && !(lane & 1)) p.acc[((size_t)mi * n + row0 + u) * ng + g] = v;
+                    p.acc[((size_t)mi * p.n + row0 + ur) * ng + (l.dw0 >> 2)] = v;
                 } else {
-                    double part = (act && !(lane & 1)) ? (double)half_bits_to_float(S[st].scale) * (double)v : 0.0;
-                    part = seg_sum_f64(part, pow2 ? L : 64);
-                    // the last lane of a power-of-two segment holds its sum; otherwise lane 63
-                    // holds the (single) row's sum
-                    const int i = lane - st * rps;
-                    const bool mine = i >= 0 && i < rps;
-                    const double t = __shfl(part, !mine ? 0 : pow2 ? i * L + L - 1 : 63, 64);
-                    yv[mi] += mine ? t : 0.0;
+                    red_acc[(mi * NB + ur) * 32 + gi] = v;
+                    if (mi == 0) red_sc[ur * 32 + gi] = S[st].scale;
                 }
             }
         }
     }
-
-    if (!ACC && lane < nrows) {
+    if (!ACC) {
+        // Row rj's G group terms are summed by the LPR lanes of segment rj.
+        constexpr int LPR = 64 / NB;                     // lanes per row
+        constexpr int EPL = LPR >= 32 ? 1 : 32 / LPR;    // term slots per lane
+        const int rj = lane / LPR;
+        const int e0 = (lane % LPR) * EPL;               // (one row: lanes 32..63 have no slot)
+        double sc[EPL];
 #pragma unroll
-        for (int mi = 0; mi < M; ++mi) p.y[(size_t)mi * n + row0 + lane] = (float)yv[mi];
+        for (int e = 0; e < EPL; ++e) sc[e] = (double)half_bits_to_float(red_sc[rj * 32 + min(e0 + e, 31)]);
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+            double t = 0.0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                if (e0 + e < g.G) t += sc[e] * (double)red_acc[(mi * NB + rj) * 32 + min(e0 + e, 31)];
+            t = seg_sum_f64(t, LPR);
+            const double rowsum = __shfl(t, (min(lane, NB - 1) + 1) * LPR - 1, 64);
+            yv[mi] += lane < nrows ? rowsum : 0.0;
+        }
     }
 }
 
@@ -332,7 +366,8 @@ template <int M, bool ACC, int NB>
 __global__ __launch_bounds__(kBlock) void bitcos_gemv_kernel(GroupArgs ga) {
     __shared__ uint4 s_ent4[(kByteLutEntries + 1) / 2];
     __shared__ uint32_t s_base8[256];
-    __shared__ double s_red[kWaves][ACC ? 1 : M * NB * 32];
+    __shared__ int32_t s_red_acc[kWaves][ACC ? 1 : M * NB * 32];
+    __shared__ uint16_t s_red_sc[kWaves][ACC ? 2 : NB * 32];
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(kByteLut.ent);
         for (int i = threadIdx.x; i < (kByteLutEntries + 1) / 2; i += kBlock) s_ent4[i] = src[i];
@@ -344,43 +379,94 @@ __global__ __launch_bounds__(kBlock) void bitcos_gemv_kernel(GroupArgs ga) {
     // The wave index is uniform across the wave: say so, so that all unit bookkeeping lives in
     // scalar registers and the loops are not compiled as divergent.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    double *red = s_red[wave];
+    const int lane = threadIdx.x & 63;
+    int32_t *red_acc = s_red_acc[wave];
+    uint16_t *red_sc = s_red_sc[wave];
     // Blocks are dealt to the XCDs round-robin; renumber them so that consecutive virtual blocks
-    // sit on one XCD, and give consecutive units to consecutive virtual waves.
+    // sit on one XCD. Each wave takes a contiguous range of units (adjacent rows share sign-stream
+    // lines and x stays hot in its XCD's L2).
     const int nblk = gridDim.x;
     const int vblk = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int nwaves = nblk * kWaves;
-    const int rpu = ga.rows_per_unit;
+    const int vw = vblk * kWaves + wave;
+    int u, u_end, pi;
+    if (ga.ranges) {
+        u = uniform_i32(ga.ranges[vw].begin);
+        u_end = uniform_i32(ga.ranges[vw].end);
+        pi = uniform_i32(ga.ranges[vw].problem);
+    } else {
+        const int nw = nblk * kWaves;
+        const int share = (ga.units + nw - 1) / nw;
+        u = min(vw * share, ga.units);
+        u_end = min(u + share, ga.units);
+        pi = 0;
+    }
+    if (u >= u_end) return;
 
-    int pi = 0;  // current problem (table mode); units are visited in increasing order
-    Problem p = ga.table ? ga.table[0] : ga.one;
-    for (int u = vblk * kWaves + wave; u < ga.units; u += nwaves) {
-        if (ga.table) {
-            bool moved = false;
-            while (pi + 1 < ga.count && ga.table[pi + 1].unit_begin <= u) {
-                ++pi;
-                moved = true;
-            }
-            if (moved) p = ga.table[pi];
+    Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
+    const bool more = ga.table && pi + 1 < ga.count;
+    Problem pn = more ? uniform_problem(ga.table[pi + 1]) : p;  // next GEMV, fetched ahead
+    int c = 0;
+    uint32_t cur_v = 0;
+    double yv[M];
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) yv[mi] = 0.0;
+
+    Batch<M, NB> cur;
+    issue_batch<M, NB>(p, u, c, true, cur);
+    while (true) {
+        // position of the next batch: the unit's next chunk, or the next unit's first chunk
+        const bool last_chunk = c + 1 >= nchunks_of(p);
+        int u2 = u, c2 = c + 1;
+        bool switch_p = false;
+        if (last_chunk) {
+            u2 = u + 1;
+            c2 = 0;
+            switch_p = ga.table && pi + 1 < ga.count && u2 >= pn.unit_begin;
         }
-        Rsrc r;
-        r.bm = make_rsrc(p.codes, p.codes_bytes);
-        r.sg = make_rsrc(p.signs, p.sign_bytes);
-        r.sc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)(p.k >> 7) * 2u);
-        r.x = make_rsrc(p.x, (uint32_t)ga.m * (uint32_t)p.k);
-        const int row0 = (u - p.unit_begin) * rpu;
-        run_unit<M, ACC, NB>(p, r, row0, min(rpu, p.n - row0), lut, red);
+        const bool has_next = u2 < u_end;
+        const Problem &p2 = switch_p ? pn : p;
+
+        Staged S[NB];
+        stage_batch<M, ACC, NB>(p, u, c, cur, cur_v, S);
+        TG_SCHED_FENCE();
+        Batch<M, NB> nxt;
+        issue_batch<M, NB>(has_next ? p2 : p, has_next ? u2 : u, has_next ? c2 : c, has_next, nxt);
+        TG_SCHED_FENCE();
+        finish_batch<M, ACC, NB>(p, u, c, S, cur.xr, lut, red_acc, red_sc, yv);
+
+        if (last_chunk) {
+            const int row0 = (u - p.unit_begin) * NB;
+            if (!ACC && lane < min(NB, p.n - row0)) {
+#pragma unroll
+                for (int mi = 0; mi < M; ++mi) p.y[(size_t)mi * p.n + row0 + lane] = (float)yv[mi];
+            }
+#pragma unroll
+            for (int mi = 0; mi < M; ++mi) yv[mi] = 0.0;
+        }
+        if (!has_next) break;
+        if (switch_p) {
+            ++pi;
+            p = pn;
+            if (pi + 1 < ga.count) pn = uniform_problem(ga.table[pi + 1]);
+        }
+        u = u2;
+        c = c2;
+        cur = nxt;
     }
 }
 
 template <int M, int NB>
 hipError_t launch_nb(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    // Two 512-thread blocks per CU (the 53 KB decode table allows no more); a persistent grid of at
-    // most that many blocks, a multiple of 8 so that every XCD gets the same number.
-    const int cap = device_cus() * 2;
-    int blocks = std::min((g.units + kWaves - 1) / kWaves, cap);
-    if (blocks > 8) blocks = blocks / 8 * 8;
-    blocks = std::max(1, blocks);
+    int blocks;
+    if (g.ranges) {
+        blocks = g.waves / kWaves;  // the table's per-wave ranges fix the grid
+    } else {
+        // one wave per unit up to two 512-thread blocks per CU (the 53 KB decode table allows no
+        // more), a multiple of 8 so that every XCD gets the same number
+        blocks = std::min((g.units + kWaves - 1) / kWaves, device_cus() * kBitcosBlocksPerCu);
+        if (blocks > 8) blocks = blocks / 8 * 8;
+        blocks = std::max(1, blocks);
+    }
     if (acc_out)
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, true, NB>), dim3(blocks), dim3(kBlock), 0, s, g);
     else
@@ -388,14 +474,21 @@ hipError_t launch_nb(const GroupArgs &g, bool acc_out, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Largest batch (rows per unit) that keeps a wave within 128 registers, so that two 512-thread
+// blocks fit a CU: 4 rows for one activation row, 2 for two, 1 for three.
+template <int M>
+constexpr int kMaxRowsPerUnit = M == 1 ? 4 : M == 2 ? 2 : 1;
+
 template <int M>
 hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
+    if (g.rows_per_unit > kMaxRowsPerUnit<M>) return hipErrorInvalidValue;
     switch (g.rows_per_unit) {
         case 1: return launch_nb<M, 1>(g, acc_out, s);
-        case 2: return launch_nb<M, 2>(g, acc_out, s);
-        case 4: return launch_nb<M, 4>(g, acc_out, s);
-        case 8:
-            if constexpr (M == 1) return launch_nb<M, 8>(g, acc_out, s);
+        case 2:
+            if constexpr (kMaxRowsPerUnit<M> >= 2) return launch_nb<M, 2>(g, acc_out, s);
+            return hipErrorInvalidValue;
+        case 4:
+            if constexpr (kMaxRowsPerUnit<M> >= 4) return launch_nb<M, 4>(g, acc_out, s);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
@@ -404,15 +497,17 @@ hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
 }  // namespace
 
 // Rows per unit for BITCOS: a power of two (the batch size). Enough units to give every wave slot
-// one, but at least the rows one tail step covers (so tail lanes are not left idle); at most 8 for
-// one activation row and 4 for more (the LDS scratch grows with both).
-int bitcos_rows_per_unit(int64_t n, int64_t k, int m) {
-    const int64_t slots = (int64_t)device_cus() * 2 * kWaves;
+// one, but at least the rows one tail step covers (so tail lanes are not left idle), and at most
+// what keeps a wave within 128 registers. `table`: a grouped launch, where work is plentiful and
+// the largest batch is used.
+int bitcos_rows_per_unit(int64_t n, int64_t k, int m, bool table) {
+    const int64_t cap = m == 1 ? kMaxRowsPerUnit<1> : m == 2 ? kMaxRowsPerUnit<2> : kMaxRowsPerUnit<3>;
+    if (table) return (int)cap;
+    const int64_t slots = (int64_t)device_cus() * kBitcosBlocksPerCu * kWaves;
     const int64_t kd = k >> 5;
     const int64_t tail = kd % kChunkDwords;
     const int64_t L = tail >> 1;
     const int64_t rps = (tail && (L & (L - 1)) == 0) ? 64 / L : 1;
-    const int64_t cap = m == 1 ? 8 : 4;
     int64_t rpu = (n + slots - 1) / slots;
     rpu = std::max(rpu, std::min(rps, cap));
     int nb = 1;

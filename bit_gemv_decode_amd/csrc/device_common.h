@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tg_internal.h"
+
 namespace tg {
 
 // DPP control codes (GFX9 encoding).
@@ -103,8 +105,40 @@ __device__ __forceinline__ u32x4 buf_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Wave-uniform copies of values the compiler cannot prove uniform (e.g. loaded from a table in
+// global memory with a vector load): buffer resources built from them then live in scalar
+// registers instead of being rebuilt per lane in a loop around every load.
+__device__ __forceinline__ int32_t uniform_i32(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return (T *)(uintptr_t)(lo | (hi << 32));
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// A GEMV description (read from a table, or passed by value) as wave-uniform values.
+__device__ __forceinline__ Problem uniform_problem(const Problem &q) {
+    Problem p;
+    p.codes = uniform_ptr(q.codes);
+    p.signs = uniform_ptr(q.signs);
+    p.rowoff = uniform_ptr(q.rowoff);
+    p.scales = uniform_ptr(q.scales);
+    p.x = uniform_ptr(q.x);
+    p.y = uniform_ptr(q.y);
+    p.acc = uniform_ptr(q.acc);
+    p.codes_bytes = uniform_u32(q.codes_bytes);
+    p.sign_bytes = uniform_u32(q.sign_bytes);
+    p.n = uniform_i32(q.n);
+    p.k = uniform_i32(q.k);
+    p.unit_begin = uniform_i32(q.unit_begin);
+    p.reserved = 0;
+    return p;
 }
 
 }  // namespace tg

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void t5_gemv_valu(GroupArgs ga) {
     // table mode: all waves work through the GEMVs one after the other
     const int count = ga.table ? ga.count : 1;
     for (int pi = 0; pi < count; ++pi) {
-        const Problem a = ga.table ? ga.table[pi] : ga.one;
+        const Problem a = uniform_problem(ga.table ? ga.table[pi] : ga.one);
         const int n = a.n, k = a.k, ng = k >> 7;
         const int ntiles = (n + kTileRows - 1) / kTileRows;
         const int nwaves = gridDim.x * kWaves;

@@ -30,16 +30,28 @@ struct Problem {
     int32_t reserved;
 };
 
+// Work units a wave processes: [begin, end), starting in GEMV `problem` of the table.
+struct WaveRange {
+    int32_t begin, end, problem, reserved;
+};
+
 // Arguments of one launch: either a single GEMV passed by value (table == nullptr) or a device
 // table of `count` GEMVs sharing one format and one m, processed by one persistent grid.
 struct GroupArgs {
     const Problem *table;
+    const WaveRange *ranges;  // per-wave unit ranges (table mode); nullptr: equal contiguous shares
     int32_t count;
     int32_t units;            // total work units over all GEMVs
     int32_t m;                // activation rows (1 .. 3 on the vector path)
     int32_t rows_per_unit;    // rows one wave processes as a unit
+    int32_t waves;            // waves the launch must have (table mode: ranges has this many entries)
+    int32_t reserved;
     Problem one;
 };
+
+// Launch geometry of the BITCOS kernel: waves per block and blocks per CU.
+constexpr int kBitcosWavesPerBlock = 8;
+constexpr int kBitcosBlocksPerCu = 2;
 
 // Host-side checks of a descriptor; `limit` is the buffer length when known (0 = trust bytes_total).
 int check_desc(const tg_desc *d, uint64_t limit);
@@ -48,14 +60,18 @@ int check_desc(const tg_desc *d, uint64_t limit);
 Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, const int8_t *x, float *y,
                      int32_t *acc);
 
-// Rows per work unit the launcher of `fmt` uses for a GEMV of this shape and m.
-int rows_per_unit(int fmt, int64_t n, int64_t k, int m);
+// Rows per work unit the launcher of `fmt` uses for a GEMV of this shape and m (`table`: in a
+// grouped launch).
+int rows_per_unit(int fmt, int64_t n, int64_t k, int m, bool table);
 
 // Kernel launchers (asynchronous; return the HIP status of the launch). `g.one` or `g.table` holds
 // the problems; the launchers set grid sizes themselves.
 hipError_t launch_bitcos(const GroupArgs &g, bool acc_out, hipStream_t s);
 hipError_t launch_t5(const GroupArgs &g, bool acc_out, hipStream_t s);
 hipError_t launch_b2(const GroupArgs &g, bool acc_out, hipStream_t s);
+
+// Streaming-read reference kernel (bandwidth ceiling probe).
+hipError_t launch_stream_read(const void *buf, uint32_t bytes, uint32_t *sink, int blocks, int unroll, hipStream_t s);
 
 // Number of compute units of the current device (cached).
 int device_cus();

@@ -155,7 +155,9 @@ int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_
  *   table too small), TG_EFORMAT / TG_ECORRUPT (a descriptor), TG_ESHAPE (a section beyond 4 GiB),
  *   TG_EHIP (the copy failed). The plan stays valid while the table and every buffer it names do.
  * ternary_gemv_plan: enqueues all GEMVs of the plan on `stream` as one launch (asynchronous).
- *   Errors: TG_EINVAL (not an initialised plan), TG_EHIP.
+ *   The table splits the work for the GPU that was current at tg_plan_init; run the plan there.
+ *   Errors: TG_EINVAL (not an initialised plan, or one made for a GPU with another CU count),
+ *   TG_EHIP.
  */
 #define TG_PLAN_MAGIC 0x4E4C5054u /* "TPLN" */
 
@@ -167,7 +169,7 @@ typedef struct tg_plan {
     int32_t units;       /* work units over all GEMVs */
     int32_t rows_per_unit;
     int32_t acc_mode;    /* 1: int32 accumulator outputs */
-    int32_t reserved;
+    int32_t waves;       /* waves of the launch the table's work split was made for */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 
@@ -176,6 +178,15 @@ int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, 
                  const void *const *W, const uint16_t *const *scales, const int8_t *const *x, float *const *y,
                  int32_t *const *acc, int32_t m);
 int ternary_gemv_plan(const tg_plan *plan, void *stream);
+
+/*
+ * Bandwidth reference (not part of the GEMV): reads `bytes` bytes of device memory at buf
+ * (16-byte aligned, a multiple of 16, at most 4 GiB) with `blocks` workgroups of 4 waves, each lane
+ * keeping `unroll` (1, 2, 4 or 8) 16-byte loads in flight, and writes one XOR word per wave to
+ * sink (device, blocks * 4 words). Asynchronous. The GEMVs' effective bandwidth is reported
+ * against the rate this reaches on the same GPU. Errors: TG_EINVAL, TG_EHIP.
+ */
+int tg_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, int32_t unroll, void *stream);
 
 /* Static string for a TG_* code ("unknown error" for anything else). */
 const char *tg_strerror(int code);

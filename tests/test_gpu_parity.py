@@ -222,3 +222,34 @@ def test_dead_rows_layer_5120():
         x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
         s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
         run_case(w, x, s, fmts=[B.FMT_BITCOS], label=f"dead-rows role={role}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: B.FMT_NAMES[f])
+def test_graph_replays_match_eager(fmt):
+    """Launches captured in a HIP graph: every replay (with eager work and synchronisation between
+    replays) reproduces the eager results exactly."""
+    dev = _dev()
+    shapes = [(1024, 4096), (4096, 4096), (14336, 4096), (512, 14336)]
+    items = []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.ternary(n, k, 0.4, seed=50 + i)
+        dw = B.DeviceWeights(B.pack(fmt, w), dev)
+        x = torch.from_numpy(synth.activations(1, k, seed=60 + i)).to(dev)
+        s = torch.from_numpy(synth.scales(n, k // 128, seed=70 + i)).to(dev)
+        items.append((dw, x, s, B.ternary_gemv(dw, s, x)))
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    ys = [torch.empty((1, dw.n), dtype=torch.float32, device=dev) for dw, _, _, _ in items]
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for (dw, x, s, _), y in zip(items, ys):
+            B.ternary_gemv(dw, s, x, y, stream=st)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (dw, _, _, ref), y in zip(items, ys):
+            assert torch.equal(y, ref), f"{B.FMT_NAMES[fmt]} replay {rep} n={dw.n} k={dw.k}"
