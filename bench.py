@@ -1,12 +1,16 @@
 """Benchmark: ternary GEMV effective HBM bandwidth on MI355X (one GPU).
 
-Workload (default): the Llama3-8B-shaped decode layer set at batch 1 -- q, o 4096x4096; k, v
-1024x4096; gate, up 14336x4096; down 4096x14336 -- iid ternary weights at zero density 0.40,
-group-128 fp16 scales, int8 activations, seed 0. The layer is replicated 32 times (Llama3-8B depth)
-so the 1.5 GB BITCOS working set is far larger than the 256 MB Infinity Cache and every byte comes
-from HBM. One step = one pass over the 32 layers x 7 GEMVs in BITCOS. `value` is packed bytes read
-per second (bitmap + signs + sign index + fp16 scales), whole job. The five-trit and 2-bit formats
-are timed on the same layer set for comparison.
+Workload: the Llama3-8B-shaped decode layer set at batch 1 -- q, o 4096x4096; k, v 1024x4096;
+gate, up 14336x4096; down 4096x14336 -- iid ternary weights at zero density 0.40, group-128 fp16
+scales, int8 activations, seed 0. Each matrix is stored 32 times (one copy per layer of a 32-layer
+model), so the 1.51 GB of BITCOS weights are far larger than the 256 MB Infinity Cache and every
+byte comes from HBM. One step = one pass over the 32 x 7 = 224 GEMVs, issued as one grouped launch
+(tg_plan_init / ternary_gemv_plan). `value` is packed bytes read per second (bitmap + sign stream +
+sign index + fp16 scales), whole job.
+
+Also measured and reported beside it (same process): the same pass as 32 per-layer launches and as
+224 single-GEMV launches (captured in a HIP graph), each matrix's single-call time, the five-trit
+and 2-bit formats on the same layer set, the stream-read ceiling of this GPU, and the CPU oracle.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -26,197 +30,249 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
-REPLICAS = 32
+LAYERS = 32
 Z = 0.40
+METRIC = "ternary GEMV effective HBM GB/s (packed bytes/s) + % of MI355X peak, µs/call"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bitcos_layerset.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def make_layer(B, synth, dev, fmt):
-    """Pack the 7 matrices of one layer in `fmt`; returns per-matrix device weights, scales, x, y."""
-    import torch
-
-    mats = []
-    for role, (name, n, k) in enumerate(LAYER):
-        w = synth.ternary(n, k, Z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
-        s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
-        x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
-        p = B.pack(fmt, w)
-        mats.append(dict(name=name, n=n, k=k, packed=p, w=w, s=s,
-                         dw=B.DeviceWeights(p, dev), st=torch.from_numpy(s).to(dev),
-                         xt=torch.from_numpy(x).to(dev), y=torch.empty((1, n), dtype=torch.float32, device=dev)))
-    return mats
+def kernel_source_hash() -> str:
+    from bit_gemv_decode_amd.profiling import kernel_source_hash as h
+    return h()
 
 
-def replicate(B, mats):
-    """REPLICAS copies of every matrix's packed buffer and scales (distinct HBM addresses)."""
-    reps = []
-    for r in range(REPLICAS):
-        layer = []
-        for m in mats:
-            dw = B.DeviceWeights.from_tensor(m["dw"].desc, m["dw"].tensor.clone())
-            layer.append(dict(m, dw=dw, st=m["st"].clone()))
-        reps.append(layer)
-    return reps
+class LayerSet:
+    """The 7 matrices of one layer packed in `fmt`, stored `layers` times in device memory."""
+
+    def __init__(self, B, synth, torch, dev, fmt, layers=LAYERS):
+        self.fmt = fmt
+        self.mats = []      # per layer copy: list of dict(w=DeviceWeights, s, x, y)
+        self.host = []      # one host copy per matrix role (for the CPU baseline)
+        base = []
+        for role, (name, n, k) in enumerate(LAYER):
+            w = synth.ternary(n, k, Z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+            s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
+            x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
+            p = B.pack(fmt, w)
+            self.host.append(dict(name=name, n=n, k=k, packed=p, s=s, x=x))
+            base.append((B.DeviceWeights(p, dev), torch.from_numpy(s).to(dev), torch.from_numpy(x).to(dev)))
+        for layer in range(layers):
+            row = []
+            for (dw, s, x), (name, n, k) in zip(base, LAYER):
+                t = dw.tensor if layer == 0 else dw.tensor.clone()
+                row.append(dict(name=name, w=B.DeviceWeights.from_tensor(dw.desc, t), s=s if layer == 0 else s.clone(),
+                                x=x, y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+            self.mats.append(row)
+        self.layer_bytes = [m["w"].payload_bytes + 2 * m["w"].n * (m["w"].k // 128) for m in self.mats[0]]
+        self.step_bytes = layers * sum(self.layer_bytes)
+
+    def flat(self):
+        return [m for row in self.mats for m in row]
+
+    def plan(self, B, mats=None):
+        mats = mats if mats is not None else self.flat()
+        return B.Plan([m["w"] for m in mats], [m["x"] for m in mats], scales=[m["s"] for m in mats],
+                      ys=[m["y"] for m in mats])
 
 
-def packed_bytes(m):
-    """Algorithmic bytes one GEMV reads: packed payload plus the fp16 scales."""
-    return m["dw"].payload_bytes + 2 * m["n"] * (m["k"] // 128)
-
-
-def run_pass(B, reps, stream):
-    for layer in reps:
-        for m in layer:
-            B.ternary_gemv(m["dw"], m["st"], m["xt"], m["y"], stream=stream)
-
-
-def time_steps(B, reps, steps, warmup, stream):
-    import torch
-
+def time_launches(torch, fn, steps, warmup):
+    """Run fn() warmup times, then time `steps` calls with HIP events on the current stream."""
     for _ in range(warmup):
-        run_pass(B, reps, stream)
+        fn()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
     for _ in range(steps):
-        run_pass(B, reps, stream)
-    end.record(stream)
+        fn()
+    e1.record(cur)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3  # seconds
+    return e0.elapsed_time(e1) / 1e3  # seconds
 
 
-def per_matrix_us(B, mats, stream, iters=50):
-    """Median event-timed duration of each matrix's GEMV (cycling over fresh replicas is not needed for
-    the per-call figure, so this one is L2/MALL-warm and is reported separately)."""
-    import torch
-
-    out = {}
-    for m in mats:
-        ts = []
-        for _ in range(iters):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            B.ternary_gemv(m["dw"], m["st"], m["xt"], m["y"], stream=stream)
-            b.record(stream)
-            b.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3)
-        out[m["name"]] = float(np.median(ts))
-    return out
+def stream_ceiling(torch, bd, dev):
+    """Best rate of the stream-read reference kernel over a 2 GiB buffer (a few launch shapes)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = 2 * 1024 ** 3
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(cus * 8 * 4, dtype=torch.int32, device=dev)
+    best = 0.0
+    for bpc, unroll in ((4, 1), (2, 4), (8, 1), (1, 8)):
+        secs = time_launches(torch, lambda: bd.stream_read(buf, sink, cus * bpc, unroll), 5, 1)
+        best = max(best, nbytes * 5 / secs / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
-def cpu_baseline(O, mats, budget_s=12.0):
-    """The oracle decoding BITCOS rows from packed bytes on the host cores, over the whole layer set."""
-    total_bytes = sum(packed_bytes(m) for m in mats)
+def cpu_baseline(O, ls, budget_s=12.0):
+    """The oracle decoding BITCOS rows from packed bytes on the host cores, over one layer set."""
+    total_bytes = sum(ls.layer_bytes)
     times = []
     t_all = time.time()
     while True:
         t0 = time.perf_counter()
-        for m in mats:
-            p = m["packed"]
-            O.gemv_packed(O.FMT_BITCOS, p.section("codes"), p.sign_bytes(), p.rowoff(), m["s"], m["n"], m["k"],
-                          m["xt"].cpu().numpy())
+        for h in ls.host:
+            p = h["packed"]
+            O.gemv_packed(O.FMT_BITCOS, p.section("codes"), p.sign_bytes(), p.rowoff(), h["s"], h["n"], h["k"], h["x"])
         times.append(time.perf_counter() - t0)
-        if time.time() - t_all > budget_s or len(times) >= 5:
+        if time.time() - t_all > budget_s or len(times) >= 7:
             break
     t = float(np.median(times))
-    return dict(value=total_bytes / t / 1e9, unit="GB/s", cores=O.threads(), kind="oracle",
-                sample=f"one Llama3-8B-shaped layer set (7 GEMVs, {total_bytes / 1e6:.1f} MB BITCOS), median of "
-                       f"{len(times)} passes, {t * 1e3:.0f} ms per pass", seconds_per_pass=t)
+    return dict(value=round(total_bytes / t / 1e9, 4), unit="GB/s", cores=int(O.threads()), kind="oracle",
+                sample=f"one layer set (the 7 GEMVs, {total_bytes / 1e6:.1f} MB BITCOS, ~1/32 of a step), "
+                       f"median of {len(times)} passes, {t * 1e3:.1f} ms per pass")
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 --pmc runs, if they match this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--formats", default="bitcos,5trit,2bit")
+    ap.add_argument("--quick", action="store_true", help="only the timed BITCOS step (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the ternary GEMV is sharded by rows or by K across GPUs in a "
-              "deployment, but this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the ternary GEMV shards across GPUs by rows (or by k with one "
+              "all-reduce of the output vector) in a deployment, but this build runs on a single MI355X. "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     import bit_gemv_decode_amd as B
+    from bit_gemv_decode_amd import binding as bd
     from bit_gemv_decode_amd import synth
 
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
-    fmt_ids = {"bitcos": B.FMT_BITCOS, "5trit": B.FMT_5TRIT, "2bit": B.FMT_2BIT}
-    results = {}
-    bitcos_mats = None
-    for fname in args.formats.split(","):
-        fmt = fmt_ids[fname]
-        log(f"[bench] packing the layer set as {fname}")
-        mats = make_layer(B, synth, dev, fmt)
-        reps = replicate(B, mats)
-        step_bytes = REPLICAS * sum(packed_bytes(m) for m in mats)
-        steps = args.steps if fmt == B.FMT_BITCOS else max(5, args.steps // 5)
-        log(f"[bench] {fname}: {step_bytes / 1e9:.3f} GB per step, {steps} steps")
-        secs = time_steps(B, reps, steps, args.warmup if fmt == B.FMT_BITCOS else 3, stream)
-        per_call = per_matrix_us(B, mats, stream)
-        results[fname] = dict(gbs=step_bytes * steps / secs / 1e9, ms_per_step=secs / steps * 1e3,
-                              step_bytes=step_bytes, steps=steps, launches_per_step=REPLICAS * len(mats),
-                              per_matrix_us_warm=per_call,
-                              layer_bytes={m["name"]: packed_bytes(m) for m in mats})
-        log(f"[bench] {fname}: {results[fname]['gbs']:.1f} GB/s, {results[fname]['ms_per_step']:.3f} ms/step")
-        if fmt == B.FMT_BITCOS:
-            bitcos_mats = mats
-        del reps
-        if fmt != B.FMT_BITCOS:
-            del mats
-        torch.cuda.empty_cache()
+    log("[bench] packing the Llama3-8B-shaped layer set (BITCOS) and storing 32 layer copies")
+    ls = LayerSet(B, synth, torch, dev, B.FMT_BITCOS)
+    plan = ls.plan(B)
+    log(f"[bench] BITCOS: {ls.step_bytes / 1e9:.3f} GB per step, {plan.plan.units} work units, "
+        f"{plan.plan.waves} waves; timing {args.steps} steps")
+    secs = time_launches(torch, plan.run, args.steps, args.warmup)
+    step_s = secs / args.steps
+    gbs = ls.step_bytes / step_s / 1e9
+    log(f"[bench] BITCOS grouped: {gbs:.1f} GB/s, {step_s * 1e3:.3f} ms/step")
 
-    bc = results["bitcos"]
-    launches = bc["launches_per_step"] * bc["steps"]
-    avg_launch_s = bc["ms_per_step"] / 1e3 / bc["launches_per_step"]
-    avg_launch_bytes = bc["step_bytes"] / bc["launches_per_step"]
-    achieved = avg_launch_bytes / avg_launch_s / 1e9
+    traffic = load_traffic()
     out = {
-        "metric": "ternary GEMV effective HBM GB/s (packed bytes/s) + % of MI355X peak, us/call",
-        "value": round(bc["gbs"], 2),
+        "metric": METRIC,
+        "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(bc["ms_per_step"], 4),
+        "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded iid ternary z=0.40, fp16 scales U[0.01,0.1], int8 x U[-127,127])",
-        "config": {"workload": "Llama3-8B-shaped decode layer set, batch 1, BITCOS, x32 layer replicas",
-                   "matrices": {n: [r, c] for n, r, c in LAYER}, "zero_density": Z, "group": 128,
-                   "replicas": REPLICAS, "format": "bitcos"},
-        "pct_of_hbm_peak": round(100 * bc["gbs"] / HBM_PEAK_GBS, 2),
-        "us_per_layer": round(bc["ms_per_step"] * 1e3 / REPLICAS, 3),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "bitcos_gemv_valu<1,false>", "launches": launches,
-                     "avg_launch_us": round(avg_launch_s * 1e6, 3), "avg_launch_bytes": int(avg_launch_bytes)},
-        "formats": {f: {"gbs": round(r["gbs"], 2), "ms_per_step": round(r["ms_per_step"], 4),
-                        "step_bytes": r["step_bytes"], "per_matrix_us_warm": {k: round(v, 3) for k, v in
-                                                                              r["per_matrix_us_warm"].items()}}
-                    for f, r in results.items()},
+        "config": {"workload": "Llama3-8B-shaped decode layer set at batch 1 (q,o 4096x4096; k,v 1024x4096; "
+                               "gate,up 14336x4096; down 4096x14336), BITCOS, 32 layer copies, one grouped "
+                               "launch per step",
+                   "zero_density": Z, "group": 128, "layers": LAYERS, "gemvs_per_step": LAYERS * len(LAYER),
+                   "format": "bitcos", "m": 1},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_layer": round(step_s * 1e6 / LAYERS, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic["bytes_per_launch"] / ls.step_bytes, 4) if traffic else None),
+                     "kernel": "bitcos_gemv_kernel<1,false,4> (grouped, one launch per step)",
+                     "algorithmic_bytes_per_launch": ls.step_bytes,
+                     "avg_launch_us": round(step_s * 1e6, 2)},
     }
-    if "5trit" in results:
-        out["bitcos_vs_5trit_time"] = round(results["5trit"]["ms_per_step"] / bc["ms_per_step"], 4)
-        out["5trit_vs_bitcos_bytes"] = round(results["5trit"]["step_bytes"] / bc["step_bytes"], 4)
-    if "2bit" in results:
-        out["bitcos_vs_2bit_time"] = round(results["2bit"]["ms_per_step"] / bc["ms_per_step"], 4)
-        out["2bit_vs_bitcos_bytes"] = round(results["2bit"]["step_bytes"] / bc["step_bytes"], 4)
+    if traffic:
+        out["roofline"]["traffic_note"] = (f"HBM bytes per launch / algorithmic bytes, from rocprofv3 "
+                                           f"FETCH_SIZE+WRITE_SIZE scaled by the stream-read calibration "
+                                           f"({os.path.relpath(TRAFFIC_FILE, ROOT)})")
+    if args.quick:
+        print(json.dumps(out), flush=True)
+        return
+
+    # same pass as 32 per-layer launches (7 GEMVs each) and as 224 single-GEMV launches in a graph
+    layer_plans = [ls.plan(B, row) for row in ls.mats]
+    s_layer = time_launches(torch, lambda: [p.run() for p in layer_plans], max(3, args.steps // 4), 1)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=st):
+        for m in ls.flat():
+            B.ternary_gemv(m["w"], m["s"], m["x"], m["y"], stream=st)
+    s_call = time_launches(torch, g.replay, max(3, args.steps // 4), 1)
+    n_pl = max(3, args.steps // 4)
+    out["modes"] = {
+        "grouped_one_launch": {"gbs": round(gbs, 1), "ms_per_step": round(step_s * 1e3, 3)},
+        "per_layer_launch": {"gbs": round(ls.step_bytes * n_pl / s_layer / 1e9, 1),
+                             "ms_per_step": round(s_layer / n_pl * 1e3, 3), "launches_per_step": LAYERS},
+        "per_gemv_launch_graph": {"gbs": round(ls.step_bytes * n_pl / s_call / 1e9, 1),
+                                  "ms_per_step": round(s_call / n_pl * 1e3, 3),
+                                  "launches_per_step": LAYERS * len(LAYER)},
+    }
+    # single-call time of each matrix: a graph cycling through the 32 copies (weights from HBM)
+    per_mat = {}
+    for role, (name, n, k) in enumerate(LAYER):
+        gm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gm, stream=st):
+            for row in ls.mats:
+                m = row[role]
+                B.ternary_gemv(m["w"], m["s"], m["x"], m["y"], stream=st)
+        sm = time_launches(torch, gm.replay, 5, 1)
+        us = sm / (5 * LAYERS) * 1e6
+        per_mat[name] = {"us_per_call": round(us, 3), "gbs": round(ls.layer_bytes[role] / us / 1e3, 1)}
+        del gm
+    out["per_matrix_single_call"] = per_mat
+    del layer_plans, g
+    torch.cuda.empty_cache()
+
+    log("[bench] stream-read ceiling")
+    ceil = stream_ceiling(torch, bd, dev)
+    out["stream_read_ceiling_gbs"] = round(ceil, 1)
+    out["pct_of_stream_ceiling"] = round(100 * gbs / ceil, 2)
+
+    bitcos_host = ls
+    formats = {"bitcos": {"gbs": round(gbs, 1), "ms_per_step": round(step_s * 1e3, 3), "step_bytes": ls.step_bytes}}
+    del plan
+    for fname, fmt in (("5trit", B.FMT_5TRIT), ("2bit", B.FMT_2BIT)):
+        log(f"[bench] {fname} layer set")
+        lf = LayerSet(B, synth, torch, dev, fmt)
+        pf = lf.plan(B)
+        sf = time_launches(torch, pf.run, max(3, args.steps // 2), 1)
+        n_f = max(3, args.steps // 2)
+        formats[fname] = {"gbs": round(lf.step_bytes * n_f / sf / 1e9, 1), "ms_per_step": round(sf / n_f * 1e3, 3),
+                          "step_bytes": lf.step_bytes}
+        del pf, lf
+        torch.cuda.empty_cache()
+    out["formats"] = formats
+    out["bitcos_vs_5trit_time"] = round(formats["5trit"]["ms_per_step"] / formats["bitcos"]["ms_per_step"], 4)
+    out["5trit_vs_bitcos_bytes"] = round(formats["5trit"]["step_bytes"] / formats["bitcos"]["step_bytes"], 4)
+    out["bitcos_vs_2bit_time"] = round(formats["2bit"]["ms_per_step"] / formats["bitcos"]["ms_per_step"], 4)
+    out["2bit_vs_bitcos_bytes"] = round(formats["2bit"]["step_bytes"] / formats["bitcos"]["step_bytes"], 4)
+
     if not args.no_cpu:
         import oracle as O
 
         log("[bench] timing the CPU oracle baseline")
-        cb = cpu_baseline(O, bitcos_mats)
-        out["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
-        out["gpu_vs_cpu"] = round(bc["gbs"] / cb["value"], 1)
+        out["cpu_baseline"] = cpu_baseline(O, bitcos_host)
+        out["gpu_vs_cpu"] = round(gbs / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 

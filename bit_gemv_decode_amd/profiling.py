@@ -1,0 +1,129 @@
+"""Profiling helpers: a workload driver for rocprofv3 runs and summaries of rocprofv3's CSV output.
+
+  python -m bit_gemv_decode_amd.profiling drive
+      Runs, in one process: the stream-read kernel over a 2 GiB buffer (known bytes read), a 1 GiB
+      fill (known bytes written), then one warm-up and one timed grouped BITCOS step over the
+      Llama3-8B-shaped layer set (the same workload bench.py times).
+  python -m bit_gemv_decode_amd.profiling stats STATS_CSV OUT.md "COMMAND"
+      Writes a short markdown summary of a --kernel-trace --stats run.
+  python -m bit_gemv_decode_amd.profiling traffic FETCH_CSV WRITE_CSV OUT.json "COMMANDS"
+      From a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run of `drive`: calibrates both counters
+      against the known-size kernels and converts the BITCOS dispatch's counts into HBM bytes.
+
+The counters report KiB summed over the dispatch; the calibration factor is what the counter reads
+for the known-size kernel divided by the bytes that kernel moves.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SRC = os.path.join(PKG, "csrc", "bitcos_gemv.hip")
+READ_BYTES = 2 * 1024 ** 3
+WRITE_BYTES = 1024 ** 3
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def drive():
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import bench
+    import bit_gemv_decode_amd as B
+    from bit_gemv_decode_amd import binding as bd
+    from bit_gemv_decode_amd import synth
+
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.empty(READ_BYTES, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(cus * 4 * 4, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    bd.stream_read(buf, sink, cus * 4, 1)           # calibration: READ_BYTES read
+    torch.cuda.synchronize()
+    del buf
+    w = torch.empty(WRITE_BYTES // 4, dtype=torch.int32, device=dev)
+    w.fill_(3)                                       # calibration: WRITE_BYTES written
+    torch.cuda.synchronize()
+    del w
+    torch.cuda.empty_cache()
+    ls = bench.LayerSet(B, synth, torch, dev, B.FMT_BITCOS)
+    plan = ls.plan(B)
+    plan.run()
+    torch.cuda.synchronize()
+    plan.run()
+    torch.cuda.synchronize()
+    print(json.dumps({"step_bytes": ls.step_bytes}), flush=True)
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def stats(stats_csv, out_md, command):
+    rows = _rows(stats_csv)
+    lines = [f"# Kernel durations: `{os.path.basename(out_md)}`", "", "Command (from the repository root):", "",
+             f"    {command}", "", "| Kernel | Calls | Average (µs) | Min (µs) | Max (µs) | Share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path, counter):
+    agg = defaultdict(float)
+    names = {}
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        agg[d] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return [(d, names[d], agg[d]) for d in sorted(agg)]
+
+
+def traffic(fetch_csv, write_csv, out_json, command):
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    pick = lambda rows, key: [r for r in rows if key in r[1]]
+    f_cal = pick(fetch, "stream_read")[-1][2] * 1024 / READ_BYTES
+    w_cal = pick(write, "FillFunctor<int>")[-1][2] * 1024 / WRITE_BYTES
+    f_k = pick(fetch, "bitcos_gemv_kernel")[-1][2] * 1024 / f_cal
+    w_k = pick(write, "bitcos_gemv_kernel")[-1][2] * 1024 / w_cal
+    out = {"kernel": "bitcos_gemv_kernel (grouped step over the Llama3-8B-shaped layer set x32)",
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "fetch_calibration": round(f_cal, 5), "write_calibration": round(w_cal, 5),
+           "hbm_read_bytes_per_launch": int(f_k), "hbm_write_bytes_per_launch": int(w_k),
+           "bytes_per_launch": int(f_k + w_k), "commands": command}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1]
+    if cmd == "drive":
+        drive()
+    elif cmd == "stats":
+        stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif cmd == "traffic":
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    else:
+        raise SystemExit(f"unknown command {cmd}")
