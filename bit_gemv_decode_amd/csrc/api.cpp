@@ -8,8 +8,6 @@
 
 namespace tg {
 
-int bitcos_rows_per_unit(int64_t n, int64_t k, int m, bool table);
-
 int device_cus() {
     static int cached = 0;
     if (!cached) {
@@ -44,7 +42,8 @@ Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, co
 }
 
 int rows_per_unit(int fmt, int64_t n, int64_t k, int m, bool table) {
-    return fmt == TG_FMT_BITCOS ? bitcos_rows_per_unit(n, k, m, table) : 1;
+    (void)fmt, (void)n, (void)k, (void)m, (void)table;
+    return 1;
 }
 
 }  // namespace tg
@@ -91,9 +90,15 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
                              acc_out ? acc + (size_t)m0 * n * ng : nullptr);
         g.count = 1;
         g.m = mt;
-        g.rows_per_unit = rows_per_unit(desc->fmt, n, k, mt, false);
-        g.units = (int32_t)((n + g.rows_per_unit - 1) / g.rows_per_unit);
         g.one.unit_begin = 0;
+        if (desc->fmt == TG_FMT_BITCOS) {
+            bitcos_geometry(g.one, mt);
+            g.rows_per_unit = g.one.rpu;
+        } else {
+            g.rows_per_unit = rows_per_unit(desc->fmt, n, k, mt, false);
+            g.one.nunits = (int32_t)((n + g.rows_per_unit - 1) / g.rows_per_unit);
+        }
+        g.units = g.one.nunits;
         if (launch(desc->fmt, g, acc_out, s) != hipSuccess) return TG_EHIP;
     }
     return TG_OK;
@@ -113,15 +118,17 @@ extern "C" int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t
 
 namespace {
 
-// Waves of a persistent BITCOS launch on this device; a plan's per-wave ranges are sized for it.
-int plan_waves() { return device_cus() * kBitcosBlocksPerCu * kBitcosWavesPerBlock; }
+// Waves of a persistent BITCOS launch on this device for m activation rows; a plan's per-wave
+// ranges are sized for it (the table has room for the largest count).
+int plan_waves(int m) { return device_cus() * bitcos_waves_per_cu(m); }
+int plan_waves_max() { return device_cus() * kBitcosMaxWavesPerCu; }
 
 size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
 
 }  // namespace
 
 extern "C" size_t tg_plan_table_bytes(int32_t count) {
-    return count > 0 ? ranges_offset(count) + (size_t)plan_waves() * sizeof(WaveRange) : 0;
+    return count > 0 ? ranges_offset(count) + (size_t)plan_waves_max() * sizeof(WaveRange) : 0;
 }
 
 extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
@@ -133,7 +140,7 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
     if (((uintptr_t)table & 15) || table_bytes < tg_plan_table_bytes(count)) return TG_EINVAL;
     const int fmt = descs[0].fmt;
     std::vector<Problem> host((size_t)count);
-    int rpu = 1;
+    int rpu = 1;  // formats other than BITCOS: one value for all GEMVs
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
         int e = check_desc(d, 0);
@@ -153,12 +160,16 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr);
         host[i].unit_begin = (int32_t)units;
-        units += (d->n + rpu - 1) / rpu;
+        if (fmt == TG_FMT_BITCOS)
+            bitcos_geometry(host[i], m);
+        else
+            host[i].nunits = (int32_t)((d->n + rpu - 1) / rpu);
+        units += host[i].nunits;
         total_cost += (double)d->n * (double)d->k;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
     // Contiguous unit ranges per wave, balanced by cost (rows x k of each unit).
-    const int nw = plan_waves();
+    const int nw = fmt == TG_FMT_BITCOS ? plan_waves(m) : 1;
     std::vector<WaveRange> ranges((size_t)nw);
     {
         int32_t pi = 0;
@@ -170,8 +181,9 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
             const double target = total_cost * (double)(w + 1) / (double)nw;
             while (u < units) {
                 while (pi + 1 < count && u >= host[pi + 1].unit_begin) ++pi;
-                const int64_t row0 = (u - host[pi].unit_begin) * rpu;
-                const double cost = (double)std::min<int64_t>(rpu, host[pi].n - row0) * (double)host[pi].k;
+                const int64_t prpu = fmt == TG_FMT_BITCOS ? host[pi].rpu : rpu;
+                const int64_t row0 = (u - host[pi].unit_begin) * prpu;
+                const double cost = (double)std::min<int64_t>(prpu, host[pi].n - row0) * (double)host[pi].k;
                 if (done + 0.5 * cost > target && w + 1 < nw) break;
                 done += cost;
                 ++u;
@@ -206,7 +218,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
     if (plan->fmt == TG_FMT_BITCOS) {
-        if (plan->waves != plan_waves()) return TG_EINVAL;  // built for another device
+        if (plan->waves != plan_waves(plan->m)) return TG_EINVAL;  // built for another device
         g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
         g.waves = plan->waves;
     }

@@ -7,31 +7,33 @@
 // negative) pair into w = p - 2n (Eq. 2), contracts against int8 activations in int32 and applies
 // the group scale once per 128-element group.
 //
-// Mapping on CDNA4 (wave64):
-//   * one persistent grid serves one GEMV or a whole table of them; the work unit is a block of NB
-//     consecutive rows of one matrix, taken by one wave. Units are dealt so that consecutive units
-//     run on the same XCD (its L2 then sees whole sign-stream lines and shares x).
-//   * within a unit the wave walks k chunk by chunk. A full chunk is 4096 weights, one row per step,
-//     lane l owning bitmap dwords 2l, 2l+1 of the chunk (64 weights, half a 128-group). When k is
-//     not a multiple of 4096, the remainder of several rows is packed into one step.
-//   * the activation bytes a lane needs for its 64 weights stay in registers for every row of the
-//     unit, so x is read once per unit rather than once per row;
-//   * a lane's first sign sits at the row's running cursor plus the exclusive prefix sum of the
-//     popcounts of the lanes before it (DPP row shifts and broadcasts; the sign stream is one
-//     contiguous bit string over all rows, so rows of one step simply continue each other);
-//   * the lane fetches the <= 64 signs of its two dwords with one 3-dword load and funnel-shifts
-//     them into place (start <= bit 31 of the first dword, <= 64 bits: inside three dwords);
-//   * the Fig. 4 deposit is replaced by a table in LDS: for each presence byte pb and the
-//     popcount(pb) compact signs that follow, the table holds the 8 ternary int8 weights; it is
-//     indexed compactly, base[pb] + signs, 3^8 = 6561 entries of 8 bytes, loaded once per block;
-//   * v_dot4_i32_i8 contracts 4 weights per instruction; the two lanes of a 128-group add their
-//     int32 partials with one DPP swap and the even lane applies the fp16 scale in fp64. The group
-//     terms of all NB rows go through LDS and are summed by 64/NB lanes per row, so the fp64
-//     cross-lane reduction runs once per batch, not once per row;
-//   * a unit is one fully unrolled batch per chunk: all NB bitmap loads are issued first, then each
-//     row's scan and sign-window load, then the decodes, so NB rows of loads are in flight per wave
-//     and the compiler waits for exactly the load each step needs. All loads go through buffer
-//     resources: out-of-range reads return zero (a corrupt sign index cannot fault).
+// Mapping on CDNA4 (wave64, one 1024- or 512-thread block per CU, persistent):
+//   * a lane owns one 128-weight group of one row per step: its four bitmap dwords arrive with one
+//     16-byte load, its scale with one 2-byte load. A row of k weights takes ng = k/128 lanes; when
+//     ng <= 64 a step holds R = 64/ng consecutive rows, otherwise a row is split into chunks of 64
+//     groups, one chunk per step. A lane's activation bytes (its group's 128 x values) stay in
+//     registers for every row it sees, so x is read once per GEMV (or once per chunk pass).
+//   * sign positions: rows of a step are consecutive in the sign stream, so a lane's first sign sits
+//     at the step's cursor (from the row index, or carried from the row's previous chunk) plus the
+//     exclusive prefix sum of the popcounts of the lanes before it (DPP scan). For each bitmap dword
+//     the lane loads the three sign-stream dwords holding bits [pos - 3, pos + 61) and funnel-shifts
+//     them (pos is that dword's first sign).
+//   * the deposit of Fig. 4 is a table lookup in LDS, keyed per presence byte (the nibble-keyed
+//     lookup of Sec. II-D, Eq. 4 and Fig. 9, widened to a byte): entry (pb, s) holds the 8 ternary
+//     int8 weights for presence byte pb followed by the popcount(pb) compact signs s; 3^8 = 6561
+//     entries of 8 bytes. The entries of one pb form a block of 2^popcount(pb) entries aligned to its
+//     own size, so the entry address is (window & mask) | base: one instruction, with mask and base
+//     fetched per presence byte from a 256-entry table. That small table is kept in 32 copies, one
+//     per LDS bank, and lane l reads copy l % 32, so those reads never conflict; the copy address is
+//     one byte-permute of the bitmap dword. The per-byte sign cursor is the running popcount of the
+//     masks.
+//   * v_dot4_i32_i8 contracts 4 weights per instruction. Each group's int32 sum times its fp16 scale
+//     (exact in fp64) goes to an LDS tile; once per unit the tile's rows are summed (fp64, DPP) and
+//     stored as fp32.
+//   * loads are software-pipelined two steps ahead (bitmap) and one step ahead (signs), with the loop
+//     unrolled twice so that no register with a load in flight is ever copied. Every load goes
+//     through a buffer resource and is issued unconditionally; lanes with nothing to read use an
+//     out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
 
 #include "device_common.h"
@@ -40,479 +42,542 @@
 namespace tg {
 namespace {
 
-constexpr int kByteLutEntries = 6561;  // sum over the 256 presence bytes of 2^popcount = 3^8
+constexpr int kEntries = 6561;                 // sum over presence bytes of 2^popcount = 3^8
+constexpr uint32_t kInfoBytes = 256 * 32 * 8;  // per-byte (mask, base) in 32 bank-spread copies
+constexpr uint32_t kEntOff = kInfoBytes;       // LDS byte offset of the entry table
+constexpr uint32_t kEntBytes = kEntries * 8;
+constexpr uint32_t kTabBytes = (kEntOff + kEntBytes + 255) / 256 * 256;
 
-struct alignas(16) ByteLut {
-    uint64_t ent[kByteLutEntries + 1];  // padded to an even count for 16-byte copies
-    uint32_t base8[256];                // byte offset (8 * entry index) of presence byte pb's first entry
+struct alignas(16) Tables {
+    uint64_t ent[kEntries + 1];  // padded to an even count for 16-byte copies
+    uint32_t info[256][2];       // per presence byte: mask (popcount ones, shifted left 3), LDS base
 };
 
-constexpr ByteLut make_byte_lut() {
-    ByteLut t{};
+constexpr int popc8(uint32_t v) {
+    int c = 0;
+    for (int i = 0; i < 8; ++i) c += (v >> i) & 1;
+    return c;
+}
+
+// Blocks of entries in decreasing size: every block then starts at a multiple of its own size, so
+// a block's base has zero bits where (window & mask) has its ones.
+constexpr Tables make_tables() {
+    Tables t{};
     uint32_t e = 0;
-    for (uint32_t pb = 0; pb < 256; ++pb) {
-        t.base8[pb] = 8 * e;
-        uint32_t c = 0;
-        for (uint32_t i = 0; i < 8; ++i) c += (pb >> i) & 1;
-        for (uint32_t sc = 0; sc < (1u << c); ++sc) {
-            uint64_t v = 0;
-            uint32_t rank = 0;
-            for (uint32_t i = 0; i < 8; ++i) {
-                if ((pb >> i) & 1) {
-                    uint64_t byte = ((sc >> rank) & 1) ? 0xFFull : 0x01ull;  // -1 or +1 as int8
-                    v |= byte << (8 * i);
-                    ++rank;
+    for (int c = 8; c >= 0; --c) {
+        for (uint32_t pb = 0; pb < 256; ++pb) {
+            if (popc8(pb) != c) continue;
+            t.info[pb][0] = ((1u << c) - 1u) << 3;
+            t.info[pb][1] = kEntOff + 8 * e;
+            for (uint32_t sc = 0; sc < (1u << c); ++sc) {
+                uint64_t v = 0;
+                uint32_t rank = 0;
+                for (uint32_t i = 0; i < 8; ++i) {
+                    if ((pb >> i) & 1) {
+                        const uint64_t byte = ((sc >> rank) & 1) ? 0xFFull : 0x01ull;  // -1 or +1 as int8
+                        v |= byte << (8 * i);
+                        ++rank;
+                    }
                 }
+                t.ent[e + sc] = v;
             }
-            t.ent[e++] = v;
+            e += 1u << c;
         }
     }
     return t;
 }
 
-__device__ const ByteLut kByteLut = make_byte_lut();
+__device__ const Tables kTables = make_tables();
 
-constexpr int kWaves = kBitcosWavesPerBlock;
-constexpr int kBlock = 64 * kWaves;
-constexpr int kChunkDwords = 128;  // bitmap dwords of one full chunk (64 lanes x 2)
+template <int M>
+struct Cfg {
+    static constexpr int NB = M == 3 ? 2 : 4;     // row bundles (steps per chunk pass) per unit
+    static constexpr int WAVES = M == 1 ? 16 : 8;  // waves per block (= per CU)
+    static constexpr int BLOCK = 64 * WAVES;
+};
 
-// Scheduling fence: the compiler may not move instructions across it. Keeps the phases of a batch
-// (loads, scans, decodes) and of a decode (base reads, entry reads, dot products) apart, so that
-// the loads and LDS reads of one phase are all in flight together.
+// Scheduling fence: the compiler may not move instructions across it. Keeps the loads of the
+// pipeline stages in program order, so that each wait covers exactly the loads it needs.
 #define TG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-struct LutView {
-    const char *ent;    // LDS byte address of the entry table
-    const char *base8;  // LDS byte address of the base table (u32 per presence byte)
+// Buffer offsets. A lane with nothing to read gets kOffOff as its own (vector) offset; a pipeline
+// stage with nothing to do gets kDeadS as its wave-uniform (scalar) offset. Either way the sum lies
+// beyond every resource (bitmaps, scales and outputs are limited to less than 1 GiB, sign windows to
+// less than 512 MiB) without wrapping, so the access returns zero and makes no memory request.
+constexpr uint32_t kOffOff = 0x80000000u;
+constexpr uint32_t kDeadS = 0x7FFFFFF0u;
+
+__device__ __forceinline__ u32x4 ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t ldh(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void st1(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+}
+
+// Sign stage of one step: for each pair of bitmap dwords, the four sign-stream dwords holding bits
+// [pos - 3, pos + 93) (pos = the pair's first sign), the funnel-shift amount into them, and the sign
+// count of the pair's first dword; plus the group scale.
+struct SgBuf {
+    u32x4 s[2];
+    uint32_t sh[2];
+    uint32_t pc[2];
+    uint16_t scale;
 };
 
-// Buffer resources over the sections one GEMV reads.
-struct Rsrc {
-    __amdgpu_buffer_rsrc_t bm, sg, sc, x;
+// Wave-uniform per-GEMV values.
+struct Ctx {
+    __amdgpu_buffer_rsrc_t rbm, rsg, rsc, rro, rx, ry, racc;
+    int n, k, ng, nch, G, R, glast;
 };
 
-// Out-of-range buffer offset: a load there returns zero and makes no memory request.
-constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
-
-// One lane's share of a step after its bitmap dwords arrived: sign window and scale loads issued.
-struct Staged {
-    uint2 bm;
-    u32x3 sg;        // sign dwords q, q+1, q+2 of the stream
-    uint32_t r0;     // bit of sg.x where the lane's first sign sits
-    uint16_t scale;  // fp16 scale bits of the lane's group (value path)
-};
-
-// Sign window for a lane whose first sign is at stream position o0 (the window covers o0 .. o0+95,
-// enough for the <= 64 signs of two bitmap dwords), and the scale of its group.
+// Scan the step's bitmap popcounts and issue its sign-window and scale loads. `cur` is the stream
+// position of the step's first sign; returns the step's sign count.
 template <bool ACC>
-__device__ __forceinline__ Staged issue_signs(const Rsrc &r, uint2 bm, bool act, uint32_t o0, uint32_t scale_idx) {
-    Staged st;
-    st.bm = bm;
-    st.r0 = o0 & 31;
-    st.sg = buf_u32x3(r.sg, act ? (o0 >> 5) * 4 : kNoLoad);
-    // unconditional for every lane (a branch around a load makes the compiler wait for every load in
-    // flight); inactive lanes read nothing
-    st.scale = ACC ? (uint16_t)0 : buf_u16(r.sc, act ? scale_idx * 2 : kNoLoad);
-    return st;
+__device__ __forceinline__ uint32_t stage_signs(const Ctx &x, const u32x4 &bm, uint32_t cur, bool live,
+                                                uint32_t voff_sc, uint32_t soff_sc, SgBuf &g) {
+    const uint32_t t1 = __builtin_popcount(bm.x);
+    const uint32_t t2 = __builtin_popcount(bm.y) + t1;
+    const uint32_t t3 = __builtin_popcount(bm.z) + t2;
+    const uint32_t pc = __builtin_popcount(bm.w) + t3;
+    const uint32_t incl = wave_incl_scan(pc);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    // window start = first sign - 3, biased by +32 (the sign resource starts one dword early)
+    const uint32_t b0 = cur + 29u + incl - pc;
+    const uint32_t b2 = b0 + t2;
+    const uint32_t sd = live ? 0u : kDeadS;
+    g.s[0] = ld4(x.rsg, (b0 >> 5) << 2, sd);
+    g.s[1] = ld4(x.rsg, (b2 >> 5) << 2, sd);
+    g.sh[0] = b0;
+    g.sh[1] = b2;
+    g.pc[0] = t1;
+    g.pc[1] = t3 - t2;
+    g.scale = ACC ? (uint16_t)0 : ldh(x.rsc, voff_sc, live ? soff_sc : kDeadS);
+    return total;
 }
 
-// Decode a staged lane share: the int32 sum of the lane's 64 weights times x, per m.
-// Phase 1 needs only the bitmap: presence bytes (pre-scaled by 4 to address the base table),
-// popcounts, in-window sign cursors and the eight base-table reads. Phase 2 aligns the sign windows
-// and reads the eight table entries. Phase 3 contracts them with the activations.
+// Eight presence bytes' worth (one bitmap dword) of decode: lo/hi hold the sign-stream bits starting
+// 3 bits before the dword's first sign.
 template <int M>
-__device__ __forceinline__ void decode_staged(const Staged &st, const LutView &lut, const uint32_t (&xr)[M][16],
-                                              int (&acc)[M]) {
-    uint32_t c[8], cur[8], base[8];
+__device__ __forceinline__ void decode_dword(uint32_t bmd, uint32_t lo, uint32_t hi, const uint32_t (&xr)[M][32],
+                                             int d, const char *lds, uint32_t laneoff, int (&acc)[M]) {
+    uint2 info[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t p = i < 4 ? st.bm.x : st.bm.y;
-        const uint32_t pb4 = ((p >> (8 * (i & 3))) & 0xFFu) << 2;
-        c[i] = __builtin_popcount(pb4);
-        cur[i] = (i & 3) == 0 ? 0u : cur[i - 1] + c[i - 1];
-        base[i] = *reinterpret_cast<const uint32_t *>(lut.base8 + pb4);
+    for (int i = 0; i < 4; ++i) {
+        // (pb << 8) | laneoff: copy (lane % 32) of presence byte pb's (mask, base)
+        const uint32_t ia = __builtin_amdgcn_perm(bmd, laneoff, 0x0C0C0000u | ((4u + i) << 8));
+        info[i] = *reinterpret_cast<const uint2 *>(lds + ia);
     }
-    TG_SCHED_FENCE();
-    const uint32_t pc0 = cur[3] + c[3];  // signs of the first dword
-    const uint32_t w0 = __builtin_amdgcn_alignbit(st.sg.y, st.sg.x, st.r0);
-    const uint32_t r1 = st.r0 + pc0;  // 0 .. 63
-    const bool hi = r1 & 32;
-    const uint32_t w1 = __builtin_amdgcn_alignbit(hi ? st.sg.z : st.sg.y, hi ? st.sg.y : st.sg.x, r1 & 31);
-    uint2 e[8];
+    uint32_t cur = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t sc = __builtin_amdgcn_ubfe(i < 4 ? w0 : w1, cur[i], c[i]);
-        e[i] = *reinterpret_cast<const uint2 *>(lut.ent + base[i] + 8 * sc);
-    }
-    TG_SCHED_FENCE();
+    for (int i = 0; i < 4; ++i) {
+        // the byte's signs sit at bits 3 .. 3 + popcount of the shifted window
+        const uint32_t w = i == 0 ? lo : __builtin_amdgcn_alignbit(hi, lo, cur);
+        const uint32_t ea = (w & info[i].x) | info[i].y;
+        const uint2 e = *reinterpret_cast<const uint2 *>(lds + ea);
+        if (i < 3) cur = __builtin_popcount(info[i].x) + cur;
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-        int v = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v = dot4(e[i].x, xr[mi][2 * i], v);
-            v = dot4(e[i].y, xr[mi][2 * i + 1], v);
+        for (int mi = 0; mi < M; ++mi) {
+            acc[mi] = dot4(e.x, xr[mi][8 * d + 2 * i], acc[mi]);
+            acc[mi] = dot4(e.y, xr[mi][8 * d + 2 * i + 1], acc[mi]);
         }
-        acc[mi] = v;
     }
 }
 
-// Geometry of one chunk of k (wave-uniform). A full chunk is 4096 weights: one row per step, 64
-// lanes of 2 bitmap dwords. The tail chunk (k % 4096) gives each row L = tail/2 lanes and, when L
-// is a power of two, packs 64/L rows into a step; otherwise one row per step. Lane l sits in step
-// row l >> lg, at segment position l & (2^lg - 1); for a non-power-of-two tail lg = 6 (one
-// segment) and lanes at or past L are idle. All derived by shifts, without branches.
-struct Geo {
-    int dw_base;  // first bitmap dword of the chunk within a row
-    int L;        // lanes per row
-    int lg;       // log2 of the segment width
-    int rps;      // rows per step (1 << (6 - lg))
-    int G;        // 128-groups per row in the chunk (L / 2)
-    bool full;    // L == 64
-};
-
-__device__ __forceinline__ int nchunks_of(const Problem &p) {
-    const int kd = p.k >> 5;
-    return kd / kChunkDwords + ((kd % kChunkDwords) ? 1 : 0);
+// int32 sums of the lane's 128 weights times x, per activation row.
+template <int M>
+__device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const uint32_t (&xr)[M][32],
+                                       const char *lds, uint32_t laneoff, int (&acc)[M]) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) acc[mi] = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const u32x4 s = g.s[q];
+        const uint32_t a0 = __builtin_amdgcn_alignbit(s.y, s.x, g.sh[q]);
+        const uint32_t a1 = __builtin_amdgcn_alignbit(s.z, s.y, g.sh[q]);
+        const uint32_t a2 = __builtin_amdgcn_alignbit(s.w, s.z, g.sh[q]);
+        // the pair's second dword starts pc (0 .. 32) bits later
+        const uint64_t w01 = ((uint64_t)a1 << 32) | a0, w12 = ((uint64_t)a2 << 32) | a1;
+        const uint32_t b0 = (uint32_t)(w01 >> g.pc[q]), b1 = (uint32_t)(w12 >> g.pc[q]);
+        decode_dword<M>(q == 0 ? bm.x : bm.z, a0, a1, xr, 2 * q, lds, laneoff, acc);
+        decode_dword<M>(q == 0 ? bm.y : bm.w, b0, b1, xr, 2 * q + 1, lds, laneoff, acc);
+    }
 }
 
-__device__ __forceinline__ Geo geo_of(const Problem &p, int c) {
-    const int kd = p.k >> 5;
-    const int nfull = kd / kChunkDwords;
-    Geo g;
-    g.full = c < nfull;
-    g.dw_base = (g.full ? c : nfull) * kChunkDwords;
-    g.L = g.full ? 64 : (kd - g.dw_base) >> 1;
-    const bool pow2 = (g.L & (g.L - 1)) == 0;
-    g.lg = pow2 ? 31 - __builtin_clz((unsigned)g.L) : 6;
-    g.rps = 1 << (6 - g.lg);
-    g.G = g.L >> 1;
-    return g;
-}
-
-// Steps of a batch of nrows unit rows: ceil(nrows / rps).
-__device__ __forceinline__ int nsteps_of(const Geo &g, int nrows) {
-    return (nrows + g.rps - 1) >> (6 - g.lg);
-}
-
-// Per-lane view of a chunk geometry.
-struct LaneGeo {
-    int ri;   // row of the lane within a step
-    int seg;  // lane index within its row segment
-    bool ok;  // lane belongs to a row segment
-    int dw0;  // lane's first bitmap dword within the row
-};
-
-__device__ __forceinline__ LaneGeo lane_geo(const Geo &g, int lane) {
-    LaneGeo l;
-    l.ri = lane >> g.lg;
-    l.seg = lane & ((1 << g.lg) - 1);
-    l.ok = l.seg < g.L;
-    l.dw0 = g.dw_base + 2 * l.seg;
-    return l;
-}
-
-// Everything a batch needs before its scans: bitmap dwords of each step, the activation bytes of
-// the lane's 64 weights, and (for a unit's first chunk) the unit rows' sign cursors.
-template <int M, int NB>
-struct Batch {
-    uint32_t xr[M][16];
-    uint2 b[NB];
-    uint32_t rowoff;
-};
-
-// `live` false: issue the same instructions with out-of-range offsets (no memory traffic), so that
-// the caller needs no branch around the loads.
-template <int M, int NB>
-__device__ __forceinline__ void issue_batch(const Problem &p, int u, int c, bool live, Batch<M, NB> &bt) {
-    const int lane = threadIdx.x & 63;
-    const int kd = p.k >> 5;
-    const int row0 = (u - p.unit_begin) * NB;
-    const int nrows = min(NB, p.n - row0);
-    const Geo g = geo_of(p, c);
-    const LaneGeo l = lane_geo(g, lane);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.codes, p.codes_bytes);
-    // x first: a later wait for x then never has to wait for the (HBM) bitmap loads
+// x bytes of the lane's group (column col) for every activation row; lanes without a group read
+// nothing.
+template <int M>
+__device__ __forceinline__ void load_x(const Ctx &x, uint32_t voff, uint32_t (&xr)[M][32]) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 v = buf_u32x4(rx, (live && l.ok) ? (uint32_t)(mi * p.k + 32 * l.dw0 + 16 * j) : kNoLoad);
-            bt.xr[mi][4 * j] = v.x;
-            bt.xr[mi][4 * j + 1] = v.y;
-            bt.xr[mi][4 * j + 2] = v.z;
-            bt.xr[mi][4 * j + 3] = v.w;
+        for (int j = 0; j < 8; ++j) {
+            const u32x4 v = ld4(x.rx, voff + 16u * j, (uint32_t)(mi * x.k));
+            xr[mi][4 * j] = v.x;
+            xr[mi][4 * j + 1] = v.y;
+            xr[mi][4 * j + 2] = v.z;
+            xr[mi][4 * j + 3] = v.w;
         }
-#pragma unroll
-    for (int st = 0; st < NB; ++st) {
-        const int ur = st * g.rps + l.ri;
-        const bool act = live && l.ok && ur < nrows;
-        const u32x2 v = buf_u32x2(rb, act ? (uint32_t)((row0 + ur) * kd + l.dw0) * 4 : kNoLoad);
-        bt.b[st] = make_uint2(v.x, v.y);
-    }
-    const __amdgpu_buffer_rsrc_t ri = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
-    bt.rowoff = buf_u32(ri, (live && c == 0 && lane < nrows) ? (uint32_t)(row0 + lane) * 4 : kNoLoad);
 }
 
-// Scan each step's lane popcounts, advance the unit rows' cursors (lane u tracks unit row u) and
-// issue the sign-window and scale loads.
-template <int M, bool ACC, int NB>
-__device__ __forceinline__ void stage_batch(const Problem &p, int u, int c, const Batch<M, NB> &bt, uint32_t &cur_v,
-                                            Staged (&S)[NB]) {
-    const int lane = threadIdx.x & 63;
-    const int ng = p.k >> 7;
-    const int row0 = (u - p.unit_begin) * NB;
-    const int nrows = min(NB, p.n - row0);
-    const Geo g = geo_of(p, c);
-    const LaneGeo l = lane_geo(g, lane);
-    const int gcol = l.dw0 >> 2;
-    Rsrc r;
-    r.sg = make_rsrc(p.signs, p.sign_bytes);
-    r.sc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)ng * 2u);
-    if (c == 0) cur_v = bt.rowoff;
-    const int nsteps = nsteps_of(g, nrows);
+// x must have arrived before a loop starts: a loop entered with x as the newest loads would get
+// the waits compiled for that entry on every iteration.
+template <int M>
+__device__ __forceinline__ void wait_x(const uint32_t (&xr)[M][32]) {
 #pragma unroll
-    for (int st = 0; st < NB; ++st) {
-        if (st >= nsteps) break;  // wave-uniform: no row of the unit left for this step
-        const uint2 b = bt.b[st];
-        const uint32_t pc = __builtin_popcount(b.x) + __builtin_popcount(b.y);
-        const uint32_t incl = wave_incl_scan(pc);
-        const int ur = st * g.rps + l.ri;
-        const bool act = l.ok && ur < nrows;
-        uint32_t o0;
-        if (g.full) {
-            const uint32_t rowcur = (uint32_t)__builtin_amdgcn_readlane((int)cur_v, st);
-            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-            cur_v += lane == st ? total : 0u;
-            o0 = rowcur + incl - pc;
-        } else {
-            // inclusive sums just before this lane's row segment and at its end (the shuffles run
-            // on every lane: a lane-permute reading from a lane that is switched off returns zero)
-            const int seg_first = l.ri << g.lg;
-            const uint32_t prev = (uint32_t)__shfl((int)incl, max(seg_first - 1, 0), 64);
-            const uint32_t before = seg_first > 0 ? prev : 0u;
-            const uint32_t end = (uint32_t)__shfl((int)incl, min(seg_first + g.L - 1, 63), 64);
-            const uint32_t rowcur = (uint32_t)__shfl((int)cur_v, min(ur, 63), 64);
-            // unit row v = st*rps + i takes the total of step row i (held by lane i*L)
-            const int i = lane - st * g.rps;
-            const bool mine = i >= 0 && i < g.rps;
-            const uint32_t t = (uint32_t)__shfl((int)(end - before), mine ? i * g.L : 0, 64);
-            cur_v += mine ? t : 0u;
-            o0 = rowcur + incl - pc - before;
-        }
-        S[st] = issue_signs<ACC>(r, b, act, o0, (uint32_t)((row0 + ur) * ng + gcol));
-    }
+    for (int mi = 0; mi < M; ++mi)
+#pragma unroll
+        for (int j = 0; j < 32; j += 4) asm volatile("" ::"v"(xr[mi][j]));
 }
 
-// Decode every step of a batch. Accumulator path: store each group's int32 sum. Value path: the
-// group sums and scale bits go to the wave's LDS scratch; the batch's rows are then summed by 64/NB
-// lanes each (scale * acc in fp64) and added to the row sums held by lane u for unit row u.
-template <int M, bool ACC, int NB>
-__device__ __forceinline__ void finish_batch(const Problem &p, int u, int c, const Staged (&S)[NB],
-                                             const uint32_t (&xr)[M][16], const LutView &lut, int32_t *red_acc,
-                                             uint16_t *red_sc, double (&yv)[M]) {
+// Lane roles in the unit-end reduction: the tile's rows are summed by lpr lanes each.
+struct Red {
+    int lpr;   // lanes per row (power of two)
+    int epl;   // tile terms per lane
+    int base;  // tile index of the lane's first term
+    int cnt;   // terms the lane sums (0 .. epl)
+    int rho;   // tile row of the lane
+    bool own;  // the lane ends up holding row rho's sum (last lane of its group, rho < rows)
+};
+
+__device__ __forceinline__ Red make_red(int rows, int R, int geff, uint32_t rmagic) {
     const int lane = threadIdx.x & 63;
-    const int ng = p.k >> 7;
-    const int row0 = (u - p.unit_begin) * NB;
-    const int nrows = min(NB, p.n - row0);
-    const Geo g = geo_of(p, c);
-    const LaneGeo l = lane_geo(g, lane);
-    const int gi = l.seg >> 1;  // lane's group within the chunk
-    const int nsteps = nsteps_of(g, nrows);
+    Red r;
+    int lg = 0;
+    while ((2 << lg) * rows <= 64) ++lg;  // largest power of two with lpr * rows <= 64
+    r.lpr = 1 << lg;
+    r.epl = (geff + r.lpr - 1) >> lg;
+    r.rho = lane >> lg;
+    const int pi = lane & (r.lpr - 1);
+    const int sb = (int)(((uint32_t)r.rho * rmagic) >> 16);  // step of the row
+    const int qb = r.rho - sb * R;
+    r.base = sb * 64 + qb * geff + pi * r.epl;
+    r.cnt = min(max(geff - pi * r.epl, 0), r.epl);
+    if (r.rho >= rows) r.cnt = 0;
+    r.own = r.rho < rows && pi == r.lpr - 1;
+    return r;
+}
+
+// Row sums of a finished tile, stored as fp32: tile row rho is output row row0 + rho (stored when
+// below row_end and `live`).
+template <int M, int NB>
+__device__ __forceinline__ void reduce_store(const Ctx &x, const Red &r, const double *tile, int row0, int row_end,
+                                             bool live) {
+    double yv[M];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int st = 0; st < NB; ++st) {
-        if (st >= nsteps) break;  // wave-uniform
-        const int ur = st * g.rps + l.ri;
-        const bool act = l.ok && ur < nrows;
-        int acc[M];
-        decode_staged<M>(S[st], lut, xr, acc);
+    for (int mi = 0; mi < M; ++mi) {
+        double t = 0.0;
+        for (int e = 0; e < r.epl; ++e)
+            if (e < r.cnt) t += tile[mi * NB * 64 + r.base + e];
+        yv[mi] = seg_sum_f64(t, r.lpr);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int row = row0 + r.rho;
+    const bool own = live && r.own && row < row_end;
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi)
+        st1(__builtin_bit_cast(uint32_t, (float)yv[mi]), x.ry, own ? (uint32_t)row * 4u : kOffOff,
+            (uint32_t)(mi * x.n) * 4u);
+}
+
+// Decode stage epilogue: the group terms (int32 sum times scale, fp64) go to tile slot `slot`
+// (added to what earlier chunks left there when `add`); accumulator outputs are stored directly.
+template <int M, bool ACC, int NB>
+__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t scale, double *tile, int slot,
+                                     bool add, uint32_t voff_acc, uint32_t soff_acc) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (ACC) {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi)
+            st1((uint32_t)acc[mi], x.racc, voff_acc, soff_acc + (uint32_t)(mi * x.n * x.ng) * 4u);
+    } else {
+        const double s = (double)half_bits_to_float(scale);
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) {
-            const int v = acc[mi] + __builtin_amdgcn_update_dpp(0, acc[mi], kDppQuadSwap1, 0xF, 0xF, false);
-            if (act && !(lane & 1)) {
-                if (ACC) {
-                    p.acc[((size_t)mi * p.n + row0 + ur) * ng + (l.dw0 >> 2)] = v;
+            double *t = tile + mi * NB * 64 + slot * 64 + lane;
+            const double term = (double)acc[mi] * s;
+            *t = add ? *t + term : term;
+        }
+    }
+}
+
+// Pipeline over the steps of units [u0, u1) of one GEMV. In half-step h the bitmap of step h is
+// loaded, the signs of step h - 2 are located and loaded, and step h - 4 is decoded. The loop body
+// holds four half-steps, so every stage buffer has a fixed register home (bitmaps rotate over four,
+// sign windows over two) and no register with a load in flight is ever copied. Each stage runs
+// unconditionally (outside the live range its loads use dead offsets), apart from decode work that
+// loads nothing.
+//
+// Single-chunk GEMVs (ng <= 64): step s covers rows row_begin + s*R .. + R - 1, a unit NB steps; the
+// sign cursor runs on from step to step. Chunked GEMVs: a unit is NB rows; its steps go chunk by
+// chunk (NB steps per chunk pass), each row's cursor carried from its previous chunk.
+template <int M, bool ACC, int NB, bool CHUNKED>
+__device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const char *lds, double *tile) {
+    const int lane = threadIdx.x & 63;
+    Ctx x;
+    x.n = p.n;
+    x.k = p.k;
+    x.ng = p.ng;
+    x.nch = p.nch;
+    x.G = p.G;
+    x.R = p.R;
+    x.glast = p.glast;
+    x.rbm = make_rsrc(p.codes, p.codes_bytes);
+    // the sign resource starts 4 bytes early so that the window of a position below 3 (the stream's
+    // first bits) is in range; the 4 bytes before the sign section belong to the packed buffer
+    x.rsg = make_rsrc(reinterpret_cast<const uint8_t *>(p.signs) - 4, p.sign_bytes + 4u);
+    x.rsc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)p.ng * 2u);
+    x.rro = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
+    x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
+    x.ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)M * (uint32_t)p.n * 4u);
+    x.racc = make_rsrc(p.acc, ACC ? (uint32_t)M * (uint32_t)p.n * (uint32_t)p.ng * 4u : 0u);
+    const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
+    const int rpu = p.rpu;
+    const int row_begin = (u0 - p.unit_begin) * rpu;
+    const int row_end = min(p.n, (u1 - p.unit_begin) * rpu);
+    const uint32_t kb = (uint32_t)(p.k >> 3);  // bitmap bytes per row
+
+    uint32_t xr[M][32];
+    uint32_t cur = 0;           // single-chunk: sign cursor of the next step to scan
+    uint32_t ccur[NB] = {};     // chunked: sign cursor of each row of the unit being scanned
+    uint32_t ro = 0;            // chunked: row-index entries of the unit (lane r: row r)
+    int T;                      // steps in the range
+    // per-lane constant parts of the offsets
+    uint32_t voff_bm, voff_sc, voff_acc, voff_x;
+    Red red;
+    if constexpr (!CHUNKED) {
+        const int ql = (int)(((uint32_t)lane * p.gmagic) >> 16);  // lane / G: row within the step
+        const int jl = lane - ql * x.G;                           // group within the row
+        const bool act = lane < x.R * x.G;
+        voff_bm = act ? (uint32_t)ql * kb + (uint32_t)jl * 16u : kOffOff;
+        voff_sc = act ? (uint32_t)lane * 2u : kOffOff;  // (ql * ng + jl) = lane when ng = G
+        voff_acc = act ? (uint32_t)lane * 4u : kOffOff;
+        voff_x = act ? (uint32_t)jl * 128u : kOffOff;
+        T = (u1 - u0) * NB;
+        red = make_red(NB * x.R, x.R, x.G, p.rmagic);
+        cur = uniform_u32(buf_u32(x.rro, (uint32_t)row_begin * 4u));
+    } else {
+        voff_bm = (uint32_t)lane * 16u;
+        voff_sc = (uint32_t)lane * 2u;
+        voff_acc = (uint32_t)lane * 4u;
+        voff_x = (uint32_t)lane * 128u;
+        T = (u1 - u0) * NB * x.nch;
+        red = make_red(NB, 1, 64, p.rmagic);
+    }
+    load_x<M>(x, voff_x, xr);
+    wait_x<M>(xr);
+
+    u32x4 bm[4] = {};
+    SgBuf g[2] = {};
+    // chunked stage positions: chunk and first row of the unit of the step each stage handles
+    int cB = 0, rB = row_begin, cS = 0, rS = row_begin, cD = 0, rD = row_begin;
+
+    for (int it = 0; 4 * it - 4 < T; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int h = 4 * it + j;
+            // ---- decode step h - 4 (buffers bm[j], g[j & 1]) ----
+            {
+                const int s = h - 4;
+                const bool live = s >= 0 && s < T;
+                int acc[M] = {};
+                if (live) decode<M>(bm[j], g[j & 1], xr, lds, laneoff, acc);
+                const int slot = (j + 4 - 4) % NB;
+                if constexpr (!CHUNKED) {
+                    const int row0 = row_begin + s * x.R;
+                    const bool va = live && (lane < x.R * x.G) &&
+                                    row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
+                    emit<M, ACC, NB>(x, acc, g[j & 1].scale, tile, slot, false, va ? voff_acc : kOffOff,
+                                     live ? (uint32_t)row0 * (uint32_t)x.ng * 4u : kDeadS);
+                    if constexpr (!ACC) {
+                        if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
+                    }
                 } else {
-                    red_acc[(mi * NB + ur) * 32 + gi] = v;
-                    if (mi == 0) red_sc[ur * 32 + gi] = S[st].scale;
+                    const int row = rD + slot;
+                    const int gc = cD == x.nch - 1 ? x.glast : 64;
+                    const bool va = live && lane < gc && row < row_end;
+                    emit<M, ACC, NB>(x, acc, g[j & 1].scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                                     live ? ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u : kDeadS);
+                    if (slot == NB - 1) {
+                        if constexpr (!ACC) reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
+                        if (live) {
+                            if (++cD == x.nch) {
+                                cD = 0;
+                                rD += NB;
+                            }
+                        }
+                        TG_SCHED_FENCE();
+                        // the next decode pass's x slice, ahead of this half-step's prefetches
+                        const int gcn = cD == x.nch - 1 ? x.glast : 64;
+                        load_x<M>(x, lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff, xr);
+                    }
                 }
             }
-        }
-    }
-    if (!ACC) {
-        // Row rj's G group terms are summed by the LPR lanes of segment rj.
-        constexpr int LPR = 64 / NB;                     // lanes per row
-        constexpr int EPL = LPR >= 32 ? 1 : 32 / LPR;    // term slots per lane
-        const int rj = lane / LPR;
-        const int e0 = (lane % LPR) * EPL;               // (one row: lanes 32..63 have no slot)
-        double sc[EPL];
+            TG_SCHED_FENCE();
+            // ---- signs of step h - 2 (bitmap bm[(j + 2) & 3] -> g[j & 1]) ----
+            {
+                const int s = h - 2;
+                const bool live = s >= 0 && s < T;
+                if constexpr (!CHUNKED) {
+                    const int row0 = row_begin + s * x.R;
+                    const uint32_t total = stage_signs<ACC>(x, bm[(j + 2) & 3], cur, live, voff_sc,
+                                                            (uint32_t)row0 * (uint32_t)x.ng * 2u, g[j & 1]);
+                    if (live) cur += total;
+                } else {
+                    const int slot = (j + 4 - 2) % NB;
+                    if (slot == 0 && live && cS == 0) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) sc[e] = (double)half_bits_to_float(red_sc[rj * 32 + min(e0 + e, 31)]);
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-            double t = 0.0;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                if (e0 + e < g.G) t += sc[e] * (double)red_acc[(mi * NB + rj) * 32 + min(e0 + e, 31)];
-            t = seg_sum_f64(t, LPR);
-            const double rowsum = __shfl(t, (min(lane, NB - 1) + 1) * LPR - 1, 64);
-            yv[mi] += lane < nrows ? rowsum : 0.0;
+                        for (int r = 0; r < NB; ++r) ccur[r] = (uint32_t)__builtin_amdgcn_readlane((int)ro, r);
+                    }
+                    const uint32_t total = stage_signs<ACC>(
+                        x, bm[(j + 2) & 3], ccur[slot], live, voff_sc,
+                        ((uint32_t)(rS + slot) * (uint32_t)x.ng + (uint32_t)cS * 64u) * 2u, g[j & 1]);
+                    if (live) {
+                        ccur[slot] += total;
+                        if (slot == NB - 1 && ++cS == x.nch) {
+                            cS = 0;
+                            rS += NB;
+                        }
+                    }
+                }
+            }
+            TG_SCHED_FENCE();
+            // ---- bitmap of step h -> bm[j] ----
+            {
+                const int s = h;
+                const bool live = s < T;
+                if constexpr (!CHUNKED) {
+                    const int row0 = row_begin + s * x.R;
+                    bm[j] = ld4(x.rbm, voff_bm, live ? (uint32_t)row0 * kb : kDeadS);
+                } else {
+                    const int slot = j % NB;
+                    const int gc = cB == x.nch - 1 ? x.glast : 64;
+                    bm[j] = ld4(x.rbm, lane < gc ? voff_bm : kOffOff,
+                                live ? (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u : kDeadS);
+                    if (slot == 0) {
+                        // the unit's row-index entries, for its first chunk pass
+                        ro = ld1(x.rro, lane < NB ? (uint32_t)lane * 4u : kOffOff,
+                                 live && cB == 0 ? (uint32_t)rB * 4u : kDeadS);
+                    }
+                    if (live && slot == NB - 1 && ++cB == x.nch) {
+                        cB = 0;
+                        rB += NB;
+                    }
+                }
+            }
+            TG_SCHED_FENCE();
         }
     }
 }
 
 template <int M, bool ACC, int NB>
-__global__ __launch_bounds__(kBlock) void bitcos_gemv_kernel(GroupArgs ga) {
-    __shared__ uint4 s_ent4[(kByteLutEntries + 1) / 2];
-    __shared__ uint32_t s_base8[256];
-    __shared__ int32_t s_red_acc[kWaves][ACC ? 1 : M * NB * 32];
-    __shared__ uint16_t s_red_sc[kWaves][ACC ? 2 : NB * 32];
+__device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, const char *lds, double *tile) {
+    if (p.nch == 1)
+        run_loop<M, ACC, NB, false>(p, u0, u1, lds, tile);
+    else
+        run_loop<M, ACC, NB, true>(p, u0, u1, lds, tile);
+}
+
+template <int M, bool ACC>
+__global__ __launch_bounds__(Cfg<M>::BLOCK) void bitcos_gemv_kernel(GroupArgs ga) {
+    constexpr int NB = Cfg<M>::NB, WAVES = Cfg<M>::WAVES, BLOCK = Cfg<M>::BLOCK;
+    __shared__ uint4 s_tab[kTabBytes / 16];
+    __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     {
-        const uint4 *src = reinterpret_cast<const uint4 *>(kByteLut.ent);
-        for (int i = threadIdx.x; i < (kByteLutEntries + 1) / 2; i += kBlock) s_ent4[i] = src[i];
-        if (threadIdx.x < 256) s_base8[threadIdx.x] = kByteLut.base8[threadIdx.x];
+        uint2 *info = reinterpret_cast<uint2 *>(s_tab);
+        for (int i = threadIdx.x; i < 256 * 32; i += BLOCK)
+            info[i] = make_uint2(kTables.info[i >> 5][0], kTables.info[i >> 5][1]);
+        const uint4 *src = reinterpret_cast<const uint4 *>(kTables.ent);
+        for (int i = threadIdx.x; i < (kEntries + 1) / 2; i += BLOCK) s_tab[kEntOff / 16 + i] = src[i];
     }
     __syncthreads();
-    const LutView lut{reinterpret_cast<const char *>(s_ent4), reinterpret_cast<const char *>(s_base8)};
+    const char *lds = reinterpret_cast<const char *>(s_tab);
 
     // The wave index is uniform across the wave: say so, so that all unit bookkeeping lives in
-    // scalar registers and the loops are not compiled as divergent.
+    // scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int lane = threadIdx.x & 63;
-    int32_t *red_acc = s_red_acc[wave];
-    uint16_t *red_sc = s_red_sc[wave];
-    // Blocks are dealt to the XCDs round-robin; renumber them so that consecutive virtual blocks
-    // sit on one XCD. Each wave takes a contiguous range of units (adjacent rows share sign-stream
-    // lines and x stays hot in its XCD's L2).
+    double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
+    // Blocks are dealt to the XCDs round-robin; renumber them so that consecutive virtual blocks sit
+    // on one XCD (its L2 then sees neighbouring rows' sign-stream lines).
     const int nblk = gridDim.x;
     const int vblk = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int vw = vblk * kWaves + wave;
     int u, u_end, pi;
     if (ga.ranges) {
+        const int vw = vblk * WAVES + wave;
         u = uniform_i32(ga.ranges[vw].begin);
         u_end = uniform_i32(ga.ranges[vw].end);
         pi = uniform_i32(ga.ranges[vw].problem);
     } else {
-        const int nw = nblk * kWaves;
+        // one GEMV: shares dealt across blocks first, so that a small GEMV still spreads over CUs
+        const int nw = nblk * WAVES;
+        const int vw = wave * nblk + vblk;
         const int share = (ga.units + nw - 1) / nw;
         u = min(vw * share, ga.units);
         u_end = min(u + share, ga.units);
         pi = 0;
     }
-    if (u >= u_end) return;
-
-    Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
-    const bool more = ga.table && pi + 1 < ga.count;
-    Problem pn = more ? uniform_problem(ga.table[pi + 1]) : p;  // next GEMV, fetched ahead
-    int c = 0;
-    uint32_t cur_v = 0;
-    double yv[M];
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi) yv[mi] = 0.0;
-
-    Batch<M, NB> cur;
-    issue_batch<M, NB>(p, u, c, true, cur);
-    while (true) {
-        // position of the next batch: the unit's next chunk, or the next unit's first chunk
-        const bool last_chunk = c + 1 >= nchunks_of(p);
-        int u2 = u, c2 = c + 1;
-        bool switch_p = false;
-        if (last_chunk) {
-            u2 = u + 1;
-            c2 = 0;
-            switch_p = ga.table && pi + 1 < ga.count && u2 >= pn.unit_begin;
-        }
-        const bool has_next = u2 < u_end;
-        const Problem &p2 = switch_p ? pn : p;
-
-        Staged S[NB];
-        stage_batch<M, ACC, NB>(p, u, c, cur, cur_v, S);
-        TG_SCHED_FENCE();
-        Batch<M, NB> nxt;
-        issue_batch<M, NB>(has_next ? p2 : p, has_next ? u2 : u, has_next ? c2 : c, has_next, nxt);
-        TG_SCHED_FENCE();
-        finish_batch<M, ACC, NB>(p, u, c, S, cur.xr, lut, red_acc, red_sc, yv);
-
-        if (last_chunk) {
-            const int row0 = (u - p.unit_begin) * NB;
-            if (!ACC && lane < min(NB, p.n - row0)) {
-#pragma unroll
-                for (int mi = 0; mi < M; ++mi) p.y[(size_t)mi * p.n + row0 + lane] = (float)yv[mi];
-            }
-#pragma unroll
-            for (int mi = 0; mi < M; ++mi) yv[mi] = 0.0;
-        }
-        if (!has_next) break;
-        if (switch_p) {
-            ++pi;
-            p = pn;
-            if (pi + 1 < ga.count) pn = uniform_problem(ga.table[pi + 1]);
-        }
-        u = u2;
-        c = c2;
-        cur = nxt;
+    while (u < u_end) {
+        if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
+        const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        const int u1 = min(u_end, p.unit_begin + p.nunits);
+        if (u < u1) run_problem<M, ACC, NB>(p, u, u1, lds, tile);
+        u = max(u, u1);
+        ++pi;
     }
 }
 
-template <int M, int NB>
-hipError_t launch_nb(const GroupArgs &g, bool acc_out, hipStream_t s) {
+template <int M>
+hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
+    constexpr int WAVES = Cfg<M>::WAVES;
     int blocks;
     if (g.ranges) {
-        blocks = g.waves / kWaves;  // the table's per-wave ranges fix the grid
+        if (g.waves % WAVES) return hipErrorInvalidValue;
+        blocks = g.waves / WAVES;  // the table's per-wave ranges fix the grid
     } else {
-        // one wave per unit up to two 512-thread blocks per CU (the 53 KB decode table allows no
-        // more), a multiple of 8 so that every XCD gets the same number
-        blocks = std::min((g.units + kWaves - 1) / kWaves, device_cus() * kBitcosBlocksPerCu);
+        // at most one block per CU (the decode tables take most of the LDS); a multiple of 8 so that
+        // every XCD gets the same number
+        blocks = std::min(g.units, device_cus());
         if (blocks > 8) blocks = blocks / 8 * 8;
         blocks = std::max(1, blocks);
     }
     if (acc_out)
-        hipLaunchKernelGGL((bitcos_gemv_kernel<M, true, NB>), dim3(blocks), dim3(kBlock), 0, s, g);
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, true>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
     else
-        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, NB>), dim3(blocks), dim3(kBlock), 0, s, g);
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
     return hipGetLastError();
-}
-
-// Largest batch (rows per unit) that keeps a wave within 128 registers, so that two 512-thread
-// blocks fit a CU: 4 rows for one activation row, 2 for two, 1 for three.
-template <int M>
-constexpr int kMaxRowsPerUnit = M == 1 ? 4 : M == 2 ? 2 : 1;
-
-template <int M>
-hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    if (g.rows_per_unit > kMaxRowsPerUnit<M>) return hipErrorInvalidValue;
-    switch (g.rows_per_unit) {
-        case 1: return launch_nb<M, 1>(g, acc_out, s);
-        case 2:
-            if constexpr (kMaxRowsPerUnit<M> >= 2) return launch_nb<M, 2>(g, acc_out, s);
-            return hipErrorInvalidValue;
-        case 4:
-            if constexpr (kMaxRowsPerUnit<M> >= 4) return launch_nb<M, 4>(g, acc_out, s);
-            return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-    }
 }
 
 }  // namespace
 
-// Rows per unit for BITCOS: a power of two (the batch size). Enough units to give every wave slot
-// one, but at least the rows one tail step covers (so tail lanes are not left idle), and at most
-// what keeps a wave within 128 registers. `table`: a grouped launch, where work is plentiful and
-// the largest batch is used.
-int bitcos_rows_per_unit(int64_t n, int64_t k, int m, bool table) {
-    const int64_t cap = m == 1 ? kMaxRowsPerUnit<1> : m == 2 ? kMaxRowsPerUnit<2> : kMaxRowsPerUnit<3>;
-    if (table) return (int)cap;
-    const int64_t slots = (int64_t)device_cus() * kBitcosBlocksPerCu * kWaves;
-    const int64_t kd = k >> 5;
-    const int64_t tail = kd % kChunkDwords;
-    const int64_t L = tail >> 1;
-    const int64_t rps = (tail && (L & (L - 1)) == 0) ? 64 / L : 1;
-    int64_t rpu = (n + slots - 1) / slots;
-    rpu = std::max(rpu, std::min(rps, cap));
-    int nb = 1;
-    while (nb < rpu && nb < cap) nb <<= 1;
-    return nb;
+int bitcos_waves_per_cu(int m) {
+    return m == 1 ? Cfg<1>::WAVES : m == 2 ? Cfg<2>::WAVES : Cfg<3>::WAVES;
+}
+
+void bitcos_geometry(Problem &p, int m) {
+    const int nb = m == 1 ? Cfg<1>::NB : m == 2 ? Cfg<2>::NB : Cfg<3>::NB;
+    p.ng = p.k / 128;
+    p.nch = (p.ng + 63) / 64;
+    if (p.nch == 1) {
+        p.G = p.ng;
+        p.R = 64 / p.ng;
+        p.glast = p.ng;
+        p.nbu = std::max(1, std::min(nb, 64 / p.R));
+    } else {
+        p.G = 64;
+        p.R = 1;
+        p.glast = p.ng - 64 * (p.nch - 1);
+        p.nbu = nb;
+    }
+    p.rpu = p.nbu * p.R;
+    p.gmagic = (65536u + (uint32_t)p.G - 1) / (uint32_t)p.G;
+    p.rmagic = (65536u + (uint32_t)p.R - 1) / (uint32_t)p.R;
+    p.nunits = (p.n + p.rpu - 1) / p.rpu;
 }
 
 hipError_t launch_bitcos(const GroupArgs &g, bool acc_out, hipStream_t s) {

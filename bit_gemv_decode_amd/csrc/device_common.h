@@ -137,6 +137,16 @@ __device__ __forceinline__ Problem uniform_problem(const Problem &q) {
     p.n = uniform_i32(q.n);
     p.k = uniform_i32(q.k);
     p.unit_begin = uniform_i32(q.unit_begin);
+    p.nunits = uniform_i32(q.nunits);
+    p.ng = uniform_i32(q.ng);
+    p.nch = uniform_i32(q.nch);
+    p.G = uniform_i32(q.G);
+    p.R = uniform_i32(q.R);
+    p.glast = uniform_i32(q.glast);
+    p.nbu = uniform_i32(q.nbu);
+    p.rpu = uniform_i32(q.rpu);
+    p.gmagic = uniform_u32(q.gmagic);
+    p.rmagic = uniform_u32(q.rmagic);
     p.reserved = 0;
     return p;
 }
