@@ -107,6 +107,12 @@ struct Cfg {
 constexpr uint32_t kOffOff = 0x80000000u;
 constexpr uint32_t kDeadS = 0x7FFFFFF0u;
 
+// live ? v : kDeadS without a branch (the compiler turns a select over a product into a branch).
+__device__ __forceinline__ uint32_t live_or_dead(bool live, uint32_t v) {
+    const uint32_t m = 0u - (uint32_t)live;
+    return (v & m) | (kDeadS & ~m);
+}
+
 __device__ __forceinline__ u32x4 ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
@@ -121,12 +127,11 @@ __device__ __forceinline__ void st1(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32
 }
 
 // Sign stage of one step: for each pair of bitmap dwords, the four sign-stream dwords holding bits
-// [pos - 3, pos + 93) (pos = the pair's first sign), the funnel-shift amount into them, and the sign
-// count of the pair's first dword; plus the group scale.
+// [pos - 3, pos + 93) (pos = the pair's first sign); the two funnel-shift amounts into them (bytes 0
+// and 1 of `sh`); the group scale.
 struct SgBuf {
     u32x4 s[2];
-    uint32_t sh[2];
-    uint32_t pc[2];
+    uint32_t sh;
     uint16_t scale;
 };
 
@@ -150,43 +155,49 @@ __device__ __forceinline__ uint32_t stage_signs(const Ctx &x, const u32x4 &bm, u
     // window start = first sign - 3, biased by +32 (the sign resource starts one dword early)
     const uint32_t b0 = cur + 29u + incl - pc;
     const uint32_t b2 = b0 + t2;
-    const uint32_t sd = live ? 0u : kDeadS;
+    const uint32_t sd = live_or_dead(live, 0u);
     g.s[0] = ld4(x.rsg, (b0 >> 5) << 2, sd);
     g.s[1] = ld4(x.rsg, (b2 >> 5) << 2, sd);
-    g.sh[0] = b0;
-    g.sh[1] = b2;
-    g.pc[0] = t1;
-    g.pc[1] = t3 - t2;
-    g.scale = ACC ? (uint16_t)0 : ldh(x.rsc, voff_sc, live ? soff_sc : kDeadS);
+    g.sh = __builtin_amdgcn_perm(b2, b0, 0x0C0C0400u);  // byte 0: b0, byte 1: b2 (low 5 bits used)
+    g.scale = ACC ? (uint16_t)0 : ldh(x.rsc, voff_sc, live_or_dead(live, soff_sc));
     return total;
 }
 
-// Eight presence bytes' worth (one bitmap dword) of decode: lo/hi hold the sign-stream bits starting
-// 3 bits before the dword's first sign.
+// Two bitmap dwords (64 weights) of decode. lo*/hi* hold the sign-stream bits starting 3 bits before
+// each dword's first sign. All eight per-byte (mask, base) reads go out first, then all eight entry
+// reads, then the dot products: two LDS round trips for the 64 weights.
 template <int M>
-__device__ __forceinline__ void decode_dword(uint32_t bmd, uint32_t lo, uint32_t hi, const uint32_t (&xr)[M][32],
-                                             int d, const char *lds, uint32_t laneoff, int (&acc)[M]) {
-    uint2 info[4];
+__device__ __forceinline__ void decode_pair(uint32_t bma, uint32_t bmb, uint32_t loa, uint32_t hia, uint32_t lob,
+                                            uint32_t hib, const uint32_t (&xr)[M][32], int d, const char *lds,
+                                            uint32_t laneoff, int (&acc)[M]) {
+    uint2 info[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
         // (pb << 8) | laneoff: copy (lane % 32) of presence byte pb's (mask, base)
-        const uint32_t ia = __builtin_amdgcn_perm(bmd, laneoff, 0x0C0C0000u | ((4u + i) << 8));
+        const uint32_t ia = __builtin_amdgcn_perm(i < 4 ? bma : bmb, laneoff, 0x0C0C0000u | ((4u + (i & 3)) << 8));
         info[i] = *reinterpret_cast<const uint2 *>(lds + ia);
     }
-    uint32_t cur = 0;
+    uint2 e[8];
+    uint32_t ca = 0, cb = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // the byte's signs sit at bits 3 .. 3 + popcount of the shifted window
-        const uint32_t w = i == 0 ? lo : __builtin_amdgcn_alignbit(hi, lo, cur);
-        const uint32_t ea = (w & info[i].x) | info[i].y;
-        const uint2 e = *reinterpret_cast<const uint2 *>(lds + ea);
-        if (i < 3) cur = __builtin_popcount(info[i].x) + cur;
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-            acc[mi] = dot4(e.x, xr[mi][8 * d + 2 * i], acc[mi]);
-            acc[mi] = dot4(e.y, xr[mi][8 * d + 2 * i + 1], acc[mi]);
+        // byte i's signs sit at bits 3 .. 3 + popcount of the window shifted by the bytes before it
+        const uint32_t wa = i == 0 ? loa : __builtin_amdgcn_alignbit(hia, loa, ca);
+        const uint32_t wb = i == 0 ? lob : __builtin_amdgcn_alignbit(hib, lob, cb);
+        e[i] = *reinterpret_cast<const uint2 *>(lds + ((wa & info[i].x) | info[i].y));
+        e[4 + i] = *reinterpret_cast<const uint2 *>(lds + ((wb & info[4 + i].x) | info[4 + i].y));
+        if (i < 3) {
+            ca = __builtin_popcount(info[i].x) + ca;
+            cb = __builtin_popcount(info[4 + i].x) + cb;
         }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+            acc[mi] = dot4(e[i].x, xr[mi][8 * d + 2 * i], acc[mi]);
+            acc[mi] = dot4(e[i].y, xr[mi][8 * d + 2 * i + 1], acc[mi]);
+        }
 }
 
 // int32 sums of the lane's 128 weights times x, per activation row.
@@ -198,14 +209,15 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const u32x4 s = g.s[q];
-        const uint32_t a0 = __builtin_amdgcn_alignbit(s.y, s.x, g.sh[q]);
-        const uint32_t a1 = __builtin_amdgcn_alignbit(s.z, s.y, g.sh[q]);
-        const uint32_t a2 = __builtin_amdgcn_alignbit(s.w, s.z, g.sh[q]);
-        // the pair's second dword starts pc (0 .. 32) bits later
+        const uint32_t sh = q == 0 ? g.sh : g.sh >> 8;
+        const uint32_t a0 = __builtin_amdgcn_alignbit(s.y, s.x, sh);
+        const uint32_t a1 = __builtin_amdgcn_alignbit(s.z, s.y, sh);
+        const uint32_t a2 = __builtin_amdgcn_alignbit(s.w, s.z, sh);
+        // the pair's second dword starts popcount(first dword) = 0 .. 32 bits later
+        const uint32_t pc = __builtin_popcount(q == 0 ? bm.x : bm.z);
         const uint64_t w01 = ((uint64_t)a1 << 32) | a0, w12 = ((uint64_t)a2 << 32) | a1;
-        const uint32_t b0 = (uint32_t)(w01 >> g.pc[q]), b1 = (uint32_t)(w12 >> g.pc[q]);
-        decode_dword<M>(q == 0 ? bm.x : bm.z, a0, a1, xr, 2 * q, lds, laneoff, acc);
-        decode_dword<M>(q == 0 ? bm.y : bm.w, b0, b1, xr, 2 * q + 1, lds, laneoff, acc);
+        const uint32_t b0 = (uint32_t)(w01 >> pc), b1 = (uint32_t)(w12 >> pc);
+        decode_pair<M>(q == 0 ? bm.x : bm.z, q == 0 ? bm.y : bm.w, a0, a1, b0, b1, xr, 2 * q, lds, laneoff, acc);
     }
 }
 
@@ -307,12 +319,13 @@ __device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t
     }
 }
 
-// Pipeline over the steps of units [u0, u1) of one GEMV. In half-step h the bitmap of step h is
-// loaded, the signs of step h - 2 are located and loaded, and step h - 4 is decoded. The loop body
-// holds four half-steps, so every stage buffer has a fixed register home (bitmaps rotate over four,
-// sign windows over two) and no register with a load in flight is ever copied. Each stage runs
-// unconditionally (outside the live range its loads use dead offsets), apart from decode work that
-// loads nothing.
+// Pipeline over the steps of units [u0, u1) of one GEMV. In half-step h, step h - 4 is decoded, the
+// bitmap of step h is loaded, and the signs of step h - 1 are located and loaded: a bitmap has one
+// decode's time to arrive, a sign window three (the bitmap load goes first, so that waiting for it
+// never waits for younger sign loads). The loop body holds four half-steps, so every stage
+// buffer has a fixed register home (bitmaps and sign windows rotate over four) and no register with
+// a load in flight is ever copied. Each stage runs unconditionally (outside the live range its loads
+// use dead offsets), apart from decode work that loads nothing.
 //
 // Single-chunk GEMVs (ng <= 64): step s covers rows row_begin + s*R .. + R - 1, a unit NB steps; the
 // sign cursor runs on from step to step. Chunked GEMVs: a unit is NB rows; its steps go chunk by
@@ -374,27 +387,31 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     wait_x<M>(xr);
 
     u32x4 bm[4] = {};
-    SgBuf g[2] = {};
+    SgBuf g[4] = {};
     // chunked stage positions: chunk and first row of the unit of the step each stage handles
     int cB = 0, rB = row_begin, cS = 0, rS = row_begin, cD = 0, rD = row_begin;
 
+    // Uniform branches cost each wave an instruction-fetch bubble, so the loop body has none: every
+    // stage runs on every half-step, dead steps (pipeline fill and drain) decode whatever their
+    // buffers hold into tile slots that a live step overwrites before use, and only their stores and
+    // loads are switched off (dead offsets). Scalar state advances with selects.
     for (int it = 0; 4 * it - 4 < T; ++it) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int h = 4 * it + j;
-            // ---- decode step h - 4 (buffers bm[j], g[j & 1]) ----
+            // ---- decode step h - 4 (buffers bm[j], g[j]) ----
             {
                 const int s = h - 4;
                 const bool live = s >= 0 && s < T;
-                int acc[M] = {};
-                if (live) decode<M>(bm[j], g[j & 1], xr, lds, laneoff, acc);
-                const int slot = (j + 4 - 4) % NB;
+                int acc[M];
+                decode<M>(bm[j], g[j], xr, lds, laneoff, acc);
+                const int slot = j % NB;
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && (lane < x.R * x.G) &&
                                     row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
-                    emit<M, ACC, NB>(x, acc, g[j & 1].scale, tile, slot, false, va ? voff_acc : kOffOff,
-                                     live ? (uint32_t)row0 * (uint32_t)x.ng * 4u : kDeadS);
+                    emit<M, ACC, NB>(x, acc, g[j].scale, tile, slot, false, va ? voff_acc : kOffOff,
+                                     live_or_dead(live, (uint32_t)row0 * (uint32_t)x.ng * 4u));
                     if constexpr (!ACC) {
                         if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
                     }
@@ -402,48 +419,17 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                     const int row = rD + slot;
                     const int gc = cD == x.nch - 1 ? x.glast : 64;
                     const bool va = live && lane < gc && row < row_end;
-                    emit<M, ACC, NB>(x, acc, g[j & 1].scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
-                                     live ? ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u : kDeadS);
-                    if (slot == NB - 1) {
+                    emit<M, ACC, NB>(x, acc, g[j].scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                                     live_or_dead(live, ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u));
+                    if (slot == NB - 1) {  // static: last step of a chunk pass
                         if constexpr (!ACC) reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
-                        if (live) {
-                            if (++cD == x.nch) {
-                                cD = 0;
-                                rD += NB;
-                            }
-                        }
+                        const bool wrap = live && cD == x.nch - 1;
+                        rD = wrap ? rD + NB : rD;
+                        cD = live ? (wrap ? 0 : cD + 1) : cD;
                         TG_SCHED_FENCE();
                         // the next decode pass's x slice, ahead of this half-step's prefetches
                         const int gcn = cD == x.nch - 1 ? x.glast : 64;
                         load_x<M>(x, lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff, xr);
-                    }
-                }
-            }
-            TG_SCHED_FENCE();
-            // ---- signs of step h - 2 (bitmap bm[(j + 2) & 3] -> g[j & 1]) ----
-            {
-                const int s = h - 2;
-                const bool live = s >= 0 && s < T;
-                if constexpr (!CHUNKED) {
-                    const int row0 = row_begin + s * x.R;
-                    const uint32_t total = stage_signs<ACC>(x, bm[(j + 2) & 3], cur, live, voff_sc,
-                                                            (uint32_t)row0 * (uint32_t)x.ng * 2u, g[j & 1]);
-                    if (live) cur += total;
-                } else {
-                    const int slot = (j + 4 - 2) % NB;
-                    if (slot == 0 && live && cS == 0) {
-#pragma unroll
-                        for (int r = 0; r < NB; ++r) ccur[r] = (uint32_t)__builtin_amdgcn_readlane((int)ro, r);
-                    }
-                    const uint32_t total = stage_signs<ACC>(
-                        x, bm[(j + 2) & 3], ccur[slot], live, voff_sc,
-                        ((uint32_t)(rS + slot) * (uint32_t)x.ng + (uint32_t)cS * 64u) * 2u, g[j & 1]);
-                    if (live) {
-                        ccur[slot] += total;
-                        if (slot == NB - 1 && ++cS == x.nch) {
-                            cS = 0;
-                            rS += NB;
-                        }
                     }
                 }
             }
@@ -454,20 +440,52 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                 const bool live = s < T;
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
-                    bm[j] = ld4(x.rbm, voff_bm, live ? (uint32_t)row0 * kb : kDeadS);
+                    bm[j] = ld4(x.rbm, voff_bm, live_or_dead(live, (uint32_t)row0 * kb));
                 } else {
                     const int slot = j % NB;
                     const int gc = cB == x.nch - 1 ? x.glast : 64;
                     bm[j] = ld4(x.rbm, lane < gc ? voff_bm : kOffOff,
-                                live ? (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u : kDeadS);
+                                live_or_dead(live, (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u));
                     if (slot == 0) {
                         // the unit's row-index entries, for its first chunk pass
                         ro = ld1(x.rro, lane < NB ? (uint32_t)lane * 4u : kOffOff,
-                                 live && cB == 0 ? (uint32_t)rB * 4u : kDeadS);
+                                 live_or_dead(live && cB == 0, (uint32_t)rB * 4u));
                     }
-                    if (live && slot == NB - 1 && ++cB == x.nch) {
-                        cB = 0;
-                        rB += NB;
+                    if (slot == NB - 1) {
+                        const bool wrap = live && cB == x.nch - 1;
+                        rB = wrap ? rB + NB : rB;
+                        cB = live ? (wrap ? 0 : cB + 1) : cB;
+                    }
+                }
+            }
+            TG_SCHED_FENCE();
+            // ---- signs of step h - 1 (bitmap bm[(j + 3) & 3] -> g[(j + 3) & 3]) ----
+            {
+                const int s = h - 1;
+                const bool live = s >= 0 && s < T;
+                if constexpr (!CHUNKED) {
+                    const int row0 = row_begin + s * x.R;
+                    const uint32_t total = stage_signs<ACC>(x, bm[(j + 3) & 3], cur, live, voff_sc,
+                                                            (uint32_t)row0 * (uint32_t)x.ng * 2u, g[(j + 3) & 3]);
+                    cur += live ? total : 0u;
+                } else {
+                    const int slot = (j + 3) % NB;
+                    if (slot == 0) {  // static: a chunk pass starts; its first pass takes the row index
+                        const bool first = live && cS == 0;
+#pragma unroll
+                        for (int r = 0; r < NB; ++r) {
+                            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)ro, r);
+                            ccur[r] = first ? v : ccur[r];
+                        }
+                    }
+                    const uint32_t total = stage_signs<ACC>(
+                        x, bm[(j + 3) & 3], ccur[slot], live, voff_sc,
+                        ((uint32_t)(rS + slot) * (uint32_t)x.ng + (uint32_t)cS * 64u) * 2u, g[(j + 3) & 3]);
+                    ccur[slot] += live ? total : 0u;
+                    if (slot == NB - 1) {
+                        const bool wrap = live && cS == x.nch - 1;
+                        rS = wrap ? rS + NB : rS;
+                        cS = live ? (wrap ? 0 : cS + 1) : cS;
                     }
                 }
             }
