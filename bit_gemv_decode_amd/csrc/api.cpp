@@ -41,11 +41,6 @@ Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, co
     return p;
 }
 
-int rows_per_unit(int fmt, int64_t n, int64_t k, int m, bool table) {
-    (void)fmt, (void)n, (void)k, (void)m, (void)table;
-    return 1;
-}
-
 }  // namespace tg
 
 using namespace tg;
@@ -54,10 +49,14 @@ namespace {
 
 constexpr int kVectorMaxM = 3;  // activation rows one vector-path launch handles
 
-// The kernels address every section with 32-bit byte offsets.
+// The kernels address each section with 32-bit byte offsets, and their switched-off accesses use
+// offsets of 2^31 and more: bitmaps/codes, scales and outputs must stay below 1 GiB, sign windows
+// (positions counted in bits) below 512 MiB.
 bool fits_offsets(const tg_desc *d, int32_t m) {
-    const uint64_t lim = 0xFFFFFFFFull;
-    return d->bytes_codes <= lim && d->bytes_signs <= lim && (uint64_t)d->n * (uint64_t)(d->k / TG_GROUP) * 2 <= lim &&
+    const uint64_t lim = 1ull << 30;
+    const uint64_t ng = (uint64_t)(d->k / TG_GROUP);
+    return d->bytes_codes < lim && d->bytes_signs < (lim >> 1) && (uint64_t)d->n * ng * 4 * (uint64_t)m < lim &&
+           (uint64_t)d->n * 4 * (uint64_t)m < lim &&
            (uint64_t)m * (uint64_t)d->k <= lim;
 }
 
@@ -91,13 +90,8 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
-        if (desc->fmt == TG_FMT_BITCOS) {
-            bitcos_geometry(g.one, mt);
-            g.rows_per_unit = g.one.rpu;
-        } else {
-            g.rows_per_unit = rows_per_unit(desc->fmt, n, k, mt, false);
-            g.one.nunits = (int32_t)((n + g.rows_per_unit - 1) / g.rows_per_unit);
-        }
+        gemv_geometry(g.one, mt);
+        g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
         if (launch(desc->fmt, g, acc_out, s) != hipSuccess) return TG_EHIP;
     }
@@ -118,10 +112,10 @@ extern "C" int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t
 
 namespace {
 
-// Waves of a persistent BITCOS launch on this device for m activation rows; a plan's per-wave
-// ranges are sized for it (the table has room for the largest count).
-int plan_waves(int m) { return device_cus() * bitcos_waves_per_cu(m); }
-int plan_waves_max() { return device_cus() * kBitcosMaxWavesPerCu; }
+// Waves of a persistent launch on this device for m activation rows; a plan's per-wave ranges are
+// sized for it (the table has room for the largest count).
+int plan_waves(int m) { return device_cus() * gemv_waves_per_cu(m); }
+int plan_waves_max() { return device_cus() * kMaxWavesPerCu; }
 
 size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
 
@@ -140,7 +134,7 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
     if (((uintptr_t)table & 15) || table_bytes < tg_plan_table_bytes(count)) return TG_EINVAL;
     const int fmt = descs[0].fmt;
     std::vector<Problem> host((size_t)count);
-    int rpu = 1;  // formats other than BITCOS: one value for all GEMVs
+    int rpu = 1;  // largest rows per unit (informational)
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
         int e = check_desc(d, 0);
@@ -151,7 +145,6 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         if (acc_mode ? (!acc[i] || ((uintptr_t)acc[i] & 3))
                      : (!y[i] || !scales[i] || ((uintptr_t)y[i] & 3) || ((uintptr_t)scales[i] & 1)))
             return TG_EINVAL;
-        rpu = std::max(rpu, rows_per_unit(fmt, d->n, d->k, m, true));
     }
     int64_t units = 0;
     double total_cost = 0;
@@ -160,16 +153,14 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr);
         host[i].unit_begin = (int32_t)units;
-        if (fmt == TG_FMT_BITCOS)
-            bitcos_geometry(host[i], m);
-        else
-            host[i].nunits = (int32_t)((d->n + rpu - 1) / rpu);
+        gemv_geometry(host[i], m);
+        rpu = std::max(rpu, (int)host[i].rpu);
         units += host[i].nunits;
         total_cost += (double)d->n * (double)d->k;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
     // Contiguous unit ranges per wave, balanced by cost (rows x k of each unit).
-    const int nw = fmt == TG_FMT_BITCOS ? plan_waves(m) : 1;
+    const int nw = plan_waves(m);
     std::vector<WaveRange> ranges((size_t)nw);
     {
         int32_t pi = 0;
@@ -181,7 +172,7 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
             const double target = total_cost * (double)(w + 1) / (double)nw;
             while (u < units) {
                 while (pi + 1 < count && u >= host[pi + 1].unit_begin) ++pi;
-                const int64_t prpu = fmt == TG_FMT_BITCOS ? host[pi].rpu : rpu;
+                const int64_t prpu = host[pi].rpu;
                 const int64_t row0 = (u - host[pi].unit_begin) * prpu;
                 const double cost = (double)std::min<int64_t>(prpu, host[pi].n - row0) * (double)host[pi].k;
                 if (done + 0.5 * cost > target && w + 1 < nw) break;
@@ -217,11 +208,9 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
-    if (plan->fmt == TG_FMT_BITCOS) {
-        if (plan->waves != plan_waves(plan->m)) return TG_EINVAL;  // built for another device
-        g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
-        g.waves = plan->waves;
-    }
+    if (plan->waves != plan_waves(plan->m)) return TG_EINVAL;  // built for another device
+    g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
+    g.waves = plan->waves;
     g.count = plan->count;
     g.units = plan->units;
     g.m = plan->m;

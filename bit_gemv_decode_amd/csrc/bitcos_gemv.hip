@@ -36,8 +36,7 @@
 //     out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
 
-#include "device_common.h"
-#include "tg_internal.h"
+#include "gemv_pipeline.h"
 
 namespace tg {
 namespace {
@@ -89,43 +88,6 @@ constexpr Tables make_tables() {
 
 __device__ const Tables kTables = make_tables();
 
-template <int M>
-struct Cfg {
-    static constexpr int NB = M == 3 ? 2 : 4;     // row bundles (steps per chunk pass) per unit
-    static constexpr int WAVES = M == 1 ? 16 : 8;  // waves per block (= per CU)
-    static constexpr int BLOCK = 64 * WAVES;
-};
-
-// Scheduling fence: the compiler may not move instructions across it. Keeps the loads of the
-// pipeline stages in program order, so that each wait covers exactly the loads it needs.
-#define TG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// Buffer offsets. A lane with nothing to read gets kOffOff as its own (vector) offset; a pipeline
-// stage with nothing to do gets kDeadS as its wave-uniform (scalar) offset. Either way the sum lies
-// beyond every resource (bitmaps, scales and outputs are limited to less than 1 GiB, sign windows to
-// less than 512 MiB) without wrapping, so the access returns zero and makes no memory request.
-constexpr uint32_t kOffOff = 0x80000000u;
-constexpr uint32_t kDeadS = 0x7FFFFFF0u;
-
-// live ? v : kDeadS without a branch (the compiler turns a select over a product into a branch).
-__device__ __forceinline__ uint32_t live_or_dead(bool live, uint32_t v) {
-    const uint32_t m = 0u - (uint32_t)live;
-    return (v & m) | (kDeadS & ~m);
-}
-
-__device__ __forceinline__ u32x4 ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint32_t ld1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint16_t ldh(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-__device__ __forceinline__ void st1(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
-}
-
 // Sign stage of one step: for each pair of bitmap dwords, the four sign-stream dwords holding bits
 // [pos - 3, pos + 93) (pos = the pair's first sign); the two funnel-shift amounts into them (bytes 0
 // and 1 of `sh`); the group scale.
@@ -133,12 +95,6 @@ struct SgBuf {
     u32x4 s[2];
     uint32_t sh;
     uint16_t scale;
-};
-
-// Wave-uniform per-GEMV values.
-struct Ctx {
-    __amdgpu_buffer_rsrc_t rbm, rsg, rsc, rro, rx, ry, racc;
-    int n, k, ng, nch, G, R, glast;
 };
 
 // Scan the step's bitmap popcounts and issue its sign-window and scale loads. `cur` is the stream
@@ -218,104 +174,6 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
         const uint64_t w01 = ((uint64_t)a1 << 32) | a0, w12 = ((uint64_t)a2 << 32) | a1;
         const uint32_t b0 = (uint32_t)(w01 >> pc), b1 = (uint32_t)(w12 >> pc);
         decode_pair<M>(q == 0 ? bm.x : bm.z, q == 0 ? bm.y : bm.w, a0, a1, b0, b1, xr, 2 * q, lds, laneoff, acc);
-    }
-}
-
-// x bytes of the lane's group (column col) for every activation row; lanes without a group read
-// nothing.
-template <int M>
-__device__ __forceinline__ void load_x(const Ctx &x, uint32_t voff, uint32_t (&xr)[M][32]) {
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const u32x4 v = ld4(x.rx, voff + 16u * j, (uint32_t)(mi * x.k));
-            xr[mi][4 * j] = v.x;
-            xr[mi][4 * j + 1] = v.y;
-            xr[mi][4 * j + 2] = v.z;
-            xr[mi][4 * j + 3] = v.w;
-        }
-}
-
-// x must have arrived before a loop starts: a loop entered with x as the newest loads would get
-// the waits compiled for that entry on every iteration.
-template <int M>
-__device__ __forceinline__ void wait_x(const uint32_t (&xr)[M][32]) {
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi)
-#pragma unroll
-        for (int j = 0; j < 32; j += 4) asm volatile("" ::"v"(xr[mi][j]));
-}
-
-// Lane roles in the unit-end reduction: the tile's rows are summed by lpr lanes each.
-struct Red {
-    int lpr;   // lanes per row (power of two)
-    int epl;   // tile terms per lane
-    int base;  // tile index of the lane's first term
-    int cnt;   // terms the lane sums (0 .. epl)
-    int rho;   // tile row of the lane
-    bool own;  // the lane ends up holding row rho's sum (last lane of its group, rho < rows)
-};
-
-__device__ __forceinline__ Red make_red(int rows, int R, int geff, uint32_t rmagic) {
-    const int lane = threadIdx.x & 63;
-    Red r;
-    int lg = 0;
-    while ((2 << lg) * rows <= 64) ++lg;  // largest power of two with lpr * rows <= 64
-    r.lpr = 1 << lg;
-    r.epl = (geff + r.lpr - 1) >> lg;
-    r.rho = lane >> lg;
-    const int pi = lane & (r.lpr - 1);
-    const int sb = (int)(((uint32_t)r.rho * rmagic) >> 16);  // step of the row
-    const int qb = r.rho - sb * R;
-    r.base = sb * 64 + qb * geff + pi * r.epl;
-    r.cnt = min(max(geff - pi * r.epl, 0), r.epl);
-    if (r.rho >= rows) r.cnt = 0;
-    r.own = r.rho < rows && pi == r.lpr - 1;
-    return r;
-}
-
-// Row sums of a finished tile, stored as fp32: tile row rho is output row row0 + rho (stored when
-// below row_end and `live`).
-template <int M, int NB>
-__device__ __forceinline__ void reduce_store(const Ctx &x, const Red &r, const double *tile, int row0, int row_end,
-                                             bool live) {
-    double yv[M];
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi) {
-        double t = 0.0;
-        for (int e = 0; e < r.epl; ++e)
-            if (e < r.cnt) t += tile[mi * NB * 64 + r.base + e];
-        yv[mi] = seg_sum_f64(t, r.lpr);
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int row = row0 + r.rho;
-    const bool own = live && r.own && row < row_end;
-#pragma unroll
-    for (int mi = 0; mi < M; ++mi)
-        st1(__builtin_bit_cast(uint32_t, (float)yv[mi]), x.ry, own ? (uint32_t)row * 4u : kOffOff,
-            (uint32_t)(mi * x.n) * 4u);
-}
-
-// Decode stage epilogue: the group terms (int32 sum times scale, fp64) go to tile slot `slot`
-// (added to what earlier chunks left there when `add`); accumulator outputs are stored directly.
-template <int M, bool ACC, int NB>
-__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t scale, double *tile, int slot,
-                                     bool add, uint32_t voff_acc, uint32_t soff_acc) {
-    const int lane = threadIdx.x & 63;
-    if constexpr (ACC) {
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi)
-            st1((uint32_t)acc[mi], x.racc, voff_acc, soff_acc + (uint32_t)(mi * x.n * x.ng) * 4u);
-    } else {
-        const double s = (double)half_bits_to_float(scale);
-#pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-            double *t = tile + mi * NB * 64 + slot * 64 + lane;
-            const double term = (double)acc[mi] * s;
-            *t = add ? *t + term : term;
-        }
     }
 }
 
@@ -521,25 +379,8 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void bitcos_gemv_kernel(GroupArgs ga
     // scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
-    // Blocks are dealt to the XCDs round-robin; renumber them so that consecutive virtual blocks sit
-    // on one XCD (its L2 then sees neighbouring rows' sign-stream lines).
-    const int nblk = gridDim.x;
-    const int vblk = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
     int u, u_end, pi;
-    if (ga.ranges) {
-        const int vw = vblk * WAVES + wave;
-        u = uniform_i32(ga.ranges[vw].begin);
-        u_end = uniform_i32(ga.ranges[vw].end);
-        pi = uniform_i32(ga.ranges[vw].problem);
-    } else {
-        // one GEMV: shares dealt across blocks first, so that a small GEMV still spreads over CUs
-        const int nw = nblk * WAVES;
-        const int vw = wave * nblk + vblk;
-        const int share = (ga.units + nw - 1) / nw;
-        u = min(vw * share, ga.units);
-        u_end = min(u + share, ga.units);
-        pi = 0;
-    }
+    wave_range<WAVES>(ga, wave, u, u_end, pi);
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
         const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
@@ -552,18 +393,8 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void bitcos_gemv_kernel(GroupArgs ga
 
 template <int M>
 hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    constexpr int WAVES = Cfg<M>::WAVES;
-    int blocks;
-    if (g.ranges) {
-        if (g.waves % WAVES) return hipErrorInvalidValue;
-        blocks = g.waves / WAVES;  // the table's per-wave ranges fix the grid
-    } else {
-        // at most one block per CU (the decode tables take most of the LDS); a multiple of 8 so that
-        // every XCD gets the same number
-        blocks = std::min(g.units, device_cus());
-        if (blocks > 8) blocks = blocks / 8 * 8;
-        blocks = std::max(1, blocks);
-    }
+    const int blocks = grid_blocks<Cfg<M>::WAVES>(g);
+    if (blocks < 1) return hipErrorInvalidValue;
     if (acc_out)
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, true>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
     else
@@ -573,11 +404,11 @@ hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
 
 }  // namespace
 
-int bitcos_waves_per_cu(int m) {
+int gemv_waves_per_cu(int m) {
     return m == 1 ? Cfg<1>::WAVES : m == 2 ? Cfg<2>::WAVES : Cfg<3>::WAVES;
 }
 
-void bitcos_geometry(Problem &p, int m) {
+void gemv_geometry(Problem &p, int m) {
     const int nb = m == 1 ? Cfg<1>::NB : m == 2 ? Cfg<2>::NB : Cfg<3>::NB;
     p.ng = p.k / 128;
     p.nch = (p.ng + 63) / 64;

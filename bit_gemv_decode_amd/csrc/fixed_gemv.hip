@@ -1,0 +1,373 @@
+// Ternary GEMV for the fixed-size group codes, on gfx950 (int8 activations, fp16 group scales):
+//   five-trit -- five ternary weights per byte as base-3 digits (digit = weight + 1, first weight least
+//                significant), 26 bytes per 128-weight group ("Breaking the 1.58-bit Barrier for
+//                Ternary LLMs", Sec. I; "Sub-Two-Bit Ternary Weight Storage with Table-Free Arithmetic
+//                Decoding", abstract);
+//   2-bit     -- four weights per byte, code = weight + 1 in two bits, first weight lowest (the
+//                "2-bit packing" of Table I in the first paper).
+//
+// Same persistent work geometry and unit-end reduction as the BITCOS kernel (gemv_pipeline.h): a lane
+// owns one group per step. A group's code bytes sit at a fixed place, so there is no dependent load:
+// the codes of step h are loaded while step h - 3 is decoded (four code buffers rotate in a loop body
+// of four steps). Decode is one LDS table read per code byte:
+//   2-bit:     byte -> its 4 weights as int8 (one v_dot4_i32_i8 against 4 activation bytes);
+//   five-trit: byte -> weights 0..3 as int8 plus weight 4 in a second word. The activation bytes are
+//              permuted once per slice into matching words: xa[j] = x[5j .. 5j+3] and, for each run
+//              of four code bytes, xb[q] = the four activations of their fifth weights, so a run of
+//              four bytes (20 weights) takes five dot products.
+// The tables are kept in bank-spread copies (lane l reads copy l % 64 or l % 32), so table reads do
+// not conflict; a copy's address is one byte-permute of the code word.
+#include <algorithm>
+
+#include "gemv_pipeline.h"
+
+namespace tg {
+namespace {
+
+// LDS tables: 256 entries, spread so that lane l reads its own copy: 2-bit entries are 4 bytes (64
+// copies, 256 bytes per entry value), five-trit entries 8 bytes (32 copies).
+constexpr uint32_t kLutBytes = 256 * 256;
+
+struct alignas(16) FixedTables {
+    uint32_t b2[256];     // 2-bit: code byte -> 4 int8 weights
+    uint32_t t5[256][2];  // five-trit: code byte -> weights 0..3 as int8, weight 4 as int8 in word 1
+};
+
+constexpr FixedTables make_fixed_tables() {
+    FixedTables t{};
+    for (uint32_t b = 0; b < 256; ++b) {
+        uint32_t v = 0;
+        for (uint32_t i = 0; i < 4; ++i) {
+            const uint32_t c = (b >> (2 * i)) & 3u;          // code 3 is invalid; read as weight 0
+            const uint32_t w = c == 3 ? 0u : (c + 255u) & 0xFFu;  // c - 1 as int8
+            v |= w << (8 * i);
+        }
+        t.b2[b] = v;
+        uint32_t d = b < 243 ? b : 121;  // invalid bytes read as five zero weights
+        uint32_t lo = 0, hi = 0;
+        for (uint32_t i = 0; i < 5; ++i) {
+            const uint32_t w = (d % 3 + 255u) & 0xFFu;  // digit - 1 as int8
+            d /= 3;
+            if (i < 4)
+                lo |= w << (8 * i);
+            else
+                hi = w;
+        }
+        t.t5[b][0] = lo;
+        t.t5[b][1] = hi;
+    }
+    return t;
+}
+
+__device__ const FixedTables kFixedTables = make_fixed_tables();
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<TG_FMT_2BIT> {
+    static constexpr uint32_t kGroupBytes = 32;
+    static constexpr int kXWords = 32;  // activation words per lane and row of x
+};
+template <>
+struct Fmt<TG_FMT_5TRIT> {
+    static constexpr uint32_t kGroupBytes = 26;
+    static constexpr int kXWords = 33;  // xa[0..25], xb[0..6]
+};
+
+// One step's codes: eight words from the dword-aligned address at or below the group start, the
+// bit shift that realigns them (five-trit groups start on 2-byte boundaries), and the scale.
+struct CodeBuf {
+    u32x4 c[2];
+    uint32_t sh;
+    uint16_t scale;
+};
+
+// The lane's activation words for its group column: plain bytes for 2-bit, the permuted words for
+// five-trit (see the file comment).
+template <int FMT, int M>
+__device__ __forceinline__ void load_xf(const Ctx &x, uint32_t voff, uint32_t (&xf)[M][Fmt<FMT>::kXWords]) {
+    uint32_t xr[M][32];
+    load_x<M>(x, voff, xr);
+    if constexpr (FMT == TG_FMT_2BIT) {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi)
+#pragma unroll
+            for (int j = 0; j < 32; ++j) xf[mi][j] = xr[mi][j];
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+            auto xw = [&](int w) -> uint32_t { return w < 32 ? xr[mi][w] : 0u; };
+#pragma unroll
+            for (int j = 0; j < 26; ++j) {
+                const int w = (5 * j) >> 2, o = (5 * j) & 3;
+                xf[mi][j] = o == 0 ? xw(w) : __builtin_amdgcn_alignbit(xw(w + 1), xw(w), 8 * o);
+            }
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                // activation bytes 20q+4, 20q+9, 20q+14, 20q+19: byte 0 of word 5q+1, byte 1 of 5q+2,
+                // byte 2 of 5q+3, byte 3 of 5q+4 (zero past the group)
+                const uint32_t lo = __builtin_amdgcn_perm(xw(5 * q + 2), xw(5 * q + 1), 0x0C0C0500u);
+                const uint32_t hi = __builtin_amdgcn_perm(xw(5 * q + 4), xw(5 * q + 3), 0x0C0C0702u);
+                xf[mi][26 + q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+        }
+    }
+}
+
+template <int FMT, int M>
+__device__ __forceinline__ void wait_xf(const uint32_t (&xf)[M][Fmt<FMT>::kXWords]) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi)
+#pragma unroll
+        for (int j = 0; j < Fmt<FMT>::kXWords; ++j) asm volatile("" ::"v"(xf[mi][j]));
+}
+
+// int32 sums of the lane's 128 weights times x, per activation row.
+template <int FMT, int M>
+__device__ __forceinline__ void decode_fixed(const CodeBuf &b, const uint32_t (&xf)[M][Fmt<FMT>::kXWords],
+                                             const char *lds, uint32_t laneoff, int (&acc)[M]) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) acc[mi] = 0;
+    uint32_t w[8] = {b.c[0].x, b.c[0].y, b.c[0].z, b.c[0].w, b.c[1].x, b.c[1].y, b.c[1].z, b.c[1].w};
+    if constexpr (FMT == TG_FMT_2BIT) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // (byte << 8) | (lane % 64) * 4: lane's copy of the byte's entry
+                const uint32_t a = __builtin_amdgcn_perm(w[d], laneoff, 0x0C0C0000u | ((4u + i) << 8));
+                const uint32_t e = *reinterpret_cast<const uint32_t *>(lds + a);
+#pragma unroll
+                for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(e, xf[mi][4 * d + i], acc[mi]);
+            }
+    } else {
+        // realign: the group's 26 bytes start at bit sh (0 or 16) of w[0]
+#pragma unroll
+        for (int d = 0; d < 7; ++d) w[d] = __builtin_amdgcn_alignbit(w[d + 1], w[d], b.sh);
+#pragma unroll
+        for (int q = 0; q < 7; ++q) {
+            uint32_t hi4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * q + i;  // code byte
+                if (j < 26) {
+                    const uint32_t a = __builtin_amdgcn_perm(w[q], laneoff, 0x0C0C0000u | ((4u + i) << 8));
+                    const uint2 e = *reinterpret_cast<const uint2 *>(lds + a);
+#pragma unroll
+                    for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(e.x, xf[mi][j], acc[mi]);
+                    hi4[i] = e.y;
+                } else {
+                    hi4[i] = 0;
+                }
+            }
+            const uint32_t lo = __builtin_amdgcn_perm(hi4[1], hi4[0], 0x0C0C0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(hi4[3], hi4[2], 0x0C0C0400u);
+            const uint32_t w4 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+#pragma unroll
+            for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(w4, xf[mi][26 + q], acc[mi]);
+        }
+    }
+}
+
+// Pipeline over the steps of units [u0, u1) of one GEMV: in half-step h, step h - 3 is decoded and
+// the codes of step h are loaded (four code buffers rotate with the four half-steps of the loop
+// body). Every stage runs on every half-step; dead steps use dead offsets and decode into tile slots
+// a live step overwrites first.
+template <int FMT, int M, bool ACC, int NB, bool CHUNKED>
+__device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, const char *lds, double *tile) {
+    constexpr uint32_t GB = Fmt<FMT>::kGroupBytes;
+    constexpr int XW = Fmt<FMT>::kXWords;
+    const int lane = threadIdx.x & 63;
+    Ctx x;
+    x.n = p.n;
+    x.k = p.k;
+    x.ng = p.ng;
+    x.nch = p.nch;
+    x.G = p.G;
+    x.R = p.R;
+    x.glast = p.glast;
+    // a five-trit group's last load reaches up to 6 bytes past its 26; the packed buffer keeps at least
+    // 16 zero bytes after the codes section, so the resource covers them
+    x.rbm = make_rsrc(p.codes, p.codes_bytes + 16u);
+    x.rsc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)p.ng * 2u);
+    x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
+    x.ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)M * (uint32_t)p.n * 4u);
+    x.racc = make_rsrc(p.acc, ACC ? (uint32_t)M * (uint32_t)p.n * (uint32_t)p.ng * 4u : 0u);
+    const uint32_t laneoff = FMT == TG_FMT_2BIT ? (uint32_t)lane << 2 : (uint32_t)(lane & 31) << 3;
+    const int rpu = p.rpu;
+    const int row_begin = (u0 - p.unit_begin) * rpu;
+    const int row_end = min(p.n, (u1 - p.unit_begin) * rpu);
+    const uint32_t ng = (uint32_t)p.ng;
+
+    uint32_t xf[M][XW];
+    int T;
+    uint32_t voff_sc, voff_acc, voff_x, lane_grp;  // lane_grp: the lane's group index offset in a step
+    bool act;
+    Red red;
+    if constexpr (!CHUNKED) {
+        const int ql = (int)(((uint32_t)lane * p.gmagic) >> 16);
+        const int jl = lane - ql * x.G;
+        act = lane < x.R * x.G;
+        lane_grp = (uint32_t)lane;  // ql * ng + jl with ng = G
+        voff_sc = act ? (uint32_t)lane * 2u : kOffOff;
+        voff_acc = act ? (uint32_t)lane * 4u : kOffOff;
+        voff_x = act ? (uint32_t)jl * 128u : kOffOff;
+        T = (u1 - u0) * NB;
+        red = make_red(NB * x.R, x.R, x.G, p.rmagic);
+    } else {
+        act = true;
+        lane_grp = (uint32_t)lane;
+        voff_sc = (uint32_t)lane * 2u;
+        voff_acc = (uint32_t)lane * 4u;
+        voff_x = (uint32_t)lane * 128u;
+        T = (u1 - u0) * NB * x.nch;
+        red = make_red(NB, 1, 64, p.rmagic);
+    }
+    load_xf<FMT, M>(x, voff_x, xf);
+    wait_xf<FMT, M>(xf);
+
+    CodeBuf cb[4] = {};
+    int cD = 0, rD = row_begin, cB = 0, rB = row_begin;
+
+    for (int it = 0; 4 * it - 3 < T; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int h = 4 * it + j;
+            // ---- decode step h - 3 (buffer cb[(j + 1) & 3]) ----
+            {
+                const int s = h - 3;
+                const bool live = s >= 0 && s < T;
+                const CodeBuf &b = cb[(j + 1) & 3];
+                int acc[M];
+                decode_fixed<FMT, M>(b, xf, lds, laneoff, acc);
+                const int slot = (j + 1) % NB;
+                if constexpr (!CHUNKED) {
+                    const int row0 = row_begin + s * x.R;
+                    const bool va = live && act && row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
+                    emit<M, ACC, NB>(x, acc, b.scale, tile, slot, false, va ? voff_acc : kOffOff,
+                                     live_or_dead(live, (uint32_t)row0 * ng * 4u));
+                    if constexpr (!ACC) {
+                        if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
+                    }
+                } else {
+                    const int row = rD + slot;
+                    const int gc = cD == x.nch - 1 ? x.glast : 64;
+                    const bool va = live && lane < gc && row < row_end;
+                    emit<M, ACC, NB>(x, acc, b.scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                                     live_or_dead(live, ((uint32_t)row * ng + (uint32_t)cD * 64u) * 4u));
+                    if (slot == NB - 1) {  // static: last step of a chunk pass
+                        if constexpr (!ACC) reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
+                        const bool wrap = live && cD == x.nch - 1;
+                        rD = wrap ? rD + NB : rD;
+                        cD = live ? (wrap ? 0 : cD + 1) : cD;
+                        TG_SCHED_FENCE();
+                        const int gcn = cD == x.nch - 1 ? x.glast : 64;
+                        load_xf<FMT, M>(x, lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff, xf);
+                    }
+                }
+            }
+            TG_SCHED_FENCE();
+            // ---- codes and scale of step h -> cb[j] ----
+            {
+                const int s = h;
+                const bool live = s < T;
+                uint32_t grp, soff_sc;  // global group index of the lane's group, scale offset
+                bool la;
+                if constexpr (!CHUNKED) {
+                    const int row0 = row_begin + s * x.R;
+                    grp = (uint32_t)row0 * ng + lane_grp;
+                    soff_sc = (uint32_t)row0 * ng * 2u;
+                    la = live && act;
+                } else {
+                    const int slot = j % NB;
+                    const int gc = cB == x.nch - 1 ? x.glast : 64;
+                    grp = (uint32_t)(rB + slot) * ng + (uint32_t)cB * 64u + lane_grp;
+                    soff_sc = ((uint32_t)(rB + slot) * ng + (uint32_t)cB * 64u) * 2u;
+                    la = live && lane < gc;
+                    if (slot == NB - 1) {
+                        const bool wrap = live && cB == x.nch - 1;
+                        rB = wrap ? rB + NB : rB;
+                        cB = live ? (wrap ? 0 : cB + 1) : cB;
+                    }
+                }
+                const uint32_t off = grp * GB;
+                const uint32_t a4 = la ? off & ~3u : kOffOff;
+                cb[j].c[0] = ld4(x.rbm, a4, 0u);
+                cb[j].c[1] = ld4(x.rbm, a4 + 16u, 0u);
+                cb[j].sh = (off & 3u) << 3;
+                cb[j].scale = ACC ? (uint16_t)0 : ldh(x.rsc, la ? voff_sc : kOffOff, live_or_dead(live, soff_sc));
+            }
+            TG_SCHED_FENCE();
+        }
+    }
+}
+
+template <int FMT, int M, bool ACC>
+__global__ __launch_bounds__(Cfg<M>::BLOCK) void fixed_gemv_kernel(GroupArgs ga) {
+    constexpr int NB = Cfg<M>::NB, WAVES = Cfg<M>::WAVES, BLOCK = Cfg<M>::BLOCK;
+    __shared__ uint4 s_lut[kLutBytes / 16];
+    __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
+    {
+        uint32_t *l = reinterpret_cast<uint32_t *>(s_lut);
+        if constexpr (FMT == TG_FMT_2BIT) {
+            for (int i = threadIdx.x; i < 256 * 64; i += BLOCK) l[i] = kFixedTables.b2[i >> 6];
+        } else {
+            for (int i = threadIdx.x; i < 256 * 32; i += BLOCK) {
+                l[2 * i] = kFixedTables.t5[i >> 5][0];
+                l[2 * i + 1] = kFixedTables.t5[i >> 5][1];
+            }
+        }
+    }
+    __syncthreads();
+    const char *lds = reinterpret_cast<const char *>(s_lut);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
+    int u, u_end, pi;
+    wave_range<WAVES>(ga, wave, u, u_end, pi);
+    while (u < u_end) {
+        if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
+        const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        const int u1 = min(u_end, p.unit_begin + p.nunits);
+        if (u < u1) {
+            if (p.nch == 1)
+                run_fixed<FMT, M, ACC, NB, false>(p, u, u1, lds, tile);
+            else
+                run_fixed<FMT, M, ACC, NB, true>(p, u, u1, lds, tile);
+        }
+        u = max(u, u1);
+        ++pi;
+    }
+}
+
+template <int FMT, int M>
+hipError_t launch_fixed_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
+    const int blocks = grid_blocks<Cfg<M>::WAVES>(g);
+    if (blocks < 1) return hipErrorInvalidValue;
+    if (acc_out)
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, true>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
+    else
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fixed(const GroupArgs &g, bool acc_out, hipStream_t s) {
+    switch (g.m) {
+        case 1: return launch_fixed_m<FMT, 1>(g, acc_out, s);
+        case 2: return launch_fixed_m<FMT, 2>(g, acc_out, s);
+        case 3: return launch_fixed_m<FMT, 3>(g, acc_out, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_t5(const GroupArgs &g, bool acc_out, hipStream_t s) {
+    return launch_fixed<TG_FMT_5TRIT>(g, acc_out, s);
+}
+
+hipError_t launch_b2(const GroupArgs &g, bool acc_out, hipStream_t s) {
+    return launch_fixed<TG_FMT_2BIT>(g, acc_out, s);
+}
+
+}  // namespace tg

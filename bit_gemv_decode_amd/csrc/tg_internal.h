@@ -28,7 +28,7 @@ struct Problem {
     int32_t n, k;             // rows, reduction length (k % 128 == 0)
     int32_t unit_begin;       // index of this GEMV's first work unit within its launch
     int32_t nunits;           // work units of this GEMV
-    // BITCOS work geometry (filled by bitcos_geometry; other formats leave it zero)
+    // work geometry (filled by gemv_geometry)
     int32_t ng;               // 128-groups per row
     int32_t nch;              // chunks of at most 64 groups per row
     int32_t G;                // groups per row in a full chunk (ng when nch == 1, else 64)
@@ -54,19 +54,19 @@ struct GroupArgs {
     int32_t count;
     int32_t units;            // total work units over all GEMVs
     int32_t m;                // activation rows (1 .. 3 on the vector path)
-    int32_t rows_per_unit;    // rows one wave processes as a unit (5-trit, 2-bit)
+    int32_t rows_per_unit;    // unused (each GEMV's rows per unit are in Problem::rpu)
     int32_t waves;            // waves the launch must have (table mode: ranges has this many entries)
     int32_t reserved;
     Problem one;
 };
 
-// Waves per CU of a BITCOS launch for m activation rows (one block per CU: the decode tables fill
-// most of the LDS).
-int bitcos_waves_per_cu(int m);
-constexpr int kBitcosMaxWavesPerCu = 16;
+// Waves per CU of a GEMV launch for m activation rows (one block per CU: the decode tables fill most
+// of the LDS).
+int gemv_waves_per_cu(int m);
+constexpr int kMaxWavesPerCu = 16;
 
-// Fill the BITCOS work geometry of p (p.n, p.k set) for m activation rows.
-void bitcos_geometry(Problem &p, int m);
+// Fill the work geometry of p (p.n, p.k set) for m activation rows (the same for every format).
+void gemv_geometry(Problem &p, int m);
 
 // Host-side checks of a descriptor; `limit` is the buffer length when known (0 = trust bytes_total).
 int check_desc(const tg_desc *d, uint64_t limit);
@@ -75,9 +75,6 @@ int check_desc(const tg_desc *d, uint64_t limit);
 Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, const int8_t *x, float *y,
                      int32_t *acc);
 
-// Rows per work unit the launcher of a non-BITCOS format uses (BITCOS keeps its own per GEMV in
-// Problem::rpu).
-int rows_per_unit(int fmt, int64_t n, int64_t k, int m, bool table);
 
 // Kernel launchers (asynchronous; return the HIP status of the launch). `g.one` or `g.table` holds
 // the problems; the launchers set grid sizes themselves.
