@@ -24,14 +24,19 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-KERNEL_SRC = os.path.join(PKG, "csrc", "bitcos_gemv.hip")
+# the BITCOS kernel's source and the device headers it compiles from
+KERNEL_SRCS = [os.path.join(PKG, "csrc", f) for f in ("bitcos_gemv.hip", "gemv_pipeline.h", "device_common.h",
+                                                         "tg_internal.h")]
 READ_BYTES = 2 * 1024 ** 3
 WRITE_BYTES = 1024 ** 3
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def drive():
