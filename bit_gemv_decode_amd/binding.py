@@ -26,7 +26,6 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_describe", "tg_validate", "tg_unpack",
            "ternary_gemv", "ternary_gemv_acc", "tg_plan_table_bytes", "tg_plan_init", "ternary_gemv_plan",
            "tg_stream_read", "tg_strerror", "tg_version"]
-PLAN_MAX_M = 3
 
 
 class TgError(RuntimeError):

@@ -60,7 +60,19 @@ bool fits_offsets(const tg_desc *d, int32_t m) {
            (uint64_t)m * (uint64_t)d->k <= lim;
 }
 
+// BITCOS with at least kMfmaMinM activation rows goes to the matrix-core kernel in one launch.
+bool use_mfma(int fmt, int32_t m) { return fmt == TG_FMT_BITCOS && m >= kMfmaMinM; }
+
+// Work geometry of one GEMV for a launch of m activation rows.
+void geometry(Problem &p, int fmt, int32_t m) {
+    if (use_mfma(fmt, m))
+        mfma_geometry(p);
+    else
+        gemv_geometry(p, m);
+}
+
 hipError_t launch(int fmt, const GroupArgs &g, bool acc_out, hipStream_t s) {
+    if (use_mfma(fmt, g.m)) return launch_bitcos_mfma(g, acc_out, s);
     switch (fmt) {
         case TG_FMT_BITCOS: return launch_bitcos(g, acc_out, s);
         case TG_FMT_5TRIT: return launch_t5(g, acc_out, s);
@@ -81,16 +93,18 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
     if (!fits_offsets(desc, m)) return TG_ESHAPE;
     hipStream_t s = (hipStream_t)stream;
     const int64_t n = desc->n, k = desc->k, ng = k / TG_GROUP;
-    // Activation rows go in launches of at most three (each launch reads the weights once).
-    for (int32_t m0 = 0; m0 < m; m0 += kVectorMaxM) {
-        const int32_t mt = std::min<int32_t>(kVectorMaxM, m - m0);
+    // Activation rows go in launches of at most three on the vector path (each launch reads the
+    // weights once); the matrix-core path takes all of them in one launch.
+    const int32_t step = use_mfma(desc->fmt, m) ? m : kVectorMaxM;
+    for (int32_t m0 = 0; m0 < m; m0 += step) {
+        const int32_t mt = std::min<int32_t>(step, m - m0);
         GroupArgs g{};
         g.one = make_problem(desc, W, scales, x + (size_t)m0 * k, acc_out ? nullptr : y + (size_t)m0 * n,
                              acc_out ? acc + (size_t)m0 * n * ng : nullptr);
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
-        gemv_geometry(g.one, mt);
+        geometry(g.one, desc->fmt, mt);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
         if (launch(desc->fmt, g, acc_out, s) != hipSuccess) return TG_EHIP;
@@ -114,8 +128,11 @@ namespace {
 
 // Waves of a persistent launch on this device for m activation rows; a plan's per-wave ranges are
 // sized for it (the table has room for the largest count).
-int plan_waves(int m) { return device_cus() * gemv_waves_per_cu(m); }
-int plan_waves_max() { return device_cus() * kMaxWavesPerCu; }
+int plan_waves(int fmt, int m) { return device_cus() * (use_mfma(fmt, m) ? kMfmaWavesPerCu : gemv_waves_per_cu(m)); }
+int plan_waves_max() { return device_cus() * std::max(kMaxWavesPerCu, kMfmaWavesPerCu); }
+
+// Largest m a plan of this format takes (one launch per plan).
+int plan_max_m(int fmt) { return fmt == TG_FMT_BITCOS ? TG_MAX_M : kVectorMaxM; }
 
 size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
 
@@ -128,11 +145,12 @@ extern "C" size_t tg_plan_table_bytes(int32_t count) {
 extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                             const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
                             float *const *y, int32_t *const *acc, int32_t m) {
-    if (!plan || !table || !descs || !W || !x || count < 1 || m < 1 || m > kVectorMaxM) return TG_EINVAL;
+    if (!plan || !table || !descs || !W || !x || count < 1 || m < 1) return TG_EINVAL;
     const bool acc_mode = acc != nullptr;
     if (acc_mode ? false : (!y || !scales)) return TG_EINVAL;
     if (((uintptr_t)table & 15) || table_bytes < tg_plan_table_bytes(count)) return TG_EINVAL;
     const int fmt = descs[0].fmt;
+    if (m > plan_max_m(fmt)) return TG_EINVAL;
     std::vector<Problem> host((size_t)count);
     int rpu = 1;  // largest rows per unit (informational)
     for (int32_t i = 0; i < count; ++i) {
@@ -153,14 +171,14 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr);
         host[i].unit_begin = (int32_t)units;
-        gemv_geometry(host[i], m);
+        geometry(host[i], fmt, m);
         rpu = std::max(rpu, (int)host[i].rpu);
         units += host[i].nunits;
         total_cost += (double)d->n * (double)d->k;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
     // Contiguous unit ranges per wave, balanced by cost (rows x k of each unit).
-    const int nw = plan_waves(m);
+    const int nw = plan_waves(fmt, m);
     std::vector<WaveRange> ranges((size_t)nw);
     {
         int32_t pi = 0;
@@ -204,11 +222,11 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
 
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
-        plan->m > kVectorMaxM)
+        plan->m > plan_max_m(plan->fmt))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
-    if (plan->waves != plan_waves(plan->m)) return TG_EINVAL;  // built for another device
+    if (plan->waves != plan_waves(plan->fmt, plan->m)) return TG_EINVAL;  // built for another device
     g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
     g.waves = plan->waves;
     g.count = plan->count;

@@ -36,57 +36,11 @@
 //     out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
 
+#include "bitcos_tables.h"
 #include "gemv_pipeline.h"
 
 namespace tg {
 namespace {
-
-constexpr int kEntries = 6561;                 // sum over presence bytes of 2^popcount = 3^8
-constexpr uint32_t kInfoBytes = 256 * 32 * 8;  // per-byte (mask, base) in 32 bank-spread copies
-constexpr uint32_t kEntOff = kInfoBytes;       // LDS byte offset of the entry table
-constexpr uint32_t kEntBytes = kEntries * 8;
-constexpr uint32_t kTabBytes = (kEntOff + kEntBytes + 255) / 256 * 256;
-
-struct alignas(16) Tables {
-    uint64_t ent[kEntries + 1];  // padded to an even count for 16-byte copies
-    uint32_t info[256][2];       // per presence byte: mask (popcount ones, shifted left 3), LDS base
-};
-
-constexpr int popc8(uint32_t v) {
-    int c = 0;
-    for (int i = 0; i < 8; ++i) c += (v >> i) & 1;
-    return c;
-}
-
-// Blocks of entries in decreasing size: every block then starts at a multiple of its own size, so
-// a block's base has zero bits where (window & mask) has its ones.
-constexpr Tables make_tables() {
-    Tables t{};
-    uint32_t e = 0;
-    for (int c = 8; c >= 0; --c) {
-        for (uint32_t pb = 0; pb < 256; ++pb) {
-            if (popc8(pb) != c) continue;
-            t.info[pb][0] = ((1u << c) - 1u) << 3;
-            t.info[pb][1] = kEntOff + 8 * e;
-            for (uint32_t sc = 0; sc < (1u << c); ++sc) {
-                uint64_t v = 0;
-                uint32_t rank = 0;
-                for (uint32_t i = 0; i < 8; ++i) {
-                    if ((pb >> i) & 1) {
-                        const uint64_t byte = ((sc >> rank) & 1) ? 0xFFull : 0x01ull;  // -1 or +1 as int8
-                        v |= byte << (8 * i);
-                        ++rank;
-                    }
-                }
-                t.ent[e + sc] = v;
-            }
-            e += 1u << c;
-        }
-    }
-    return t;
-}
-
-__device__ const Tables kTables = make_tables();
 
 // Sign stage of one step: for each pair of bitmap dwords, the four sign-stream dwords holding bits
 // [pos - 3, pos + 93) (pos = the pair's first sign); the two funnel-shift amounts into them (bytes 0
@@ -365,13 +319,7 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void bitcos_gemv_kernel(GroupArgs ga
     constexpr int NB = Cfg<M>::NB, WAVES = Cfg<M>::WAVES, BLOCK = Cfg<M>::BLOCK;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
-    {
-        uint2 *info = reinterpret_cast<uint2 *>(s_tab);
-        for (int i = threadIdx.x; i < 256 * 32; i += BLOCK)
-            info[i] = make_uint2(kTables.info[i >> 5][0], kTables.info[i >> 5][1]);
-        const uint4 *src = reinterpret_cast<const uint4 *>(kTables.ent);
-        for (int i = threadIdx.x; i < (kEntries + 1) / 2; i += BLOCK) s_tab[kEntOff / 16 + i] = src[i];
-    }
+    load_bitcos_tables<BLOCK>(s_tab);
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
 

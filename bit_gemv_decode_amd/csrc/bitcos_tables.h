@@ -1,0 +1,80 @@
+// LDS decode tables of the BITCOS kernels ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec.
+// II-A and Fig. 4: the deposit of compact signs onto present positions, done here by lookup).
+//
+// Entry (pb, s) holds the 8 ternary weights, as int8, of presence byte pb with compact signs s (its
+// popcount(pb) sign bits, first sign lowest; a set sign bit gives -1, a clear one +1, absent
+// positions 0): 3^8 = 6561 entries of 8 bytes. The entries of one presence byte form a block of
+// 2^popcount(pb) entries, and blocks are laid out in decreasing size, so each block starts at a
+// multiple of its own size: the LDS address of an entry is (window & mask) | base, where window
+// holds the compact signs at bits 3 and up, mask = (2^popcount(pb) - 1) << 3 and base is the block's
+// LDS byte address. (mask, base) per presence byte come from a 256-entry table kept in 32 copies,
+// one per LDS bank: lane l reads copy l % 32 at (pb << 8) | (l % 32) << 3, so these reads never
+// conflict.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace tg {
+namespace {
+
+constexpr int kEntries = 6561;                 // sum over presence bytes of 2^popcount = 3^8
+constexpr uint32_t kInfoBytes = 256 * 32 * 8;  // per-byte (mask, base) in 32 bank-spread copies
+constexpr uint32_t kEntOff = kInfoBytes;       // LDS byte offset of the entry table
+constexpr uint32_t kEntBytes = kEntries * 8;
+constexpr uint32_t kTabBytes = (kEntOff + kEntBytes + 255) / 256 * 256;
+
+struct alignas(16) Tables {
+    uint64_t ent[kEntries + 1];  // padded to an even count for 16-byte copies
+    uint32_t info[256][2];       // per presence byte: mask (popcount ones, shifted left 3), LDS base
+};
+
+constexpr int popc8(uint32_t v) {
+    int c = 0;
+    for (int i = 0; i < 8; ++i) c += (v >> i) & 1;
+    return c;
+}
+
+// Blocks of entries in decreasing size: every block then starts at a multiple of its own size, so
+// a block's base has zero bits where (window & mask) has its ones.
+constexpr Tables make_tables() {
+    Tables t{};
+    uint32_t e = 0;
+    for (int c = 8; c >= 0; --c) {
+        for (uint32_t pb = 0; pb < 256; ++pb) {
+            if (popc8(pb) != c) continue;
+            t.info[pb][0] = ((1u << c) - 1u) << 3;
+            t.info[pb][1] = kEntOff + 8 * e;
+            for (uint32_t sc = 0; sc < (1u << c); ++sc) {
+                uint64_t v = 0;
+                uint32_t rank = 0;
+                for (uint32_t i = 0; i < 8; ++i) {
+                    if ((pb >> i) & 1) {
+                        const uint64_t byte = ((sc >> rank) & 1) ? 0xFFull : 0x01ull;  // -1 or +1 as int8
+                        v |= byte << (8 * i);
+                        ++rank;
+                    }
+                }
+                t.ent[e + sc] = v;
+            }
+            e += 1u << c;
+        }
+    }
+    return t;
+}
+
+__device__ const Tables kTables = make_tables();
+
+// Copy both tables into LDS (s_tab: kTabBytes); the caller synchronises the block afterwards.
+template <int BLOCK>
+__device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
+    uint2 *info = reinterpret_cast<uint2 *>(s_tab);
+    for (int i = threadIdx.x; i < 256 * 32; i += BLOCK)
+        info[i] = make_uint2(kTables.info[i >> 5][0], kTables.info[i >> 5][1]);
+    const uint4 *src = reinterpret_cast<const uint4 *>(kTables.ent);
+    for (int i = threadIdx.x; i < (kEntries + 1) / 2; i += BLOCK) s_tab[kEntOff / 16 + i] = src[i];
+}
+
+}  // namespace
+}  // namespace tg

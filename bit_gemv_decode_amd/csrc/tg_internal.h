@@ -68,6 +68,14 @@ constexpr int kMaxWavesPerCu = 16;
 // Fill the work geometry of p (p.n, p.k set) for m activation rows (the same for every format).
 void gemv_geometry(Problem &p, int m);
 
+// Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
+// units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU.
+constexpr int kMfmaMinM = 4;
+constexpr int kMfmaTiles = 4;
+constexpr int kMfmaWavesPerCu = 8;
+void mfma_geometry(Problem &p);
+hipError_t launch_bitcos_mfma(const GroupArgs &g, bool acc_out, hipStream_t s);
+
 // Host-side checks of a descriptor; `limit` is the buffer length when known (0 = trust bytes_total).
 int check_desc(const tg_desc *d, uint64_t limit);
 

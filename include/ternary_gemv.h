@@ -123,6 +123,12 @@ int tg_unpack(const void *packed, size_t bytes, int8_t *w_out);
  * GPU GEMV (asynchronous). desc: host copy of the descriptor of the packed buffer whose device copy
  * is W (bytes_total bytes, the same image as the host buffer). scales: device fp16 [n][k/128] bit
  * patterns. x: device int8 [m][k]. y: device float [m][n]. 1 <= m <= TG_MAX_M.
+ * Paths: m <= 3 uses the vector kernels (int8 dot products in int32, "Breaking the 1.58-bit Barrier
+ * for Ternary LLMs", Sec. II-C); five-trit and 2-bit with m > 3 run them in launches of up to three
+ * rows. BITCOS with m >= 4 is the thin-batch path: one launch decodes each weight once into int8
+ * operands of int8 matrix-core products against X padded to 16 rows (the same paper, Sec. III:
+ * batched decoding becomes a matrix product). Every path produces the same exact int32 group sums
+ * and the same fp32 outputs.
  * The kernels trust W's contents as far as its descriptor describes them (validate host buffers
  * with tg_validate before upload); every device read stays inside the sections the descriptor
  * names even for corrupt contents, so a corrupt buffer gives wrong numbers, not a fault.
@@ -138,7 +144,8 @@ int ternary_gemv(const tg_desc *desc, const void *W, const uint16_t *scales, con
 int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_t *acc, int32_t m, void *stream);
 
 /*
- * Grouped launch: several GEMVs of one format and one activation-row count m (1 <= m <= 3) run as
+ * Grouped launch: several GEMVs of one format and one activation-row count m (1 <= m <= 3; BITCOS
+ * 1 <= m <= TG_MAX_M, on the thin-batch path from m = 4) run as
  * one persistent kernel. This is the batched form of the same operation (each GEMV is computed
  * exactly as ternary_gemv / ternary_gemv_acc compute it); it removes the per-launch ramp and lets
  * the memory pipeline stay full across matrices, e.g. the q/k/v or gate/up projections of a decode
@@ -151,7 +158,8 @@ int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_
  *   fills the host struct *plan. descs, W, scales, x, y, acc are host arrays of `count` entries;
  *   W/scales/x/y/acc entries are device pointers. Pass acc == NULL for fp32 outputs y (then y and
  *   scales are required), or acc != NULL for int32 accumulators (y and scales may be NULL).
- *   Errors: TG_EINVAL (null or misaligned pointer, mixed formats, count < 1, m outside [1, 3],
+ *   Errors: TG_EINVAL (null or misaligned pointer, mixed formats, count < 1, m outside the range
+ *   above,
  *   table too small), TG_EFORMAT / TG_ECORRUPT (a descriptor), TG_ESHAPE (a section beyond 4 GiB),
  *   TG_EHIP (the copy failed). The plan stays valid while the table and every buffer it names do.
  * ternary_gemv_plan: enqueues all GEMVs of the plan on `stream` as one launch (asynchronous).

@@ -167,7 +167,12 @@ def test_plan_argument_errors_before_any_gpu_work():
     assert L.tg_plan_init(None, dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
     assert L.tg_plan_init(ctypes.byref(plan), None, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
     assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 0, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
-    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 4) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 17) == -1
+    # m above 3 is for BITCOS (thin-batch path) only
+    d5one = (binding.TgDesc * 1)(B.pack_5trit(w).desc)
+    d2one = (binding.TgDesc * 1)(B.pack_2bit(w).desc)
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, d5one, ptrs, ptrs, ptrs, ptrs, None, 4) == -1
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, d2one, ptrs, ptrs, ptrs, ptrs, None, 4) == -1
     assert L.tg_plan_init(ctypes.byref(plan), ctypes.c_void_p(264), nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs,
                           None, 1) == -1
     assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes - 1, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1

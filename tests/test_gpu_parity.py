@@ -123,8 +123,10 @@ def test_non_default_stream():
 PLAN_SHAPES = [(96, 4096), (40, 5120), (33, 14336), (7, 2560), (130, 1024), (1, 128), (64, 384), (9, 25600)]
 
 
-@pytest.mark.parametrize("m", [1, 2, 3])
-@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: B.FMT_NAMES[f])
+PLAN_CASES = [(f, m) for f in FMTS for m in (1, 2, 3)] + [(B.FMT_BITCOS, m) for m in (4, 7, 16)]
+
+
+@pytest.mark.parametrize("fmt,m", PLAN_CASES, ids=[f"{B.FMT_NAMES[f]}-m{m}" for f, m in PLAN_CASES])
 def test_plan_matches_oracle(fmt, m):
     dev = _dev()
     _say(f"[gpu] plan fmt={B.FMT_NAMES[fmt]} m={m} shapes={PLAN_SHAPES}")
