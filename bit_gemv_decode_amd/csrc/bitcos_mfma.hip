@@ -15,17 +15,26 @@
 // at the same k positions (the k order inside an operand is the same for A and B, so the products
 // sum over exactly the group's 128 k). The result lane l holds is C[4q + i][l % 16], i = 0..3.
 //
-// A wave takes units of T consecutive 16-row tiles and walks their groups in order, so each row's
-// sign cursor runs on from group to group (starting at the row index entry). Inside a group the four
-// lanes of a row find their first sign with an exclusive prefix sum of their dwords' popcounts over
-// lanes l, l + 16, l + 32, l + 48 (two permlane swaps, no LDS). The decode per bitmap byte is the
-// lookup of the BITCOS tables (two LDS reads), whose entries are already the 8 int8 weights of the
-// B operand. The activation operand is loaded once per group and shared by the T tiles.
+// Memory side. A wave owns units of T tiles (16T consecutive rows) over whole rows and walks them in
+// chunks of 8 groups (1024 weights). Per chunk and row, the four lanes of the row load the row's
+// bitmap bytes of the chunk (128 contiguous bytes), its 8 scales and the chunk's stretch of the sign
+// stream (36 dwords from the chunk's first sign) with a few wide loads, instead of small pieces of
+// 16 rows per group: the address unit sees a handful of instructions per cache line. Across lanes
+// the data is then rearranged without memory traffic: a 4 x 4 transpose over the four lane rows
+// (permlane16/permlane32 swaps) hands each lane its bitmap dword of every group, the scales are
+// gathered the same way, and the sign stretch goes to a per-wave LDS buffer from which each lane
+// reads its own three-dword window per group (its first sign follows from the row cursor plus an
+// exclusive prefix of the popcounts of lanes l, l + 16, l + 32, l + 48, again by permlane swaps).
+// The decode per bitmap byte is the lookup of the BITCOS tables (two LDS reads); its entries are
+// already the 8 int8 weights of the B operand.
 //
-// Loads are software-pipelined like the vector kernels: the bitmap of step h, the signs,
-// activations and scales of step h - 2 and the decode of step h - 4 share one half-step, in a loop
-// body of four half-steps with fixed register homes, every load issued unconditionally (dead steps
-// use out-of-range offsets, which return zero without a memory request).
+// Pipeline, in half-steps h (one group step of all T tiles each): decode + products of step h - 4,
+// sign windows of step h - 3, activation operand of step h - 2; chunk c's data is rearranged at the
+// half-step where its first sign window is read, its bitmaps and scales were loaded six half-steps
+// earlier and its sign stretch at the previous chunk's rearrangement. The loop body is one chunk
+// (eight half-steps), fully unrolled, so every stage buffer has a fixed register home. Loads are
+// issued unconditionally; dead ones use out-of-range offsets, which return zero without a memory
+// request.
 #include <algorithm>
 
 #include "bitcos_tables.h"
@@ -39,23 +48,55 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = kMfmaWavesPerCu;  // waves per block (one block per CU)
 constexpr int kBlock = 64 * kWaves;
 constexpr int kT = kMfmaTiles;           // 16-row tiles per unit
-constexpr int kLagS = 2;                 // half-steps between a bitmap load and its sign stage
+constexpr int kCG = 8;                   // groups per chunk
+constexpr int kSW = 36;                  // staged sign-stream dwords per row and chunk
+constexpr int kSWL = kSW / 4;            // ... loaded by each lane of the row
+constexpr uint32_t kStageDwords = kT * 16 * kSW;  // per wave
 
-__device__ __forceinline__ u32x3 ld3(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+// (a, b) -> (a', b'): lane rows 1 and 3 of a take rows 0 and 2 of b, and rows 0 and 2 of b take rows 1
+// and 3 of a (lane row = 16 consecutive lanes).
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+// Lane rows 2 and 3 of a take rows 0 and 1 of b, and rows 0 and 1 of b take rows 2 and 3 of a.
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
 }
 
-#ifndef TG_MFMA_PHASE_FENCE
-#define TG_MFMA_PHASE_FENCE() TG_SCHED_FENCE()
-#endif
+// 4 x 4 transpose between lane rows and registers: afterwards r[d] in lane row q holds what r[q] held
+// in lane row d.
+__device__ __forceinline__ void transpose4(uint32_t &r0, uint32_t &r1, uint32_t &r2, uint32_t &r3) {
+    swap16(r0, r1);
+    swap16(r2, r3);
+    swap32(r0, r2);
+    swap32(r1, r3);
+}
+
+// v of lane rows 0..3 (same lane within the row), returned to every lane: out[a] = v of lane row a.
+__device__ __forceinline__ void gather4(uint32_t v, uint32_t (&out)[4]) {
+    uint32_t e = v, o = v;
+    swap16(e, o);  // e: rows (0, 0, 2, 2); o: rows (1, 1, 3, 3)
+    uint32_t e2 = e, o2 = o;
+    swap32(e, e2);  // e: row 0, e2: row 2
+    swap32(o, o2);  // o: row 1, o2: row 3
+    out[0] = e;
+    out[1] = o;
+    out[2] = e2;
+    out[3] = o2;
+}
 
 // The weights of every tile's bitmap dword for one step, as two B operands (16 int8 each) per tile.
-// sg/sh: the sign-stream dwords and funnel shift giving the stream from 3 bits before the dword's
-// first sign. The per-byte (mask, base) reads of all tiles go out first, then all entry reads: two
-// LDS round trips per step.
+// sw: the sign-stream dwords and sh the funnel shift giving the stream from 3 bits before the dword's
+// first sign. The per-byte (mask, base) reads of all tiles go out first, then all entry reads: two LDS
+// round trips per step.
 template <int T>
-__device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const u32x3 (&sg)[T], const uint32_t (&sh)[T],
-                                            const char *lds, uint32_t laneoff, i32x4 (&b0)[T], i32x4 (&b1)[T]) {
+__device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const uint32_t (&sw)[T][3],
+                                            const uint32_t (&sh)[T], const char *lds, uint32_t laneoff,
+                                            i32x4 (&b0)[T], i32x4 (&b1)[T]) {
     uint2 info[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -64,12 +105,11 @@ __device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const u32x
             const uint32_t ia = __builtin_amdgcn_perm(bmw[t], laneoff, 0x0C0C0000u | ((4u + i) << 8));
             info[t][i] = *reinterpret_cast<const uint2 *>(lds + ia);
         }
-    TG_MFMA_PHASE_FENCE();
     uint2 e[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const uint32_t lo = __builtin_amdgcn_alignbit(sg[t].y, sg[t].x, sh[t]);
-        const uint32_t hi = __builtin_amdgcn_alignbit(sg[t].z, sg[t].y, sh[t]);
+        const uint32_t lo = __builtin_amdgcn_alignbit(sw[t][1], sw[t][0], sh[t]);
+        const uint32_t hi = __builtin_amdgcn_alignbit(sw[t][2], sw[t][1], sh[t]);
         uint32_t c = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -78,7 +118,6 @@ __device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const u32x
             if (i < 3) c = __builtin_popcount(info[t][i].x) + c;
         }
     }
-    TG_MFMA_PHASE_FENCE();
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         b0[t] = i32x4{(int)e[t][0].x, (int)e[t][0].y, (int)e[t][1].x, (int)e[t][1].y};
@@ -86,16 +125,33 @@ __device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const u32x
     }
 }
 
+// Position of a chunk in the wave's stream: first row of its unit and chunk index within the rows.
+struct CPos {
+    int row, cu;
+};
+
+__device__ __forceinline__ CPos next_chunk(CPos c, int nck) {
+    const bool wrap = c.cu == nck - 1;
+    return CPos{wrap ? c.row + 16 * kT : c.row, wrap ? 0 : c.cu + 1};
+}
+
 template <bool ACC>
-__device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int mrows, const char *lds) {
+__device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int mrows, const char *lds,
+                                         uint32_t *stg) {
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15;  // weight row within a tile; activation row of the A operand
     const int q = lane >> 4;   // quarter of the group
     const int ng = p.ng;
+    const int nck = (ng + kCG - 1) / kCG;
     const uint32_t kb = (uint32_t)(p.k >> 3);  // bitmap bytes per row
     const __amdgpu_buffer_rsrc_t rbm = make_rsrc(p.codes, p.codes_bytes);
-    // the sign resource starts 4 bytes early so that a window starting below bit 3 is in range
-    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(reinterpret_cast<const uint8_t *>(p.signs) - 4, p.sign_bytes + 4u);
+    // Sign stretches: the resource starts 4 bytes early (a window may start up to 3 bits before the
+    // stream) and runs to the end of the row index, which follows the sign section in the packed
+    // buffer, so a stretch that starts inside the stream is read whole.
+    const uint32_t sg_bytes = (uint32_t)(reinterpret_cast<const uint8_t *>(p.rowoff) -
+                                         reinterpret_cast<const uint8_t *>(p.signs)) +
+                              (uint32_t)(p.n + 1) * 4u + 4u;
+    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(reinterpret_cast<const uint8_t *>(p.signs) - 4, sg_bytes);
     const __amdgpu_buffer_rsrc_t rro = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)ng * 2u);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)mrows * (uint32_t)p.k);
@@ -105,149 +161,251 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const uint32_t m_odd = (q & 1) ? ~0u : 0u, m_hi = (q >> 1) ? ~0u : 0u;
     const uint32_t voff_x = lr < mrows ? (uint32_t)lr * (uint32_t)p.k + 32u * (uint32_t)q : kOffOff;
+    // this lane's row slot in the staging buffer, per tile
+    uint32_t *stg_row[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) stg_row[t] = stg + (t * 16 + lr) * kSW;
 
-    const int S = (u1 - u0) * ng;  // steps: (unit, group) in order
-    const int row_first = (u0 - p.unit_begin) * 16 * kT;
+    const int NC = (u1 - u0) * nck;  // chunks of the range
+    const CPos c0{(u0 - p.unit_begin) * 16 * kT, 0};
 
-    uint32_t bm[4][kT] = {}, ro[4][kT] = {}, sh[4][kT] = {}, sc[4][kT] = {}, cur[kT];
-    u32x3 sg[4][kT] = {};
+    // chunk stage buffers
+    uint32_t rawb[kT][8] = {};      // bitmap bytes of the next chunk as loaded: groups 2q, 2q + 1
+    uint32_t raws[kT][2] = {};      // scales of the next chunk as loaded: groups 2q, 2q + 1
+    uint32_t rawsg[kT][kSWL] = {};  // sign stretch of the next chunk, quarter q
+    uint32_t ro_cur[kT] = {}, ro_nxt[kT] = {};  // row index entries of chunks ci + 1 and ci + 2
+    uint32_t bmc[kT][kCG] = {};     // current chunk: the lane's bitmap dword of each group
+    uint32_t scc[kT][4] = {};       // current chunk: scales of groups 2a, 2a + 1 (low, high half)
+    uint32_t d0c[kT] = {}, d0n[kT] = {};  // first staged dword (resource dword index) of chunks ci, ci + 1
+    uint32_t cbn[kT] = {};          // sign cursor at the start of chunk ci + 1 (row-uniform)
+    uint32_t cur[kT] = {};          // running sign cursor of the sign-window stage
+    // step stage buffers
+    uint32_t bms[2][kT] = {}, sws[2][kT][3] = {}, shs[2][kT] = {}, scs[2][kT] = {};
     u32x4 xa[4] = {}, xb[4] = {};
     double facc[kT][4];
 #pragma unroll
-    for (int t = 0; t < kT; ++t) {
-        cur[t] = 0;
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) facc[t][i] = 0.0;
-    }
-    // stage positions: first row of the unit and group of the step each stage handles
-    int rB = row_first, gB = 0, rS = row_first, gS = 0, rD = row_first, gD = 0;
 
-    for (int it = 0; 4 * it - 4 < S; ++it) {
+    // Chunk loads: bitmaps and scales of chunk c into rawb / raws (groups past the row end read zero).
+    auto load_chunk = [&](CPos c, bool live) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int h = 4 * it + j;
-            // ---- decode step h - 4 (slot j) ----
+        for (int t = 0; t < kT; ++t) {
+            const uint32_t rowb = (uint32_t)(c.row + 16 * t + lr);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int g = c.cu * kCG + 2 * q + e;
+                const bool ok = live && g < ng;
+                const u32x4 v = ld4(rbm, ok ? rowb * kb + (uint32_t)g * 16u : kOffOff, 0u);
+                rawb[t][4 * e] = v.x;
+                rawb[t][4 * e + 1] = v.y;
+                rawb[t][4 * e + 2] = v.z;
+                rawb[t][4 * e + 3] = v.w;
+                if constexpr (!ACC)
+                    raws[t][e] = ldh(rsc, ok ? (rowb * (uint32_t)ng + (uint32_t)g) * 2u : kOffOff, 0u);
+            }
+        }
+    };
+    // Row index entries of chunk c when it starts a unit (else zero) into ro_nxt.
+    auto load_ro = [&](CPos c, bool live) {
+        const uint32_t soff = live_or_dead(live && c.cu == 0, (uint32_t)c.row * 4u);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) ro_nxt[t] = ld1(rro, (uint32_t)(16 * t + lr) * 4u, soff);
+    };
+    // Sign stretches of the chunk whose first sign is cbn: quarter q of the kSW dwords from the dword
+    // holding the bit 3 before it.
+    auto load_signs = [&](bool live) {
+        const uint32_t sd = live_or_dead(live, 0u);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            d0n[t] = (cbn[t] + 29u) >> 5;  // the resource starts one dword early: +32 - 3
+            const uint32_t vo = (d0n[t] + (uint32_t)(kSWL * q)) * 4u;
+            const u32x4 a = ld4(rsg, vo, sd);
+            const u32x4 b = ld4(rsg, vo + 16u, sd);
+            rawsg[t][0] = a.x;
+            rawsg[t][1] = a.y;
+            rawsg[t][2] = a.z;
+            rawsg[t][3] = a.w;
+            rawsg[t][4] = b.x;
+            rawsg[t][5] = b.y;
+            rawsg[t][6] = b.z;
+            rawsg[t][7] = b.w;
+            rawsg[t][8] = ld1(rsg, vo + 32u, sd);
+        }
+    };
+
+    // ---- prologue: chunk 0's data, the row index of chunk 1 ----
+    {
+        const bool live0 = NC > 0;
+        load_ro(c0, live0);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) cbn[t] = ro_nxt[t];  // waits for the row index of chunk 0
+        load_signs(live0);
+        load_chunk(c0, live0);
+        load_ro(next_chunk(c0, nck), NC > 1);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) ro_cur[t] = ro_nxt[t];
+    }
+
+    CPos prev = c0, cp = c0;  // chunks ci - 1 and ci (prev is dead at ci = 0)
+    for (int ci = 0; ci <= NC; ++ci) {
+        const CPos nx = next_chunk(cp, nck), nn = next_chunk(nx, nck);
+        const bool live_prev = ci >= 1, live_cur = ci < NC;
+#pragma unroll
+        for (int j = 0; j < kCG; ++j) {
+            // ---- decode and products of step h - 4: chunk (j < 4 ? prev : cur), position (j - 4) & 7 ----
             {
-                const int s = h - 4;
-                const bool live = s >= 0 && s < S;
+                const int pos = (j - 4) & 7;
+                const CPos c = j < 4 ? prev : cp;
+                const bool live = j < 4 ? live_prev : live_cur;
+                const int sl = j & 1;  // slot of step h - 4
                 i32x4 b0[kT], b1[kT], cc[kT];
-                decode_step<kT>(bm[j], sg[j], sh[j], lds, laneoff, b0, b1);
+                decode_step<kT>(bms[sl], sws[sl], shs[sl], lds, laneoff, b0, b1);
 #pragma unroll
                 for (int t = 0; t < kT; ++t) {
-                    cc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xa[j], b0[t], i32x4{0, 0, 0, 0}, 0, 0, 0);
-                    cc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xb[j], b1[t], cc[t], 0, 0, 0);
+                    cc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xa[j & 3], b0[t], i32x4{0, 0, 0, 0}, 0, 0,
+                                                                  0);
+                    cc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xb[j & 3], b1[t], cc[t], 0, 0, 0);
                 }
+                const int g = c.cu * kCG + pos;
 #pragma unroll
                 for (int t = 0; t < kT; ++t) {
-                    const i32x4 c = cc[t];
-                    const int row = rD + 16 * t + lr;
+                    const i32x4 cv = cc[t];
+                    const int row = c.row + 16 * t + lr;
                     if constexpr (ACC) {
                         // acc[m][row][g]: the unit's first row and the group go in the scalar offset
-                        const uint32_t soff = live_or_dead(live, ((uint32_t)rD * (uint32_t)ng + (uint32_t)gD) * 4u);
+                        const uint32_t soff =
+                            live_or_dead(live && g < ng, ((uint32_t)c.row * (uint32_t)ng + (uint32_t)g) * 4u);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int m = 4 * q + i;
-                            st1((uint32_t)c[i], racc,
+                            st1((uint32_t)cv[i], racc,
                                 m < mrows && row < p.n
                                     ? ((uint32_t)(m * p.n) + (uint32_t)(16 * t + lr)) * (uint32_t)ng * 4u
                                     : kOffOff,
                                 soff);
                         }
                     } else {
-                        const double sd = (double)half_bits_to_float((uint16_t)sc[j][t]);
+                        const double sd = (double)half_bits_to_float((uint16_t)scs[sl][t]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) facc[t][i] = __builtin_fma((double)c[i], sd, facc[t][i]);
+                        for (int i = 0; i < 4; ++i) facc[t][i] = __builtin_fma((double)cv[i], sd, facc[t][i]);
                     }
                 }
                 if constexpr (!ACC) {
-                    if (live && gD == ng - 1) {  // the unit's rows are complete
+                    if (pos == kCG - 1) {               // static: the chunk's last step
+                        if (live && c.cu == nck - 1) {  // the unit's rows are complete
 #pragma unroll
-                        for (int t = 0; t < kT; ++t) {
-                            const int row = rD + 16 * t + lr;
+                            for (int t = 0; t < kT; ++t) {
+                                const int row = c.row + 16 * t + lr;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int m = 4 * q + i;
-                                st1(__builtin_bit_cast(uint32_t, (float)facc[t][i]), ry,
-                                    m < mrows && row < p.n ? (uint32_t)(m * p.n + row) * 4u : kOffOff, 0u);
-                                facc[t][i] = 0.0;
+                                for (int i = 0; i < 4; ++i) {
+                                    const int m = 4 * q + i;
+                                    st1(__builtin_bit_cast(uint32_t, (float)facc[t][i]), ry,
+                                        m < mrows && row < p.n ? (uint32_t)(m * p.n + row) * 4u : kOffOff, 0u);
+                                    facc[t][i] = 0.0;
+                                }
                             }
                         }
                     }
                 }
-                const bool wrap = gD == ng - 1;
-                rD = live && wrap ? rD + 16 * kT : rD;
-                gD = live ? (wrap ? 0 : gD + 1) : gD;
             }
             TG_SCHED_FENCE();
-            // ---- bitmap of step h (slot j) and, at a unit's first group, its rows' index entries ----
+            // ---- activation operand of step h - 2: chunk (j < 2 ? prev : cur), position (j - 2) & 7 ----
             {
-                const bool live = h < S;
-                const uint32_t soff = live_or_dead(live, (uint32_t)rB * kb + (uint32_t)gB * 16u);
-                const uint32_t soff_ro = live_or_dead(live && gB == 0, (uint32_t)rB * 4u);
-#pragma unroll
-                for (int t = 0; t < kT; ++t) {
-                    bm[j][t] = ld1(rbm, (uint32_t)(16 * t + lr) * kb + 4u * (uint32_t)q, soff);
-                    ro[j][t] = ld1(rro, (uint32_t)(16 * t + lr) * 4u, soff_ro);
-                }
-                const bool wrap = gB == ng - 1;
-                rB = live && wrap ? rB + 16 * kT : rB;
-                gB = live ? (wrap ? 0 : gB + 1) : gB;
+                const int pos = (j - 2) & 7;
+                const CPos c = j < 2 ? prev : cp;
+                const bool live = j < 2 ? live_prev : live_cur;
+                const uint32_t soff = live_or_dead(live, (uint32_t)(c.cu * kCG + pos) * 128u);
+                xa[(j + 2) & 3] = ld4(rx, voff_x, soff);
+                xb[(j + 2) & 3] = ld4(rx, voff_x + 16u, soff);
             }
             TG_SCHED_FENCE();
-            // ---- signs, activations and scales of step h - kLagS (slot (j - kLagS) & 3) ----
-            {
-                const int s = h - kLagS;
-                const int k3 = (j + 4 - kLagS) & 3;
-                const bool live = s >= 0 && s < S;
-                const uint32_t sd = live_or_dead(live, 0u);
-                const bool first = gS == 0;
+            if (j == 3) {
+                // ---- chunk ci's data to its stage homes; chunk ci + 1's sign stretches ----
 #pragma unroll
                 for (int t = 0; t < kT; ++t) {
-                    const uint32_t c = __builtin_popcount(bm[k3][t]);
-                    // lanes of one row: quarters 0..3 at l, l + 16, l + 32, l + 48
-                    const auto ev = __builtin_amdgcn_permlane16_swap(c, c, false, false);  // quarters (0,0,2,2), (1,1,3,3)
-                    const uint32_t pair = ev[0] + ev[1];                                     // c0 + c1 or c2 + c3
-                    const auto hv = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);  // c0 + c1, c2 + c3
-                    const uint32_t base = first ? ro[k3][t] : cur[t];
-                    const uint32_t pos = base + (ev[0] & m_odd) + (hv[0] & m_hi);
-                    cur[t] = base + hv[0] + hv[1];
-                    // window from 3 bits before the first sign, biased by +32 (resource starts 4 bytes early)
-                    const uint32_t b = pos + 29u;
-                    sg[k3][t] = ld3(rsg, (b >> 5) << 2, sd);
-                    sh[k3][t] = b;
-                }
-                const uint32_t soff_x = live_or_dead(live, (uint32_t)gS * 128u);
-                xa[k3] = ld4(rx, voff_x, soff_x);
-                xb[k3] = ld4(rx, voff_x + 16u, soff_x);
-                if constexpr (!ACC) {
-                    const uint32_t soff_sc = live_or_dead(live, ((uint32_t)rS * (uint32_t)ng + (uint32_t)gS) * 2u);
+                    // bitmap: lane row a loaded groups 2a, 2a + 1; lane row q wants dword q of each group
+                    transpose4(rawb[t][0], rawb[t][1], rawb[t][2], rawb[t][3]);
+                    transpose4(rawb[t][4], rawb[t][5], rawb[t][6], rawb[t][7]);
 #pragma unroll
-                    for (int t = 0; t < kT; ++t)
-                        sc[k3][t] = ldh(rsc, (uint32_t)(16 * t + lr) * (uint32_t)ng * 2u, soff_sc);
+                    for (int a = 0; a < 4; ++a) {
+                        bmc[t][2 * a] = rawb[t][a];
+                        bmc[t][2 * a + 1] = rawb[t][4 + a];
+                    }
+                    if constexpr (!ACC) gather4(raws[t][0] | (raws[t][1] << 16), scc[t]);
+                    // the sign stretch to this wave's LDS rows
+#pragma unroll
+                    for (int i = 0; i < kSWL; ++i) stg_row[t][kSWL * q + i] = rawsg[t][i];
+                    d0c[t] = d0n[t];
+                    cur[t] = cbn[t];
+                    // row total of the chunk's signs, and the next chunk's first sign
+                    uint32_t cnt = 0;
+#pragma unroll
+                    for (int g = 0; g < kCG; ++g) cnt = __builtin_popcount(bmc[t][g]) + cnt;
+                    uint32_t ce = cnt, co = cnt;
+                    swap16(ce, co);
+                    uint32_t pr = ce + co, pr2 = pr;
+                    swap32(pr, pr2);
+                    cbn[t] = nx.cu == 0 ? ro_cur[t] : cbn[t] + pr + pr2;
                 }
-                const bool wrap = gS == ng - 1;
-                rS = live && wrap ? rS + 16 * kT : rS;
-                gS = live ? (wrap ? 0 : gS + 1) : gS;
+                load_ro(nn, ci + 2 < NC);
+                load_signs(ci + 1 < NC);
+            }
+            TG_SCHED_FENCE();
+            if (j == 5) load_chunk(nx, ci + 1 < NC);
+            TG_SCHED_FENCE();
+            // ---- sign windows of step h - 3: chunk (j < 3 ? prev : cur), position (j - 3) & 7 ----
+            {
+                const int pos = (j - 3) & 7;
+                const int sl = (j + 1) & 1;  // slot of step h - 3
+#pragma unroll
+                for (int t = 0; t < kT; ++t) {
+                    const uint32_t bw = bmc[t][pos];
+                    const uint32_t c = __builtin_popcount(bw);
+                    uint32_t ev = c, od = c;
+                    swap16(ev, od);  // quarters (0, 0, 2, 2) and (1, 1, 3, 3)
+                    uint32_t pr = ev + od, pr2 = pr;
+                    swap32(pr, pr2);  // c0 + c1 and c2 + c3
+                    const uint32_t pq = cur[t] + (ev & m_odd) + (pr & m_hi);
+                    cur[t] += pr + pr2;
+                    const uint32_t b = pq + 29u;  // window from 3 bits before the first sign, +32 bias
+                    const uint32_t *src = stg_row[t] + ((b >> 5) - d0c[t]);
+                    sws[sl][t][0] = src[0];
+                    sws[sl][t][1] = src[1];
+                    sws[sl][t][2] = src[2];
+                    shs[sl][t] = b;
+                    bms[sl][t] = bw;
+                    scs[sl][t] = (scc[t][pos >> 1] >> (16 * (pos & 1))) & 0xFFFFu;
+                }
             }
             TG_SCHED_FENCE();
         }
+        if (ci + 1 <= NC) {
+#pragma unroll
+            for (int t = 0; t < kT; ++t) ro_cur[t] = ro_nxt[t];
+        }
+        prev = cp;
+        cp = nx;
     }
 }
 
 template <bool ACC>
 __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
     __shared__ uint4 s_tab[kTabBytes / 16];
+    __shared__ uint32_t s_stage[kWaves * kStageDwords];
     load_bitcos_tables<kBlock>(s_tab);
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    uint32_t *stg = s_stage + wave * kStageDwords;
     int u, u_end, pi;
     wave_range<kWaves>(ga, wave, u, u_end, pi);
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
         const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_mfma<ACC>(p, u, u1, ga.m, lds);
+        if (u < u1) run_mfma<ACC>(p, u, u1, ga.m, lds, stg);
         u = max(u, u1);
         ++pi;
     }

@@ -71,7 +71,7 @@ void gemv_geometry(Problem &p, int m);
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
 // units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU.
 constexpr int kMfmaMinM = 4;
-constexpr int kMfmaTiles = 4;
+constexpr int kMfmaTiles = 2;
 constexpr int kMfmaWavesPerCu = 8;
 void mfma_geometry(Problem &p);
 hipError_t launch_bitcos_mfma(const GroupArgs &g, bool acc_out, hipStream_t s);
