@@ -141,6 +141,208 @@ def load_traffic():
     return t
 
 
+# ----- measurement suite: every configuration of the workload table, beside the headline step -----
+
+def replicas(B, dw0, count):
+    """`count` device copies of one packed matrix (distinct memory, same bytes)."""
+    return [dw0] + [B.DeviceWeights.from_tensor(dw0.desc, dw0.tensor.clone()) for _ in range(count - 1)]
+
+
+def packed_bytes(dw):
+    return dw.payload_bytes + 2 * dw.n * (dw.k // 128)
+
+
+def per_call_us(torch, calls, warmup=10):
+    """Eager launches of calls() (a list of thunks); one HIP event between consecutive launches, so
+    each duration includes its launch gap. Returns median, p10, p90 in microseconds."""
+    for f in calls[:warmup]:
+        f()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    ev[0].record()
+    for i, f in enumerate(calls):
+        f()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(len(calls))])
+    return {"median_us": round(float(np.median(d)), 3), "p10_us": round(float(np.percentile(d, 10)), 3),
+            "p90_us": round(float(np.percentile(d, 90)), 3), "calls": len(calls)}
+
+
+def sustained(torch, B, dws, xs, ss, ys, launches=5):
+    """One grouped launch over all GEMVs: packed bytes per second and ms per launch."""
+    plan = B.Plan(dws, xs, scales=ss, ys=ys)
+    secs = time_launches(torch, plan.run, launches, 1)
+    total = sum(packed_bytes(d) for d in dws)
+    return {"gbs": round(total * launches / secs / 1e9, 1), "ms_per_launch": round(secs / launches * 1e3, 4),
+            "bytes_per_launch": total}
+
+
+def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label=""):
+    """One matrix shape in `fmts`, `reps` device copies each: per-call stats cycling through the copies
+    (>= 200 calls), and the grouped sustained rate measured `rounds` times with the format order
+    rotated every round; format comparisons are medians of per-round time ratios."""
+    w = synth.ternary(n, k, z, seed=0)
+    s = torch.from_numpy(synth.scales(n, k // 128, seed=0)).to(dev)
+    x = torch.from_numpy(synth.activations(m, k, seed=0)).to(dev)
+    sets = {}
+    for f in fmts:
+        dw0 = B.DeviceWeights(B.pack(f, w), dev)
+        sets[f] = replicas(B, dw0, reps)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    out = {"n": n, "k": k, "m": m, "z": z, "replicas": reps, "x_bytes": m * k, "y_bytes": 4 * m * n}
+    rates = {f: [] for f in fmts}
+    for r in range(rounds):
+        order = fmts[r % len(fmts):] + fmts[:r % len(fmts)]
+        for f in order:
+            dws = sets[f]
+            rates[f].append(sustained(torch, B, dws, [x] * len(dws), [s] * len(dws), [y] * len(dws), launches=3))
+    for f in fmts:
+        dws = sets[f]
+        ncalls = max(200, len(dws))
+        calls = [(lambda d=dws[i % len(dws)]: B.ternary_gemv(d, s, x, y)) for i in range(ncalls)]
+        pc = per_call_us(torch, calls)
+        pc["gbs_at_median"] = round(packed_bytes(dws[0]) / pc["median_us"] / 1e3, 1)
+        ms = [r["ms_per_launch"] for r in rates[f]]
+        out[B.FMT_NAMES[f]] = {"packed_bytes": packed_bytes(dws[0]),
+                               "sustained_gbs_median": round(float(np.median([r["gbs"] for r in rates[f]])), 1),
+                               "sustained_ms_per_launch_median": round(float(np.median(ms)), 4),
+                               "per_call": pc}
+    if B.FMT_BITCOS in fmts:
+        for f in fmts:
+            if f == B.FMT_BITCOS:
+                continue
+            ratio = [a["ms_per_launch"] / b["ms_per_launch"] for a, b in zip(rates[f], rates[B.FMT_BITCOS])]
+            out[f"time_{B.FMT_NAMES[f]}_over_bitcos"] = round(float(np.median(ratio)), 4)
+            out[f"bytes_{B.FMT_NAMES[f]}_over_bitcos"] = round(packed_bytes(sets[f][0]) /
+                                                              packed_bytes(sets[B.FMT_BITCOS][0]), 4)
+    del sets
+    torch.cuda.empty_cache()
+    log(f"[suite] {label} done")
+    return out
+
+
+def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
+    """gate 14336x4096 and down 4096x14336 at z = 0.44, BITCOS, activation rows m in `ms`."""
+    out = {}
+    for name, n, k, role in (("gate", 14336, 4096, 4), ("down", 4096, 14336, 6)):
+        w = synth.ternary(n, k, 0.44, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+        s = torch.from_numpy(synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))).to(dev)
+        dws = replicas(B, B.DeviceWeights(B.pack_bitcos(w), dev), reps)
+        for m in ms:
+            x = torch.from_numpy(synth.activations(m, k, seed=m)).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            st = sustained(torch, B, dws, [x] * reps, [s] * reps, [y] * reps)
+            calls = [(lambda d=dws[i % reps]: B.ternary_gemv(d, s, x, y)) for i in range(max(200, reps))]
+            pc = per_call_us(torch, calls)
+            out[f"{name}_m{m}"] = {"n": n, "k": k, "m": m, "path": "matrix-core" if m >= 4 else "vector",
+                                   "sustained_gbs": st["gbs"], "sustained_us_per_gemv": round(st["ms_per_launch"] * 1e3 / reps, 3),
+                                   "per_call": pc, "packed_bytes": packed_bytes(dws[0]), "x_bytes": m * k,
+                                   "y_bytes": 4 * m * n}
+        del dws
+        torch.cuda.empty_cache()
+    log("[suite] thin batch done")
+    return out
+
+
+def suite_70b(torch, B, synth, dev, layers=64, z=0.47):
+    """Llama-70B-shaped layer stack at batch 1 (q, o 5120x5120; k, v 1024x5120; gate, up 25600x5120;
+    down 5120x25600), 1219 dead FFN rows per layer at the same indices in gate and up. One layer is
+    generated and stored `layers` times (6.08 GB of BITCOS for 64), so every byte comes from HBM."""
+    shapes = [("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
+              ("gate", 25600, 5120), ("up", 25600, 5120), ("down", 5120, 25600)]
+    dead = synth.dead_rows(25600, 1219, seed=0)
+    base = []
+    for role, (name, n, k) in enumerate(shapes):
+        w = synth.ternary(n, k, z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+        if name in ("gate", "up"):
+            w[dead] = 0
+        s = torch.from_numpy(synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))).to(dev)
+        x = torch.from_numpy(synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))).to(dev)
+        base.append((B.DeviceWeights(B.pack_bitcos(w), dev), s, x, n))
+        del w
+    dws, xs, ss, ys = [], [], [], []
+    for layer in range(layers):
+        for dw0, s, x, n in base:
+            dws.append(dw0 if layer == 0 else B.DeviceWeights.from_tensor(dw0.desc, dw0.tensor.clone()))
+            xs.append(x)
+            ss.append(s)
+            ys.append(torch.empty((1, n), dtype=torch.float32, device=dev))
+    st = sustained(torch, B, dws, xs, ss, ys, launches=5)
+    per_layer = [B.Plan(dws[7 * l:7 * l + 7], xs[7 * l:7 * l + 7], scales=ss[7 * l:7 * l + 7], ys=ys[7 * l:7 * l + 7])
+                 for l in range(layers)]
+    sl = time_launches(torch, lambda: [p.run() for p in per_layer], 3, 1)
+    out = {"layers": layers, "z": z, "dead_rows_per_layer": int(dead.size), "bytes_per_pass": st["bytes_per_launch"],
+           "grouped_one_launch": {"gbs": st["gbs"], "us_per_pass": round(st["ms_per_launch"] * 1e3, 1)},
+           "per_layer_launch": {"gbs": round(st["bytes_per_launch"] * 3 / sl / 1e9, 1),
+                                "us_per_pass": round(sl / 3 * 1e6, 1)}}
+    del dws, per_layer
+    torch.cuda.empty_cache()
+    log("[suite] 70B-shaped stack done")
+    return out
+
+
+def suite_cpu(O, B, synth):
+    """The oracle from packed BITCOS bytes on one core and on all cores (2560x2560 and 4096x4096)."""
+    import subprocess
+    try:
+        model = [l.split(":", 1)[1].strip() for l in subprocess.run(["lscpu"], capture_output=True, text=True).stdout.splitlines()
+                 if l.startswith("Model name")][0]
+    except Exception:
+        model = "unknown"
+    cores = len(os.sched_getaffinity(0))
+    out = {"cpu_model": model, "cores_available": cores}
+    for n, k, z in ((2560, 2560, 0.42), (4096, 4096, 0.40)):
+        w = synth.ternary(n, k, z, seed=0)
+        p = B.pack_bitcos(w)
+        s = synth.scales(n, k // 128, seed=0)
+        x = synth.activations(1, k, seed=0)
+        nbytes = p.desc.bytes_payload + 2 * n * (k // 128)
+        res = {}
+        for th in (1, cores):
+            O.set_threads(th)
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                O.gemv_packed(O.FMT_BITCOS, p.section("codes"), p.sign_bytes(), p.rowoff(), s, n, k, x)
+                ts.append(time.perf_counter() - t0)
+            t = float(np.median(ts))
+            res[f"threads_{th}"] = {"ms": round(t * 1e3, 3), "gbs": round(nbytes / t / 1e9, 4)}
+        out[f"{n}x{k}"] = res
+    O.set_threads(cores)
+    return out
+
+
+def run_suite(path):
+    import torch
+
+    import bit_gemv_decode_amd as B
+    from bit_gemv_decode_amd import binding as bd
+    from bit_gemv_decode_amd import synth
+
+    dev = torch.device("cuda:0")
+    F = [B.FMT_BITCOS, B.FMT_5TRIT, B.FMT_2BIT]
+    res = {"command": f"python3 bench.py --suite {path}", "device": torch.cuda.get_device_name(0),
+           "hbm_peak_gbs": HBM_PEAK_GBS,
+           "note": "packed bytes = bitmap + sign stream + row index + fp16 scales (BITCOS) or codes + fp16 "
+                   "scales; x and y bytes are listed apart; per-call times are HIP-event intervals between "
+                   "consecutive eager launches (launch gaps included), cycling through the copies"}
+    log("[suite] stream-read ceiling")
+    res["stream_read_ceiling_gbs"] = round(stream_ceiling(torch, bd, dev), 1)
+    res["single_2560"] = suite_single(torch, B, synth, dev, 2560, 2560, 0.42, 768, F, label="2560x2560")
+    res["zero_density_8192"] = {str(z): suite_single(torch, B, synth, dev, 8192, 8192, z, 96, F, label=f"8192 z={z}")
+                                for z in (0.30, 0.375, 0.42, 0.47, 0.515)}
+    res["thin_batch"] = suite_thin(torch, B, synth, dev)
+    res["llama70b_stack"] = suite_70b(torch, B, synth, dev)
+    import oracle as O
+    log("[suite] CPU oracle")
+    res["cpu_oracle"] = suite_cpu(O, B, synth)
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"suite": path}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,12 +350,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--quick", action="store_true", help="only the timed BITCOS step (for profiling runs)")
+    ap.add_argument("--suite", metavar="PATH", help="run the measurement suite over every workload "
+                    "configuration instead (several minutes) and write its JSON report to PATH")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the ternary GEMV shards across GPUs by rows (or by k with one "
               "all-reduce of the output vector) in a deployment, but this build runs on a single MI355X. "
               "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.suite:
+        run_suite(args.suite)
+        return
 
     import torch
 
@@ -196,7 +404,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic["bytes_per_launch"] / ls.step_bytes, 4) if traffic else None),
-                     "kernel": "bitcos_gemv_kernel<1,false,4> (grouped, one launch per step)",
+                     "kernel": "bitcos_gemv_kernel<1,false> (grouped, one launch per step)",
                      "algorithmic_bytes_per_launch": ls.step_bytes,
                      "avg_launch_us": round(step_s * 1e6, 2)},
     }

@@ -67,6 +67,8 @@ def lib():
         L.oracle_gemv_packed.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -202,3 +204,8 @@ def gemv_packed(fmt: int, a: np.ndarray, b: np.ndarray | None, rowoff: np.ndarra
 
 def threads() -> int:
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of later oracle calls (timing only: results do not depend on it)."""
+    lib().oracle_set_threads(int(n))

@@ -283,6 +283,17 @@ int oracle_gemv_packed(int fmt, const uint8_t *a, const uint8_t *b, const uint32
     return bad ? -1 : 0;
 }
 
+/* Threads later parallel regions of this library use (n >= 1; no effect without OpenMP). Used to time
+ * the CPU baseline on one core and on all cores; it changes no result. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads an OpenMP parallel region of this library uses (1 without OpenMP). */
 int oracle_threads(void) {
     int t = 1;
