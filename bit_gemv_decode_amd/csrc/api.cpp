@@ -136,6 +136,23 @@ int plan_max_m(int fmt) { return fmt == TG_FMT_BITCOS ? TG_MAX_M : kVectorMaxM; 
 
 size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
 
+// Extra cost of a chunk pass of the vector path, in steps: the lanes reload their activation slice
+// (measured on MI355X over the Llama3-8B layer set: about half a step for BITCOS, whose steps are
+// longer, one step for the fixed-size codes).
+double pass_cost(int fmt) { return fmt == TG_FMT_BITCOS ? 0.5 : 1.0; }
+
+// Relative time of work unit u of p, for splitting a plan's units across waves. Every step of the
+// vector path costs about the same (one 128-weight group per lane, however many lanes are busy), so a
+// unit costs its step count, plus the activation reloads of chunked rows; a unit of the matrix-core
+// path costs its chunk count (all units of one plan take the same path).
+double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u) {
+    const int64_t row0 = (u - p.unit_begin) * (int64_t)p.rpu;
+    const int64_t rows = std::min<int64_t>(p.rpu, (int64_t)p.n - row0);
+    if (mfma) return (double)((p.ng + 7) / 8);
+    if (p.nch == 1) return (double)((rows + p.R - 1) / p.R);
+    return (double)rows * ((double)p.nch + pass_cost(fmt));
+}
+
 }  // namespace
 
 extern "C" size_t tg_plan_table_bytes(int32_t count) {
@@ -165,7 +182,6 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
             return TG_EINVAL;
     }
     int64_t units = 0;
-    double total_cost = 0;
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
@@ -174,10 +190,14 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         geometry(host[i], fmt, m);
         rpu = std::max(rpu, (int)host[i].rpu);
         units += host[i].nunits;
-        total_cost += (double)d->n * (double)d->k;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
-    // Contiguous unit ranges per wave, balanced by cost (rows x k of each unit).
+    const bool mfma = use_mfma(fmt, m);
+    double total_cost = 0;
+    for (int32_t i = 0; i < count; ++i)
+        for (int64_t u = host[i].unit_begin; u < host[i].unit_begin + host[i].nunits; ++u)
+            total_cost += unit_cost(host[i], fmt, mfma, u);
+    // Contiguous unit ranges per wave, balanced by the cost model above.
     const int nw = plan_waves(fmt, m);
     std::vector<WaveRange> ranges((size_t)nw);
     {
@@ -190,9 +210,7 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
             const double target = total_cost * (double)(w + 1) / (double)nw;
             while (u < units) {
                 while (pi + 1 < count && u >= host[pi + 1].unit_begin) ++pi;
-                const int64_t prpu = host[pi].rpu;
-                const int64_t row0 = (u - host[pi].unit_begin) * prpu;
-                const double cost = (double)std::min<int64_t>(prpu, host[pi].n - row0) * (double)host[pi].k;
+                const double cost = unit_cost(host[pi], fmt, mfma, u);
                 if (done + 0.5 * cost > target && w + 1 < nw) break;
                 done += cost;
                 ++u;

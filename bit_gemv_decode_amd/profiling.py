@@ -25,8 +25,8 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 # the BITCOS kernel's source and the device headers it compiles from
-KERNEL_SRCS = [os.path.join(PKG, "csrc", f) for f in ("bitcos_gemv.hip", "bitcos_tables.h", "gemv_pipeline.h", "device_common.h",
-                                                         "tg_internal.h")]
+KERNEL_SRCS = [os.path.join(PKG, "csrc", f)
+               for f in ("bitcos_gemv.hip", "bitcos_tables.h", "gemv_pipeline.h", "device_common.h")]
 READ_BYTES = 2 * 1024 ** 3
 WRITE_BYTES = 1024 ** 3
 
