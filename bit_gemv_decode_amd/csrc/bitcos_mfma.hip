@@ -1,10 +1,12 @@
 // Thin-batch BITCOS GEMV on matrix cores (gfx950): m = 4 .. 16 activation rows read the packed
 // weights once.
 //
-// Once activations form a small matrix, decoding turns the ternary weights into int8 operands of a
-// matrix product ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. III: batched decoding is a
-// matrix product; the int8 path of Sec. II-C: w = p - 2n by Eq. 2, int32 per-group sums times the
-// group scale). Here the product is v_mfma_i32_16x16x64_i8 with
+// Once activations form a small matrix the GEMV is a matrix product, and the ternary weights are
+// expanded into int8 operands of a matrix engine (the untitled page on a NUMA-aware decode engine for
+// ternary models, Sec. 6.5 and its appendix "Ternary GEMM on AMX", where 2-bit rows are expanded into
+// int8 tiles). The values follow the int8 path of "Breaking the 1.58-bit Barrier for Ternary LLMs",
+// Sec. II-C: w = p - 2n by Eq. 2, int32 per-group sums times the group scale. Here the product is
+// v_mfma_i32_16x16x64_i8 with
 //   A = X[m][k]  (16 activation rows, rows at and beyond m read as zero),
 //   B = W^T      (16 weight rows of one tile, decoded in registers),
 // so C[m][row] comes out per 128-weight group in int32 and takes that group's fp16 scale in fp64.

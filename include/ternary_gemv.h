@@ -126,9 +126,10 @@ int tg_unpack(const void *packed, size_t bytes, int8_t *w_out);
  * Paths: m <= 3 uses the vector kernels (int8 dot products in int32, "Breaking the 1.58-bit Barrier
  * for Ternary LLMs", Sec. II-C); five-trit and 2-bit with m > 3 run them in launches of up to three
  * rows. BITCOS with m >= 4 is the thin-batch path: one launch decodes each weight once into int8
- * operands of int8 matrix-core products against X padded to 16 rows (the same paper, Sec. III:
- * batched decoding becomes a matrix product). Every path produces the same exact int32 group sums
- * and the same fp32 outputs.
+ * operands of int8 matrix-core products against X padded to 16 rows (a batch turns the GEMV into a
+ * matrix product; the untitled page on a NUMA-aware decode engine for ternary models, Sec. 6.5 and
+ * its appendix "Ternary GEMM on AMX", expands ternary weights into int8 matrix-engine tiles the same
+ * way). Every path produces the same exact int32 group sums and the same fp32 outputs.
  * The kernels trust W's contents as far as its descriptor describes them (validate host buffers
  * with tg_validate before upload); every device read stays inside the sections the descriptor
  * names even for corrupt contents, so a corrupt buffer gives wrong numbers, not a fault.
