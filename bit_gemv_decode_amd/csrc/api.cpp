@@ -181,14 +181,24 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
                      : (!y[i] || !scales[i] || ((uintptr_t)y[i] & 3) || ((uintptr_t)scales[i] & 1)))
             return TG_EINVAL;
     }
-    int64_t units = 0;
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr);
-        host[i].unit_begin = (int32_t)units;
         geometry(host[i], fmt, m);
         rpu = std::max(rpu, (int)host[i].rpu);
+    }
+    // Work order: GEMVs of one shape next to each other (by k, then n; the caller's order within a
+    // shape). Each Problem carries its own pointers, so the order changes no result; on MI355X it
+    // keeps the waves of a CU and of an XCD on one kind of work, which measured 15 % faster on the
+    // Llama3-8B layer set than the layer-by-layer order (mixed shapes per CU run slower than the
+    // same units grouped by shape).
+    std::stable_sort(host.begin(), host.end(), [](const Problem &a, const Problem &b) {
+        return a.k != b.k ? a.k < b.k : a.n < b.n;
+    });
+    int64_t units = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        host[i].unit_begin = (int32_t)units;
         units += host[i].nunits;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
