@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-SETTLE = 30  # warm-up launches before a sustained-rate measurement (see --warmup)
+SETTLE_MS = 60.0  # GPU time of warm-up launches before a sustained-rate measurement (see --warmup)
 LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
 LAYERS = 32
@@ -93,6 +93,22 @@ def time_launches(torch, fn, steps, warmup):
     e1.record(cur)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Launch fn() until about `ms` of GPU time has passed, so that the timed launches that follow run
+    at the sustained rate, past the power transient of the first back-to-back launches."""
+    cur = torch.cuda.current_stream()
+    spent, batch = 0.0, 1
+    while spent < ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(batch):
+            fn()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+        batch = min(batch * 2, 64)
 
 
 def stream_ceiling(torch, bd, dev):
@@ -173,7 +189,8 @@ def per_call_us(torch, calls, warmup=10):
 def sustained(torch, B, dws, xs, ss, ys, launches=5):
     """One grouped launch over all GEMVs: packed bytes per second and ms per launch."""
     plan = B.Plan(dws, xs, scales=ss, ys=ys)
-    secs = time_launches(torch, plan.run, launches, SETTLE)
+    settle(torch, plan.run)
+    secs = time_launches(torch, plan.run, launches, 0)
     total = sum(packed_bytes(d) for d in dws)
     return {"gbs": round(total * launches / secs / 1e9, 1), "ms_per_launch": round(secs / launches * 1e3, 4),
             "bytes_per_launch": total}
@@ -272,7 +289,8 @@ def suite_70b(torch, B, synth, dev, layers=64, z=0.47):
     st = sustained(torch, B, dws, xs, ss, ys, launches=5)
     per_layer = [B.Plan(dws[7 * l:7 * l + 7], xs[7 * l:7 * l + 7], scales=ss[7 * l:7 * l + 7], ys=ys[7 * l:7 * l + 7])
                  for l in range(layers)]
-    sl = time_launches(torch, lambda: [p.run() for p in per_layer], 3, 8)
+    settle(torch, lambda: [p.run() for p in per_layer])
+    sl = time_launches(torch, lambda: [p.run() for p in per_layer], 3, 0)
     out = {"layers": layers, "z": z, "dead_rows_per_layer": int(dead.size), "bytes_per_pass": st["bytes_per_launch"],
            "grouped_one_launch": {"gbs": st["gbs"], "us_per_pass": round(st["ms_per_launch"] * 1e3, 1)},
            "per_layer_launch": {"gbs": round(st["bytes_per_launch"] * 3 / sl / 1e9, 1),
