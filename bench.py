@@ -186,6 +186,21 @@ def per_call_us(torch, calls, warmup=10):
             "p90_us": round(float(np.percentile(d, 90)), 3), "calls": len(calls)}
 
 
+def graph_call_us(torch, calls, reps=5):
+    """The same calls captured in one HIP graph and replayed: microseconds per call with the host
+    launch path removed (kernel time plus the gap between consecutive graph nodes)."""
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=st):
+        for f in calls:
+            f()
+    settle(torch, g.replay, ms=20.0)
+    secs = time_launches(torch, g.replay, reps, 0)
+    del g
+    return round(secs / (reps * len(calls)) * 1e6, 3)
+
+
 def sustained(torch, B, dws, xs, ss, ys, launches=5):
     """One grouped launch over all GEMVs: packed bytes per second and ms per launch."""
     plan = B.Plan(dws, xs, scales=ss, ys=ys)
@@ -221,6 +236,8 @@ def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label
         calls = [(lambda d=dws[i % len(dws)]: B.ternary_gemv(d, s, x, y)) for i in range(ncalls)]
         pc = per_call_us(torch, calls)
         pc["gbs_at_median"] = round(packed_bytes(dws[0]) / pc["median_us"] / 1e3, 1)
+        pc["graph_us_per_call"] = graph_call_us(torch, calls)
+        pc["graph_gbs"] = round(packed_bytes(dws[0]) / pc["graph_us_per_call"] / 1e3, 1)
         ms = [r["ms_per_launch"] for r in rates[f]]
         out[B.FMT_NAMES[f]] = {"packed_bytes": packed_bytes(dws[0]),
                                "sustained_gbs_median": round(float(np.median([r["gbs"] for r in rates[f]])), 1),
@@ -253,6 +270,7 @@ def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
             st = sustained(torch, B, dws, [x] * reps, [s] * reps, [y] * reps)
             calls = [(lambda d=dws[i % reps]: B.ternary_gemv(d, s, x, y)) for i in range(max(200, reps))]
             pc = per_call_us(torch, calls)
+            pc["graph_us_per_call"] = graph_call_us(torch, calls)
             out[f"{name}_m{m}"] = {"n": n, "k": k, "m": m, "path": "matrix-core" if m >= 4 else "vector",
                                    "sustained_gbs": st["gbs"], "sustained_us_per_gemv": round(st["ms_per_launch"] * 1e3 / reps, 3),
                                    "per_call": pc, "packed_bytes": packed_bytes(dws[0]), "x_bytes": m * k,
@@ -345,7 +363,8 @@ def run_suite(path):
            "hbm_peak_gbs": HBM_PEAK_GBS,
            "note": "packed bytes = bitmap + sign stream + row index + fp16 scales (BITCOS) or codes + fp16 "
                    "scales; x and y bytes are listed apart; per-call times are HIP-event intervals between "
-                   "consecutive eager launches (launch gaps included), cycling through the copies"}
+                   "consecutive eager launches (launch gaps included), cycling through the copies; "
+                   "graph_us_per_call replays the same calls from one HIP graph (host launch path removed)"}
     log("[suite] stream-read ceiling")
     res["stream_read_ceiling_gbs"] = round(stream_ceiling(torch, bd, dev), 1)
     res["single_2560"] = suite_single(torch, B, synth, dev, 2560, 2560, 0.42, 768, F, label="2560x2560")
