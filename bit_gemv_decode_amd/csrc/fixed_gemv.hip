@@ -308,14 +308,21 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void fixed_gemv_kernel(GroupArgs ga)
     __shared__ uint4 s_lut[kLutBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     {
-        uint32_t *l = reinterpret_cast<uint32_t *>(s_lut);
+        // one load per thread: its consecutive copies all belong to one code byte, so the fill is
+        // one memory round trip
+        const int t = threadIdx.x;
         if constexpr (FMT == TG_FMT_2BIT) {
-            for (int i = threadIdx.x; i < 256 * 64; i += BLOCK) l[i] = kFixedTables.b2[i >> 6];
+            constexpr int kPer = 256 * 64 / BLOCK;  // 4-byte copies per thread
+            static_assert(kPer % 4 == 0 && 64 % kPer == 0, "a thread's copies must share a code byte");
+            const uint32_t v = kFixedTables.b2[(t * kPer) >> 6];
+#pragma unroll
+            for (int j = 0; j < kPer / 4; ++j) s_lut[t * (kPer / 4) + j] = make_uint4(v, v, v, v);
         } else {
-            for (int i = threadIdx.x; i < 256 * 32; i += BLOCK) {
-                l[2 * i] = kFixedTables.t5[i >> 5][0];
-                l[2 * i + 1] = kFixedTables.t5[i >> 5][1];
-            }
+            constexpr int kPer = 256 * 32 / BLOCK;  // 8-byte copies per thread
+            static_assert(kPer % 2 == 0 && 32 % kPer == 0, "a thread's copies must share a code byte");
+            const uint32_t lo = kFixedTables.t5[(t * kPer) >> 5][0], hi = kFixedTables.t5[(t * kPer) >> 5][1];
+#pragma unroll
+            for (int j = 0; j < kPer / 2; ++j) s_lut[t * (kPer / 2) + j] = make_uint4(lo, hi, lo, hi);
         }
     }
     __syncthreads();
