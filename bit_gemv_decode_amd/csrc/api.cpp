@@ -68,7 +68,7 @@ void geometry(Problem &p, int fmt, int32_t m) {
     if (use_mfma(fmt, m))
         mfma_geometry(p);
     else
-        gemv_geometry(p, m);
+        gemv_geometry(p, fmt, m);
 }
 
 hipError_t launch(int fmt, const GroupArgs &g, bool acc_out, hipStream_t s) {
@@ -136,10 +136,10 @@ int plan_max_m(int fmt) { return fmt == TG_FMT_BITCOS ? TG_MAX_M : kVectorMaxM; 
 
 size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
 
-// Extra cost of a chunk pass of the vector path, in steps: the lanes reload their activation slice
-// (measured on MI355X over the Llama3-8B layer set: about half a step for BITCOS, whose steps are
-// longer, one step for the fixed-size codes).
-double pass_cost(int fmt) { return fmt == TG_FMT_BITCOS ? 0.5 : 1.0; }
+// Extra cost per row of a chunk pass of the vector path, in steps: the lanes reload their activation
+// slice once per pass of a unit, shared by its rows (measured on MI355X over the Llama3-8B layer set:
+// about two steps per pass for BITCOS, whose steps are longer, four for the fixed-size codes).
+double pass_cost(int fmt, int rows_per_unit) { return (fmt == TG_FMT_BITCOS ? 2.0 : 4.0) / rows_per_unit; }
 
 // Relative time of work unit u of p, for splitting a plan's units across waves. Every step of the
 // vector path costs about the same (one 128-weight group per lane, however many lanes are busy), so a
@@ -150,7 +150,7 @@ double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u) {
     const int64_t rows = std::min<int64_t>(p.rpu, (int64_t)p.n - row0);
     if (mfma) return (double)((p.ng + 7) / 8);
     if (p.nch == 1) return (double)((rows + p.R - 1) / p.R);
-    return (double)rows * ((double)p.nch + pass_cost(fmt));
+    return (double)rows * ((double)p.nch + pass_cost(fmt, p.rpu));
 }
 
 }  // namespace

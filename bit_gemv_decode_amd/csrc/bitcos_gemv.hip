@@ -7,7 +7,7 @@
 // negative) pair into w = p - 2n (Eq. 2), contracts against int8 activations in int32 and applies
 // the group scale once per 128-element group.
 //
-// Mapping on CDNA4 (wave64, one 1024- or 512-thread block per CU, persistent):
+// Mapping on CDNA4 (wave64, one persistent block per CU: 768 threads at m = 1, 512 at m = 2, 3):
 //   * a lane owns one 128-weight group of one row per step: its four bitmap dwords arrive with one
 //     16-byte load, its scale with one 2-byte load. A row of k weights takes ng = k/128 lanes; when
 //     ng <= 64 a step holds R = 64/ng consecutive rows, otherwise a row is split into chunks of 64
@@ -29,9 +29,10 @@
 //     masks.
 //   * v_dot4_i32_i8 contracts 4 weights per instruction. Each group's int32 sum times its fp16 scale
 //     (exact in fp64) goes to an LDS tile; once per unit the tile's rows are summed (fp64, DPP) and
-//     stored as fp32.
+//     stored as fp32. Chunked rows at m = 1 keep those terms in registers instead (one fp64 per row
+//     of the unit and lane) and reduce them over the wave at the unit's end.
 //   * loads are software-pipelined two steps ahead (bitmap) and one step ahead (signs), with the loop
-//     unrolled twice so that no register with a load in flight is ever copied. Every load goes
+//     unrolled at least twice so that no register with a load in flight is ever copied. Every load goes
 //     through a buffer resource and is issued unconditionally; lanes with nothing to read use an
 //     out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
@@ -141,9 +142,16 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
 //
 // Single-chunk GEMVs (ng <= 64): step s covers rows row_begin + s*R .. + R - 1, a unit NB steps; the
 // sign cursor runs on from step to step. Chunked GEMVs: a unit is NB rows; its steps go chunk by
-// chunk (NB steps per chunk pass), each row's cursor carried from its previous chunk.
+// chunk (NB steps per chunk pass), each row's cursor carried from its previous chunk. With NB > 4 the
+// body holds NB half-steps and the stage slots are taken modulo NB.
 template <int M, bool ACC, int NB, bool CHUNKED>
 __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const char *lds, double *tile) {
+    // Chunked rows at m = 1: units of 8 rows (the activation slice is reloaded once per pass, so
+    // longer passes halve those reloads), each lane summing its group terms of the unit's rows in
+    // registers across passes; the rows are reduced over the wave once, at the unit's end.
+    constexpr bool RACC = CHUNKED && M == 1;
+    constexpr int U = NB > 4 ? NB : 4;  // half-steps per loop body
+    static_assert(U % NB == 0 && U % 4 == 0, "static stage positions");
     const int lane = threadIdx.x & 63;
     Ctx x;
     x.n = p.n;
@@ -171,6 +179,9 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     uint32_t xr[M][32];
     uint32_t cur = 0;           // single-chunk: sign cursor of the next step to scan
     uint32_t ccur[NB] = {};     // chunked: sign cursor of each row of the unit being scanned
+    double facc[RACC ? NB : 1];  // chunked, m = 1: the lane's running term of each row of the unit
+#pragma unroll
+    for (int r = 0; r < (RACC ? NB : 1); ++r) facc[r] = 0.0;
     uint32_t ro = 0;            // chunked: row-index entries of the unit (lane r: row r)
     int T;                      // steps in the range
     // per-lane constant parts of the offsets
@@ -207,22 +218,23 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     // stage runs on every half-step, dead steps (pipeline fill and drain) decode whatever their
     // buffers hold into tile slots that a live step overwrites before use, and only their stores and
     // loads are switched off (dead offsets). Scalar state advances with selects.
-    for (int it = 0; 4 * it - 4 < T; ++it) {
+    for (int it = 0; U * it - 4 < T; ++it) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int h = 4 * it + j;
-            // ---- decode step h - 4 (buffers bm[j], g[j]) ----
+        for (int j = 0; j < U; ++j) {
+            const int h = U * it + j;
+            const int jb = j & 3;  // stage buffer slot
+            // ---- decode step h - 4 (buffers bm[jb], g[jb]) ----
             {
                 const int s = h - 4;
                 const bool live = s >= 0 && s < T;
                 int acc[M];
-                decode<M>(bm[j], g[j], xr, lds, laneoff, acc);
-                const int slot = j % NB;
+                decode<M>(bm[jb], g[jb], xr, lds, laneoff, acc);
+                const int slot = (j + U - 4) % NB;  // step h - 4 within its unit (pass)
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && (lane < x.R * x.G) &&
                                     row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
-                    emit<M, ACC, NB>(x, acc, g[j].scale, tile, slot, false, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB>(x, acc, g[jb].scale, tile, slot, false, va ? voff_acc : kOffOff,
                                      live_or_dead(live, (uint32_t)row0 * (uint32_t)x.ng * 4u));
                     if constexpr (!ACC) {
                         if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
@@ -231,10 +243,30 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                     const int row = rD + slot;
                     const int gc = cD == x.nch - 1 ? x.glast : 64;
                     const bool va = live && lane < gc && row < row_end;
-                    emit<M, ACC, NB>(x, acc, g[j].scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
-                                     live_or_dead(live, ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u));
+                    if constexpr (RACC && !ACC) {
+                        const double term = (double)acc[0] * (double)half_bits_to_float(g[jb].scale);
+                        facc[slot] = cD != 0 ? facc[slot] + term : term;
+                    } else {
+                        emit<M, ACC, NB>(x, acc, g[jb].scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                                         live_or_dead(live, ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u));
+                    }
                     if (slot == NB - 1) {  // static: last step of a chunk pass
-                        if constexpr (!ACC) reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
+                        if constexpr (RACC && !ACC) {
+                            // the unit's rows are complete after the last pass: lane r gets row r
+                            double yl = 0.0;
+                            if (cD == x.nch - 1) {
+#pragma unroll
+                                for (int r = 0; r < NB; ++r) {
+                                    const double tot = wave_total_f64(facc[r]);
+                                    yl = lane == r ? tot : yl;
+                                }
+                            }
+                            const bool own = live && cD == x.nch - 1 && lane < NB && rD + lane < row_end;
+                            st1(__builtin_bit_cast(uint32_t, (float)yl), x.ry, own ? (uint32_t)(rD + lane) * 4u : kOffOff,
+                                0u);
+                        } else if constexpr (!ACC) {
+                            reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
+                        }
                         const bool wrap = live && cD == x.nch - 1;
                         rD = wrap ? rD + NB : rD;
                         cD = live ? (wrap ? 0 : cD + 1) : cD;
@@ -246,18 +278,18 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                 }
             }
             TG_SCHED_FENCE();
-            // ---- bitmap of step h -> bm[j] ----
+            // ---- bitmap of step h -> bm[jb] ----
             {
                 const int s = h;
                 const bool live = s < T;
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
-                    bm[j] = ld4(x.rbm, voff_bm, live_or_dead(live, (uint32_t)row0 * kb));
+                    bm[jb] = ld4(x.rbm, voff_bm, live_or_dead(live, (uint32_t)row0 * kb));
                 } else {
                     const int slot = j % NB;
                     const int gc = cB == x.nch - 1 ? x.glast : 64;
-                    bm[j] = ld4(x.rbm, lane < gc ? voff_bm : kOffOff,
-                                live_or_dead(live, (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u));
+                    bm[jb] = ld4(x.rbm, lane < gc ? voff_bm : kOffOff,
+                                 live_or_dead(live, (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u));
                     if (slot == 0) {
                         // the unit's row-index entries, for its first chunk pass
                         ro = ld1(x.rro, lane < NB ? (uint32_t)lane * 4u : kOffOff,
@@ -281,7 +313,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                                                             (uint32_t)row0 * (uint32_t)x.ng * 2u, g[(j + 3) & 3]);
                     cur += live ? total : 0u;
                 } else {
-                    const int slot = (j + 3) % NB;
+                    const int slot = (j + U - 1) % NB;  // step h - 1 within its unit (pass)
                     if (slot == 0) {  // static: a chunk pass starts; its first pass takes the row index
                         const bool first = live && cS == 0;
 #pragma unroll
@@ -311,7 +343,7 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
     if (p.nch == 1)
         run_loop<M, ACC, NB, false>(p, u0, u1, lds, tile);
     else
-        run_loop<M, ACC, NB, true>(p, u0, u1, lds, tile);
+        run_loop<M, ACC, M == 1 ? kChunkRows1 : NB, true>(p, u0, u1, lds, tile);
 }
 
 template <int M, bool ACC>
@@ -356,7 +388,7 @@ int gemv_waves_per_cu(int m) {
     return m == 1 ? Cfg<1>::WAVES : m == 2 ? Cfg<2>::WAVES : Cfg<3>::WAVES;
 }
 
-void gemv_geometry(Problem &p, int m) {
+void gemv_geometry(Problem &p, int fmt, int m) {
     const int nb = m == 1 ? Cfg<1>::NB : m == 2 ? Cfg<2>::NB : Cfg<3>::NB;
     p.ng = p.k / 128;
     p.nch = (p.ng + 63) / 64;
@@ -369,7 +401,7 @@ void gemv_geometry(Problem &p, int m) {
         p.G = 64;
         p.R = 1;
         p.glast = p.ng - 64 * (p.nch - 1);
-        p.nbu = nb;
+        p.nbu = fmt == TG_FMT_BITCOS && m == 1 ? kChunkRows1 : nb;
     }
     p.rpu = p.nbu * p.R;
     p.gmagic = (65536u + (uint32_t)p.G - 1) / (uint32_t)p.G;

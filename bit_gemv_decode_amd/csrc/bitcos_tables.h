@@ -67,26 +67,39 @@ constexpr Tables make_tables() {
 __device__ const Tables kTables = make_tables();
 
 // Copy both tables into LDS (s_tab: kTabBytes); the caller synchronises the block afterwards. Each
-// thread issues all of its loads before any LDS write (one 8-byte load serves all of its (mask,
-// base) copies, which belong to one presence byte), so the fill costs about one memory round trip
-// (0.7-1 us per launch on MI355X, measured with a kernel that stops after the fill).
+// thread issues all of its loads before any LDS write (one 8-byte load serves 8 consecutive (mask,
+// base) copies of one presence byte), so the fill costs about one memory round trip (0.7-1 us per
+// launch on MI355X, measured with a kernel that stops after the fill).
 template <int BLOCK>
 __device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
-    constexpr int kInfoPer = 256 * 32 / BLOCK;  // (mask, base) copies written per thread
-    static_assert(kInfoPer % 2 == 0 && 32 % kInfoPer == 0, "a thread's copies must share a presence byte");
+    // (mask, base) copies in units of 8 consecutive copies of one presence byte (64 bytes)
+    constexpr int kUnits = 256 * 32 / 8;
+    constexpr int kUnitPer = (kUnits + BLOCK - 1) / BLOCK;
     constexpr int kEntVec = (kEntries + 1) / 2;  // 16-byte vectors of the entry table
     constexpr int kEntPer = (kEntVec + BLOCK - 1) / BLOCK;
     const int t = threadIdx.x;
-    const uint2 inf = reinterpret_cast<const uint2 *>(kTables.info)[(t * kInfoPer) >> 5];
+    const uint2 *inf = reinterpret_cast<const uint2 *>(kTables.info);
     const uint4 *src = reinterpret_cast<const uint4 *>(kTables.ent);
+    uint2 iv[kUnitPer];
     uint4 ev[kEntPer];
+#pragma unroll
+    for (int r = 0; r < kUnitPer; ++r) {
+        const int u = t + r * BLOCK;
+        iv[r] = u < kUnits ? inf[u >> 2] : make_uint2(0, 0);
+    }
 #pragma unroll
     for (int r = 0; r < kEntPer; ++r) {
         const int i = t + r * BLOCK;
         ev[r] = i < kEntVec ? src[i] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < kInfoPer / 2; ++j) s_tab[t * (kInfoPer / 2) + j] = make_uint4(inf.x, inf.y, inf.x, inf.y);
+    for (int r = 0; r < kUnitPer; ++r) {
+        const int u = t + r * BLOCK;
+        if (u < kUnits) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s_tab[u * 4 + c] = make_uint4(iv[r].x, iv[r].y, iv[r].x, iv[r].y);
+        }
+    }
 #pragma unroll
     for (int r = 0; r < kEntPer; ++r) {
         const int i = t + r * BLOCK;

@@ -308,21 +308,30 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void fixed_gemv_kernel(GroupArgs ga)
     __shared__ uint4 s_lut[kLutBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     {
-        // one load per thread: its consecutive copies all belong to one code byte, so the fill is
-        // one memory round trip
+        // units of 64 bytes (16 copies of a 2-bit entry, 8 of a five-trit one), one load each, all
+        // loads before any LDS write: the fill is one memory round trip
+        constexpr int kUnits = kLutBytes / 64;
+        constexpr int kUnitPer = (kUnits + BLOCK - 1) / BLOCK;
         const int t = threadIdx.x;
-        if constexpr (FMT == TG_FMT_2BIT) {
-            constexpr int kPer = 256 * 64 / BLOCK;  // 4-byte copies per thread
-            static_assert(kPer % 4 == 0 && 64 % kPer == 0, "a thread's copies must share a code byte");
-            const uint32_t v = kFixedTables.b2[(t * kPer) >> 6];
+        uint2 v[kUnitPer];
 #pragma unroll
-            for (int j = 0; j < kPer / 4; ++j) s_lut[t * (kPer / 4) + j] = make_uint4(v, v, v, v);
-        } else {
-            constexpr int kPer = 256 * 32 / BLOCK;  // 8-byte copies per thread
-            static_assert(kPer % 2 == 0 && 32 % kPer == 0, "a thread's copies must share a code byte");
-            const uint32_t lo = kFixedTables.t5[(t * kPer) >> 5][0], hi = kFixedTables.t5[(t * kPer) >> 5][1];
+        for (int r = 0; r < kUnitPer; ++r) {
+            const int u = t + r * BLOCK;
+            if constexpr (FMT == TG_FMT_2BIT)
+                v[r] = make_uint2(u < kUnits ? kFixedTables.b2[u >> 2] : 0u, 0u);
+            else
+                v[r] = u < kUnits ? make_uint2(kFixedTables.t5[u >> 2][0], kFixedTables.t5[u >> 2][1])
+                                  : make_uint2(0, 0);
+        }
 #pragma unroll
-            for (int j = 0; j < kPer / 2; ++j) s_lut[t * (kPer / 2) + j] = make_uint4(lo, hi, lo, hi);
+        for (int r = 0; r < kUnitPer; ++r) {
+            const int u = t + r * BLOCK;
+            if (u < kUnits) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    s_lut[u * 4 + c] = FMT == TG_FMT_2BIT ? make_uint4(v[r].x, v[r].x, v[r].x, v[r].x)
+                                                         : make_uint4(v[r].x, v[r].y, v[r].x, v[r].y);
+            }
         }
     }
     __syncthreads();

@@ -20,7 +20,7 @@ namespace {
 template <int M>
 struct Cfg {
     static constexpr int NB = M == 3 ? 2 : 4;     // row bundles (steps per chunk pass) per unit
-    static constexpr int WAVES = M == 1 ? 16 : 8;  // waves per block (= per CU)
+    static constexpr int WAVES = M == 1 ? 12 : 8;  // waves per block (= per CU)
     static constexpr int BLOCK = 64 * WAVES;
 };
 

@@ -65,8 +65,12 @@ struct GroupArgs {
 int gemv_waves_per_cu(int m);
 constexpr int kMaxWavesPerCu = 16;
 
-// Fill the work geometry of p (p.n, p.k set) for m activation rows (the same for every format).
-void gemv_geometry(Problem &p, int m);
+// Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
+constexpr int kChunkRows1 = 8;
+
+// Fill the work geometry of p (p.n, p.k set) for m activation rows on the vector path (the same for
+// every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 rows).
+void gemv_geometry(Problem &p, int fmt, int m);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
 // units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU.
