@@ -25,9 +25,10 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-# the BITCOS kernel's source and the device headers it compiles from
+# the BITCOS kernel's source, the device headers it compiles from and the planner that divides its work
 KERNEL_SRCS = [os.path.join(PKG, "csrc", f)
-               for f in ("bitcos_gemv.hip", "bitcos_tables.h", "gemv_pipeline.h", "device_common.h")]
+               for f in ("bitcos_gemv.hip", "bitcos_tables.h", "gemv_pipeline.h", "device_common.h",
+                         "tg_internal.h", "api.cpp")]
 READ_BYTES = 2 * 1024 ** 3
 WRITE_BYTES = 1024 ** 3
 
