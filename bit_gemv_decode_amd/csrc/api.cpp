@@ -128,7 +128,7 @@ namespace {
 
 // Waves of a persistent launch on this device for m activation rows; a plan's per-wave ranges are
 // sized for it (the table has room for the largest count).
-int plan_waves(int fmt, int m) { return device_cus() * (use_mfma(fmt, m) ? kMfmaWavesPerCu : gemv_waves_per_cu(m)); }
+int plan_waves(int fmt, int m) { return device_cus() * (use_mfma(fmt, m) ? kMfmaWavesPerCu : gemv_waves(fmt, m)); }
 int plan_waves_max() { return device_cus() * std::max(kMaxWavesPerCu, kMfmaWavesPerCu); }
 
 // Largest m a plan of this format takes (one launch per plan).

@@ -347,8 +347,9 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
 }
 
 template <int M, bool ACC>
-__global__ __launch_bounds__(Cfg<M>::BLOCK) void bitcos_gemv_kernel(GroupArgs ga) {
-    constexpr int NB = Cfg<M>::NB, WAVES = Cfg<M>::WAVES, BLOCK = Cfg<M>::BLOCK;
+__global__ __launch_bounds__((Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(GroupArgs ga) {
+    using C = Cfg<M, TG_FMT_BITCOS>;
+    constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     load_bitcos_tables<BLOCK>(s_tab);
@@ -373,23 +374,20 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void bitcos_gemv_kernel(GroupArgs ga
 
 template <int M>
 hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    const int blocks = grid_blocks<Cfg<M>::WAVES>(g);
+    using C = Cfg<M, TG_FMT_BITCOS>;
+    const int blocks = grid_blocks<C::WAVES>(g);
     if (blocks < 1) return hipErrorInvalidValue;
     if (acc_out)
-        hipLaunchKernelGGL((bitcos_gemv_kernel<M, true>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     else
-        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int gemv_waves_per_cu(int m) {
-    return m == 1 ? Cfg<1>::WAVES : m == 2 ? Cfg<2>::WAVES : Cfg<3>::WAVES;
-}
-
 void gemv_geometry(Problem &p, int fmt, int m) {
-    const int nb = m == 1 ? Cfg<1>::NB : m == 2 ? Cfg<2>::NB : Cfg<3>::NB;
+    const int nb = m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
     p.ng = p.k / 128;
     p.nch = (p.ng + 63) / 64;
     if (p.nch == 1) {

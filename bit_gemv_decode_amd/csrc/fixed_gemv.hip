@@ -303,8 +303,9 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
 }
 
 template <int FMT, int M, bool ACC>
-__global__ __launch_bounds__(Cfg<M>::BLOCK) void fixed_gemv_kernel(GroupArgs ga) {
-    constexpr int NB = Cfg<M>::NB, WAVES = Cfg<M>::WAVES, BLOCK = Cfg<M>::BLOCK;
+__global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupArgs ga) {
+    using C = Cfg<M, FMT>;
+    constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
     __shared__ uint4 s_lut[kLutBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     {
@@ -357,12 +358,13 @@ __global__ __launch_bounds__(Cfg<M>::BLOCK) void fixed_gemv_kernel(GroupArgs ga)
 
 template <int FMT, int M>
 hipError_t launch_fixed_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    const int blocks = grid_blocks<Cfg<M>::WAVES>(g);
+    using C = Cfg<M, FMT>;
+    const int blocks = grid_blocks<C::WAVES>(g);
     if (blocks < 1) return hipErrorInvalidValue;
     if (acc_out)
-        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, true>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     else
-        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false>), dim3(blocks), dim3(Cfg<M>::BLOCK), 0, s, g);
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     return hipGetLastError();
 }
 

@@ -17,10 +17,10 @@
 namespace tg {
 namespace {
 
-template <int M>
+template <int M, int FMT>
 struct Cfg {
-    static constexpr int NB = M == 3 ? 2 : 4;     // row bundles (steps per chunk pass) per unit
-    static constexpr int WAVES = M == 1 ? 12 : 8;  // waves per block (= per CU)
+    static constexpr int NB = M == 3 ? 2 : 4;  // row bundles (steps per chunk pass) per unit
+    static constexpr int WAVES = gemv_waves(FMT, M);  // waves per block (= per CU)
     static constexpr int BLOCK = 64 * WAVES;
 };
 

@@ -60,9 +60,10 @@ struct GroupArgs {
     Problem one;
 };
 
-// Waves per CU of a GEMV launch for m activation rows (one block per CU: the decode tables fill most
-// of the LDS).
-int gemv_waves_per_cu(int m);
+// Waves per CU of a vector-path GEMV launch of format fmt for m activation rows (one block per CU:
+// the decode tables fill most of the LDS). BITCOS at m = 1 runs 12: its chunked rows keep eight fp64
+// row sums per lane, which does not fit the 128 registers of 16 waves.
+constexpr int gemv_waves(int fmt, int m) { return m > 1 ? 8 : fmt == TG_FMT_BITCOS ? 12 : 16; }
 constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
