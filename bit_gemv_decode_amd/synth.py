@@ -30,6 +30,7 @@ STREAM_W = 1
 STREAM_SCALE = 2
 STREAM_X = 3
 STREAM_DEAD = 4
+STREAM_XF = 5
 
 
 def _mix(z: np.ndarray) -> np.ndarray:
@@ -106,6 +107,16 @@ def activations(m: int, k: int, seed: int = 0, tid: int = STREAM_X) -> np.ndarra
     u = _u53(stream_key(seed, tid), 0, m * k)
     v = (u * np.uint64(255)) >> np.uint64(53)
     return (v.astype(np.int16) - 127).astype(np.int8).reshape(m, k)
+
+
+def float_activations(m: int, k: int, seed: int = 0, tid: int = STREAM_XF) -> np.ndarray:
+    """float32 [m, k]: uniform[-1, 1] times a per-128-block magnitude 10^e, e uniform[-1, 1], so that
+    blocks differ in range (as activation channels do); every value is finite and normal."""
+    key = stream_key(seed, tid)
+    u = _u53(key, 0, m * k).astype(np.float64) * 2.0**-53
+    e = _u53(key, m * k, m * (k // 128)).astype(np.float64) * 2.0**-53
+    mag = np.repeat(10.0 ** (2.0 * e - 1.0), 128)
+    return ((2.0 * u - 1.0) * mag).astype(np.float32).reshape(m, k)
 
 
 def dead_rows(n: int, count: int, seed: int = 0, tid: int = STREAM_DEAD) -> np.ndarray:

@@ -27,7 +27,7 @@ def build(force: bool = True) -> str:
     """Compile oracle.c with gcc (-O2, OpenMP over rows, no intrinsics)."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp"
-        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", "-o", tmp, SRC],
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", "-o", tmp, SRC, "-lm"],
                        check=True)
         os.replace(tmp, LIB)
     return LIB
@@ -63,6 +63,10 @@ def lib():
         L.oracle_gemv_acc.restype = None
         L.oracle_combine.argtypes = [p, p, i64, i64, i64, p]
         L.oracle_combine.restype = None
+        L.oracle_quantize_x.argtypes = [p, i64, i64, p, p]
+        L.oracle_quantize_x.restype = None
+        L.oracle_combine_xs.argtypes = [p, p, p, i64, i64, i64, p]
+        L.oracle_combine_xs.restype = None
         L.oracle_gemv_packed.argtypes = [ctypes.c_int, p, p, p, p, i64, i64, p, i64, p]
         L.oracle_gemv_packed.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
@@ -182,6 +186,36 @@ def combine(acc: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 def gemv(w: np.ndarray, scales: np.ndarray, x: np.ndarray) -> np.ndarray:
     return combine(gemv_acc(w, x), scales)
+
+
+def quantize_x(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-group int8 quantisation of float32 activations [m, k]: (int8 codes [m, k], float32 group
+    scales [m, k/128])."""
+    x = _c(np.atleast_2d(x), np.float32)
+    m, k = x.shape
+    assert k % GROUP == 0
+    xq = np.empty((m, k), np.int8)
+    xs = np.empty((m, k // GROUP), np.float32)
+    lib().oracle_quantize_x(_ptr(x), m, k, _ptr(xq), _ptr(xs))
+    return xq, xs
+
+
+def combine_xs(acc: np.ndarray, scales: np.ndarray, xs: np.ndarray) -> np.ndarray:
+    """float32 [m, n]: the fp64 sum over groups of (scale * acc) * xs, rounded once."""
+    acc = _c(acc, np.int32)
+    sc = _c(scales, np.float16).view(np.uint16)
+    m, n, ng = acc.shape
+    xs = _c(xs, np.float32)
+    assert sc.shape == (n, ng) and xs.shape == (m, ng)
+    y = np.empty((m, n), np.float32)
+    lib().oracle_combine_xs(_ptr(acc), _ptr(sc), _ptr(xs), n, ng, m, _ptr(y))
+    return y
+
+
+def gemv_xs(w: np.ndarray, scales: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """The GEMV of float32 activations quantised per group: quantise, contract, combine."""
+    xq, xs = quantize_x(x)
+    return combine_xs(gemv_acc(w, xq), scales, xs)
 
 
 FMT_BITCOS, FMT_5TRIT, FMT_2BIT = 1, 2, 3

@@ -32,7 +32,14 @@
  *   - 2-bit code: code = weight + 1, four codes per byte, the first weight in the lowest two bits;
  *     code 3 is invalid;
  *   - scales are IEEE binary16, decoded here from the format's definition.
+ *   - activation quantisation (Sec. II-C, discussion after Fig. 5: activations are quantised to int8
+ *     per group of 128 on the int8 path; the quantiser itself is not given): symmetric absmax per
+ *     group of 128 consecutive k of one activation row, sigma = max|x| / 127 and q = x / sigma
+ *     rounded to nearest-even, clamped to [-127, 127]; an all-zero group has sigma = 0 and q = 0.
+ *     Both divisions are single-precision IEEE operations, so the integer codes are decided in fp32.
+ *     The group's activation scale multiplies its term once, beside the weight scale.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -235,6 +242,52 @@ void oracle_combine(const int32_t *acc, const uint16_t *scales, int64_t n, int64
             double s = 0.0;
             for (int64_t g = 0; g < ng; g++)
                 s += oracle_half_to_double(scales[r * ng + g]) * (double)acc[(mi * n + r) * ng + g];
+            y[mi * n + r] = (float)s;
+        }
+}
+
+/* ---------- per-group int8 activation quantisation ---------- */
+
+/* x: float [m][k] (finite values), k a multiple of 128. xq: int8 [m][k]; xs: float [m][k/128], the
+ * group's activation scale sigma. Per group: a = max |x|; sigma = a / 127 (fp32); each code is
+ * x / sigma (fp32) rounded to nearest-even and clamped to [-127, 127]; a = 0 gives sigma = 0 and
+ * codes 0. */
+void oracle_quantize_x(const float *x, int64_t m, int64_t k, int8_t *xq, float *xs) {
+    int64_t ng = k / ORACLE_GROUP;
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t g = 0; g < ng; g++) {
+            const float *v = x + mi * k + g * ORACLE_GROUP;
+            int8_t *q = xq + mi * k + g * ORACLE_GROUP;
+            float a = 0.0f;
+            for (int c = 0; c < ORACLE_GROUP; c++) {
+                float t = fabsf(v[c]);
+                if (t > a) a = t;
+            }
+            volatile float sigma = a / 127.0f; /* volatile: keep the fp32 rounding of each step */
+            xs[mi * ng + g] = sigma;
+            for (int c = 0; c < ORACLE_GROUP; c++) {
+                int code = 0;
+                if (a > 0.0f) {
+                    volatile float ratio = v[c] / sigma;
+                    float r = nearbyintf(ratio); /* default rounding mode: nearest, ties to even */
+                    code = r > 127.0f ? 127 : r < -127.0f ? -127 : (int)r;
+                }
+                q[c] = (int8_t)code;
+            }
+        }
+}
+
+/* y[mi][r] = (float) sum_g ((double) scale[r][g] * (double) acc[mi][r][g]) * (double) xs[mi][g]:
+ * the definition with each group's activation scale applied beside its weight scale, groups in
+ * ascending order, rounded once. */
+void oracle_combine_xs(const int32_t *acc, const uint16_t *scales, const float *xs, int64_t n, int64_t ng, int64_t m,
+                       float *y) {
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t r = 0; r < n; r++) {
+            double s = 0.0;
+            for (int64_t g = 0; g < ng; g++)
+                s += (oracle_half_to_double(scales[r * ng + g]) * (double)acc[(mi * n + r) * ng + g]) *
+                     (double)xs[mi * ng + g];
             y[mi * n + r] = (float)s;
         }
 }
