@@ -9,8 +9,10 @@ byte comes from HBM. One step = one pass over the 32 x 7 = 224 GEMVs, issued as 
 sign index + fp16 scales), whole job.
 
 Also measured and reported beside it (same process): the same pass as 32 per-layer launches and as
-224 single-GEMV launches (captured in a HIP graph), each matrix's single-call time, the five-trit
-and 2-bit formats on the same layer set, the stream-read ceiling of this GPU, and the CPU oracle.
+224 single-GEMV launches (captured in a HIP graph), each matrix's single-call time, the pass on
+float activations quantised per group (quantiser time per call, grouped GEMV with activation group
+scales), the five-trit and 2-bit formats on the same layer set, the stream-read ceiling of this GPU,
+and the CPU oracle.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -144,6 +146,39 @@ def cpu_baseline(O, ls, budget_s=12.0):
     return dict(value=round(total_bytes / t / 1e9, 4), unit="GB/s", cores=int(O.threads()), kind="oracle",
                 sample=f"one layer set (the 7 GEMVs, {total_bytes / 1e6:.1f} MB BITCOS, ~1/32 of a step), "
                        f"median of {len(times)} passes, {t * 1e3:.1f} ms per pass")
+
+
+def activation_quant(torch, B, synth, ls, dev, steps, warmup):
+    """The same layer set on float activations quantised per group of 128: the quantiser's time per
+    call (graph-replayed, host launch path removed) and the grouped step of the GEMV with activation
+    group scales over the quantised rows (one quantised row per matrix role, shared by its 32 copies)."""
+    xq, xsc = [], []
+    for role, (name, n, k) in enumerate(LAYER):
+        xf = synth.float_activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_XF))
+        q, sc = B.quantize_x(torch.from_numpy(xf).to(dev))
+        xq.append(q)
+        xsc.append(sc)
+    mats = [(role, m) for row in ls.mats for role, m in enumerate(row)]
+    plan = B.Plan([m["w"] for _, m in mats], [xq[r] for r, _ in mats], scales=[m["s"] for _, m in mats],
+                  ys=[m["y"] for _, m in mats], x_scales=[xsc[r] for r, _ in mats])
+    secs = time_launches(torch, plan.run, steps, warmup)
+    step_s = secs / steps
+    out = {"gemv_xs_grouped": {"gbs": round(ls.step_bytes / step_s / 1e9, 1), "ms_per_step": round(step_s * 1e3, 4)}}
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    for m, k in ((1, 4096), (1, 14336), (16, 14336)):
+        xf = torch.from_numpy(synth.float_activations(m, k, seed=1)).to(dev)
+        q = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sc = torch.empty((m, k // 128), dtype=torch.float32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(32):
+                B.quantize_x(xf, q, sc, stream=st)
+        t = time_launches(torch, g.replay, 5, 1)
+        out[f"quantize_m{m}_k{k}_us"] = round(t / (5 * 32) * 1e6, 3)
+        del g
+    del plan
+    return out
 
 
 def load_traffic():
@@ -492,6 +527,9 @@ def main():
     out["per_matrix_single_call"] = per_mat
     del layer_plans, g
     torch.cuda.empty_cache()
+
+    log("[bench] float activations: quantiser and GEMV with activation group scales")
+    out["activation_quant"] = activation_quant(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
 
     log("[bench] stream-read ceiling")
     ceil = stream_ceiling(torch, bd, dev)

@@ -4,9 +4,9 @@ The compute path is libternary_gemv.so (C ABI in include/ternary_gemv.h; HIP ker
 this package is its Python binding plus the seeded synthetic-input generator.
 """
 from .binding import (FMT_2BIT, FMT_5TRIT, FMT_BITCOS, FMT_NAMES, TG_GROUP, TG_MAX_M, DeviceWeights, Packed,
-                      Plan, TgError, describe, pack, pack_2bit, pack_5trit, pack_bitcos, ternary_gemv, ternary_gemv_acc,
-                      unpack, validate)
+                      Plan, TgError, describe, pack, pack_2bit, pack_5trit, pack_bitcos, quantize_x, ternary_gemv,
+                      ternary_gemv_acc, ternary_gemv_xs, unpack, validate)
 
 __all__ = ["FMT_BITCOS", "FMT_5TRIT", "FMT_2BIT", "FMT_NAMES", "TG_GROUP", "TG_MAX_M", "DeviceWeights", "Packed",
            "Plan", "TgError", "describe", "pack", "pack_bitcos", "pack_5trit", "pack_2bit", "ternary_gemv",
-           "ternary_gemv_acc", "unpack", "validate"]
+           "ternary_gemv_acc", "ternary_gemv_xs", "quantize_x", "unpack", "validate"]

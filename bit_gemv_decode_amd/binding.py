@@ -24,8 +24,8 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 
 # Every symbol include/ternary_gemv.h declares.
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_describe", "tg_validate", "tg_unpack",
-           "ternary_gemv", "ternary_gemv_acc", "tg_plan_table_bytes", "tg_plan_init", "ternary_gemv_plan",
-           "tg_stream_read", "tg_strerror", "tg_version"]
+           "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "tg_plan_table_bytes",
+           "tg_plan_init", "tg_plan_init_xs", "ternary_gemv_plan", "tg_stream_read", "tg_strerror", "tg_version"]
 
 
 class TgError(RuntimeError):
@@ -75,6 +75,13 @@ def lib():
         L.ternary_gemv.restype = ctypes.c_int
         L.ternary_gemv_acc.argtypes = [ctypes.POINTER(TgDesc), p, p, p, ctypes.c_int32, p]
         L.ternary_gemv_acc.restype = ctypes.c_int
+        L.tg_quantize_x.argtypes = [p, ctypes.c_int32, i64, p, p, p]
+        L.tg_quantize_x.restype = ctypes.c_int
+        L.ternary_gemv_xs.argtypes = [ctypes.POINTER(TgDesc), p, p, p, p, p, ctypes.c_int32, p]
+        L.ternary_gemv_xs.restype = ctypes.c_int
+        L.tg_plan_init_xs.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p,
+                                      p, p, p, ctypes.c_int32]
+        L.tg_plan_init_xs.restype = ctypes.c_int
         L.tg_plan_table_bytes.argtypes = [ctypes.c_int32]
         L.tg_plan_table_bytes.restype = sz
         L.tg_plan_init.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p, p, p,
@@ -268,15 +275,68 @@ def ternary_gemv_acc(w: DeviceWeights, x, acc=None, stream=None):
     return acc
 
 
+def quantize_x(x, xq=None, x_scales=None, stream=None):
+    """Per-group int8 quantisation of float32 activations [m, k] (tg_quantize_x): returns (xq int8
+    [m, k], x_scales float32 [m, k/128]). Asynchronous."""
+    import torch
+
+    _require_cuda(x, torch.float32, "x")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scales is None:
+        x_scales = torch.empty((m, k // TG_GROUP), dtype=torch.float32, device=x.device)
+    _require_cuda(xq, torch.int8, "xq")
+    _require_cuda(x_scales, torch.float32, "x_scales")
+    if tuple(xq.shape) != (m, k) or tuple(x_scales.shape) != (m, k // TG_GROUP):
+        raise ValueError("xq or x_scales has the wrong shape")
+    _check(lib().tg_quantize_x(ctypes.c_void_p(x.data_ptr()), m, k, ctypes.c_void_p(xq.data_ptr()),
+                               ctypes.c_void_p(x_scales.data_ptr()), _stream_handle(stream)), "tg_quantize_x")
+    return xq, x_scales
+
+
+def ternary_gemv_xs(w: DeviceWeights, scales, xq, x_scales, y=None, stream=None):
+    """y[m, n] = sum_g scales[n, g] * x_scales[m, g] * acc[m, n, g] on quantised activations
+    (ternary_gemv_xs). Asynchronous."""
+    import torch
+
+    _require_cuda(w.tensor, torch.uint8, "weights")
+    _require_cuda(scales, torch.float16, "scales")
+    _require_cuda(xq, torch.int8, "xq")
+    _require_cuda(x_scales, torch.float32, "x_scales")
+    if xq.dim() == 1:
+        xq = xq.view(1, -1)
+    if x_scales.dim() == 1:
+        x_scales = x_scales.view(1, -1)
+    m = xq.shape[0]
+    if (xq.shape[1] != w.k or tuple(scales.shape) != (w.n, w.k // TG_GROUP)
+            or tuple(x_scales.shape) != (m, w.k // TG_GROUP)):
+        raise ValueError("shape mismatch between weights, scales, xq and x_scales")
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=xq.device)
+    _require_cuda(y, torch.float32, "y")
+    if tuple(y.shape) != (m, w.n):
+        raise ValueError("y has the wrong shape")
+    _check(lib().ternary_gemv_xs(ctypes.byref(w.desc), ctypes.c_void_p(w.tensor.data_ptr()),
+                                 ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(xq.data_ptr()),
+                                 ctypes.c_void_p(x_scales.data_ptr()), ctypes.c_void_p(y.data_ptr()), m,
+                                 _stream_handle(stream)), "ternary_gemv_xs")
+    return y
+
+
 class Plan:
     """Several GEMVs of one format run as one launch (tg_plan_init / ternary_gemv_plan).
 
     weights: list of DeviceWeights; xs: int8 [m, k] device tensors; scales and ys (fp16 [n, k/128],
-    float32 [m, n]) for fp32 outputs, or accs (int32 [m, n, k/128]) for accumulator outputs. The plan
-    keeps references to every tensor it names, and its device table, for its lifetime.
+    float32 [m, n]) for fp32 outputs, or accs (int32 [m, n, k/128]) for accumulator outputs. With
+    x_scales (float32 [m, k/128] per GEMV) the xs are quantised activations and every group term is
+    also multiplied by its activation group scale (tg_plan_init_xs). The plan keeps references to
+    every tensor it names, and its device table, for its lifetime.
     """
 
-    def __init__(self, weights, xs, scales=None, ys=None, accs=None):
+    def __init__(self, weights, xs, scales=None, ys=None, accs=None, x_scales=None):
         import torch
 
         count = len(weights)
@@ -284,10 +344,12 @@ class Plan:
             raise ValueError("one x per weight matrix is required")
         acc_mode = accs is not None
         if acc_mode:
-            if len(accs) != count:
-                raise ValueError("one acc per weight matrix is required")
+            if len(accs) != count or x_scales is not None:
+                raise ValueError("one acc per weight matrix is required (and no x_scales)")
         elif scales is None or ys is None or len(scales) != count or len(ys) != count:
             raise ValueError("scales and ys (one per matrix) are required for fp32 outputs")
+        if x_scales is not None and len(x_scales) != count:
+            raise ValueError("one x_scales per weight matrix is required")
         m = xs[0].shape[0] if xs[0].dim() == 2 else 1
         for i, w in enumerate(weights):
             _require_cuda(w.tensor, torch.uint8, "weights")
@@ -303,6 +365,10 @@ class Plan:
                 _require_cuda(ys[i], torch.float32, "y")
                 if tuple(scales[i].shape) != (w.n, w.k // TG_GROUP) or tuple(ys[i].shape) != (m, w.n):
                     raise ValueError("scales or y has the wrong shape")
+                if x_scales is not None:
+                    _require_cuda(x_scales[i], torch.float32, "x_scales")
+                    if tuple(x_scales[i].reshape(m, -1).shape) != (m, w.k // TG_GROUP):
+                        raise ValueError("x_scales has the wrong shape")
         L = lib()
         nbytes = L.tg_plan_table_bytes(count)
         self.table = torch.empty(nbytes, dtype=torch.uint8, device=xs[0].device)
@@ -310,10 +376,15 @@ class Plan:
         P = ctypes.c_void_p * count
         ptr = lambda ts: P(*[t.data_ptr() for t in ts]) if ts is not None else None
         self.plan = TgPlan()
-        self._keep = (list(weights), list(xs), scales, ys, accs)
-        _check(L.tg_plan_init(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count, descs,
-                              ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(ys), ptr(accs), m),
-               "tg_plan_init")
+        self._keep = (list(weights), list(xs), scales, ys, accs, x_scales)
+        if x_scales is not None:
+            _check(L.tg_plan_init_xs(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count,
+                                     descs, ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(x_scales),
+                                     ptr(ys), m), "tg_plan_init_xs")
+        else:
+            _check(L.tg_plan_init(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count,
+                                  descs, ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(ys), ptr(accs),
+                                  m), "tg_plan_init")
 
     def run(self, stream=None):
         _check(lib().ternary_gemv_plan(ctypes.byref(self.plan), _stream_handle(stream)), "ternary_gemv_plan")

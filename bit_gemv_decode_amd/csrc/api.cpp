@@ -22,7 +22,7 @@ int device_cus() {
 }
 
 Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, const int8_t *x, float *y,
-                     int32_t *acc) {
+                     int32_t *acc, const float *xs) {
     const uint8_t *base = (const uint8_t *)W;
     Problem p{};
     p.codes = base + d->off_codes;
@@ -36,6 +36,7 @@ Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, co
     p.x = x;
     p.y = y;
     p.acc = acc;
+    p.xs = xs;
     p.n = (int32_t)d->n;
     p.k = (int32_t)d->k;
     return p;
@@ -71,20 +72,22 @@ void geometry(Problem &p, int fmt, int32_t m) {
         gemv_geometry(p, fmt, m);
 }
 
-hipError_t launch(int fmt, const GroupArgs &g, bool acc_out, hipStream_t s) {
-    if (use_mfma(fmt, g.m)) return launch_bitcos_mfma(g, acc_out, s);
+hipError_t launch(int fmt, const GroupArgs &g, int out, hipStream_t s) {
+    if (use_mfma(fmt, g.m)) return launch_bitcos_mfma(g, out, s);
     switch (fmt) {
-        case TG_FMT_BITCOS: return launch_bitcos(g, acc_out, s);
-        case TG_FMT_5TRIT: return launch_t5(g, acc_out, s);
-        case TG_FMT_2BIT: return launch_b2(g, acc_out, s);
+        case TG_FMT_BITCOS: return launch_bitcos(g, out, s);
+        case TG_FMT_5TRIT: return launch_t5(g, out, s);
+        case TG_FMT_2BIT: return launch_b2(g, out, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, const int8_t *x, float *y, int32_t *acc,
-                int32_t m, void *stream, bool acc_out) {
+int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, const int8_t *x, const float *xs,
+                float *y, int32_t *acc, int32_t m, void *stream, int out) {
+    const bool acc_out = out == kOutAcc;
     if (!desc || !W || !x || m < 1 || m > TG_MAX_M) return TG_EINVAL;
     if (acc_out ? !acc : (!y || !scales)) return TG_EINVAL;
+    if (out == kOutYxs && (!xs || ((uintptr_t)xs & 3))) return TG_EINVAL;
     // 16-byte vector loads of W sections and x rows; 4-byte stores of y / acc; 2-byte scales.
     if (((uintptr_t)W & 15) || ((uintptr_t)x & 15)) return TG_EINVAL;
     if (acc_out ? ((uintptr_t)acc & 3) : (((uintptr_t)y & 3) || ((uintptr_t)scales & 1))) return TG_EINVAL;
@@ -100,14 +103,15 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         const int32_t mt = std::min<int32_t>(step, m - m0);
         GroupArgs g{};
         g.one = make_problem(desc, W, scales, x + (size_t)m0 * k, acc_out ? nullptr : y + (size_t)m0 * n,
-                             acc_out ? acc + (size_t)m0 * n * ng : nullptr);
+                             acc_out ? acc + (size_t)m0 * n * ng : nullptr,
+                             out == kOutYxs ? xs + (size_t)m0 * ng : nullptr);
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
         geometry(g.one, desc->fmt, mt);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
-        if (launch(desc->fmt, g, acc_out, s) != hipSuccess) return TG_EHIP;
+        if (launch(desc->fmt, g, out, s) != hipSuccess) return TG_EHIP;
     }
     return TG_OK;
 }
@@ -116,12 +120,25 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
 
 extern "C" int ternary_gemv(const tg_desc *desc, const void *W, const uint16_t *scales, const int8_t *x, float *y,
                             int32_t m, void *stream) {
-    return gemv_common(desc, W, scales, x, y, nullptr, m, stream, false);
+    return gemv_common(desc, W, scales, x, nullptr, y, nullptr, m, stream, kOutY);
+}
+
+extern "C" int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, const int8_t *xq,
+                               const float *xs, float *y, int32_t m, void *stream) {
+    return gemv_common(desc, W, scales, xq, xs, y, nullptr, m, stream, kOutYxs);
+}
+
+extern "C" int tg_quantize_x(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, void *stream) {
+    if (!x || !xq || !xs || m < 1 || m > TG_MAX_M) return TG_EINVAL;
+    if (((uintptr_t)x & 7) || ((uintptr_t)xq & 1) || ((uintptr_t)xs & 3)) return TG_EINVAL;
+    if (k < TG_GROUP || k % TG_GROUP || k > (int64_t)1 << 30) return TG_ESHAPE;
+    return launch_quantize_x(x, (int64_t)m * (k / TG_GROUP), xq, xs, (hipStream_t)stream) == hipSuccess ? TG_OK
+                                                                                                      : TG_EHIP;
 }
 
 extern "C" int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_t *acc, int32_t m,
                                 void *stream) {
-    return gemv_common(desc, W, nullptr, x, nullptr, acc, m, stream, true);
+    return gemv_common(desc, W, nullptr, x, nullptr, nullptr, acc, m, stream, kOutAcc);
 }
 
 namespace {
@@ -159,12 +176,14 @@ extern "C" size_t tg_plan_table_bytes(int32_t count) {
     return count > 0 ? ranges_offset(count) + (size_t)plan_waves_max() * sizeof(WaveRange) : 0;
 }
 
-extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
-                            const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
-                            float *const *y, int32_t *const *acc, int32_t m) {
+namespace {
+
+int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                     const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
+                     const float *const *xs, float *const *y, int32_t *const *acc, int32_t m) {
     if (!plan || !table || !descs || !W || !x || count < 1 || m < 1) return TG_EINVAL;
     const bool acc_mode = acc != nullptr;
-    if (acc_mode ? false : (!y || !scales)) return TG_EINVAL;
+    if (acc_mode ? xs != nullptr : (!y || !scales)) return TG_EINVAL;
     if (((uintptr_t)table & 15) || table_bytes < tg_plan_table_bytes(count)) return TG_EINVAL;
     const int fmt = descs[0].fmt;
     if (m > plan_max_m(fmt)) return TG_EINVAL;
@@ -180,11 +199,12 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
         if (acc_mode ? (!acc[i] || ((uintptr_t)acc[i] & 3))
                      : (!y[i] || !scales[i] || ((uintptr_t)y[i] & 3) || ((uintptr_t)scales[i] & 1)))
             return TG_EINVAL;
+        if (xs && (!xs[i] || ((uintptr_t)xs[i] & 3))) return TG_EINVAL;
     }
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
-                               acc_mode ? acc[i] : nullptr);
+                               acc_mode ? acc[i] : nullptr, xs ? xs[i] : nullptr);
         geometry(host[i], fmt, m);
         rpu = std::max(rpu, (int)host[i].rpu);
     }
@@ -242,15 +262,30 @@ extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int3
     plan->count = count;
     plan->units = (int32_t)units;
     plan->rows_per_unit = rpu;
-    plan->acc_mode = acc_mode ? 1 : 0;
+    plan->acc_mode = acc_mode ? kOutAcc : xs ? kOutYxs : kOutY;
     plan->waves = nw;
     plan->table = table;
     return TG_OK;
 }
 
+}  // namespace
+
+extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                            const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
+                            float *const *y, int32_t *const *acc, int32_t m) {
+    return plan_init_common(plan, table, table_bytes, count, descs, W, scales, x, nullptr, y, acc, m);
+}
+
+extern "C" int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                               const void *const *W, const uint16_t *const *scales, const int8_t *const *xq,
+                               const float *const *xs, float *const *y, int32_t m) {
+    if (!xs) return TG_EINVAL;
+    return plan_init_common(plan, table, table_bytes, count, descs, W, scales, xq, xs, y, nullptr, m);
+}
+
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
-        plan->m > plan_max_m(plan->fmt))
+        plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs)
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
@@ -261,7 +296,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     g.units = plan->units;
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
-    return launch(plan->fmt, g, plan->acc_mode != 0, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
+    return launch(plan->fmt, g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
 }
 
 extern "C" int tg_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, int32_t unroll,

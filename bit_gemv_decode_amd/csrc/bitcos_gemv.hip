@@ -144,7 +144,7 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
 // sign cursor runs on from step to step. Chunked GEMVs: a unit is NB rows; its steps go chunk by
 // chunk (NB steps per chunk pass), each row's cursor carried from its previous chunk. With NB > 4 the
 // body holds NB half-steps and the stage slots are taken modulo NB.
-template <int M, bool ACC, int NB, bool CHUNKED>
+template <int M, bool ACC, int NB, bool CHUNKED, bool XS>
 __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     // Chunked rows at m = 1: units of 8 rows (the activation slice is reloaded once per pass, so
     // longer passes halve those reloads), each lane summing its group terms of the unit's rows in
@@ -170,6 +170,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
     x.ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)M * (uint32_t)p.n * 4u);
     x.racc = make_rsrc(p.acc, ACC ? (uint32_t)M * (uint32_t)p.n * (uint32_t)p.ng * 4u : 0u);
+    x.rxs = make_rsrc(p.xs, XS ? (uint32_t)M * (uint32_t)p.ng * 4u : 0u);
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const int rpu = p.rpu;
     const int row_begin = (u0 - p.unit_begin) * rpu;
@@ -177,6 +178,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     const uint32_t kb = (uint32_t)(p.k >> 3);  // bitmap bytes per row
 
     uint32_t xr[M][32];
+    float xsv[M];               // activation group scales of the lane's group (1 without them)
     uint32_t cur = 0;           // single-chunk: sign cursor of the next step to scan
     uint32_t ccur[NB] = {};     // chunked: sign cursor of each row of the unit being scanned
     double facc[RACC ? NB : 1];  // chunked, m = 1: the lane's running term of each row of the unit
@@ -207,7 +209,9 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
         red = make_red(NB, 1, 64, p.rmagic);
     }
     load_x<M>(x, voff_x, xr);
+    load_xs<M, XS>(x, voff_x, xsv);
     wait_x<M>(xr);
+    wait_xs<M, XS>(xsv);
 
     u32x4 bm[4] = {};
     SgBuf g[4] = {};
@@ -234,7 +238,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && (lane < x.R * x.G) &&
                                     row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
-                    emit<M, ACC, NB>(x, acc, g[jb].scale, tile, slot, false, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB, XS>(x, acc, g[jb].scale, xsv, tile, slot, false, va ? voff_acc : kOffOff,
                                      live_or_dead(live, (uint32_t)row0 * (uint32_t)x.ng * 4u));
                     if constexpr (!ACC) {
                         if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
@@ -244,10 +248,11 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                     const int gc = cD == x.nch - 1 ? x.glast : 64;
                     const bool va = live && lane < gc && row < row_end;
                     if constexpr (RACC && !ACC) {
-                        const double term = (double)acc[0] * (double)half_bits_to_float(g[jb].scale);
+                        double term = (double)acc[0] * (double)half_bits_to_float(g[jb].scale);
+                        if constexpr (XS) term *= (double)xsv[0];
                         facc[slot] = cD != 0 ? facc[slot] + term : term;
                     } else {
-                        emit<M, ACC, NB>(x, acc, g[jb].scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                        emit<M, ACC, NB, XS>(x, acc, g[jb].scale, xsv, tile, slot, cD != 0, va ? voff_acc : kOffOff,
                                          live_or_dead(live, ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u));
                     }
                     if (slot == NB - 1) {  // static: last step of a chunk pass
@@ -273,7 +278,9 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                         TG_SCHED_FENCE();
                         // the next decode pass's x slice, ahead of this half-step's prefetches
                         const int gcn = cD == x.nch - 1 ? x.glast : 64;
-                        load_x<M>(x, lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff, xr);
+                        const uint32_t vx = lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff;
+                        load_x<M>(x, vx, xr);
+                        load_xs<M, XS>(x, vx, xsv);
                     }
                 }
             }
@@ -338,15 +345,15 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     }
 }
 
-template <int M, bool ACC, int NB>
+template <int M, bool ACC, int NB, bool XS>
 __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     if (p.nch == 1)
-        run_loop<M, ACC, NB, false>(p, u0, u1, lds, tile);
+        run_loop<M, ACC, NB, false, XS>(p, u0, u1, lds, tile);
     else
-        run_loop<M, ACC, M == 1 ? kChunkRows1 : NB, true>(p, u0, u1, lds, tile);
+        run_loop<M, ACC, M == 1 ? kChunkRows1 : NB, true, XS>(p, u0, u1, lds, tile);
 }
 
-template <int M, bool ACC>
+template <int M, bool ACC, bool XS>
 __global__ __launch_bounds__((Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
     constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
@@ -366,21 +373,23 @@ __global__ __launch_bounds__((Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_ke
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
         const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_problem<M, ACC, NB>(p, u, u1, lds, tile);
+        if (u < u1) run_problem<M, ACC, NB, XS>(p, u, u1, lds, tile);
         u = max(u, u1);
         ++pi;
     }
 }
 
 template <int M>
-hipError_t launch_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
+hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
     using C = Cfg<M, TG_FMT_BITCOS>;
     const int blocks = grid_blocks<C::WAVES>(g);
     if (blocks < 1) return hipErrorInvalidValue;
-    if (acc_out)
-        hipLaunchKernelGGL((bitcos_gemv_kernel<M, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    if (out == kOutAcc)
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, true, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    else if (out == kOutYxs)
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     else
-        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     return hipGetLastError();
 }
 
@@ -407,11 +416,11 @@ void gemv_geometry(Problem &p, int fmt, int m) {
     p.nunits = (p.n + p.rpu - 1) / p.rpu;
 }
 
-hipError_t launch_bitcos(const GroupArgs &g, bool acc_out, hipStream_t s) {
+hipError_t launch_bitcos(const GroupArgs &g, int out, hipStream_t s) {
     switch (g.m) {
-        case 1: return launch_m<1>(g, acc_out, s);
-        case 2: return launch_m<2>(g, acc_out, s);
-        case 3: return launch_m<3>(g, acc_out, s);
+        case 1: return launch_m<1>(g, out, s);
+        case 2: return launch_m<2>(g, out, s);
+        case 3: return launch_m<3>(g, out, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -54,6 +54,7 @@ constexpr int kCG = 8;                   // groups per chunk
 constexpr int kSW = 36;                  // staged sign-stream dwords per row and chunk
 constexpr int kSWL = kSW / 4;            // ... loaded by each lane of the row
 constexpr uint32_t kStageDwords = kT * 16 * kSW;  // per wave
+constexpr uint32_t kXsDwords = kCG * 16;          // per wave: a chunk's activation scales, [group][m]
 
 // (a, b) -> (a', b'): lane rows 1 and 3 of a take rows 0 and 2 of b, and rows 0 and 2 of b take rows 1
 // and 3 of a (lane row = 16 consecutive lanes).
@@ -137,7 +138,11 @@ __device__ __forceinline__ CPos next_chunk(CPos c, int nck) {
     return CPos{wrap ? c.row + 16 * kT : c.row, wrap ? 0 : c.cu + 1};
 }
 
-template <bool ACC>
+// With XS each group's term is also multiplied by its activation group scales xs[m][g]: lane (lr, q)
+// loads xs[lr][g] of two groups of the next chunk with its other chunk loads, the values go to a per-wave
+// LDS buffer [group][m] when the chunk's data is rearranged, and each step's sign-window stage reads
+// the four scales of its rows m = 4q .. 4q + 3 with one 16-byte LDS read.
+template <bool ACC, bool XS>
 __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int mrows, const char *lds,
                                          uint32_t *stg) {
     const int lane = threadIdx.x & 63;
@@ -160,6 +165,8 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)mrows * (uint32_t)p.n * 4u);
     const __amdgpu_buffer_rsrc_t racc =
         make_rsrc(p.acc, ACC ? (uint32_t)mrows * (uint32_t)p.n * (uint32_t)ng * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.xs, XS ? (uint32_t)mrows * (uint32_t)ng * 4u : 0u);
+    uint32_t *const sxs = stg + kStageDwords;  // XS: the chunk's activation scales, [group][m]
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const uint32_t m_odd = (q & 1) ? ~0u : 0u, m_hi = (q >> 1) ? ~0u : 0u;
     const uint32_t voff_x = lr < mrows ? (uint32_t)lr * (uint32_t)p.k + 32u * (uint32_t)q : kOffOff;
@@ -183,6 +190,8 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     uint32_t cur[kT] = {};          // running sign cursor of the sign-window stage
     // step stage buffers
     uint32_t bms[2][kT] = {}, sws[2][kT][3] = {}, shs[2][kT] = {}, scs[2][kT] = {};
+    uint32_t rawx[2] = {};          // XS: xs[lr][g] of groups 2q, 2q + 1 of the next chunk as loaded
+    u32x4 xss[2] = {};              // XS: step stage, xs[4q + i][g] of the step's group
     u32x4 xa[4] = {}, xb[4] = {};
     double facc[kT][4];
 #pragma unroll
@@ -206,6 +215,14 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
                 rawb[t][4 * e + 3] = v.w;
                 if constexpr (!ACC)
                     raws[t][e] = ldh(rsc, ok ? (rowb * (uint32_t)ng + (uint32_t)g) * 2u : kOffOff, 0u);
+            }
+        }
+        if constexpr (XS) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int g = c.cu * kCG + 2 * q + e;
+                const bool ok = live && g < ng && lr < mrows;
+                rawx[e] = ld1(rxs, ok ? ((uint32_t)lr * (uint32_t)ng + (uint32_t)g) * 4u : kOffOff, 0u);
             }
         }
     };
@@ -291,7 +308,15 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
                     } else {
                         const double sd = (double)half_bits_to_float((uint16_t)scs[sl][t]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) facc[t][i] = __builtin_fma((double)cv[i], sd, facc[t][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            // scale times activation scale is exact in fp64 (11 + 24 significant bits),
+                            // and so is its product with the int32 sum inside the fma
+                            // (the element goes through a scalar first: a bit cast of a vector element
+                            // expression reinterprets the vector's first element)
+                            const uint32_t xv = xss[sl][i];
+                            const double f = XS ? sd * (double)__builtin_bit_cast(float, xv) : sd;
+                            facc[t][i] = __builtin_fma((double)cv[i], f, facc[t][i]);
+                        }
                     }
                 }
                 if constexpr (!ACC) {
@@ -351,6 +376,11 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
                     swap32(pr, pr2);
                     cbn[t] = nx.cu == 0 ? ro_cur[t] : cbn[t] + pr + pr2;
                 }
+                if constexpr (XS) {
+                    // chunk ci's activation scales to the wave's LDS buffer: group 2q + e, row lr
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) sxs[(2 * q + e) * 16 + lr] = rawx[e];
+                }
                 load_ro(nn, ci + 2 < NC);
                 load_signs(ci + 1 < NC);
             }
@@ -380,6 +410,11 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
                     bms[sl][t] = bw;
                     scs[sl][t] = (scc[t][pos >> 1] >> (16 * (pos & 1))) & 0xFFFFu;
                 }
+                if constexpr (XS) {
+                    // read as the uint32_t words they were written as (one 16-byte LDS read)
+                    const uint32_t *src = sxs + pos * 16 + 4 * q;
+                    xss[sl] = u32x4{src[0], src[1], src[2], src[3]};
+                }
             }
             TG_SCHED_FENCE();
         }
@@ -392,22 +427,23 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     }
 }
 
-template <bool ACC>
+template <bool ACC, bool XS>
 __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
+    constexpr uint32_t kWaveDwords = kStageDwords + (XS ? kXsDwords : 0u);
     __shared__ uint4 s_tab[kTabBytes / 16];
-    __shared__ uint32_t s_stage[kWaves * kStageDwords];
+    __shared__ __attribute__((aligned(16))) uint32_t s_stage[kWaves * kWaveDwords];
     load_bitcos_tables<kBlock>(s_tab);
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    uint32_t *stg = s_stage + wave * kStageDwords;
+    uint32_t *stg = s_stage + wave * kWaveDwords;
     int u, u_end, pi;
     wave_range<kWaves>(ga, wave, u, u_end, pi);
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
         const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_mfma<ACC>(p, u, u1, ga.m, lds, stg);
+        if (u < u1) run_mfma<ACC, XS>(p, u, u1, ga.m, lds, stg);
         u = max(u, u1);
         ++pi;
     }
@@ -428,14 +464,16 @@ void mfma_geometry(Problem &p) {
     p.nunits = (p.n + p.rpu - 1) / p.rpu;
 }
 
-hipError_t launch_bitcos_mfma(const GroupArgs &g, bool acc_out, hipStream_t s) {
+hipError_t launch_bitcos_mfma(const GroupArgs &g, int out, hipStream_t s) {
     if (g.m < kMfmaMinM || g.m > TG_MAX_M) return hipErrorInvalidValue;
     const int blocks = grid_blocks<kWaves>(g);
     if (blocks < 1) return hipErrorInvalidValue;
-    if (acc_out)
-        hipLaunchKernelGGL((bitcos_mfma_kernel<true>), dim3(blocks), dim3(kBlock), 0, s, g);
+    if (out == kOutAcc)
+        hipLaunchKernelGGL((bitcos_mfma_kernel<true, false>), dim3(blocks), dim3(kBlock), 0, s, g);
+    else if (out == kOutYxs)
+        hipLaunchKernelGGL((bitcos_mfma_kernel<false, true>), dim3(blocks), dim3(kBlock), 0, s, g);
     else
-        hipLaunchKernelGGL((bitcos_mfma_kernel<false>), dim3(blocks), dim3(kBlock), 0, s, g);
+        hipLaunchKernelGGL((bitcos_mfma_kernel<false, false>), dim3(blocks), dim3(kBlock), 0, s, g);
     return hipGetLastError();
 }
 

@@ -132,6 +132,7 @@ __device__ __forceinline__ Problem uniform_problem(const Problem &q) {
     p.x = uniform_ptr(q.x);
     p.y = uniform_ptr(q.y);
     p.acc = uniform_ptr(q.acc);
+    p.xs = uniform_ptr(q.xs);
     p.codes_bytes = uniform_u32(q.codes_bytes);
     p.sign_bytes = uniform_u32(q.sign_bytes);
     p.n = uniform_i32(q.n);

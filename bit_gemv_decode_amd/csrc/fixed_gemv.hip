@@ -173,7 +173,7 @@ __device__ __forceinline__ void decode_fixed(const CodeBuf &b, const uint32_t (&
 // the codes of step h are loaded (four code buffers rotate with the four half-steps of the loop
 // body). Every stage runs on every half-step; dead steps use dead offsets and decode into tile slots
 // a live step overwrites first.
-template <int FMT, int M, bool ACC, int NB, bool CHUNKED>
+template <int FMT, int M, bool ACC, int NB, bool CHUNKED, bool XS>
 __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     constexpr uint32_t GB = Fmt<FMT>::kGroupBytes;
     constexpr int XW = Fmt<FMT>::kXWords;
@@ -193,6 +193,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
     x.ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)M * (uint32_t)p.n * 4u);
     x.racc = make_rsrc(p.acc, ACC ? (uint32_t)M * (uint32_t)p.n * (uint32_t)p.ng * 4u : 0u);
+    x.rxs = make_rsrc(p.xs, XS ? (uint32_t)M * (uint32_t)p.ng * 4u : 0u);
     const uint32_t laneoff = FMT == TG_FMT_2BIT ? (uint32_t)lane << 2 : (uint32_t)(lane & 31) << 3;
     const int rpu = p.rpu;
     const int row_begin = (u0 - p.unit_begin) * rpu;
@@ -200,6 +201,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     const uint32_t ng = (uint32_t)p.ng;
 
     uint32_t xf[M][XW];
+    float xsv[M];  // activation group scales of the lane's group (1 without them)
     int T;
     uint32_t voff_sc, voff_acc, voff_x, lane_grp;  // lane_grp: the lane's group index offset in a step
     bool act;
@@ -224,7 +226,9 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
         red = make_red(NB, 1, 64, p.rmagic);
     }
     load_xf<FMT, M>(x, voff_x, xf);
+    load_xs<M, XS>(x, voff_x, xsv);
     wait_xf<FMT, M>(xf);
+    wait_xs<M, XS>(xsv);
 
     CodeBuf cb[4] = {};
     int cD = 0, rD = row_begin, cB = 0, rB = row_begin;
@@ -244,7 +248,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && act && row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
-                    emit<M, ACC, NB>(x, acc, b.scale, tile, slot, false, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB, XS>(x, acc, b.scale, xsv, tile, slot, false, va ? voff_acc : kOffOff,
                                      live_or_dead(live, (uint32_t)row0 * ng * 4u));
                     if constexpr (!ACC) {
                         if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
@@ -253,7 +257,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                     const int row = rD + slot;
                     const int gc = cD == x.nch - 1 ? x.glast : 64;
                     const bool va = live && lane < gc && row < row_end;
-                    emit<M, ACC, NB>(x, acc, b.scale, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB, XS>(x, acc, b.scale, xsv, tile, slot, cD != 0, va ? voff_acc : kOffOff,
                                      live_or_dead(live, ((uint32_t)row * ng + (uint32_t)cD * 64u) * 4u));
                     if (slot == NB - 1) {  // static: last step of a chunk pass
                         if constexpr (!ACC) reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
@@ -262,7 +266,9 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                         cD = live ? (wrap ? 0 : cD + 1) : cD;
                         TG_SCHED_FENCE();
                         const int gcn = cD == x.nch - 1 ? x.glast : 64;
-                        load_xf<FMT, M>(x, lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff, xf);
+                        const uint32_t vx = lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff;
+                        load_xf<FMT, M>(x, vx, xf);
+                        load_xs<M, XS>(x, vx, xsv);
                     }
                 }
             }
@@ -302,7 +308,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     }
 }
 
-template <int FMT, int M, bool ACC>
+template <int FMT, int M, bool ACC, bool XS>
 __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupArgs ga) {
     using C = Cfg<M, FMT>;
     constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
@@ -347,9 +353,9 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
         const int u1 = min(u_end, p.unit_begin + p.nunits);
         if (u < u1) {
             if (p.nch == 1)
-                run_fixed<FMT, M, ACC, NB, false>(p, u, u1, lds, tile);
+                run_fixed<FMT, M, ACC, NB, false, XS>(p, u, u1, lds, tile);
             else
-                run_fixed<FMT, M, ACC, NB, true>(p, u, u1, lds, tile);
+                run_fixed<FMT, M, ACC, NB, true, XS>(p, u, u1, lds, tile);
         }
         u = max(u, u1);
         ++pi;
@@ -357,35 +363,37 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
 }
 
 template <int FMT, int M>
-hipError_t launch_fixed_m(const GroupArgs &g, bool acc_out, hipStream_t s) {
+hipError_t launch_fixed_m(const GroupArgs &g, int out, hipStream_t s) {
     using C = Cfg<M, FMT>;
     const int blocks = grid_blocks<C::WAVES>(g);
     if (blocks < 1) return hipErrorInvalidValue;
-    if (acc_out)
-        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    if (out == kOutAcc)
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, true, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    else if (out == kOutYxs)
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     else
-        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_fixed(const GroupArgs &g, bool acc_out, hipStream_t s) {
+hipError_t launch_fixed(const GroupArgs &g, int out, hipStream_t s) {
     switch (g.m) {
-        case 1: return launch_fixed_m<FMT, 1>(g, acc_out, s);
-        case 2: return launch_fixed_m<FMT, 2>(g, acc_out, s);
-        case 3: return launch_fixed_m<FMT, 3>(g, acc_out, s);
+        case 1: return launch_fixed_m<FMT, 1>(g, out, s);
+        case 2: return launch_fixed_m<FMT, 2>(g, out, s);
+        case 3: return launch_fixed_m<FMT, 3>(g, out, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_t5(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    return launch_fixed<TG_FMT_5TRIT>(g, acc_out, s);
+hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s) {
+    return launch_fixed<TG_FMT_5TRIT>(g, out, s);
 }
 
-hipError_t launch_b2(const GroupArgs &g, bool acc_out, hipStream_t s) {
-    return launch_fixed<TG_FMT_2BIT>(g, acc_out, s);
+hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s) {
+    return launch_fixed<TG_FMT_2BIT>(g, out, s);
 }
 
 }  // namespace tg

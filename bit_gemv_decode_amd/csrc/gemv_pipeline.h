@@ -56,7 +56,7 @@ __device__ __forceinline__ void st1(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32
 
 // Wave-uniform per-GEMV values.
 struct Ctx {
-    __amdgpu_buffer_rsrc_t rbm, rsg, rsc, rro, rx, ry, racc;
+    __amdgpu_buffer_rsrc_t rbm, rsg, rsc, rro, rx, ry, racc, rxs;
     int n, k, ng, nch, G, R, glast;
 };
 
@@ -84,6 +84,25 @@ __device__ __forceinline__ void wait_x(const uint32_t (&xr)[M][32]) {
     for (int mi = 0; mi < M; ++mi)
 #pragma unroll
         for (int j = 0; j < 32; j += 4) asm volatile("" ::"v"(xr[mi][j]));
+}
+
+// Activation group scale of the lane's group (the group whose x bytes load_x reads at voff, i.e. group
+// voff / 128 of each activation row) for every activation row, when the GEMV has them (XS); lanes
+// without a group (voff = kOffOff, which stays out of range after the shift) read zero. Without
+// activation scales every factor is 1.
+template <int M, bool XS>
+__device__ __forceinline__ void load_xs(const Ctx &x, uint32_t voff, float (&xsv)[M]) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi)
+        xsv[mi] = XS ? __builtin_bit_cast(float, ld1(x.rxs, voff >> 5, (uint32_t)(mi * x.ng) * 4u)) : 1.0f;
+}
+
+template <int M, bool XS>
+__device__ __forceinline__ void wait_xs(const float (&xsv)[M]) {
+    if constexpr (XS) {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) asm volatile("" ::"v"(xsv[mi]));
+    }
 }
 
 // Lane roles in the unit-end reduction: the tile's rows are summed by lpr lanes each.
@@ -137,11 +156,12 @@ __device__ __forceinline__ void reduce_store(const Ctx &x, const Red &r, const d
             (uint32_t)(mi * x.n) * 4u);
 }
 
-// Decode stage epilogue: the group terms (int32 sum times scale, fp64) go to tile slot `slot`
-// (added to what earlier chunks left there when `add`); accumulator outputs are stored directly.
-template <int M, bool ACC, int NB>
-__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t scale, double *tile, int slot,
-                                     bool add, uint32_t voff_acc, uint32_t soff_acc) {
+// Decode stage epilogue: the group terms (int32 sum times scale, times the activation group scale
+// when XS; fp64, every product exact) go to tile slot `slot` (added to what earlier chunks left there
+// when `add`); accumulator outputs are stored directly.
+template <int M, bool ACC, int NB, bool XS>
+__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t scale, const float (&xsv)[M],
+                                     double *tile, int slot, bool add, uint32_t voff_acc, uint32_t soff_acc) {
     const int lane = threadIdx.x & 63;
     if constexpr (ACC) {
 #pragma unroll
@@ -152,7 +172,8 @@ __device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) {
             double *t = tile + mi * NB * 64 + slot * 64 + lane;
-            const double term = (double)acc[mi] * s;
+            double term = (double)acc[mi] * s;
+            if constexpr (XS) term *= (double)xsv[mi];
             *t = add ? *t + term : term;
         }
     }

@@ -23,6 +23,7 @@ struct Problem {
     const int8_t *x;          // int8 [m][k]
     float *y;                 // float [m][n] (value path)
     int32_t *acc;             // int32 [m][n][k/128] (accumulator path)
+    const float *xs;          // float [m][k/128] activation group scales (value path with them), else null
     uint32_t codes_bytes;     // bytes of the codes section
     uint32_t sign_bytes;      // bytes of the sign section
     int32_t n, k;             // rows, reduction length (k % 128 == 0)
@@ -79,21 +80,28 @@ constexpr int kMfmaMinM = 4;
 constexpr int kMfmaTiles = 2;
 constexpr int kMfmaWavesPerCu = 8;
 void mfma_geometry(Problem &p);
-hipError_t launch_bitcos_mfma(const GroupArgs &g, bool acc_out, hipStream_t s);
+hipError_t launch_bitcos_mfma(const GroupArgs &g, int out, hipStream_t s);
 
 // Host-side checks of a descriptor; `limit` is the buffer length when known (0 = trust bytes_total).
 int check_desc(const tg_desc *d, uint64_t limit);
 
 // Fill a Problem from a checked descriptor and the caller's pointers.
 Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, const int8_t *x, float *y,
-                     int32_t *acc);
+                     int32_t *acc, const float *xs = nullptr);
 
+
+// What a GEMV launch writes: fp32 y, the int32 per-group accumulators, or fp32 y with each group's
+// term also multiplied by its activation group scale xs[m][g].
+enum OutMode { kOutY = 0, kOutAcc = 1, kOutYxs = 2 };
 
 // Kernel launchers (asynchronous; return the HIP status of the launch). `g.one` or `g.table` holds
 // the problems; the launchers set grid sizes themselves.
-hipError_t launch_bitcos(const GroupArgs &g, bool acc_out, hipStream_t s);
-hipError_t launch_t5(const GroupArgs &g, bool acc_out, hipStream_t s);
-hipError_t launch_b2(const GroupArgs &g, bool acc_out, hipStream_t s);
+hipError_t launch_bitcos(const GroupArgs &g, int out, hipStream_t s);
+hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s);
+hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s);
+
+// Per-group int8 quantisation of `groups` runs of 128 fp32 activations (one wave per group).
+hipError_t launch_quantize_x(const float *x, int64_t groups, int8_t *xq, float *xs, hipStream_t s);
 
 // Streaming-read reference kernel (bandwidth ceiling probe).
 hipError_t launch_stream_read(const void *buf, uint32_t bytes, uint32_t *sink, int blocks, int unroll, hipStream_t s);

@@ -145,6 +145,30 @@ int ternary_gemv(const tg_desc *desc, const void *W, const uint16_t *scales, con
 int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_t *acc, int32_t m, void *stream);
 
 /*
+ * Activations quantised per group ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-C, the
+ * int8 path after Fig. 5: activations are quantised to int8 per group of 128 and each group's scale
+ * is applied once per group, beside the weight scale). The page does not spell out the quantiser;
+ * this library uses the symmetric absmax form.
+ *
+ * tg_quantize_x (device, asynchronous): x is device float [m][k] (finite values), k a multiple of 128,
+ *   1 <= m <= TG_MAX_M. For each group of 128 consecutive elements of a row:
+ *       sigma = max |x| / 127                       (IEEE fp32 division, nearest-even)
+ *       xq    = clamp(rint_even(x / sigma), -127, 127)   (IEEE fp32 division), 0 where sigma = 0
+ *   and writes xq (device int8 [m][k]) and xs (device float [m][k/128], the sigmas). The codes are
+ *   decided in fp32, so they are exact and reproducible. Alignment: x 8 bytes, xq 2, xs 4.
+ *   Errors: TG_EINVAL (null or misaligned pointer, m out of range), TG_ESHAPE (k < 128, k % 128 != 0
+ *   or k > 2^30), TG_EHIP.
+ *
+ * ternary_gemv_xs (device, asynchronous): ternary_gemv on quantised activations xq with their group
+ *   scales xs (device float [m][k/128], 4-byte aligned):
+ *       y[m][n] = sum_g scale[n][g] * xs[m][g] * acc[m][n][g]     (each term exact in fp64, fp32 store)
+ *   Same paths, arguments and errors as ternary_gemv; a null or misaligned xs is TG_EINVAL.
+ */
+int tg_quantize_x(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, void *stream);
+int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, const int8_t *xq, const float *xs,
+                    float *y, int32_t m, void *stream);
+
+/*
  * Grouped launch: several GEMVs of one format and one activation-row count m (1 <= m <= 3; BITCOS
  * 1 <= m <= TG_MAX_M, on the thin-batch path from m = 4) run as
  * one persistent kernel. This is the batched form of the same operation (each GEMV is computed
@@ -177,7 +201,7 @@ typedef struct tg_plan {
     int32_t count;       /* GEMVs in the table */
     int32_t units;       /* work units over all GEMVs */
     int32_t rows_per_unit;
-    int32_t acc_mode;    /* 1: int32 accumulator outputs */
+    int32_t acc_mode;    /* 0: fp32 y; 1: int32 accumulator outputs; 2: fp32 y with activation group scales */
     int32_t waves;       /* waves of the launch the table's work split was made for */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
@@ -186,6 +210,12 @@ size_t tg_plan_table_bytes(int32_t count);
 int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                  const void *const *W, const uint16_t *const *scales, const int8_t *const *x, float *const *y,
                  int32_t *const *acc, int32_t m);
+/* tg_plan_init for ternary_gemv_xs outputs: every GEMV of the plan takes quantised activations xq[i]
+ * and their group scales xs[i] (device float [m][k/128], 4-byte aligned) and writes fp32 y[i]. Same
+ * rules and errors as tg_plan_init with acc == NULL; a null xs array or entry is TG_EINVAL. */
+int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                    const void *const *W, const uint16_t *const *scales, const int8_t *const *xq,
+                    const float *const *xs, float *const *y, int32_t m);
 int ternary_gemv_plan(const tg_plan *plan, void *stream);
 
 /*

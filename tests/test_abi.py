@@ -192,3 +192,42 @@ def test_plan_argument_errors_before_any_gpu_work():
     # running a plan that was never initialised
     assert L.ternary_gemv_plan(ctypes.byref(binding.TgPlan()), None) == -1
     assert L.ternary_gemv_plan(None, None) == -1
+
+
+def test_activation_quantisation_argument_errors_before_any_gpu_work():
+    L = binding.lib()
+    dummy = ctypes.c_void_p(256)
+    # tg_quantize_x: null or misaligned pointers, m out of range -> TG_EINVAL; bad k -> TG_ESHAPE
+    assert L.tg_quantize_x(None, 1, 128, dummy, dummy, None) == -1
+    assert L.tg_quantize_x(dummy, 1, 128, None, dummy, None) == -1
+    assert L.tg_quantize_x(dummy, 1, 128, dummy, None, None) == -1
+    assert L.tg_quantize_x(dummy, 0, 128, dummy, dummy, None) == -1
+    assert L.tg_quantize_x(dummy, 17, 128, dummy, dummy, None) == -1
+    assert L.tg_quantize_x(ctypes.c_void_p(260), 1, 128, dummy, dummy, None) == -1
+    assert L.tg_quantize_x(dummy, 1, 128, ctypes.c_void_p(257), dummy, None) == -1
+    assert L.tg_quantize_x(dummy, 1, 128, dummy, ctypes.c_void_p(258), None) == -1
+    assert L.tg_quantize_x(dummy, 1, 0, dummy, dummy, None) == -3
+    assert L.tg_quantize_x(dummy, 1, 192, dummy, dummy, None) == -3
+    assert L.tg_quantize_x(dummy, 1, (1 << 30) + 128, dummy, dummy, None) == -3
+    # ternary_gemv_xs: the ternary_gemv checks plus a null or misaligned activation-scale pointer
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = B.pack_bitcos(w).desc
+    assert L.ternary_gemv_xs(ctypes.byref(d), dummy, dummy, dummy, None, dummy, 1, None) == -1
+    assert L.ternary_gemv_xs(ctypes.byref(d), dummy, dummy, dummy, ctypes.c_void_p(258), dummy, 1, None) == -1
+    assert L.ternary_gemv_xs(ctypes.byref(d), dummy, dummy, dummy, dummy, dummy, 0, None) == -1
+    assert L.ternary_gemv_xs(ctypes.byref(d), dummy, None, dummy, dummy, dummy, 1, None) == -1
+    d2 = binding.TgDesc.from_buffer_copy(d)
+    d2.magic = 0
+    assert L.ternary_gemv_xs(ctypes.byref(d2), dummy, dummy, dummy, dummy, dummy, 1, None) == -4
+    # tg_plan_init_xs: a null activation-scale array or entry, or a misaligned entry
+    descs = (binding.TgDesc * 1)(d)
+    P1 = ctypes.c_void_p * 1
+    ptrs = P1(256)
+    plan = binding.TgPlan()
+    nbytes = L.tg_plan_table_bytes(1)
+    assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, None, ptrs, 1) == -1
+    assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, P1(None), ptrs, 1) == -1
+    assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, P1(258), ptrs, 1) == -1
+    assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    bad = (binding.TgDesc * 1)(d2)
+    assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, bad, ptrs, ptrs, ptrs, ptrs, ptrs, 1) == -4
