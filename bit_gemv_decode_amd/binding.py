@@ -47,7 +47,8 @@ class TgDesc(ctypes.Structure):
 class TgPlan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("fmt", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("count", ctypes.c_int32), ("units", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
-                ("acc_mode", ctypes.c_int32), ("waves", ctypes.c_int32), ("table", ctypes.c_void_p)]
+                ("acc_mode", ctypes.c_int32), ("waves", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("table", ctypes.c_void_p)]
 
 
 _lib = None

@@ -61,19 +61,23 @@ bool fits_offsets(const tg_desc *d, int32_t m) {
            (uint64_t)m * (uint64_t)d->k <= lim;
 }
 
-// BITCOS with at least kMfmaMinM activation rows goes to the matrix-core kernel in one launch.
-bool use_mfma(int fmt, int32_t m) { return fmt == TG_FMT_BITCOS && m >= kMfmaMinM; }
+// Whether a BITCOS GEMV with m activation rows and k-long rows runs on the matrix-core kernel (in one
+// launch for all m rows): always from kMfmaAlwaysM rows, and at kMfmaMinM rows for long rows.
+bool use_mfma(int fmt, int32_t m, int64_t k) {
+    return fmt == TG_FMT_BITCOS &&
+           (m >= kMfmaAlwaysM || (m >= kMfmaMinM && k / TG_GROUP > kMfmaLongRowGroups));
+}
 
-// Work geometry of one GEMV for a launch of m activation rows.
-void geometry(Problem &p, int fmt, int32_t m) {
-    if (use_mfma(fmt, m))
+// Work geometry of one GEMV for a launch of m activation rows on the chosen path.
+void geometry(Problem &p, int fmt, int32_t m, bool mfma) {
+    if (mfma)
         mfma_geometry(p);
     else
         gemv_geometry(p, fmt, m);
 }
 
-hipError_t launch(int fmt, const GroupArgs &g, int out, hipStream_t s) {
-    if (use_mfma(fmt, g.m)) return launch_bitcos_mfma(g, out, s);
+hipError_t launch(int fmt, const GroupArgs &g, int out, bool mfma, hipStream_t s) {
+    if (mfma) return launch_bitcos_mfma(g, out, s);
     switch (fmt) {
         case TG_FMT_BITCOS: return launch_bitcos(g, out, s);
         case TG_FMT_5TRIT: return launch_t5(g, out, s);
@@ -98,7 +102,8 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
     const int64_t n = desc->n, k = desc->k, ng = k / TG_GROUP;
     // Activation rows go in launches of at most three on the vector path (each launch reads the
     // weights once); the matrix-core path takes all of them in one launch.
-    const int32_t step = use_mfma(desc->fmt, m) ? m : kVectorMaxM;
+    const bool mfma = use_mfma(desc->fmt, m, desc->k);
+    const int32_t step = mfma ? m : kVectorMaxM;
     for (int32_t m0 = 0; m0 < m; m0 += step) {
         const int32_t mt = std::min<int32_t>(step, m - m0);
         GroupArgs g{};
@@ -108,10 +113,10 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
-        geometry(g.one, desc->fmt, mt);
+        geometry(g.one, desc->fmt, mt, mfma);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
-        if (launch(desc->fmt, g, out, s) != hipSuccess) return TG_EHIP;
+        if (launch(desc->fmt, g, out, mfma, s) != hipSuccess) return TG_EHIP;
     }
     return TG_OK;
 }
@@ -145,7 +150,7 @@ namespace {
 
 // Waves of a persistent launch on this device for m activation rows; a plan's per-wave ranges are
 // sized for it (the table has room for the largest count).
-int plan_waves(int fmt, int m) { return device_cus() * (use_mfma(fmt, m) ? kMfmaWavesPerCu : gemv_waves(fmt, m)); }
+int plan_waves(int fmt, int m, bool mfma) { return device_cus() * (mfma ? kMfmaWavesPerCu : gemv_waves(fmt, m)); }
 int plan_waves_max() { return device_cus() * std::max(kMaxWavesPerCu, kMfmaWavesPerCu); }
 
 // Largest m a plan of this format takes (one launch per plan).
@@ -205,7 +210,18 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         const tg_desc *d = &descs[i];
         host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr, xs ? xs[i] : nullptr);
-        geometry(host[i], fmt, m);
+    }
+    // One launch takes one path: the matrix-core kernel when every GEMV would take it on its own, or
+    // (at m = kMfmaMinM) when the GEMVs that would take it hold most of the plan's weights.
+    double w_mfma = 0, w_all = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const double wts = (double)descs[i].n * (double)descs[i].k;
+        w_all += wts;
+        if (use_mfma(fmt, m, descs[i].k)) w_mfma += wts;
+    }
+    const bool mfma = fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
+    for (int32_t i = 0; i < count; ++i) {
+        geometry(host[i], fmt, m, mfma);
         rpu = std::max(rpu, (int)host[i].rpu);
     }
     // Work order: GEMVs of one shape next to each other (by k, then n; the caller's order within a
@@ -222,13 +238,12 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         units += host[i].nunits;
         if (units > 0x7FFFFFFF) return TG_ESHAPE;
     }
-    const bool mfma = use_mfma(fmt, m);
     double total_cost = 0;
     for (int32_t i = 0; i < count; ++i)
         for (int64_t u = host[i].unit_begin; u < host[i].unit_begin + host[i].nunits; ++u)
             total_cost += unit_cost(host[i], fmt, mfma, u);
     // Contiguous unit ranges per wave, balanced by the cost model above.
-    const int nw = plan_waves(fmt, m);
+    const int nw = plan_waves(fmt, m, mfma);
     std::vector<WaveRange> ranges((size_t)nw);
     {
         int32_t pi = 0;
@@ -264,6 +279,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     plan->rows_per_unit = rpu;
     plan->acc_mode = acc_mode ? kOutAcc : xs ? kOutYxs : kOutY;
     plan->waves = nw;
+    plan->path = mfma ? 1 : 0;
     plan->table = table;
     return TG_OK;
 }
@@ -285,18 +301,20 @@ extern "C" int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, i
 
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
-        plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs)
+        plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs ||
+        plan->path < 0 || plan->path > 1 || (plan->path == 1 && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
-    if (plan->waves != plan_waves(plan->fmt, plan->m)) return TG_EINVAL;  // built for another device
+    const bool mfma = plan->path == 1;
+    if (plan->waves != plan_waves(plan->fmt, plan->m, mfma)) return TG_EINVAL;  // built for another device
     g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
     g.waves = plan->waves;
     g.count = plan->count;
     g.units = plan->units;
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
-    return launch(plan->fmt, g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
+    return launch(plan->fmt, g, plan->acc_mode, mfma, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
 }
 
 extern "C" int tg_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, int32_t unroll,

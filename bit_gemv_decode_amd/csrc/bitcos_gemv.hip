@@ -7,7 +7,7 @@
 // negative) pair into w = p - 2n (Eq. 2), contracts against int8 activations in int32 and applies
 // the group scale once per 128-element group.
 //
-// Mapping on CDNA4 (wave64, one persistent block per CU: 768 threads at m = 1, 512 at m = 2, 3):
+// Mapping on CDNA4 (wave64, one persistent block per CU: 1024 threads at m = 1, 512 at m = 2, 3):
 //   * a lane owns one 128-weight group of one row per step: its four bitmap dwords arrive with one
 //     16-byte load, its scale with one 2-byte load. A row of k weights takes ng = k/128 lanes; when
 //     ng <= 64 a step holds R = 64/ng consecutive rows, otherwise a row is split into chunks of 64
@@ -31,8 +31,8 @@
 //     (exact in fp64) goes to an LDS tile; once per unit the tile's rows are summed (fp64, DPP) and
 //     stored as fp32. Chunked rows at m = 1 keep those terms in registers instead (one fp64 per row
 //     of the unit and lane) and reduce them over the wave at the unit's end.
-//   * loads are software-pipelined two steps ahead (bitmap) and one step ahead (signs), with the loop
-//     unrolled at least twice so that no register with a load in flight is ever copied. Every load goes
+//   * loads are software-pipelined: a step's bitmap four half-steps before its decode, its sign
+//     windows two, with the loop unrolled so that no register with a load in flight is ever copied. Every load goes
 //     through a buffer resource and is issued unconditionally; lanes with nothing to read use an
 //     out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
@@ -133,9 +133,9 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
 }
 
 // Pipeline over the steps of units [u0, u1) of one GEMV. In half-step h, step h - 4 is decoded, the
-// bitmap of step h is loaded, and the signs of step h - 1 are located and loaded: a bitmap has one
-// decode's time to arrive, a sign window three (the bitmap load goes first, so that waiting for it
-// never waits for younger sign loads). The loop body holds four half-steps, so every stage
+// bitmap of step h is loaded, and the signs of step h - LAG (LAG = 2 for units of four or more steps,
+// else 1) are located and loaded: a bitmap has LAG half-steps to arrive, a sign window 4 - LAG (the
+// bitmap load goes first, so that waiting for it never waits for younger sign loads). The loop body holds four half-steps, so every stage
 // buffer has a fixed register home (bitmaps and sign windows rotate over four) and no register with
 // a load in flight is ever copied. Each stage runs unconditionally (outside the live range its loads
 // use dead offsets), apart from decode work that loads nothing.
@@ -152,6 +152,11 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     constexpr bool RACC = CHUNKED && M == 1;
     constexpr int U = NB > 4 ? NB : 4;  // half-steps per loop body
     static_assert(U % NB == 0 && U % 4 == 0, "static stage positions");
+    // Half-steps between a step's bitmap load and its sign stage: two, so that the bitmap and the sign
+    // windows each have two half-steps to arrive (measured 2 % faster than one and three on MI355X,
+    // and it frees the registers that let 16 waves share a CU at m = 1). Units of fewer than four
+    // steps keep one: the row-index entries loaded with a unit's first bitmap must survive until then.
+    constexpr int LAG = NB >= 4 ? 2 : 1;
     const int lane = threadIdx.x & 63;
     Ctx x;
     x.n = p.n;
@@ -310,17 +315,18 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                 }
             }
             TG_SCHED_FENCE();
-            // ---- signs of step h - 1 (bitmap bm[(j + 3) & 3] -> g[(j + 3) & 3]) ----
+            // ---- signs of step h - LAG (bitmap bm[(j + 4 - LAG) & 3] -> g[(j + 4 - LAG) & 3]) ----
             {
-                const int s = h - 1;
+                const int s = h - LAG;
                 const bool live = s >= 0 && s < T;
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
-                    const uint32_t total = stage_signs<ACC>(x, bm[(j + 3) & 3], cur, live, voff_sc,
-                                                            (uint32_t)row0 * (uint32_t)x.ng * 2u, g[(j + 3) & 3]);
+                    const uint32_t total = stage_signs<ACC>(x, bm[(j + 4 - LAG) & 3], cur, live, voff_sc,
+                                                            (uint32_t)row0 * (uint32_t)x.ng * 2u,
+                                                            g[(j + 4 - LAG) & 3]);
                     cur += live ? total : 0u;
                 } else {
-                    const int slot = (j + U - 1) % NB;  // step h - 1 within its unit (pass)
+                    const int slot = (j + U - LAG) % NB;  // step h - LAG within its unit (pass)
                     if (slot == 0) {  // static: a chunk pass starts; its first pass takes the row index
                         const bool first = live && cS == 0;
 #pragma unroll
@@ -330,8 +336,8 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                         }
                     }
                     const uint32_t total = stage_signs<ACC>(
-                        x, bm[(j + 3) & 3], ccur[slot], live, voff_sc,
-                        ((uint32_t)(rS + slot) * (uint32_t)x.ng + (uint32_t)cS * 64u) * 2u, g[(j + 3) & 3]);
+                        x, bm[(j + 4 - LAG) & 3], ccur[slot], live, voff_sc,
+                        ((uint32_t)(rS + slot) * (uint32_t)x.ng + (uint32_t)cS * 64u) * 2u, g[(j + 4 - LAG) & 3]);
                     ccur[slot] += live ? total : 0u;
                     if (slot == NB - 1) {
                         const bool wrap = live && cS == x.nch - 1;

@@ -61,10 +61,9 @@ struct GroupArgs {
     Problem one;
 };
 
-// Waves per CU of a vector-path GEMV launch of format fmt for m activation rows (one block per CU:
-// the decode tables fill most of the LDS). BITCOS at m = 1 runs 12: its chunked rows keep eight fp64
-// row sums per lane, which does not fit the 128 registers of 16 waves.
-constexpr int gemv_waves(int fmt, int m) { return m > 1 ? 8 : fmt == TG_FMT_BITCOS ? 12 : 16; }
+// Waves per CU of a vector-path GEMV launch for m activation rows (one block per CU: the decode
+// tables fill most of the LDS): 16 at m = 1 (128 registers per lane), 8 at m = 2, 3.
+constexpr int gemv_waves(int fmt, int m) { return (void)fmt, m > 1 ? 8 : 16; }
 constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
@@ -75,8 +74,13 @@ constexpr int kChunkRows1 = 8;
 void gemv_geometry(Problem &p, int fmt, int m);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
-// units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU.
-constexpr int kMfmaMinM = 4;
+// units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU. It is
+// taken from m = 3, and at m = 2 for rows of more than 64 groups (measured on MI355X, z = 0.44:
+// 4096 x 14336 at m = 2 and 3 runs 1.23x and 2.6x faster there than on the vector kernel,
+// 14336 x 4096 at m = 3 1.06x faster, at m = 2 1.2x slower).
+constexpr int kMfmaMinM = 2;
+constexpr int kMfmaAlwaysM = 3;  // from this m every BITCOS GEMV takes the matrix-core path
+constexpr int kMfmaLongRowGroups = 64;  // at m = 2, rows of more groups than this take it
 constexpr int kMfmaTiles = 2;
 constexpr int kMfmaWavesPerCu = 8;
 void mfma_geometry(Problem &p);

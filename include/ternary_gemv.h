@@ -123,9 +123,10 @@ int tg_unpack(const void *packed, size_t bytes, int8_t *w_out);
  * GPU GEMV (asynchronous). desc: host copy of the descriptor of the packed buffer whose device copy
  * is W (bytes_total bytes, the same image as the host buffer). scales: device fp16 [n][k/128] bit
  * patterns. x: device int8 [m][k]. y: device float [m][n]. 1 <= m <= TG_MAX_M.
- * Paths: m <= 3 uses the vector kernels (int8 dot products in int32, "Breaking the 1.58-bit Barrier
- * for Ternary LLMs", Sec. II-C); five-trit and 2-bit with m > 3 run them in launches of up to three
- * rows. BITCOS with m >= 4 is the thin-batch path: one launch decodes each weight once into int8
+ * Paths: the vector kernels (int8 dot products in int32, "Breaking the 1.58-bit Barrier for Ternary
+ * LLMs", Sec. II-C) take up to three activation rows per launch; five-trit and 2-bit with m > 3 run
+ * them in launches of up to three rows. BITCOS with m >= 3, or m = 2 with k > 8192, takes the
+ * thin-batch path instead: one launch decodes each weight once into int8
  * operands of int8 matrix-core products against X padded to 16 rows (a batch turns the GEMV into a
  * matrix product; the untitled page on a NUMA-aware decode engine for ternary models, Sec. 6.5 and
  * its appendix "Ternary GEMM on AMX", expands ternary weights into int8 matrix-engine tiles the same
@@ -170,7 +171,7 @@ int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, 
 
 /*
  * Grouped launch: several GEMVs of one format and one activation-row count m (1 <= m <= 3; BITCOS
- * 1 <= m <= TG_MAX_M, on the thin-batch path from m = 4) run as
+ * 1 <= m <= TG_MAX_M) run as
  * one persistent kernel. This is the batched form of the same operation (each GEMV is computed
  * exactly as ternary_gemv / ternary_gemv_acc compute it); it removes the per-launch ramp and lets
  * the memory pipeline stay full across matrices, e.g. the q/k/v or gate/up projections of a decode
@@ -178,8 +179,10 @@ int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, 
  *
  * tg_plan_table_bytes(count): bytes of device memory the table of `count` GEMVs needs.
  * tg_plan_init: checks every descriptor and pointer (the same rules as ternary_gemv; all formats
- *   equal), then writes the table into `table` (caller-owned DEVICE memory of at least
- *   tg_plan_table_bytes(count) bytes, 16-byte aligned) with a synchronous host-to-device copy, and
+ *   equal), chooses one path for the launch (BITCOS: the thin-batch kernel from m = 3, and at m = 2
+ *   when GEMVs with k > 8192 hold most of the weights; else the vector kernels), then writes the
+ *   table into `table` (caller-owned DEVICE memory of at least tg_plan_table_bytes(count) bytes,
+ *   16-byte aligned) with a synchronous host-to-device copy, and
  *   fills the host struct *plan. descs, W, scales, x, y, acc are host arrays of `count` entries;
  *   W/scales/x/y/acc entries are device pointers. Pass acc == NULL for fp32 outputs y (then y and
  *   scales are required), or acc != NULL for int32 accumulators (y and scales may be NULL).
@@ -203,6 +206,7 @@ typedef struct tg_plan {
     int32_t rows_per_unit;
     int32_t acc_mode;    /* 0: fp32 y; 1: int32 accumulator outputs; 2: fp32 y with activation group scales */
     int32_t waves;       /* waves of the launch the table's work split was made for */
+    int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS) */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 

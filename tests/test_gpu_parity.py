@@ -255,3 +255,32 @@ def test_graph_replays_match_eager(fmt):
         torch.cuda.synchronize()
         for (dw, _, _, ref), y in zip(items, ys):
             assert torch.equal(y, ref), f"{B.FMT_NAMES[fmt]} replay {rep} n={dw.n} k={dw.k}"
+
+
+# Plans of long rows only (k > 8192) at m = 2 take the thin-batch matrix-core path; mixed with shorter
+# rows that hold most of the weights they stay on the vector kernels. Both must match the oracle.
+@pytest.mark.parametrize("shapes,path", [([(33, 14336), (9, 25600), (20, 16384)], 1),
+                                          ([(33, 14336), (300, 4096)], 0)], ids=["long-rows", "mixed"])
+def test_plan_m2_path_choice(shapes, path):
+    dev = _dev()
+    m = 2
+    _say(f"[gpu] plan m=2 path={path} shapes={shapes}")
+    dws, xs, ss, ys, refs = [], [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.ternary(n, k, 0.44, seed=500 + i)
+        x = synth.activations(m, k, seed=600 + i)
+        s = synth.scales(n, k // 128, seed=700 + i)
+        acc_ref = O.gemv_acc(w, x)
+        refs.append((O.combine(acc_ref, s), acc_ref, s))
+        dws.append(B.DeviceWeights(B.pack_bitcos(w), dev))
+        xs.append(torch.from_numpy(x).to(dev))
+        ss.append(torch.from_numpy(s).to(dev))
+        ys.append(torch.full((m, n), float("nan"), dtype=torch.float32, device=dev))
+    plan = B.Plan(dws, xs, scales=ss, ys=ys)
+    assert plan.plan.path == path
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (n, k) in enumerate(shapes):
+        y_ref, acc_ref, s = refs[i]
+        ok, ndiff = y_tolerance_ok(ys[i].cpu().numpy(), y_ref, acc_ref, s)
+        assert ok and ndiff == 0, f"plan m=2 {n}x{k}: within tolerance {ok}, {ndiff} differ"
