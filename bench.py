@@ -243,7 +243,7 @@ def sustained(torch, B, dws, xs, ss, ys, launches=5):
     secs = time_launches(torch, plan.run, launches, 0)
     total = sum(packed_bytes(d) for d in dws)
     return {"gbs": round(total * launches / secs / 1e9, 1), "ms_per_launch": round(secs / launches * 1e3, 4),
-            "bytes_per_launch": total}
+            "bytes_per_launch": total, "path": "matrix-core" if plan.plan.path == 1 else "vector"}
 
 
 def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label=""):
@@ -306,7 +306,7 @@ def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
             calls = [(lambda d=dws[i % reps]: B.ternary_gemv(d, s, x, y)) for i in range(max(200, reps))]
             pc = per_call_us(torch, calls)
             pc["graph_us_per_call"] = graph_call_us(torch, calls)
-            out[f"{name}_m{m}"] = {"n": n, "k": k, "m": m, "path": "matrix-core" if m >= 4 else "vector",
+            out[f"{name}_m{m}"] = {"n": n, "k": k, "m": m, "path": st["path"],
                                    "sustained_gbs": st["gbs"], "sustained_us_per_gemv": round(st["ms_per_launch"] * 1e3 / reps, 3),
                                    "per_call": pc, "packed_bytes": packed_bytes(dws[0]), "x_bytes": m * k,
                                    "y_bytes": 4 * m * n}
