@@ -154,9 +154,10 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     static_assert(U % NB == 0 && U % 4 == 0, "static stage positions");
     // Half-steps between a step's bitmap load and its sign stage: two, so that the bitmap and the sign
     // windows each have two half-steps to arrive (measured 2 % faster than one and three on MI355X,
-    // and it frees the registers that let 16 waves share a CU at m = 1). Units of fewer than four
-    // steps keep one: the row-index entries loaded with a unit's first bitmap must survive until then.
-    constexpr int LAG = NB >= 4 ? 2 : 1;
+    // and it frees the registers that let 16 waves share a CU at m = 1). The row-index entries loaded
+    // with a unit's first bitmap are read by its first sign stage; with units of two steps they sit
+    // in two registers that alternate from unit to unit. m = 3 chunked (two-step units) keeps one.
+    constexpr int LAG = (NB >= 4 || M == 1) ? 2 : 1;
     const int lane = threadIdx.x & 63;
     Ctx x;
     x.n = p.n;
@@ -189,7 +190,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     double facc[RACC ? NB : 1];  // chunked, m = 1: the lane's running term of each row of the unit
 #pragma unroll
     for (int r = 0; r < (RACC ? NB : 1); ++r) facc[r] = 0.0;
-    uint32_t ro = 0;            // chunked: row-index entries of the unit (lane r: row r)
+    uint32_t ro[2] = {0, 0};    // chunked: row-index entries of the unit (lane r: row r), by unit parity
     int T;                      // steps in the range
     // per-lane constant parts of the offsets
     uint32_t voff_bm, voff_sc, voff_acc, voff_x;
@@ -304,7 +305,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                                  live_or_dead(live, (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u));
                     if (slot == 0) {
                         // the unit's row-index entries, for its first chunk pass
-                        ro = ld1(x.rro, lane < NB ? (uint32_t)lane * 4u : kOffOff,
+                        ro[(j / NB) & 1] = ld1(x.rro, lane < NB ? (uint32_t)lane * 4u : kOffOff,
                                  live_or_dead(live && cB == 0, (uint32_t)rB * 4u));
                     }
                     if (slot == NB - 1) {
@@ -331,7 +332,8 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                         const bool first = live && cS == 0;
 #pragma unroll
                         for (int r = 0; r < NB; ++r) {
-                            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)ro, r);
+                            const uint32_t v =
+                                (uint32_t)__builtin_amdgcn_readlane((int)ro[((j + U - LAG) % U / NB) & 1], r);
                             ccur[r] = first ? v : ccur[r];
                         }
                     }
@@ -356,7 +358,14 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
     if (p.nch == 1)
         run_loop<M, ACC, NB, false, XS>(p, u0, u1, lds, tile);
     else
-        run_loop<M, ACC, M == 1 ? kChunkRows1 : NB, true, XS>(p, u0, u1, lds, tile);
+        if constexpr (M == 1) {
+            if (p.nbu == kChunkRows1Fine)
+                run_loop<1, ACC, kChunkRows1Fine, true, XS>(p, u0, u1, lds, tile);
+            else
+                run_loop<1, ACC, kChunkRows1, true, XS>(p, u0, u1, lds, tile);
+        } else {
+            run_loop<M, ACC, NB, true, XS>(p, u0, u1, lds, tile);
+        }
 }
 
 template <int M, bool ACC, bool XS>
@@ -401,7 +410,7 @@ hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
 
 }  // namespace
 
-void gemv_geometry(Problem &p, int fmt, int m) {
+void gemv_geometry(Problem &p, int fmt, int m, bool fine) {
     const int nb = m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
     p.ng = p.k / 128;
     p.nch = (p.ng + 63) / 64;
@@ -414,7 +423,7 @@ void gemv_geometry(Problem &p, int fmt, int m) {
         p.G = 64;
         p.R = 1;
         p.glast = p.ng - 64 * (p.nch - 1);
-        p.nbu = fmt == TG_FMT_BITCOS && m == 1 ? kChunkRows1 : nb;
+        p.nbu = fmt == TG_FMT_BITCOS && m == 1 ? (fine ? kChunkRows1Fine : kChunkRows1) : nb;
     }
     p.rpu = p.nbu * p.R;
     p.gmagic = (65536u + (uint32_t)p.G - 1) / (uint32_t)p.G;

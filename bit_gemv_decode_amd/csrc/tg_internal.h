@@ -68,10 +68,13 @@ constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
 constexpr int kChunkRows1 = 8;
+// ... or of kChunkRows1Fine rows when units of kChunkRows1 are too coarse to spread a launch's work
+// evenly over its waves (small plans, single calls).
+constexpr int kChunkRows1Fine = 2;
 
 // Fill the work geometry of p (p.n, p.k set) for m activation rows on the vector path (the same for
 // every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 rows).
-void gemv_geometry(Problem &p, int fmt, int m);
+void gemv_geometry(Problem &p, int fmt, int m, bool fine = false);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
 // units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU. It is

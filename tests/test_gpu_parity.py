@@ -284,3 +284,40 @@ def test_plan_m2_path_choice(shapes, path):
         y_ref, acc_ref, s = refs[i]
         ok, ndiff = y_tolerance_ok(ys[i].cpu().numpy(), y_ref, acc_ref, s)
         assert ok and ndiff == 0, f"plan m=2 {n}x{k}: within tolerance {ok}, {ndiff} differ"
+
+
+def test_plan_coarse_chunked_units():
+    """A plan with more work units than the launch has waves keeps 8-row units for chunked rows (small
+    plans and single calls use 2-row units): one 4096x4096 matrix referenced often enough to exceed
+    the wave count, plus chunked 14336- and 25600-long rows, all against the oracle."""
+    dev = _dev()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    reps = (cus * 16) // 512 + 1  # 512 units per 4096x4096 GEMV at m = 1
+    _say(f"[gpu] coarse plan: {reps} x 4096x4096 + chunked rows")
+    big = synth.ternary(4096, 4096, 0.4, seed=800)
+    xb = synth.activations(1, 4096, seed=801)
+    sb = synth.scales(4096, 32, seed=802)
+    refs = [(O.combine(O.gemv_acc(big, xb), sb))]
+    dw_big = B.DeviceWeights(B.pack_bitcos(big), dev)
+    xbt, sbt = torch.from_numpy(xb).to(dev), torch.from_numpy(sb).to(dev)
+    dws, xs, ss = [dw_big] * reps, [xbt] * reps, [sbt] * reps
+    chunked = []
+    for i, (n, k) in enumerate([(37, 14336), (11, 25600)]):
+        w = synth.ternary(n, k, 0.45, seed=810 + i)
+        x = synth.activations(1, k, seed=820 + i)
+        s = synth.scales(n, k // 128, seed=830 + i)
+        acc_ref = O.gemv_acc(w, x)
+        chunked.append((O.combine(acc_ref, s), acc_ref, s))
+        dws.append(B.DeviceWeights(B.pack_bitcos(w), dev))
+        xs.append(torch.from_numpy(x).to(dev))
+        ss.append(torch.from_numpy(s).to(dev))
+    ys = [torch.full((1, d.n), float("nan"), dtype=torch.float32, device=dev) for d in dws]
+    plan = B.Plan(dws, xs, scales=ss, ys=ys)
+    assert plan.plan.units >= cus * 16 and plan.plan.rows_per_unit == 8
+    plan.run()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        assert np.array_equal(ys[i].cpu().numpy(), refs[0]), f"coarse plan copy {i}"
+    for (y_ref, acc_ref, s), y in zip(chunked, ys[reps:]):
+        ok, ndiff = y_tolerance_ok(y.cpu().numpy(), y_ref, acc_ref, s)
+        assert ok and ndiff == 0, f"coarse plan chunked: within tolerance {ok}, {ndiff} differ"
