@@ -314,6 +314,13 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
     constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
     __shared__ uint4 s_lut[kLutBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
+    // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
+    // those two dependent scalar round trips overlap the fill instead of following it.
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    int u, u_end, pi;
+    wave_range<WAVES>(ga, wave, u, u_end, pi);
+    const bool bad0 = ga.table && pi >= ga.count;
+    const Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
     {
         // units of 64 bytes (16 copies of a 2-bit entry, 8 of a five-trit one), one load each, all
         // loads before any LDS write: the fill is one memory round trip
@@ -343,13 +350,12 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
     }
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_lut);
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
-    int u, u_end, pi;
-    wave_range<WAVES>(ga, wave, u, u_end, pi);
+    bool first = true;
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
-        const Problem p = uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
         if (u < u1) {
             if (p.nch == 1)
