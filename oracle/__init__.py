@@ -67,6 +67,16 @@ def lib():
         L.oracle_quantize_x.restype = None
         L.oracle_combine_xs.argtypes = [p, p, p, i64, i64, i64, p]
         L.oracle_combine_xs.restype = None
+        L.oracle_t5b_blocks.argtypes = [i64]
+        L.oracle_t5b_blocks.restype = i64
+        L.oracle_t5b_pack.argtypes = [p, i64, i64, p]
+        L.oracle_t5b_pack.restype = ctypes.c_int
+        L.oracle_t5b_unpack.argtypes = [p, i64, i64, p]
+        L.oracle_t5b_unpack.restype = ctypes.c_int
+        L.oracle_gemv_acc_blocks.argtypes = [p, i64, i64, p, i64, p]
+        L.oracle_gemv_acc_blocks.restype = None
+        L.oracle_combine_tensor.argtypes = [p, ctypes.c_float, i64, i64, i64, p]
+        L.oracle_combine_tensor.restype = None
         L.oracle_gemv_packed.argtypes = [ctypes.c_int, p, p, p, p, i64, i64, p, i64, p]
         L.oracle_gemv_packed.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
@@ -142,6 +152,49 @@ def t5_unpack(codes: np.ndarray, n: int, k: int) -> np.ndarray:
     if lib().oracle_t5_unpack(_ptr(codes), n, k, _ptr(w)):
         raise ValueError("invalid five-trit code")
     return w
+
+
+def t5b_blocks(k: int) -> int:
+    return int(lib().oracle_t5b_blocks(k))
+
+
+def t5b_pack(w: np.ndarray) -> np.ndarray:
+    """uint8 [n, blocks, 32]: five-trit bytes in blocks of 160 weights (padding digits weight 0)."""
+    w = _c(w, np.int8)
+    n, k = w.shape
+    out = np.zeros((n, t5b_blocks(k), 32), np.uint8)
+    if lib().oracle_t5b_pack(_ptr(w), n, k, _ptr(out)):
+        raise ValueError("t5b pack rejected the input")
+    return out
+
+
+def t5b_unpack(codes: np.ndarray, n: int, k: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    assert codes.size == n * t5b_blocks(k) * 32
+    w = np.empty((n, k), np.int8)
+    if lib().oracle_t5b_unpack(_ptr(codes), n, k, _ptr(w)):
+        raise ValueError("invalid t5b code")
+    return w
+
+
+def gemv_acc_blocks(w: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """int32 [m, n, blocks]: exact sums of W*x over each 160-weight block of each row."""
+    w = _c(w, np.int8)
+    x = _c(np.atleast_2d(x), np.int8)
+    n, k = w.shape
+    m = x.shape[0]
+    acc = np.empty((m, n, t5b_blocks(k)), np.int32)
+    lib().oracle_gemv_acc_blocks(_ptr(w), n, k, _ptr(x), m, _ptr(acc))
+    return acc
+
+
+def combine_tensor(acc: np.ndarray, scale: float) -> np.ndarray:
+    """float32 [m, n]: the per-tensor scale times the exact row sum, rounded once."""
+    acc = _c(acc, np.int32)
+    m, n, nb = acc.shape
+    y = np.empty((m, n), np.float32)
+    lib().oracle_combine_tensor(_ptr(acc), float(np.float32(scale)), n, nb, m, _ptr(y))
+    return y
 
 
 def b2_pack(w: np.ndarray) -> np.ndarray:

@@ -18,6 +18,8 @@
  *     Arithmetic Decoding", abstract): five ternary digits per byte, 3^5 = 243 <= 256, and a block
  *     of 128 weights takes ceil(128/5) = 26 bytes.
  *   - 2-bit packing (Table I, "2-bit packing" column): two bits per weight.
+ *   - t5b ("Sub-Two-Bit Ternary Weight Storage ...", abstract): the five-trit construction in blocks
+ *     of 160 weights (32 bytes, 1.600 bits per weight) with one scale per tensor.
  *   - the GEMV contract (Sec. II-C, discussion after Fig. 5): int8 activations, dot products
  *     accumulated in int32 per group of 128 reduction elements, the group's 16-bit scale applied
  *     once per group. The oracle computes the dense definition: acc = sum of W*x over the group,
@@ -193,6 +195,79 @@ int oracle_t5_unpack(const uint8_t *in, int64_t n, int64_t k, int8_t *w) {
         }
     }
     return 0;
+}
+
+/* ---------- t5b: five-trit bytes in blocks of 160 weights, one scale per tensor ---------- */
+
+/*
+ * "Sub-Two-Bit Ternary Weight Storage with Table-Free Arithmetic Decoding" (abstract): the same
+ * base-3 construction at a block length of 160 (32 bytes, 1.600 bits per weight), the scale carried
+ * once per tensor. Readings: blocks run along each row, block b of row r holding weights
+ * 160b .. 160b + 159; byte j of a block holds weights 160b + 5j .. 160b + 5j + 4 as digits weight + 1,
+ * the first weight least significant; positions at or past k are padding digits of value 1
+ * (weight 0).
+ */
+int64_t oracle_t5b_blocks(int64_t k) { return (k + 159) / 160; }
+
+int oracle_t5b_pack(const int8_t *w, int64_t n, int64_t k, uint8_t *out) {
+    if (k < 1 || oracle_count_nonzero(w, n * k) < 0) return -1;
+    int64_t nb = oracle_t5b_blocks(k);
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nb; b++)
+            for (int j = 0; j < 32; j++) {
+                int value = 0, place = 1;
+                for (int i = 0; i < 5; i++) {
+                    int64_t col = 160 * b + 5 * j + i;
+                    int digit = col < k ? w[r * k + col] + 1 : 1;
+                    value += digit * place;
+                    place *= 3;
+                }
+                out[(r * nb + b) * 32 + j] = (uint8_t)value;
+            }
+    return 0;
+}
+
+/* Returns 0, or -1 if a byte is >= 243 or a padding digit is not the weight-0 digit. */
+int oracle_t5b_unpack(const uint8_t *in, int64_t n, int64_t k, int8_t *w) {
+    int64_t nb = oracle_t5b_blocks(k);
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nb; b++)
+            for (int j = 0; j < 32; j++) {
+                int value = in[(r * nb + b) * 32 + j];
+                if (value >= 243) return -1;
+                for (int i = 0; i < 5; i++) {
+                    int digit = value % 3;
+                    value /= 3;
+                    int64_t col = 160 * b + 5 * j + i;
+                    if (col < k) w[r * k + col] = (int8_t)(digit - 1);
+                    else if (digit != 1) return -1;
+                }
+            }
+    return 0;
+}
+
+/* acc[mi][r][b] = sum over the k of block b (160 b <= k < min(160 b + 160, k)) of W[r][k] * x[mi][k]. */
+void oracle_gemv_acc_blocks(const int8_t *w, int64_t n, int64_t k, const int8_t *x, int64_t m, int32_t *acc) {
+    int64_t nb = oracle_t5b_blocks(k);
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t r = 0; r < n; r++)
+            for (int64_t b = 0; b < nb; b++) {
+                int32_t s = 0;
+                for (int64_t c = 160 * b; c < 160 * (b + 1) && c < k; c++)
+                    s += (int32_t)w[r * k + c] * (int32_t)x[mi * k + c];
+                acc[(mi * n + r) * nb + b] = s;
+            }
+}
+
+/* y[mi][r] = (float)((double) scale * (double) sum_b acc[mi][r][b]): the per-tensor scale applied to
+ * the exact integer row sum, rounded once. */
+void oracle_combine_tensor(const int32_t *acc, float scale, int64_t n, int64_t nb, int64_t m, float *y) {
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t r = 0; r < n; r++) {
+            int64_t s = 0;
+            for (int64_t b = 0; b < nb; b++) s += acc[(mi * n + r) * nb + b];
+            y[mi * n + r] = (float)((double)scale * (double)s);
+        }
 }
 
 /* ---------- 2-bit codes ---------- */
