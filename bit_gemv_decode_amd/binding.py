@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(PKG, "libternary_gemv.so")
 TG_GROUP = 128
 TG_MAX_M = 16
 TG_HEADER_BYTES = 256
-FMT_BITCOS, FMT_5TRIT, FMT_2BIT = 1, 2, 3
-FMT_NAMES = {FMT_BITCOS: "bitcos", FMT_5TRIT: "5trit", FMT_2BIT: "2bit"}
+FMT_BITCOS, FMT_5TRIT, FMT_2BIT, FMT_T5B = 1, 2, 3, 4
+FMT_NAMES = {FMT_BITCOS: "bitcos", FMT_5TRIT: "5trit", FMT_2BIT: "2bit", FMT_T5B: "t5b"}
+T5B_BLOCK = 160
 ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4: "TG_EFORMAT",
           -5: "TG_ECORRUPT", -6: "TG_ENOSPACE", -7: "TG_EHIP"}
 
 # Every symbol include/ternary_gemv.h declares.
-EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_describe", "tg_validate", "tg_unpack",
+EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_pack_t5b", "tg_describe", "tg_validate", "tg_unpack",
            "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "tg_plan_table_bytes",
            "tg_plan_init", "tg_plan_init_xs", "ternary_gemv_plan", "tg_stream_read", "tg_strerror", "tg_version"]
 
@@ -41,7 +42,7 @@ class TgDesc(ctypes.Structure):
                 ("off_signs", ctypes.c_uint64), ("bytes_signs", ctypes.c_uint64),
                 ("off_index", ctypes.c_uint64), ("bytes_index", ctypes.c_uint64),
                 ("bytes_total", ctypes.c_uint64), ("bytes_payload", ctypes.c_uint64),
-                ("reserved", ctypes.c_uint64 * 2)]
+                ("tensor_scale", ctypes.c_uint32), ("reserved32", ctypes.c_uint32), ("reserved", ctypes.c_uint64)]
 
 
 class TgPlan(ctypes.Structure):
@@ -66,6 +67,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [p, i64, i64, p, sz, ctypes.POINTER(sz)]
             f.restype = ctypes.c_int
+        L.tg_pack_t5b.argtypes = [p, i64, i64, ctypes.c_float, p, sz, ctypes.POINTER(sz)]
+        L.tg_pack_t5b.restype = ctypes.c_int
         L.tg_describe.argtypes = [p, sz, ctypes.POINTER(TgDesc)]
         L.tg_describe.restype = ctypes.c_int
         L.tg_validate.argtypes = [p, sz]
@@ -138,17 +141,17 @@ class Packed:
         return self.section("index").view(np.uint32)
 
 
-def _pack(fn_name: str, w: np.ndarray) -> Packed:
+def _pack(fn_name: str, w: np.ndarray, *extra) -> Packed:
     w = np.ascontiguousarray(w, dtype=np.int8)
     if w.ndim != 2:
         raise ValueError("weights must be a 2-D [n, k] int8 array")
     n, k = w.shape
     fn = getattr(lib(), fn_name)
     need = ctypes.c_size_t(0)
-    _check(fn(_host_ptr(w), n, k, None, 0, ctypes.byref(need)), fn_name)
+    _check(fn(_host_ptr(w), n, k, *extra, None, 0, ctypes.byref(need)), fn_name)
     buf = np.empty(need.value, dtype=np.uint8)
     got = ctypes.c_size_t(0)
-    _check(fn(_host_ptr(w), n, k, _host_ptr(buf), buf.size, ctypes.byref(got)), fn_name)
+    _check(fn(_host_ptr(w), n, k, *extra, _host_ptr(buf), buf.size, ctypes.byref(got)), fn_name)
     return Packed(buf)
 
 
@@ -164,11 +167,21 @@ def pack_2bit(w: np.ndarray) -> Packed:
     return _pack("tg_pack_2bit", w)
 
 
-PACKERS = {FMT_BITCOS: pack_bitcos, FMT_5TRIT: pack_5trit, FMT_2BIT: pack_2bit}
+def pack_t5b(w: np.ndarray, scale: float = 1.0) -> Packed:
+    """t5b: five-trit bytes in 160-weight blocks, with the per-tensor scale in the descriptor."""
+    return _pack("tg_pack_t5b", w, ctypes.c_float(scale))
 
 
-def pack(fmt: int, w: np.ndarray) -> Packed:
-    return PACKERS[fmt](w)
+PACKERS = {FMT_BITCOS: pack_bitcos, FMT_5TRIT: pack_5trit, FMT_2BIT: pack_2bit, FMT_T5B: pack_t5b}
+
+
+def pack(fmt: int, w: np.ndarray, **kw) -> Packed:
+    return PACKERS[fmt](w, **kw)
+
+
+def groups_per_row(fmt: int, k: int) -> int:
+    """Per-row count of the GEMV's group sums: 128-weight groups, or t5b's 160-weight blocks."""
+    return -(-k // T5B_BLOCK) if fmt == FMT_T5B else k // TG_GROUP
 
 
 def describe(buf: np.ndarray) -> TgDesc:
@@ -234,30 +247,39 @@ def _require_cuda(t, dtype, name):
 
 
 def ternary_gemv(w: DeviceWeights, scales, x, y=None, stream=None):
-    """y[m, n] = sum_g scales[n, g] * acc[m, n, g] (see include/ternary_gemv.h). Asynchronous."""
+    """y[m, n] = sum_g scales[n, g] * acc[m, n, g] (see include/ternary_gemv.h); for t5b weights
+    scales is None and y = tensor scale * W x. Asynchronous."""
     import torch
 
     _require_cuda(w.tensor, torch.uint8, "weights")
-    _require_cuda(scales, torch.float16, "scales")
     _require_cuda(x, torch.int8, "x")
     if x.dim() == 1:
         x = x.view(1, -1)
     m = x.shape[0]
-    if x.shape[1] != w.k or tuple(scales.shape) != (w.n, w.k // TG_GROUP):
-        raise ValueError("shape mismatch between weights, scales and x")
+    if w.fmt == FMT_T5B:
+        if scales is not None:
+            raise ValueError("t5b weights carry their scale; pass scales=None")
+    else:
+        _require_cuda(scales, torch.float16, "scales")
+        if tuple(scales.shape) != (w.n, w.k // TG_GROUP):
+            raise ValueError("shape mismatch between weights and scales")
+    if x.shape[1] != w.k:
+        raise ValueError("shape mismatch between weights and x")
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
     _require_cuda(y, torch.float32, "y")
     if tuple(y.shape) != (m, w.n):
         raise ValueError("y has the wrong shape")
     _check(lib().ternary_gemv(ctypes.byref(w.desc), ctypes.c_void_p(w.tensor.data_ptr()),
-                              ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(x.data_ptr()),
+                              ctypes.c_void_p(scales.data_ptr() if scales is not None else None),
+                              ctypes.c_void_p(x.data_ptr()),
                               ctypes.c_void_p(y.data_ptr()), m, _stream_handle(stream)), "ternary_gemv")
     return y
 
 
 def ternary_gemv_acc(w: DeviceWeights, x, acc=None, stream=None):
-    """int32 per-group accumulators acc[m, n, k/128] (bit-exact entry point). Asynchronous."""
+    """int32 per-group accumulators acc[m, n, groups] (bit-exact entry point; groups = k/128, or
+    ceil(k/160) blocks for t5b). Asynchronous."""
     import torch
 
     _require_cuda(w.tensor, torch.uint8, "weights")
@@ -268,7 +290,7 @@ def ternary_gemv_acc(w: DeviceWeights, x, acc=None, stream=None):
     if x.shape[1] != w.k:
         raise ValueError("x has the wrong length")
     if acc is None:
-        acc = torch.empty((m, w.n, w.k // TG_GROUP), dtype=torch.int32, device=x.device)
+        acc = torch.empty((m, w.n, groups_per_row(w.fmt, w.k)), dtype=torch.int32, device=x.device)
     _require_cuda(acc, torch.int32, "acc")
     _check(lib().ternary_gemv_acc(ctypes.byref(w.desc), ctypes.c_void_p(w.tensor.data_ptr()),
                                   ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(acc.data_ptr()), m,
@@ -347,8 +369,11 @@ class Plan:
         if acc_mode:
             if len(accs) != count or x_scales is not None:
                 raise ValueError("one acc per weight matrix is required (and no x_scales)")
-        elif scales is None or ys is None or len(scales) != count or len(ys) != count:
-            raise ValueError("scales and ys (one per matrix) are required for fp32 outputs")
+        elif ys is None or len(ys) != count:
+            raise ValueError("ys (one per matrix) are required for fp32 outputs")
+        t5b = weights[0].fmt == FMT_T5B
+        if not acc_mode and (t5b != (scales is None) or (scales is not None and len(scales) != count)):
+            raise ValueError("scales (one per matrix) are required for fp32 outputs, and must be None for t5b")
         if x_scales is not None and len(x_scales) != count:
             raise ValueError("one x_scales per weight matrix is required")
         m = xs[0].shape[0] if xs[0].dim() == 2 else 1
@@ -359,13 +384,16 @@ class Plan:
                 raise ValueError("every x must be [m, k] with the same m")
             if acc_mode:
                 _require_cuda(accs[i], torch.int32, "acc")
-                if tuple(accs[i].shape) != (m, w.n, w.k // TG_GROUP):
+                if tuple(accs[i].shape) != (m, w.n, groups_per_row(w.fmt, w.k)):
                     raise ValueError("acc has the wrong shape")
             else:
-                _require_cuda(scales[i], torch.float16, "scales")
                 _require_cuda(ys[i], torch.float32, "y")
-                if tuple(scales[i].shape) != (w.n, w.k // TG_GROUP) or tuple(ys[i].shape) != (m, w.n):
-                    raise ValueError("scales or y has the wrong shape")
+                if tuple(ys[i].shape) != (m, w.n):
+                    raise ValueError("y has the wrong shape")
+                if scales is not None:
+                    _require_cuda(scales[i], torch.float16, "scales")
+                    if tuple(scales[i].shape) != (w.n, w.k // TG_GROUP):
+                        raise ValueError("scales has the wrong shape")
                 if x_scales is not None:
                     _require_cuda(x_scales[i], torch.float32, "x_scales")
                     if tuple(x_scales[i].reshape(m, -1).shape) != (m, w.k // TG_GROUP):

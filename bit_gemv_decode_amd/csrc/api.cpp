@@ -39,6 +39,7 @@ Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, co
     p.xs = xs;
     p.n = (int32_t)d->n;
     p.k = (int32_t)d->k;
+    if (d->fmt == TG_FMT_T5B) memcpy(&p.tscale, &d->tensor_scale, 4);
     return p;
 }
 
@@ -55,7 +56,7 @@ constexpr int kVectorMaxM = 3;  // activation rows one vector-path launch handle
 // (positions counted in bits) below 512 MiB.
 bool fits_offsets(const tg_desc *d, int32_t m) {
     const uint64_t lim = 1ull << 30;
-    const uint64_t ng = (uint64_t)(d->k / TG_GROUP);
+    const uint64_t ng = (uint64_t)groups_per_row(d->fmt, d->k);
     return d->bytes_codes < lim && d->bytes_signs < (lim >> 1) && (uint64_t)d->n * ng * 4 * (uint64_t)m < lim &&
            (uint64_t)d->n * 4 * (uint64_t)m < lim &&
            (uint64_t)m * (uint64_t)d->k <= lim;
@@ -100,6 +101,7 @@ hipError_t launch(int fmt, const GroupArgs &g, int out, bool mfma, hipStream_t s
         case TG_FMT_BITCOS: return launch_bitcos(g, out, s);
         case TG_FMT_5TRIT: return launch_t5(g, out, s);
         case TG_FMT_2BIT: return launch_b2(g, out, s);
+        case TG_FMT_T5B: return launch_t5b(g, out, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -108,7 +110,11 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
                 float *y, int32_t *acc, int32_t m, void *stream, int out) {
     const bool acc_out = out == kOutAcc;
     if (!desc || !W || !x || m < 1 || m > TG_MAX_M) return TG_EINVAL;
-    if (acc_out ? !acc : (!y || !scales)) return TG_EINVAL;
+    // t5b carries its scale in the descriptor: no per-group scales, and no activation group scales
+    // (its 160-weight blocks do not follow the activations' 128-groups)
+    const bool t5b = desc->fmt == TG_FMT_T5B;
+    if (t5b && (scales || out == kOutYxs)) return TG_EINVAL;
+    if (acc_out ? !acc : (!y || (!t5b && !scales))) return TG_EINVAL;
     if (out == kOutYxs && (!xs || ((uintptr_t)xs & 3))) return TG_EINVAL;
     // 16-byte vector loads of W sections and x rows; 4-byte stores of y / acc; 2-byte scales.
     if (((uintptr_t)W & 15) || ((uintptr_t)x & 15)) return TG_EINVAL;
@@ -117,7 +123,7 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
     if (e) return e;
     if (!fits_offsets(desc, m)) return TG_ESHAPE;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t n = desc->n, k = desc->k, ng = k / TG_GROUP;
+    const int64_t n = desc->n, k = desc->k, ng = groups_per_row(desc->fmt, k);
     // Activation rows go in launches of at most three on the vector path (each launch reads the
     // weights once); the matrix-core path takes all of them in one launch.
     const bool mfma = use_mfma(desc->fmt, m, desc->k);
@@ -208,9 +214,11 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
                      const float *const *xs, float *const *y, int32_t *const *acc, int32_t m) {
     if (!plan || !table || !descs || !W || !x || count < 1 || m < 1) return TG_EINVAL;
     const bool acc_mode = acc != nullptr;
-    if (acc_mode ? xs != nullptr : (!y || !scales)) return TG_EINVAL;
-    if (((uintptr_t)table & 15) || table_bytes < tg_plan_table_bytes(count)) return TG_EINVAL;
     const int fmt = descs[0].fmt;
+    const bool t5b = fmt == TG_FMT_T5B;  // scale in the descriptor; no activation group scales
+    if (t5b && (scales || xs)) return TG_EINVAL;
+    if (acc_mode ? xs != nullptr : (!y || (!t5b && !scales))) return TG_EINVAL;
+    if (((uintptr_t)table & 15) || table_bytes < tg_plan_table_bytes(count)) return TG_EINVAL;
     if (m > plan_max_m(fmt)) return TG_EINVAL;
     std::vector<Problem> host((size_t)count);
     int rpu = 1;  // largest rows per unit (informational)
@@ -222,13 +230,13 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         if (!fits_offsets(d, m)) return TG_ESHAPE;
         if (!W[i] || !x[i] || ((uintptr_t)W[i] & 15) || ((uintptr_t)x[i] & 15)) return TG_EINVAL;
         if (acc_mode ? (!acc[i] || ((uintptr_t)acc[i] & 3))
-                     : (!y[i] || !scales[i] || ((uintptr_t)y[i] & 3) || ((uintptr_t)scales[i] & 1)))
+                     : (!y[i] || ((uintptr_t)y[i] & 3) || (!t5b && (!scales[i] || ((uintptr_t)scales[i] & 1)))))
             return TG_EINVAL;
         if (xs && (!xs[i] || ((uintptr_t)xs[i] & 3))) return TG_EINVAL;
     }
     for (int32_t i = 0; i < count; ++i) {
         const tg_desc *d = &descs[i];
-        host[i] = make_problem(d, W[i], acc_mode ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
+        host[i] = make_problem(d, W[i], acc_mode || t5b ? nullptr : scales[i], x[i], acc_mode ? nullptr : y[i],
                                acc_mode ? acc[i] : nullptr, xs ? xs[i] : nullptr);
     }
     // One launch takes one path: the matrix-core kernel when every GEMV would take it on its own, or

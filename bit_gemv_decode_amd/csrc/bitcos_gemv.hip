@@ -244,7 +244,8 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && (lane < x.R * x.G) &&
                                     row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
-                    emit<M, ACC, NB, XS>(x, acc, g[jb].scale, xsv, tile, slot, false, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB, XS>(x, acc, (double)half_bits_to_float(g[jb].scale), xsv, tile, slot, false,
+                                         va ? voff_acc : kOffOff,
                                      live_or_dead(live, (uint32_t)row0 * (uint32_t)x.ng * 4u));
                     if constexpr (!ACC) {
                         if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
@@ -258,7 +259,8 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                         if constexpr (XS) term *= (double)xsv[0];
                         facc[slot] = cD != 0 ? facc[slot] + term : term;
                     } else {
-                        emit<M, ACC, NB, XS>(x, acc, g[jb].scale, xsv, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                        emit<M, ACC, NB, XS>(x, acc, (double)half_bits_to_float(g[jb].scale), xsv, tile, slot,
+                                             cD != 0, va ? voff_acc : kOffOff,
                                          live_or_dead(live, ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u));
                     }
                     if (slot == NB - 1) {  // static: last step of a chunk pass
@@ -415,7 +417,7 @@ hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
 
 void gemv_geometry(Problem &p, int fmt, int m, bool fine) {
     const int nb = m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
-    p.ng = p.k / 128;
+    p.ng = (int32_t)groups_per_row(fmt, p.k);
     p.nch = (p.ng + 63) / 64;
     if (p.nch == 1) {
         p.G = p.ng;

@@ -148,7 +148,7 @@ __device__ __forceinline__ Problem uniform_problem(const Problem &q) {
     p.rpu = uniform_i32(q.rpu);
     p.gmagic = uniform_u32(q.gmagic);
     p.rmagic = uniform_u32(q.rmagic);
-    p.reserved = 0;
+    p.tscale = __builtin_bit_cast(float, uniform_u32(__builtin_bit_cast(uint32_t, q.tscale)));
     return p;
 }
 

@@ -4,7 +4,10 @@
 //                Ternary LLMs", Sec. I; "Sub-Two-Bit Ternary Weight Storage with Table-Free Arithmetic
 //                Decoding", abstract);
 //   2-bit     -- four weights per byte, code = weight + 1 in two bits, first weight lowest (the
-//                "2-bit packing" of Table I in the first paper).
+//                "2-bit packing" of Table I in the first paper);
+//   t5b       -- the five-trit code in aligned 32-byte blocks of 160 weights with one scale per tensor
+//                (the second paper's t5b): a lane owns one block, its 160 activation bytes and its
+//                block sum; the epilogue applies the tensor scale instead of a group scale.
 //
 // Same persistent work geometry and unit-end reduction as the BITCOS kernel (gemv_pipeline.h): a lane
 // owns one group per step. A group's code bytes sit at a fixed place, so there is no dependent load:
@@ -66,12 +69,20 @@ struct Fmt;
 template <>
 struct Fmt<TG_FMT_2BIT> {
     static constexpr uint32_t kGroupBytes = 32;
-    static constexpr int kXWords = 32;  // activation words per lane and row of x
+    static constexpr int kXWords = 32;      // activation words per lane and row of x
+    static constexpr uint32_t kXBytes = 128;  // activation bytes of one group
 };
 template <>
 struct Fmt<TG_FMT_5TRIT> {
     static constexpr uint32_t kGroupBytes = 26;
     static constexpr int kXWords = 33;  // xa[0..25], xb[0..6]
+    static constexpr uint32_t kXBytes = 128;
+};
+template <>
+struct Fmt<TG_FMT_T5B> {
+    static constexpr uint32_t kGroupBytes = 32;  // a 160-weight block
+    static constexpr int kXWords = 40;           // xa[0..31], xb[0..7]
+    static constexpr uint32_t kXBytes = 160;
 };
 
 // One step's codes: eight words from the dword-aligned address at or below the group start, the
@@ -86,6 +97,37 @@ struct CodeBuf {
 // five-trit (see the file comment).
 template <int FMT, int M>
 __device__ __forceinline__ void load_xf(const Ctx &x, uint32_t voff, uint32_t (&xf)[M][Fmt<FMT>::kXWords]) {
+    if constexpr (FMT == TG_FMT_T5B) {
+        // the block's 160 activation bytes (ten 16-byte loads; past k they meet padding weights of
+        // zero, so whatever they read adds nothing), then the five-trit permutation over 32 bytes
+        uint32_t xr[M][40];
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi)
+#pragma unroll
+            for (int j = 0; j < 10; ++j) {
+                const u32x4 v = ld4(x.rx, voff + 16u * j, (uint32_t)(mi * x.k));
+                xr[mi][4 * j] = v.x;
+                xr[mi][4 * j + 1] = v.y;
+                xr[mi][4 * j + 2] = v.z;
+                xr[mi][4 * j + 3] = v.w;
+            }
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) {
+            auto xw = [&](int w) -> uint32_t { return w < 40 ? xr[mi][w] : 0u; };
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int w = (5 * j) >> 2, o = (5 * j) & 3;
+                xf[mi][j] = o == 0 ? xw(w) : __builtin_amdgcn_alignbit(xw(w + 1), xw(w), 8 * o);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t lo = __builtin_amdgcn_perm(xw(5 * q + 2), xw(5 * q + 1), 0x0C0C0500u);
+                const uint32_t hi = __builtin_amdgcn_perm(xw(5 * q + 4), xw(5 * q + 3), 0x0C0C0702u);
+                xf[mi][32 + q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+        }
+        return;
+    }
     uint32_t xr[M][32];
     load_x<M>(x, voff, xr);
     if constexpr (FMT == TG_FMT_2BIT) {
@@ -141,16 +183,21 @@ __device__ __forceinline__ void decode_fixed(const CodeBuf &b, const uint32_t (&
                 for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(e, xf[mi][4 * d + i], acc[mi]);
             }
     } else {
-        // realign: the group's 26 bytes start at bit sh (0 or 16) of w[0]
+        // five-trit: realign (the group's 26 bytes start at bit sh, 0 or 16, of w[0]); t5b blocks of
+        // 32 bytes are aligned
+        constexpr int kBytes = FMT == TG_FMT_T5B ? 32 : 26;
+        constexpr int kRuns = (kBytes + 3) / 4;
+        if constexpr (FMT == TG_FMT_5TRIT) {
 #pragma unroll
-        for (int d = 0; d < 7; ++d) w[d] = __builtin_amdgcn_alignbit(w[d + 1], w[d], b.sh);
+            for (int d = 0; d < 7; ++d) w[d] = __builtin_amdgcn_alignbit(w[d + 1], w[d], b.sh);
+        }
 #pragma unroll
-        for (int q = 0; q < 7; ++q) {
+        for (int q = 0; q < kRuns; ++q) {
             uint32_t hi4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 4 * q + i;  // code byte
-                if (j < 26) {
+                if (j < kBytes) {
                     const uint32_t a = __builtin_amdgcn_perm(w[q], laneoff, 0x0C0C0000u | ((4u + i) << 8));
                     const uint2 e = *reinterpret_cast<const uint2 *>(lds + a);
 #pragma unroll
@@ -164,7 +211,7 @@ __device__ __forceinline__ void decode_fixed(const CodeBuf &b, const uint32_t (&
             const uint32_t hi = __builtin_amdgcn_perm(hi4[3], hi4[2], 0x0C0C0400u);
             const uint32_t w4 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 #pragma unroll
-            for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(w4, xf[mi][26 + q], acc[mi]);
+            for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(w4, xf[mi][kBytes + q], acc[mi]);
         }
     }
 }
@@ -178,6 +225,11 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     constexpr uint32_t GB = Fmt<FMT>::kGroupBytes;
     constexpr int XW = Fmt<FMT>::kXWords;
     const int lane = threadIdx.x & 63;
+    // weight scale of a group: its fp16 scale, or the tensor scale of t5b
+    const double tscale = (double)p.tscale;
+    auto gscale = [&](const CodeBuf &b) -> double {
+        return FMT == TG_FMT_T5B ? tscale : (double)half_bits_to_float(b.scale);
+    };
     Ctx x;
     x.n = p.n;
     x.k = p.k;
@@ -189,7 +241,8 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     // a five-trit group's last load reaches up to 6 bytes past its 26; the packed buffer keeps at least
     // 16 zero bytes after the codes section, so the resource covers them
     x.rbm = make_rsrc(p.codes, p.codes_bytes + 16u);
-    x.rsc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)p.ng * 2u);
+    // t5b has no per-group scales: its tensor scale comes with the GEMV
+    x.rsc = make_rsrc(p.scales, ACC || FMT == TG_FMT_T5B ? 0u : (uint32_t)p.n * (uint32_t)p.ng * 2u);
     x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
     x.ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)M * (uint32_t)p.n * 4u);
     x.racc = make_rsrc(p.acc, ACC ? (uint32_t)M * (uint32_t)p.n * (uint32_t)p.ng * 4u : 0u);
@@ -213,7 +266,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
         lane_grp = (uint32_t)lane;  // ql * ng + jl with ng = G
         voff_sc = act ? (uint32_t)lane * 2u : kOffOff;
         voff_acc = act ? (uint32_t)lane * 4u : kOffOff;
-        voff_x = act ? (uint32_t)jl * 128u : kOffOff;
+        voff_x = act ? (uint32_t)jl * Fmt<FMT>::kXBytes : kOffOff;
         T = (u1 - u0) * NB;
         red = make_red(NB * x.R, x.R, x.G, p.rmagic);
     } else {
@@ -221,7 +274,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
         lane_grp = (uint32_t)lane;
         voff_sc = (uint32_t)lane * 2u;
         voff_acc = (uint32_t)lane * 4u;
-        voff_x = (uint32_t)lane * 128u;
+        voff_x = (uint32_t)lane * Fmt<FMT>::kXBytes;
         T = (u1 - u0) * NB * x.nch;
         red = make_red(NB, 1, 64, p.rmagic);
     }
@@ -248,7 +301,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && act && row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
-                    emit<M, ACC, NB, XS>(x, acc, b.scale, xsv, tile, slot, false, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB, XS>(x, acc, gscale(b), xsv, tile, slot, false, va ? voff_acc : kOffOff,
                                      live_or_dead(live, (uint32_t)row0 * ng * 4u));
                     if constexpr (!ACC) {
                         if (slot == NB - 1) reduce_store<M, NB>(x, red, tile, row0 - (NB - 1) * x.R, row_end, live);
@@ -257,7 +310,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                     const int row = rD + slot;
                     const int gc = cD == x.nch - 1 ? x.glast : 64;
                     const bool va = live && lane < gc && row < row_end;
-                    emit<M, ACC, NB, XS>(x, acc, b.scale, xsv, tile, slot, cD != 0, va ? voff_acc : kOffOff,
+                    emit<M, ACC, NB, XS>(x, acc, gscale(b), xsv, tile, slot, cD != 0, va ? voff_acc : kOffOff,
                                      live_or_dead(live, ((uint32_t)row * ng + (uint32_t)cD * 64u) * 4u));
                     if (slot == NB - 1) {  // static: last step of a chunk pass
                         if constexpr (!ACC) reduce_store<M, NB>(x, red, tile, rD, row_end, live && cD == x.nch - 1);
@@ -266,7 +319,8 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                         cD = live ? (wrap ? 0 : cD + 1) : cD;
                         TG_SCHED_FENCE();
                         const int gcn = cD == x.nch - 1 ? x.glast : 64;
-                        const uint32_t vx = lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff;
+                        const uint32_t vx =
+                            lane < gcn ? voff_x + (uint32_t)cD * (64u * Fmt<FMT>::kXBytes) : kOffOff;
                         load_xf<FMT, M>(x, vx, xf);
                         load_xs<M, XS>(x, vx, xsv);
                     }
@@ -301,7 +355,8 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                 cb[j].c[0] = ld4(x.rbm, a4, 0u);
                 cb[j].c[1] = ld4(x.rbm, a4 + 16u, 0u);
                 cb[j].sh = (off & 3u) << 3;
-                cb[j].scale = ACC ? (uint16_t)0 : ldh(x.rsc, la ? voff_sc : kOffOff, live_or_dead(live, soff_sc));
+                cb[j].scale = ACC || FMT == TG_FMT_T5B ? (uint16_t)0
+                                                       : ldh(x.rsc, la ? voff_sc : kOffOff, live_or_dead(live, soff_sc));
             }
             TG_SCHED_FENCE();
         }
@@ -375,8 +430,12 @@ hipError_t launch_fixed_m(const GroupArgs &g, int out, hipStream_t s) {
     if (blocks < 1) return hipErrorInvalidValue;
     if (out == kOutAcc)
         hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, true, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
-    else if (out == kOutYxs)
-        hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    else if (out == kOutYxs) {
+        if constexpr (FMT == TG_FMT_T5B)
+            return hipErrorInvalidValue;  // t5b has no activation group scales
+        else
+            hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    }
     else
         hipLaunchKernelGGL((fixed_gemv_kernel<FMT, M, false, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     return hipGetLastError();
@@ -400,6 +459,11 @@ hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s) {
 
 hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s) {
     return launch_fixed<TG_FMT_2BIT>(g, out, s);
+}
+
+hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s) {
+    if (out == kOutYxs) return hipErrorInvalidValue;  // no activation group scales for t5b
+    return launch_fixed<TG_FMT_T5B>(g, out, s);
 }
 
 }  // namespace tg

@@ -156,11 +156,11 @@ __device__ __forceinline__ void reduce_store(const Ctx &x, const Red &r, const d
             (uint32_t)(mi * x.n) * 4u);
 }
 
-// Decode stage epilogue: the group terms (int32 sum times scale, times the activation group scale
-// when XS; fp64, every product exact) go to tile slot `slot` (added to what earlier chunks left there
+// Decode stage epilogue: the group terms (int32 sum times the group's weight scale s, times the
+// activation group scale when XS; fp64, every product exact) go to tile slot `slot` (added to what earlier chunks left there
 // when `add`); accumulator outputs are stored directly.
 template <int M, bool ACC, int NB, bool XS>
-__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t scale, const float (&xsv)[M],
+__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], double s, const float (&xsv)[M],
                                      double *tile, int slot, bool add, uint32_t voff_acc, uint32_t soff_acc) {
     const int lane = threadIdx.x & 63;
     if constexpr (ACC) {
@@ -168,7 +168,6 @@ __device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], uint16_t
         for (int mi = 0; mi < M; ++mi)
             st1((uint32_t)acc[mi], x.racc, voff_acc, soff_acc + (uint32_t)(mi * x.n * x.ng) * 4u);
     } else {
-        const double s = (double)half_bits_to_float(scale);
 #pragma unroll
         for (int mi = 0; mi < M; ++mi) {
             double *t = tile + mi * NB * 64 + slot * 64 + lane;

@@ -124,8 +124,10 @@ uint64_t count_nonzero(const int8_t *w, int64_t n, int64_t k, std::vector<uint32
 
 int check_desc(const tg_desc *d, uint64_t limit) {
     if (!d) return TG_EINVAL;
-    if (d->magic != TG_MAGIC || d->version != TG_VERSION || d->group != TG_GROUP) return TG_EFORMAT;
-    if (d->fmt != TG_FMT_BITCOS && d->fmt != TG_FMT_5TRIT && d->fmt != TG_FMT_2BIT) return TG_EFORMAT;
+    if (d->magic != TG_MAGIC || d->version != TG_VERSION) return TG_EFORMAT;
+    if (d->fmt != TG_FMT_BITCOS && d->fmt != TG_FMT_5TRIT && d->fmt != TG_FMT_2BIT && d->fmt != TG_FMT_T5B)
+        return TG_EFORMAT;
+    if (d->group != (d->fmt == TG_FMT_T5B ? kT5bBlock : TG_GROUP)) return TG_EFORMAT;
     if (d->n < 1 || d->k < 1 || d->k % TG_GROUP || d->n > (1ll << 31) - 1 || d->k > (1ll << 31) - 1) return TG_ECORRUPT;
     uint64_t n = (uint64_t)d->n, k = (uint64_t)d->k;
     if (n > UINT64_MAX / 4 / k) return TG_ECORRUPT;
@@ -146,7 +148,9 @@ int check_desc(const tg_desc *d, uint64_t limit) {
         if (d->bytes_payload != d->bytes_codes + sign_bytes + d->bytes_index) return TG_ECORRUPT;
         if ((d->bytes_signs / 4) > 0xFFFFFFFFull) return TG_ECORRUPT;
     } else {
-        uint64_t want = d->fmt == TG_FMT_5TRIT ? n * (k / TG_GROUP) * 26 : n * k / 4;
+        uint64_t want = d->fmt == TG_FMT_5TRIT ? n * (k / TG_GROUP) * 26
+                        : d->fmt == TG_FMT_T5B ? n * t5b_blocks(k) * 32
+                                               : n * k / 4;
         if (d->bytes_codes != want || d->bytes_signs || d->bytes_index) return TG_ECORRUPT;
         if (d->bytes_total - d->off_codes - d->bytes_codes < kSignPad) return TG_ECORRUPT;  // read slack
         if (d->bytes_payload != want) return TG_ECORRUPT;
@@ -302,6 +306,50 @@ extern "C" int tg_pack_2bit(const int8_t *w, int64_t n, int64_t k, void *out, si
     return TG_OK;
 }
 
+extern "C" int tg_pack_t5b(const int8_t *w, int64_t n, int64_t k, float scale, void *out, size_t out_cap,
+                           size_t *out_bytes) {
+    int e = shape_ok(w, n, k, out_bytes);
+    if (e) return e;
+    if (!(scale == scale) || scale - scale != 0.0f) return TG_EINVAL;  // NaN or infinite
+    if (!all_ternary(w, n * k)) return TG_ENOTTERNARY;
+    std::vector<uint32_t> row_nnz;
+    uint64_t nnz = count_nonzero(w, n, k, &row_nnz);
+    tg_desc d;
+    fill_header(&d, TG_FMT_T5B, n, k, nnz);
+    d.group = kT5bBlock;
+    memcpy(&d.tensor_scale, &scale, 4);
+    const int64_t nb = (int64_t)t5b_blocks((uint64_t)k);
+    d.off_codes = TG_HEADER_BYTES;
+    d.bytes_codes = (uint64_t)n * nb * 32;
+    d.bytes_total = align_up(d.off_codes + d.bytes_codes + kSignPad, kAlign);
+    d.bytes_payload = d.bytes_codes;
+    *out_bytes = d.bytes_total;
+    if (!out) return TG_OK;
+    if (out_cap < d.bytes_total) return TG_ENOSPACE;
+    uint8_t *base = (uint8_t *)out;
+    memset(base, 0, TG_HEADER_BYTES);
+    memcpy(base, &d, sizeof(d));
+    memset(base + d.off_codes + d.bytes_codes, 0, d.bytes_total - d.off_codes - d.bytes_codes);
+    uint8_t *codes = base + d.off_codes;
+    parallel_rows(n, n * k, [&](int64_t lo, int64_t hi) {
+        for (int64_t r = lo; r < hi; r++)
+            for (int64_t b = 0; b < nb; b++) {
+                uint8_t *dst = codes + (r * nb + b) * 32;
+                for (int j = 0; j < 32; j++) {
+                    // Horner from the last digit; positions past k hold the weight-0 digit
+                    unsigned v = 0;
+                    for (int i = 4; i >= 0; i--) {
+                        const int64_t col = kT5bBlock * b + 5 * j + i;
+                        const unsigned digit = col < k ? (unsigned)(w[r * k + col] + 1) : 1u;
+                        v = v * 3 + digit;
+                    }
+                    dst[j] = (uint8_t)v;
+                }
+            }
+    });
+    return TG_OK;
+}
+
 extern "C" int tg_describe(const void *packed, size_t bytes, tg_desc *out) {
     if (!packed || !out) return TG_EINVAL;
     if (bytes < TG_HEADER_BYTES) return TG_EFORMAT;
@@ -336,7 +384,22 @@ int validate_contents(const uint8_t *base, const tg_desc &d) {
     parallel_rows(n, n * k / 4, [&](int64_t lo, int64_t hi) {
         uint64_t local = 0;
         for (int64_t r = lo; r < hi; r++) {
-            if (d.fmt == TG_FMT_5TRIT) {
+            if (d.fmt == TG_FMT_T5B) {
+                const int64_t nb = (int64_t)t5b_blocks((uint64_t)k);
+                for (int64_t b = 0; b < nb; b++) {
+                    const uint8_t *src = codes + (r * nb + b) * 32;
+                    for (int j = 0; j < 32; j++) {
+                        unsigned v = src[j];
+                        if (v >= 243) { err = TG_ECORRUPT; return; }
+                        for (int i = 0; i < 5; i++) {
+                            unsigned digit = v % 3;
+                            v /= 3;
+                            if (kT5bBlock * b + 5 * j + i < k) local += digit != 1;
+                            else if (digit != 1) { err = TG_ECORRUPT; return; }
+                        }
+                    }
+                }
+            } else if (d.fmt == TG_FMT_5TRIT) {
                 for (int64_t g = 0; g < ng; g++) {
                     const uint8_t *src = codes + (r * ng + g) * 26;
                     for (int b = 0; b < 26; b++) {
@@ -404,6 +467,19 @@ extern "C" int tg_unpack(const void *packed, size_t bytes, int8_t *w_out) {
                     }
                 }
             }
+        });
+    } else if (d.fmt == TG_FMT_T5B) {
+        const int64_t nb = (int64_t)t5b_blocks((uint64_t)k);
+        parallel_rows(n, n * k, [&](int64_t lo, int64_t hi) {
+            for (int64_t r = lo; r < hi; r++)
+                for (int64_t b = 0; b < nb; b++)
+                    for (int j = 0; j < 32; j++) {
+                        unsigned v = codes[(r * nb + b) * 32 + j];
+                        for (int i = 0; i < 5; i++, v /= 3) {
+                            const int64_t col = kT5bBlock * b + 5 * j + i;
+                            if (col < k) w_out[r * k + col] = (int8_t)((int)(v % 3) - 1);
+                        }
+                    }
         });
     } else if (d.fmt == TG_FMT_5TRIT) {
         parallel_rows(n, n * k, [&](int64_t lo, int64_t hi) {

@@ -13,6 +13,15 @@ constexpr uint64_t kSignPad = 16;     // zero bytes after the sign stream (room 
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+// t5b: weights per block (one group of the kernels' work geometry) and blocks per row of k weights.
+constexpr int kT5bBlock = 160;
+inline constexpr uint64_t t5b_blocks(uint64_t k) { return (k + kT5bBlock - 1) / kT5bBlock; }
+
+// Per-row group count of a format: 128-weight scale groups, or t5b's 160-weight blocks.
+inline constexpr int64_t groups_per_row(int fmt, int64_t k) {
+    return fmt == TG_FMT_T5B ? (int64_t)t5b_blocks((uint64_t)k) : k / TG_GROUP;
+}
+
 // One GEMV as the kernels see it: device pointers into one packed buffer plus the caller's
 // scales, activations and outputs. Filled on the host from a checked descriptor.
 struct Problem {
@@ -22,7 +31,7 @@ struct Problem {
     const uint16_t *scales;   // fp16 [n][k/128] (value path)
     const int8_t *x;          // int8 [m][k]
     float *y;                 // float [m][n] (value path)
-    int32_t *acc;             // int32 [m][n][k/128] (accumulator path)
+    int32_t *acc;             // int32 [m][n][groups] (accumulator path)
     const float *xs;          // float [m][k/128] activation group scales (value path with them), else null
     uint32_t codes_bytes;     // bytes of the codes section
     uint32_t sign_bytes;      // bytes of the sign section
@@ -39,7 +48,7 @@ struct Problem {
     int32_t rpu;              // rows per unit (nbu * R)
     uint32_t gmagic;          // ceil(65536 / G): lane / G as (lane * gmagic) >> 16 for lane < 64
     uint32_t rmagic;          // ceil(65536 / R): likewise for R
-    int32_t reserved;
+    float tscale;             // t5b: the per-tensor scale (other formats: unused)
 };
 
 // Work units a wave processes: [begin, end), starting in GEMV `problem` of the table.
@@ -106,6 +115,7 @@ enum OutMode { kOutY = 0, kOutAcc = 1, kOutYxs = 2 };
 hipError_t launch_bitcos(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s);
+hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s);
 
 // Per-group int8 quantisation of `groups` runs of 128 fp32 activations (one wave per group).
 hipError_t launch_quantize_x(const float *x, int64_t groups, int8_t *xq, float *xs, hipStream_t s);

@@ -27,6 +27,13 @@
  *       padding digits of value 1. Bytes >= 243 are invalid.
  *   TG_FMT_2BIT -- two bits per weight (Table I's "2-bit packing"): code c = w + 1, four codes per
  *       byte, the first weight in the lowest two bits. Code 3 is invalid.
+ *   TG_FMT_T5B -- the five-trit code in blocks of 160 weights with one scale per tensor ("Sub-Two-Bit
+ *       Ternary Weight Storage with Table-Free Arithmetic Decoding", abstract: t5b, 32 bytes per
+ *       block, 1.600 bits per weight). Block b of a row holds weights 160b .. 160b + 159; byte j of
+ *       a block holds weights 160b + 5j .. + 4 as digits w + 1, the first weight least significant;
+ *       positions past k are padding digits of value 1. The fp32 tensor scale is stored in the
+ *       descriptor (tensor_scale); there are no per-group scales, and the per-group quantities
+ *       (accumulators) are per 160-weight block: acc[m][n][ceil(k/160)], y = scale * sum_k W x.
  *
  * Scales are IEEE binary16, row-major [n][k/128], and are passed separately from the packed weights.
  *
@@ -57,7 +64,7 @@ extern "C" {
 #define TG_VERSION 1u
 #define TG_HEADER_BYTES 256u /* the descriptor occupies the first 256 bytes of a packed buffer */
 
-typedef enum { TG_FMT_BITCOS = 1, TG_FMT_5TRIT = 2, TG_FMT_2BIT = 3 } tg_fmt;
+typedef enum { TG_FMT_BITCOS = 1, TG_FMT_5TRIT = 2, TG_FMT_2BIT = 3, TG_FMT_T5B = 4 } tg_fmt;
 
 enum {
     TG_OK = 0,
@@ -77,6 +84,8 @@ enum {
  *           padding up to bytes_signs), index = rowoff (4*(n+1) bytes).
  *   5TRIT:  codes = n * (k/128) * 26 bytes, row-major by (row, group). No signs or index.
  *   2BIT:   codes = n * k / 4 bytes, row-major. No signs or index.
+ *   T5B:    codes = n * ceil(k/160) * 32 bytes, row-major by (row, block). No signs or index;
+ *           group = 160 (the block length; every other format has group = TG_GROUP).
  */
 typedef struct tg_desc {
     uint32_t magic;      /* TG_MAGIC */
@@ -91,7 +100,9 @@ typedef struct tg_desc {
     uint64_t off_index, bytes_index;
     uint64_t bytes_total; /* whole buffer, header included */
     uint64_t bytes_payload; /* algorithmic bytes: codes + ceil(nnz/8) sign bytes + index (no padding, no header) */
-    uint64_t reserved[2];
+    uint32_t tensor_scale;  /* TG_FMT_T5B: the per-tensor scale, IEEE binary32 bits; 0 otherwise */
+    uint32_t reserved32;
+    uint64_t reserved;
 } tg_desc;
 
 /*
@@ -104,6 +115,9 @@ typedef struct tg_desc {
 int tg_pack_bitcos(const int8_t *w, int64_t n, int64_t k, void *out, size_t out_cap, size_t *out_bytes);
 int tg_pack_5trit(const int8_t *w, int64_t n, int64_t k, void *out, size_t out_cap, size_t *out_bytes);
 int tg_pack_2bit(const int8_t *w, int64_t n, int64_t k, void *out, size_t out_cap, size_t *out_bytes);
+/* t5b packer: as above, plus the per-tensor scale (finite; TG_EINVAL otherwise) stored in the
+ * descriptor. k must be a multiple of 128 like every format of this library. */
+int tg_pack_t5b(const int8_t *w, int64_t n, int64_t k, float scale, void *out, size_t out_cap, size_t *out_bytes);
 
 /* Read and check the descriptor of a host packed buffer of `bytes` bytes (header fields only).
  * Errors: TG_EINVAL, TG_EFORMAT (magic/version/fmt/group wrong or bytes too small),
@@ -122,10 +136,11 @@ int tg_unpack(const void *packed, size_t bytes, int8_t *w_out);
 /*
  * GPU GEMV (asynchronous). desc: host copy of the descriptor of the packed buffer whose device copy
  * is W (bytes_total bytes, the same image as the host buffer). scales: device fp16 [n][k/128] bit
- * patterns. x: device int8 [m][k]. y: device float [m][n]. 1 <= m <= TG_MAX_M.
+ * patterns (TG_FMT_T5B: must be NULL, the tensor scale comes from the descriptor). x: device int8
+ * [m][k]. y: device float [m][n]. 1 <= m <= TG_MAX_M.
  * Paths: the vector kernels (int8 dot products in int32, "Breaking the 1.58-bit Barrier for Ternary
- * LLMs", Sec. II-C) take up to three activation rows per launch; five-trit and 2-bit with m > 3 run
- * them in launches of up to three rows. BITCOS with m >= 3, or m = 2 with k > 8192, takes the
+ * LLMs", Sec. II-C) take up to three activation rows per launch; five-trit, 2-bit and t5b with m > 3
+ * run them in launches of up to three rows. BITCOS with m >= 3, or m = 2 with k > 8192, takes the
  * thin-batch path instead: one launch decodes each weight once into int8
  * operands of int8 matrix-core products against X padded to 16 rows (a batch turns the GEMV into a
  * matrix product; the untitled page on a NUMA-aware decode engine for ternary models, Sec. 6.5 and

@@ -231,3 +231,32 @@ def test_activation_quantisation_argument_errors_before_any_gpu_work():
     assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
     bad = (binding.TgDesc * 1)(d2)
     assert L.tg_plan_init_xs(ctypes.byref(plan), dummy, nbytes, 1, bad, ptrs, ptrs, ptrs, ptrs, ptrs, 1) == -4
+
+
+def test_t5b_argument_errors_before_any_gpu_work():
+    L = binding.lib()
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    sz = ctypes.c_size_t(0)
+    wp = w.ctypes.data_as(ctypes.c_void_p)
+    assert L.tg_pack_t5b(wp, 8, 256, ctypes.c_float(float("nan")), None, 0, ctypes.byref(sz)) == -1
+    assert L.tg_pack_t5b(wp, 8, 256, ctypes.c_float(float("inf")), None, 0, ctypes.byref(sz)) == -1
+    assert L.tg_pack_t5b(wp, 8, 200, ctypes.c_float(1.0), None, 0, ctypes.byref(sz)) == -3
+    bad = w.copy()
+    bad[0, 0] = 2
+    assert L.tg_pack_t5b(bad.ctypes.data_as(ctypes.c_void_p), 8, 256, ctypes.c_float(1.0), None, 0,
+                         ctypes.byref(sz)) == -2
+    d = B.pack_t5b(w, 0.5).desc
+    dummy = ctypes.c_void_p(256)
+    # t5b takes no per-group scales and no activation group scales
+    assert L.ternary_gemv(ctypes.byref(d), dummy, dummy, dummy, dummy, 1, None) == -1
+    assert L.ternary_gemv_xs(ctypes.byref(d), dummy, None, dummy, dummy, dummy, 1, None) == -1
+    descs = (binding.TgDesc * 1)(d)
+    P1 = ctypes.c_void_p * 1
+    plan = binding.TgPlan()
+    nbytes = L.tg_plan_table_bytes(1)
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, P1(256), P1(256), P1(256), P1(256), None,
+                          1) == -1
+    # a t5b descriptor with the other formats' group size is not a valid descriptor
+    d2 = binding.TgDesc.from_buffer_copy(d)
+    d2.group = 128
+    assert L.ternary_gemv(ctypes.byref(d2), dummy, None, dummy, dummy, 1, None) == -4

@@ -71,3 +71,30 @@ def test_descriptor_layout():
             assert d.bytes_signs >= (d.nnz + 7) // 8 + 16
         else:
             assert d.bytes_total >= d.off_codes + d.bytes_codes + 16
+
+
+@pytest.mark.parametrize("n,k,z", [(1, 128, 0.42), (3, 256, 0.0), (5, 384, 1.0), (17, 640, 0.3), (33, 2560, 0.42),
+                                   (7, 4096, 0.95), (4, 14336, 0.4), (300, 5120, 0.47)])
+def test_t5b_packer_matches_oracle_bytes(n, k, z):
+    w = synth.ternary(n, k, z, seed=n * 11 + k)
+    p = B.pack_t5b(w, 0.0375)
+    assert np.array_equal(p.section("codes").reshape(n, -1, 32), O.t5b_pack(w))
+    assert p.desc.group == 160 and p.payload_bytes == n * (-(-k // 160)) * 32
+    assert np.frombuffer(np.uint32(p.desc.tensor_scale).tobytes(), np.float32)[0] == np.float32(0.0375)
+    B.validate(p.buf)
+    assert np.array_equal(B.unpack(p.buf), w)
+    assert p.desc.nnz == int((w != 0).sum())
+
+
+def test_t5b_validate_rejects_bad_bytes_and_padding():
+    w = synth.ternary(3, 128, 0.4, seed=2)
+    p = B.pack_t5b(w, 1.0)
+    off = p.desc.off_codes
+    bad = p.buf.copy()
+    bad[off + 5] = 250  # not a five-trit byte
+    with pytest.raises(B.TgError):
+        B.validate(bad)
+    bad = p.buf.copy()
+    bad[off + 31] = 120  # k = 128: byte 31 is all padding and must encode five weight-0 digits
+    with pytest.raises(B.TgError):
+        B.validate(bad)
