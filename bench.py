@@ -29,12 +29,15 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from bit_gemv_decode_amd.binding import FMT_T5B  # noqa: E402  (numpy and ctypes only)
+
 HBM_PEAK_GBS = 8000.0
 SETTLE_MS = 60.0  # GPU time of warm-up launches before a sustained-rate measurement (see --warmup)
 LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
 LAYERS = 32
 Z = 0.40
+T5B_SCALE = 0.05  # the per-tensor scale of t5b matrices (the other formats draw per-group scales)
 METRIC = "ternary GEMV effective HBM GB/s (packed bytes/s) + % of MI355X peak, µs/call"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bitcos_layerset.json")
 
@@ -60,7 +63,8 @@ class LayerSet:
             w = synth.ternary(n, k, Z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
             s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
             x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
-            p = B.pack(fmt, w)
+            # t5b carries one scale per tensor instead of per-group scales
+            p = B.pack_t5b(w, T5B_SCALE) if fmt == B.FMT_T5B else B.pack(fmt, w)
             self.host.append(dict(name=name, n=n, k=k, packed=p, s=s, x=x))
             base.append((B.DeviceWeights(p, dev), torch.from_numpy(s).to(dev), torch.from_numpy(x).to(dev)))
         for layer in range(layers):
@@ -70,7 +74,7 @@ class LayerSet:
                 row.append(dict(name=name, w=B.DeviceWeights.from_tensor(dw.desc, t), s=s if layer == 0 else s.clone(),
                                 x=x, y=torch.empty((1, n), dtype=torch.float32, device=dev)))
             self.mats.append(row)
-        self.layer_bytes = [m["w"].payload_bytes + 2 * m["w"].n * (m["w"].k // 128) for m in self.mats[0]]
+        self.layer_bytes = [packed_bytes(m["w"]) for m in self.mats[0]]
         self.step_bytes = layers * sum(self.layer_bytes)
 
     def flat(self):
@@ -78,8 +82,8 @@ class LayerSet:
 
     def plan(self, B, mats=None):
         mats = mats if mats is not None else self.flat()
-        return B.Plan([m["w"] for m in mats], [m["x"] for m in mats], scales=[m["s"] for m in mats],
-                      ys=[m["y"] for m in mats])
+        return B.Plan([m["w"] for m in mats], [m["x"] for m in mats],
+                      scales=None if self.fmt == B.FMT_T5B else [m["s"] for m in mats], ys=[m["y"] for m in mats])
 
 
 def time_launches(torch, fn, steps, warmup):
@@ -201,6 +205,10 @@ def replicas(B, dw0, count):
 
 
 def packed_bytes(dw):
+    """Algorithmic bytes of one packed matrix: its payload plus its scales (fp16 per 128-group, or
+    the 4-byte tensor scale of t5b)."""
+    if dw.fmt == FMT_T5B:
+        return dw.payload_bytes + 4
     return dw.payload_bytes + 2 * dw.n * (dw.k // 128)
 
 
@@ -255,7 +263,7 @@ def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label
     x = torch.from_numpy(synth.activations(m, k, seed=0)).to(dev)
     sets = {}
     for f in fmts:
-        dw0 = B.DeviceWeights(B.pack(f, w), dev)
+        dw0 = B.DeviceWeights(B.pack_t5b(w, T5B_SCALE) if f == B.FMT_T5B else B.pack(f, w), dev)
         sets[f] = replicas(B, dw0, reps)
     y = torch.empty((m, n), dtype=torch.float32, device=dev)
     out = {"n": n, "k": k, "m": m, "z": z, "replicas": reps, "x_bytes": m * k, "y_bytes": 4 * m * n}
@@ -264,11 +272,13 @@ def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label
         order = fmts[r % len(fmts):] + fmts[:r % len(fmts)]
         for f in order:
             dws = sets[f]
-            rates[f].append(sustained(torch, B, dws, [x] * len(dws), [s] * len(dws), [y] * len(dws), launches=3))
+            sf = None if f == B.FMT_T5B else [s] * len(dws)
+            rates[f].append(sustained(torch, B, dws, [x] * len(dws), sf, [y] * len(dws), launches=3))
     for f in fmts:
         dws = sets[f]
         ncalls = max(200, len(dws))
-        calls = [(lambda d=dws[i % len(dws)]: B.ternary_gemv(d, s, x, y)) for i in range(ncalls)]
+        s1 = None if f == B.FMT_T5B else s
+        calls = [(lambda d=dws[i % len(dws)]: B.ternary_gemv(d, s1, x, y)) for i in range(ncalls)]
         pc = per_call_us(torch, calls)
         pc["gbs_at_median"] = round(packed_bytes(dws[0]) / pc["median_us"] / 1e3, 1)
         pc["graph_us_per_call"] = graph_call_us(torch, calls)
@@ -393,7 +403,7 @@ def run_suite(path):
     from bit_gemv_decode_amd import synth
 
     dev = torch.device("cuda:0")
-    F = [B.FMT_BITCOS, B.FMT_5TRIT, B.FMT_2BIT]
+    F = [B.FMT_BITCOS, B.FMT_5TRIT, B.FMT_2BIT, B.FMT_T5B]
     res = {"command": f"python3 bench.py --suite {path}", "device": torch.cuda.get_device_name(0),
            "hbm_peak_gbs": HBM_PEAK_GBS,
            "note": "packed bytes = bitmap + sign stream + row index + fp16 scales (BITCOS) or codes + fp16 "
@@ -539,7 +549,7 @@ def main():
     bitcos_host = ls
     formats = {"bitcos": {"gbs": round(gbs, 1), "ms_per_step": round(step_s * 1e3, 3), "step_bytes": ls.step_bytes}}
     del plan
-    for fname, fmt in (("5trit", B.FMT_5TRIT), ("2bit", B.FMT_2BIT)):
+    for fname, fmt in (("5trit", B.FMT_5TRIT), ("2bit", B.FMT_2BIT), ("t5b", B.FMT_T5B)):
         log(f"[bench] {fname} layer set")
         lf = LayerSet(B, synth, torch, dev, fmt)
         pf = lf.plan(B)
@@ -554,6 +564,8 @@ def main():
     out["5trit_vs_bitcos_bytes"] = round(formats["5trit"]["step_bytes"] / formats["bitcos"]["step_bytes"], 4)
     out["bitcos_vs_2bit_time"] = round(formats["2bit"]["ms_per_step"] / formats["bitcos"]["ms_per_step"], 4)
     out["2bit_vs_bitcos_bytes"] = round(formats["2bit"]["step_bytes"] / formats["bitcos"]["step_bytes"], 4)
+    out["bitcos_vs_t5b_time"] = round(formats["t5b"]["ms_per_step"] / formats["bitcos"]["ms_per_step"], 4)
+    out["t5b_vs_bitcos_bytes"] = round(formats["t5b"]["step_bytes"] / formats["bitcos"]["step_bytes"], 4)
 
     if not args.no_cpu:
         import oracle as O
