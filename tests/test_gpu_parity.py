@@ -321,3 +321,24 @@ def test_plan_coarse_chunked_units():
     for (y_ref, acc_ref, s), y in zip(chunked, ys[reps:]):
         ok, ndiff = y_tolerance_ok(y.cpu().numpy(), y_ref, acc_ref, s)
         assert ok and ndiff == 0, f"coarse plan chunked: within tolerance {ok}, {ndiff} differ"
+
+
+@pytest.mark.parametrize("m", [1, 3, 4])
+def test_very_long_rows(m):
+    """k = 65664: 513 groups, nine chunk passes with a one-group tail; every format (t5b: 411 blocks,
+    seven passes, a 27-block tail), the vector path and (BITCOS, m = 3, 4) the matrix-core path."""
+    n, k = 96, 65664
+    w = synth.ternary(n, k, 0.41, seed=1313)
+    x = synth.activations(m, k, seed=1314)
+    s = synth.scales(n, k // 128, seed=1315)
+    run_case(w, x, s, label=f"long rows m={m}")
+    dev = _dev()
+    acc_ref = O.gemv_acc_blocks(w, x)
+    dw = B.DeviceWeights(B.pack_t5b(w, 0.02), dev)
+    xt = torch.from_numpy(x).to(dev)
+    acc = B.ternary_gemv_acc(dw, xt)
+    y = B.ternary_gemv(dw, None, xt)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref), "t5b long rows: block sums differ"
+    y_ref = O.combine_tensor(acc_ref, 0.02)
+    assert np.allclose(y.cpu().numpy(), y_ref, rtol=1e-5, atol=1e-5 * float(np.abs(y_ref).max()))
