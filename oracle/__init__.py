@@ -77,6 +77,8 @@ def lib():
         L.oracle_gemv_acc_blocks.restype = None
         L.oracle_combine_tensor.argtypes = [p, ctypes.c_float, i64, i64, i64, p]
         L.oracle_combine_tensor.restype = None
+        L.oracle_gemv_f16.argtypes = [p, p, p, i64, i64, i64, p]
+        L.oracle_gemv_f16.restype = None
         L.oracle_gemv_packed.argtypes = [ctypes.c_int, p, p, p, p, i64, i64, p, i64, p]
         L.oracle_gemv_packed.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
@@ -239,6 +241,19 @@ def combine(acc: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 def gemv(w: np.ndarray, scales: np.ndarray, x: np.ndarray) -> np.ndarray:
     return combine(gemv_acc(w, x), scales)
+
+
+def gemv_f16(w: np.ndarray, scales: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """float32 [m, n]: the GEMV against fp16 activations [m, k], exact up to the final rounding."""
+    w = _c(w, np.int8)
+    sc = _c(scales, np.float16).view(np.uint16)
+    x16 = _c(np.atleast_2d(x), np.float16).view(np.uint16)
+    n, k = w.shape
+    m = x16.shape[0]
+    assert sc.shape == (n, k // GROUP) and x16.shape[1] == k
+    y = np.empty((m, n), np.float32)
+    lib().oracle_gemv_f16(_ptr(w), _ptr(sc), _ptr(x16), n, k, m, _ptr(y))
+    return y
 
 
 def quantize_x(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

@@ -321,6 +321,33 @@ void oracle_combine(const int32_t *acc, const uint16_t *scales, int64_t n, int64
         }
 }
 
+/* ---------- fp16 activations ---------- */
+
+/*
+ * The GEMV against fp16 activations: the weights are rebuilt as +-scale or 0 and multiplied with the
+ * activations in floating point ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-B and
+ * II-D: the AVX-512 path expands each ternary weight to +-s in fp16, the Xe2 kernel feeds fp16
+ * weights and activations to its matrix engine). Here the definition is computed exactly: x is
+ * decoded from IEEE binary16, each group's sum of +-x is exact in double (binary16 values span at
+ * most 40 bits of significance), the group scale multiplies it exactly, groups are added in
+ * ascending order and the row is rounded once to float. x16: binary16 bits [m][k].
+ */
+void oracle_gemv_f16(const int8_t *w, const uint16_t *scales, const uint16_t *x16, int64_t n, int64_t k, int64_t m,
+                     float *y) {
+    int64_t ng = k / ORACLE_GROUP;
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t r = 0; r < n; r++) {
+            double total = 0.0;
+            for (int64_t g = 0; g < ng; g++) {
+                double s = 0.0;
+                for (int64_t c = g * ORACLE_GROUP; c < (g + 1) * ORACLE_GROUP; c++)
+                    s += (double)w[r * k + c] * oracle_half_to_double(x16[mi * k + c]);
+                total += oracle_half_to_double(scales[r * ng + g]) * s;
+            }
+            y[mi * n + r] = (float)total;
+        }
+}
+
 /* ---------- per-group int8 activation quantisation ---------- */
 
 /* x: float [m][k] (finite values), k a multiple of 128. xq: int8 [m][k]; xs: float [m][k/128], the
