@@ -167,6 +167,13 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
         make_rsrc(p.acc, ACC ? (uint32_t)mrows * (uint32_t)p.n * (uint32_t)ng * 4u : 0u);
     const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.xs, XS ? (uint32_t)mrows * (uint32_t)ng * 4u : 0u);
     uint32_t *const sxs = stg + kStageDwords;  // XS: the chunk's activation scales, [group][m]
+    if constexpr (XS) {
+        // The pipeline-fill steps read this buffer before the first chunk is written to it; their
+        // products are zero, but a stale Inf or NaN bit pattern left in LDS by an earlier kernel would
+        // still turn 0 * xs into NaN in the row sums. Zero it first (in-order within the wave).
+#pragma unroll
+        for (int i = 0; i < (int)kXsDwords / 64; ++i) sxs[64 * i + lane] = 0u;
+    }
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const uint32_t m_odd = (q & 1) ? ~0u : 0u, m_hi = (q >> 1) ? ~0u : 0u;
     const uint32_t voff_x = lr < mrows ? (uint32_t)lr * (uint32_t)p.k + 32u * (uint32_t)q : kOffOff;
