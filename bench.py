@@ -185,6 +185,29 @@ def activation_quant(torch, B, synth, ls, dev, steps, warmup):
     return out
 
 
+def fp16_activations(torch, B, synth, ls, dev):
+    """The BITCOS layer set against fp16 activations (ternary_gemv_f16; one launch per GEMV, replayed
+    from a graph that cycles through the 32 copies of each matrix): per-matrix time and the pass."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    out, total_us = {}, 0.0
+    for role, (name, n, k) in enumerate(LAYER):
+        xf = synth.float_activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_XF))
+        x16 = torch.from_numpy(xf.astype(np.float16)).to(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for row in ls.mats:
+                m = row[role]
+                B.ternary_gemv_f16(m["w"], m["s"], x16, m["y"], stream=st)
+        us = time_launches(torch, g.replay, 5, 1) / (5 * LAYERS) * 1e6
+        total_us += us * LAYERS
+        out[name] = {"us_per_call": round(us, 3), "gbs": round(ls.layer_bytes[role] / us / 1e3, 1)}
+        del g
+    out["layer_set_per_gemv_graph"] = {"gbs": round(ls.step_bytes / total_us / 1e3, 1),
+                                       "ms_per_step": round(total_us / 1e3, 3)}
+    return out
+
+
 def load_traffic():
     """HBM bytes per launch from the committed rocprofv3 --pmc runs, if they match this kernel source."""
     try:
@@ -540,6 +563,9 @@ def main():
 
     log("[bench] float activations: quantiser and GEMV with activation group scales")
     out["activation_quant"] = activation_quant(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
+
+    log("[bench] fp16 activations")
+    out["fp16_activations"] = fp16_activations(torch, B, synth, ls, dev)
 
     log("[bench] stream-read ceiling")
     ceil = stream_ceiling(torch, bd, dev)

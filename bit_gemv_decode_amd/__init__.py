@@ -5,8 +5,8 @@ this package is its Python binding plus the seeded synthetic-input generator.
 """
 from .binding import (FMT_2BIT, FMT_5TRIT, FMT_BITCOS, FMT_NAMES, FMT_T5B, groups_per_row, pack_t5b, TG_GROUP, TG_MAX_M, DeviceWeights, Packed,
                       Plan, TgError, describe, pack, pack_2bit, pack_5trit, pack_bitcos, quantize_x, ternary_gemv,
-                      ternary_gemv_acc, ternary_gemv_xs, unpack, validate)
+                      ternary_gemv_acc, ternary_gemv_f16, ternary_gemv_xs, unpack, validate)
 
 __all__ = ["FMT_BITCOS", "FMT_5TRIT", "FMT_2BIT", "FMT_T5B", "FMT_NAMES", "groups_per_row", "pack_t5b", "TG_GROUP", "TG_MAX_M", "DeviceWeights", "Packed",
            "Plan", "TgError", "describe", "pack", "pack_bitcos", "pack_5trit", "pack_2bit", "ternary_gemv",
-           "ternary_gemv_acc", "ternary_gemv_xs", "quantize_x", "unpack", "validate"]
+           "ternary_gemv_acc", "ternary_gemv_xs", "ternary_gemv_f16", "quantize_x", "unpack", "validate"]

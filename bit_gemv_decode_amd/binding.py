@@ -25,7 +25,8 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 
 # Every symbol include/ternary_gemv.h declares.
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_pack_t5b", "tg_describe", "tg_validate", "tg_unpack",
-           "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "tg_plan_table_bytes",
+           "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "ternary_gemv_f16",
+           "tg_plan_table_bytes",
            "tg_plan_init", "tg_plan_init_xs", "ternary_gemv_plan", "tg_stream_read", "tg_strerror", "tg_version"]
 
 
@@ -83,6 +84,8 @@ def lib():
         L.tg_quantize_x.restype = ctypes.c_int
         L.ternary_gemv_xs.argtypes = [ctypes.POINTER(TgDesc), p, p, p, p, p, ctypes.c_int32, p]
         L.ternary_gemv_xs.restype = ctypes.c_int
+        L.ternary_gemv_f16.argtypes = [ctypes.POINTER(TgDesc), p, p, p, p, ctypes.c_int32, p]
+        L.ternary_gemv_f16.restype = ctypes.c_int
         L.tg_plan_init_xs.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p,
                                       p, p, p, ctypes.c_int32]
         L.tg_plan_init_xs.restype = ctypes.c_int
@@ -346,6 +349,30 @@ def ternary_gemv_xs(w: DeviceWeights, scales, xq, x_scales, y=None, stream=None)
                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(xq.data_ptr()),
                                  ctypes.c_void_p(x_scales.data_ptr()), ctypes.c_void_p(y.data_ptr()), m,
                                  _stream_handle(stream)), "ternary_gemv_xs")
+    return y
+
+
+def ternary_gemv_f16(w: DeviceWeights, scales, x16, y=None, stream=None):
+    """y[m, n] = sum_g scales[n, g] * sum_{k in g} W[n, k] * x16[m, k] for fp16 activations on BITCOS
+    weights (ternary_gemv_f16). Asynchronous."""
+    import torch
+
+    _require_cuda(w.tensor, torch.uint8, "weights")
+    _require_cuda(scales, torch.float16, "scales")
+    _require_cuda(x16, torch.float16, "x16")
+    if x16.dim() == 1:
+        x16 = x16.view(1, -1)
+    m = x16.shape[0]
+    if x16.shape[1] != w.k or tuple(scales.shape) != (w.n, w.k // TG_GROUP):
+        raise ValueError("shape mismatch between weights, scales and x16")
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=x16.device)
+    _require_cuda(y, torch.float32, "y")
+    if tuple(y.shape) != (m, w.n):
+        raise ValueError("y has the wrong shape")
+    _check(lib().ternary_gemv_f16(ctypes.byref(w.desc), ctypes.c_void_p(w.tensor.data_ptr()),
+                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(x16.data_ptr()),
+                                  ctypes.c_void_p(y.data_ptr()), m, _stream_handle(stream)), "ternary_gemv_f16")
     return y
 
 

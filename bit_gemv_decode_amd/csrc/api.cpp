@@ -167,6 +167,36 @@ extern "C" int tg_quantize_x(const float *x, int32_t m, int64_t k, int8_t *xq, f
                                                                                                       : TG_EHIP;
 }
 
+extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16_t *scales, const uint16_t *x16,
+                                float *y, int32_t m, void *stream) {
+    if (!desc || !W || !scales || !x16 || !y || m < 1 || m > TG_MAX_M) return TG_EINVAL;
+    if (desc->fmt != TG_FMT_BITCOS) return TG_EINVAL;
+    if (((uintptr_t)W & 15) || ((uintptr_t)x16 & 15) || ((uintptr_t)y & 3) || ((uintptr_t)scales & 1))
+        return TG_EINVAL;
+    int e = check_desc(desc, 0);
+    if (e) return e;
+    // the fp16 rows take twice the bytes of int8 ones
+    if (!fits_offsets(desc, m) || (uint64_t)m * (uint64_t)desc->k * 2 > (1ull << 30)) return TG_ESHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n = desc->n, k = desc->k;
+    for (int32_t m0 = 0; m0 < m; m0 += kF16MaxM) {
+        const int32_t mt = std::min<int32_t>(kF16MaxM, m - m0);
+        GroupArgs g{};
+        g.one = make_problem(desc, W, scales, reinterpret_cast<const int8_t *>(x16 + (size_t)m0 * k),
+                             y + (size_t)m0 * n, nullptr);
+        g.count = 1;
+        g.m = mt;
+        g.one.unit_begin = 0;
+        gemv_geometry(g.one, TG_FMT_BITCOS, mt);
+        if (want_fine({g.one}, TG_FMT_BITCOS, mt, false, device_cus() * kF16Waves))
+            gemv_geometry(g.one, TG_FMT_BITCOS, mt, true);
+        g.rows_per_unit = g.one.rpu;
+        g.units = g.one.nunits;
+        if (launch_bitcos_f16(g, s) != hipSuccess) return TG_EHIP;
+    }
+    return TG_OK;
+}
+
 extern "C" int ternary_gemv_acc(const tg_desc *desc, const void *W, const int8_t *x, int32_t *acc, int32_t m,
                                 void *stream) {
     return gemv_common(desc, W, nullptr, x, nullptr, nullptr, acc, m, stream, kOutAcc);

@@ -31,11 +31,17 @@
 //     (exact in fp64) goes to an LDS tile; once per unit the tile's rows are summed (fp64, DPP) and
 //     stored as fp32. Chunked rows at m = 1 keep those terms in registers instead (one fp64 per row
 //     of the unit and lane) and reduce them over the wave at the unit's end.
+//   * fp16 activations (Sec. II-B: the weights rebuilt as +-1 or 0 in 16-bit floating point; Sec.
+//     II-D: lookup entries holding fp16 weights): the same lookups on a second table whose entry bytes
+//     are the binary16 high bytes of +1.0 and -1.0 (low bytes zero), so one byte-permute turns two
+//     entry bytes into two fp16 weights and v_dot2_f32_f16 contracts them with two activations into
+//     an fp32 group sum. Each lane holds its group's 128 activations (256 bytes) in registers.
 //   * loads are software-pipelined: a step's bitmap four half-steps before its decode, its sign
 //     windows two, with the loop unrolled so that no register with a load in flight is ever copied. Every load goes
 //     through a buffer resource and is issued unconditionally; lanes with nothing to read use an
 //     out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
+#include <type_traits>
 
 #include "bitcos_tables.h"
 #include "gemv_pipeline.h"
@@ -74,13 +80,21 @@ __device__ __forceinline__ uint32_t stage_signs(const Ctx &x, const u32x4 &bm, u
     return total;
 }
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// acc + a.lo * b.lo + a.hi * b.hi for two fp16 pairs (products exact in fp32).
+__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, a), __builtin_bit_cast(h2v, b), acc, false);
+}
+
 // Two bitmap dwords (64 weights) of decode. lo*/hi* hold the sign-stream bits starting 3 bits before
 // each dword's first sign. All eight per-byte (mask, base) reads go out first, then all eight entry
 // reads, then the dot products: two LDS round trips for the 64 weights.
-template <int M>
+// With F16, entries come from the fp16 table and xr holds fp16 activations (two per dword).
+template <int M, bool F16, int XW, typename A>
 __device__ __forceinline__ void decode_pair(uint32_t bma, uint32_t bmb, uint32_t loa, uint32_t hia, uint32_t lob,
-                                            uint32_t hib, const uint32_t (&xr)[M][32], int d, const char *lds,
-                                            uint32_t laneoff, int (&acc)[M]) {
+                                            uint32_t hib, const uint32_t (&xr)[M][XW], int d, const char *lds,
+                                            uint32_t laneoff, A (&acc)[M]) {
     uint2 info[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -103,18 +117,35 @@ __device__ __forceinline__ void decode_pair(uint32_t bma, uint32_t bmb, uint32_t
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (F16) {
+            // weights 2j, 2j + 1 of the entry as a half2: entry bytes to bits 8..15 and 24..31
+            const uint32_t w0 = __builtin_amdgcn_perm(e[i].x, e[i].x, 0x050C040Cu);
+            const uint32_t w1 = __builtin_amdgcn_perm(e[i].x, e[i].x, 0x070C060Cu);
+            const uint32_t w2 = __builtin_amdgcn_perm(e[i].y, e[i].y, 0x050C040Cu);
+            const uint32_t w3 = __builtin_amdgcn_perm(e[i].y, e[i].y, 0x070C060Cu);
 #pragma unroll
-        for (int mi = 0; mi < M; ++mi) {
-            acc[mi] = dot4(e[i].x, xr[mi][8 * d + 2 * i], acc[mi]);
-            acc[mi] = dot4(e[i].y, xr[mi][8 * d + 2 * i + 1], acc[mi]);
+            for (int mi = 0; mi < M; ++mi) {
+                const int xi = 16 * d + 4 * i;
+                acc[mi] = fdot2(w0, xr[mi][xi], acc[mi]);
+                acc[mi] = fdot2(w1, xr[mi][xi + 1], acc[mi]);
+                acc[mi] = fdot2(w2, xr[mi][xi + 2], acc[mi]);
+                acc[mi] = fdot2(w3, xr[mi][xi + 3], acc[mi]);
+            }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < M; ++mi) {
+                acc[mi] = dot4(e[i].x, xr[mi][8 * d + 2 * i], acc[mi]);
+                acc[mi] = dot4(e[i].y, xr[mi][8 * d + 2 * i + 1], acc[mi]);
+            }
         }
+    }
 }
 
-// int32 sums of the lane's 128 weights times x, per activation row.
-template <int M>
-__device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const uint32_t (&xr)[M][32],
-                                       const char *lds, uint32_t laneoff, int (&acc)[M]) {
+// Sums of the lane's 128 weights times x, per activation row (int32; fp32 with F16).
+template <int M, bool F16, int XW, typename A>
+__device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const uint32_t (&xr)[M][XW],
+                                       const char *lds, uint32_t laneoff, A (&acc)[M]) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi) acc[mi] = 0;
 #pragma unroll
@@ -128,7 +159,7 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
         const uint32_t pc = __builtin_popcount(q == 0 ? bm.x : bm.z);
         const uint64_t w01 = ((uint64_t)a1 << 32) | a0, w12 = ((uint64_t)a2 << 32) | a1;
         const uint32_t b0 = (uint32_t)(w01 >> pc), b1 = (uint32_t)(w12 >> pc);
-        decode_pair<M>(q == 0 ? bm.x : bm.z, q == 0 ? bm.y : bm.w, a0, a1, b0, b1, xr, 2 * q, lds, laneoff, acc);
+        decode_pair<M, F16>(q == 0 ? bm.x : bm.z, q == 0 ? bm.y : bm.w, a0, a1, b0, b1, xr, 2 * q, lds, laneoff, acc);
     }
 }
 
@@ -144,8 +175,13 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
 // sign cursor runs on from step to step. Chunked GEMVs: a unit is NB rows; its steps go chunk by
 // chunk (NB steps per chunk pass), each row's cursor carried from its previous chunk. With NB > 4 the
 // body holds NB half-steps and the stage slots are taken modulo NB.
-template <int M, bool ACC, int NB, bool CHUNKED, bool XS>
+template <int M, bool ACC, int NB, bool CHUNKED, bool XS, bool F16>
 __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const char *lds, double *tile) {
+    static_assert(!(F16 && (ACC || XS)), "fp16 activations: fp32 outputs only");
+    // activation slice of a lane: 32 dwords of int8 or 64 dwords of fp16 (XB bytes)
+    constexpr int XW = F16 ? 64 : 32;
+    constexpr uint32_t XB = 4u * XW;
+    using A = typename std::conditional<F16, float, int>::type;
     // Chunked rows at m = 1: units of 8 rows (the activation slice is reloaded once per pass, so
     // longer passes halve those reloads), each lane summing its group terms of the unit's rows in
     // registers across passes; the rows are reduced over the wave once, at the unit's end.
@@ -173,7 +209,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     x.rsg = make_rsrc(reinterpret_cast<const uint8_t *>(p.signs) - 4, p.sign_bytes + 4u);
     x.rsc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)p.ng * 2u);
     x.rro = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
-    x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k);
+    x.rx = make_rsrc(p.x, (uint32_t)M * (uint32_t)p.k * (F16 ? 2u : 1u));
     x.ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)M * (uint32_t)p.n * 4u);
     x.racc = make_rsrc(p.acc, ACC ? (uint32_t)M * (uint32_t)p.n * (uint32_t)p.ng * 4u : 0u);
     x.rxs = make_rsrc(p.xs, XS ? (uint32_t)M * (uint32_t)p.ng * 4u : 0u);
@@ -183,7 +219,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     const int row_end = min(p.n, (u1 - p.unit_begin) * rpu);
     const uint32_t kb = (uint32_t)(p.k >> 3);  // bitmap bytes per row
 
-    uint32_t xr[M][32];
+    uint32_t xr[M][XW];
     float xsv[M];               // activation group scales of the lane's group (1 without them)
     uint32_t cur = 0;           // single-chunk: sign cursor of the next step to scan
     uint32_t ccur[NB] = {};     // chunked: sign cursor of each row of the unit being scanned
@@ -202,7 +238,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
         voff_bm = act ? (uint32_t)ql * kb + (uint32_t)jl * 16u : kOffOff;
         voff_sc = act ? (uint32_t)lane * 2u : kOffOff;  // (ql * ng + jl) = lane when ng = G
         voff_acc = act ? (uint32_t)lane * 4u : kOffOff;
-        voff_x = act ? (uint32_t)jl * 128u : kOffOff;
+        voff_x = act ? (uint32_t)jl * XB : kOffOff;
         T = (u1 - u0) * NB;
         red = make_red(NB * x.R, x.R, x.G, p.rmagic);
         cur = uniform_u32(buf_u32(x.rro, (uint32_t)row_begin * 4u));
@@ -210,13 +246,13 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
         voff_bm = (uint32_t)lane * 16u;
         voff_sc = (uint32_t)lane * 2u;
         voff_acc = (uint32_t)lane * 4u;
-        voff_x = (uint32_t)lane * 128u;
+        voff_x = (uint32_t)lane * XB;
         T = (u1 - u0) * NB * x.nch;
         red = make_red(NB, 1, 64, p.rmagic);
     }
-    load_x<M>(x, voff_x, xr);
+    load_x<M, XW>(x, voff_x, xr);
     load_xs<M, XS>(x, voff_x, xsv);
-    wait_x<M>(xr);
+    wait_x<M, XW>(xr);
     wait_xs<M, XS>(xsv);
 
     u32x4 bm[4] = {};
@@ -237,8 +273,8 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
             {
                 const int s = h - 4;
                 const bool live = s >= 0 && s < T;
-                int acc[M];
-                decode<M>(bm[jb], g[jb], xr, lds, laneoff, acc);
+                A acc[M];
+                decode<M, F16>(bm[jb], g[jb], xr, lds, laneoff, acc);
                 const int slot = (j + U - 4) % NB;  // step h - 4 within its unit (pass)
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
@@ -286,8 +322,8 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                         TG_SCHED_FENCE();
                         // the next decode pass's x slice, ahead of this half-step's prefetches
                         const int gcn = cD == x.nch - 1 ? x.glast : 64;
-                        const uint32_t vx = lane < gcn ? voff_x + (uint32_t)cD * 8192u : kOffOff;
-                        load_x<M>(x, vx, xr);
+                        const uint32_t vx = lane < gcn ? voff_x + (uint32_t)cD * 64u * XB : kOffOff;
+                        load_x<M, XW>(x, vx, xr);
                         load_xs<M, XS>(x, vx, xsv);
                     }
                 }
@@ -355,25 +391,27 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     }
 }
 
-template <int M, bool ACC, int NB, bool XS>
+template <int M, bool ACC, int NB, bool XS, bool F16>
 __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     if (p.nch == 1)
-        run_loop<M, ACC, NB, false, XS>(p, u0, u1, lds, tile);
+        run_loop<M, ACC, NB, false, XS, F16>(p, u0, u1, lds, tile);
     else
         if constexpr (M == 1) {
             if (p.nbu == kChunkRows1Fine)
-                run_loop<1, ACC, kChunkRows1Fine, true, XS>(p, u0, u1, lds, tile);
+                run_loop<1, ACC, kChunkRows1Fine, true, XS, F16>(p, u0, u1, lds, tile);
             else
-                run_loop<1, ACC, kChunkRows1, true, XS>(p, u0, u1, lds, tile);
+                run_loop<1, ACC, kChunkRows1, true, XS, F16>(p, u0, u1, lds, tile);
         } else {
-            run_loop<M, ACC, NB, true, XS>(p, u0, u1, lds, tile);
+            run_loop<M, ACC, NB, true, XS, F16>(p, u0, u1, lds, tile);
         }
 }
 
-template <int M, bool ACC, bool XS>
-__global__ __launch_bounds__((Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(GroupArgs ga) {
+// F16: fp16 activations, kF16Waves waves per CU (the 256-byte activation slices need the registers).
+template <int M, bool ACC, bool XS, bool F16 = false>
+__global__ __launch_bounds__((F16 ? 64 * kF16Waves : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
+    GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
-    constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
+    constexpr int NB = C::NB, WAVES = F16 ? kF16Waves : C::WAVES, BLOCK = 64 * WAVES;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
@@ -383,7 +421,7 @@ __global__ __launch_bounds__((Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_ke
     wave_range<WAVES>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
-    load_bitcos_tables<BLOCK>(s_tab);
+    load_bitcos_tables<BLOCK, F16>(s_tab);
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
@@ -393,7 +431,7 @@ __global__ __launch_bounds__((Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_ke
         const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_problem<M, ACC, NB, XS>(p, u, u1, lds, tile);
+        if (u < u1) run_problem<M, ACC, NB, XS, F16>(p, u, u1, lds, tile);
         u = max(u, u1);
         ++pi;
     }
@@ -410,6 +448,14 @@ hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     else
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_f16_m(const GroupArgs &g, hipStream_t s) {
+    const int blocks = grid_blocks<kF16Waves>(g);
+    if (blocks < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false, true>), dim3(blocks), dim3(64 * kF16Waves), 0, s, g);
     return hipGetLastError();
 }
 
@@ -434,6 +480,14 @@ void gemv_geometry(Problem &p, int fmt, int m, bool fine) {
     p.gmagic = (65536u + (uint32_t)p.G - 1) / (uint32_t)p.G;
     p.rmagic = (65536u + (uint32_t)p.R - 1) / (uint32_t)p.R;
     p.nunits = (p.n + p.rpu - 1) / p.rpu;
+}
+
+hipError_t launch_bitcos_f16(const GroupArgs &g, hipStream_t s) {
+    switch (g.m) {
+        case 1: return launch_f16_m<1>(g, s);
+        case 2: return launch_f16_m<2>(g, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_bitcos(const GroupArgs &g, int out, hipStream_t s) {

@@ -37,8 +37,10 @@ constexpr int popc8(uint32_t v) {
 }
 
 // Blocks of entries in decreasing size: every block then starts at a multiple of its own size, so
-// a block's base has zero bits where (window & mask) has its ones.
-constexpr Tables make_tables() {
+// a block's base has zero bits where (window & mask) has its ones. Entry bytes are `pos` for +1 and
+// `neg` for -1: the int8 weights (0x01, 0xFF), or for fp16 activations the high bytes of the binary16
+// weights +1.0 and -1.0 (0x3C, 0xBC; their low bytes are zero).
+constexpr Tables make_tables(uint64_t pos = 0x01, uint64_t neg = 0xFF) {
     Tables t{};
     uint32_t e = 0;
     for (int c = 8; c >= 0; --c) {
@@ -51,7 +53,7 @@ constexpr Tables make_tables() {
                 uint32_t rank = 0;
                 for (uint32_t i = 0; i < 8; ++i) {
                     if ((pb >> i) & 1) {
-                        const uint64_t byte = ((sc >> rank) & 1) ? 0xFFull : 0x01ull;  // -1 or +1 as int8
+                        const uint64_t byte = ((sc >> rank) & 1) ? neg : pos;
                         v |= byte << (8 * i);
                         ++rank;
                     }
@@ -65,12 +67,13 @@ constexpr Tables make_tables() {
 }
 
 __device__ const Tables kTables = make_tables();
+__device__ const Tables kTablesF16 = make_tables(0x3C, 0xBC);
 
 // Copy both tables into LDS (s_tab: kTabBytes); the caller synchronises the block afterwards. Each
 // thread issues all of its loads before any LDS write (one 8-byte load serves 8 consecutive (mask,
 // base) copies of one presence byte), so the fill costs about one memory round trip (0.7-1 us per
 // launch on MI355X, measured with a kernel that stops after the fill).
-template <int BLOCK>
+template <int BLOCK, bool F16 = false>
 __device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
     // (mask, base) copies in units of 8 consecutive copies of one presence byte (64 bytes)
     constexpr int kUnits = 256 * 32 / 8;
@@ -78,8 +81,9 @@ __device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
     constexpr int kEntVec = (kEntries + 1) / 2;  // 16-byte vectors of the entry table
     constexpr int kEntPer = (kEntVec + BLOCK - 1) / BLOCK;
     const int t = threadIdx.x;
-    const uint2 *inf = reinterpret_cast<const uint2 *>(kTables.info);
-    const uint4 *src = reinterpret_cast<const uint4 *>(kTables.ent);
+    const Tables &tab = F16 ? kTablesF16 : kTables;
+    const uint2 *inf = reinterpret_cast<const uint2 *>(tab.info);
+    const uint4 *src = reinterpret_cast<const uint4 *>(tab.ent);
     uint2 iv[kUnitPer];
     uint4 ev[kEntPer];
 #pragma unroll

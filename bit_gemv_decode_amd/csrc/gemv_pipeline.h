@@ -60,15 +60,15 @@ struct Ctx {
     int n, k, ng, nch, G, R, glast;
 };
 
-// x bytes of the lane's group (column col) for every activation row; lanes without a group read
-// nothing.
-template <int M>
-__device__ __forceinline__ void load_x(const Ctx &x, uint32_t voff, uint32_t (&xr)[M][32]) {
+// Activation slice of the lane's group for every activation row: XW dwords per row, 32 for int8
+// activations (128 bytes), 64 for fp16 ones (256 bytes); lanes without a group read nothing.
+template <int M, int XW = 32>
+__device__ __forceinline__ void load_x(const Ctx &x, uint32_t voff, uint32_t (&xr)[M][XW]) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const u32x4 v = ld4(x.rx, voff + 16u * j, (uint32_t)(mi * x.k));
+        for (int j = 0; j < XW / 4; ++j) {
+            const u32x4 v = ld4(x.rx, voff + 16u * j, (uint32_t)(mi * x.k * (XW / 32)));
             xr[mi][4 * j] = v.x;
             xr[mi][4 * j + 1] = v.y;
             xr[mi][4 * j + 2] = v.z;
@@ -78,12 +78,12 @@ __device__ __forceinline__ void load_x(const Ctx &x, uint32_t voff, uint32_t (&x
 
 // x must have arrived before a loop starts: a loop entered with x as the newest loads would get
 // the waits compiled for that entry on every iteration.
-template <int M>
-__device__ __forceinline__ void wait_x(const uint32_t (&xr)[M][32]) {
+template <int M, int XW = 32>
+__device__ __forceinline__ void wait_x(const uint32_t (&xr)[M][XW]) {
 #pragma unroll
     for (int mi = 0; mi < M; ++mi)
 #pragma unroll
-        for (int j = 0; j < 32; j += 4) asm volatile("" ::"v"(xr[mi][j]));
+        for (int j = 0; j < XW; j += 4) asm volatile("" ::"v"(xr[mi][j]));
 }
 
 // Activation group scale of the lane's group (the group whose x bytes load_x reads at voff, i.e. group
@@ -159,8 +159,8 @@ __device__ __forceinline__ void reduce_store(const Ctx &x, const Red &r, const d
 // Decode stage epilogue: the group terms (int32 sum times the group's weight scale s, times the
 // activation group scale when XS; fp64, every product exact) go to tile slot `slot` (added to what earlier chunks left there
 // when `add`); accumulator outputs are stored directly.
-template <int M, bool ACC, int NB, bool XS>
-__device__ __forceinline__ void emit(const Ctx &x, const int (&acc)[M], double s, const float (&xsv)[M],
+template <int M, bool ACC, int NB, bool XS, typename A>
+__device__ __forceinline__ void emit(const Ctx &x, const A (&acc)[M], double s, const float (&xsv)[M],
                                      double *tile, int slot, bool add, uint32_t voff_acc, uint32_t soff_acc) {
     const int lane = threadIdx.x & 63;
     if constexpr (ACC) {

@@ -29,7 +29,7 @@ struct Problem {
     const uint32_t *signs;    // BITCOS sign stream as little-endian dwords
     const uint32_t *rowoff;   // BITCOS per-row sign positions, n + 1 entries
     const uint16_t *scales;   // fp16 [n][k/128] (value path)
-    const int8_t *x;          // int8 [m][k]
+    const int8_t *x;          // int8 [m][k] (fp16 [m][k] on the fp16-activation path)
     float *y;                 // float [m][n] (value path)
     int32_t *acc;             // int32 [m][n][groups] (accumulator path)
     const float *xs;          // float [m][k/128] activation group scales (value path with them), else null
@@ -116,6 +116,12 @@ hipError_t launch_bitcos(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s);
+
+// BITCOS GEMV against fp16 activations (Problem::x then points to fp16 [m][k]; fp32 y): launches of
+// at most kF16MaxM activation rows, kF16Waves waves per CU, vector-path geometry.
+constexpr int kF16MaxM = 2;
+constexpr int kF16Waves = 8;
+hipError_t launch_bitcos_f16(const GroupArgs &g, hipStream_t s);
 
 // Per-group int8 quantisation of `groups` runs of 128 fp32 activations (one wave per group).
 hipError_t launch_quantize_x(const float *x, int64_t groups, int8_t *xq, float *xs, hipStream_t s);

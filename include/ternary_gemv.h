@@ -185,6 +185,23 @@ int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, 
                     float *y, int32_t m, void *stream);
 
 /*
+ * ternary_gemv_f16 (device, asynchronous): the BITCOS GEMV against fp16 activations ("Breaking the
+ * 1.58-bit Barrier for Ternary LLMs", Sec. II-B: ternary weights rebuilt as +-1 or 0 in 16-bit
+ * floating point and multiplied with the activations; Sec. II-D: lookup entries holding fp16
+ * weights). x16: device binary16 [m][k] bit patterns (finite values), 16-byte aligned.
+ *       y[m][n] = sum_g scale[n][g] * sum_{k in g} W[n][k] * x16[m][k]
+ *   Each group sum is accumulated in fp32 (products exact, at most two roundings per pair of
+ *   weights, so at most 128 roundings of partial sums no larger than sum_{k in g} |W x|), multiplied
+ *   by the group scale in fp64 (exact), summed over groups in fp64 and stored as fp32:
+ *       |y - y_exact| <= 2^-23 |y_exact| + 2^-17 * sum_g |scale[n][g]| * sum_{k in g} |W x|.
+ *   Launches of at most two activation rows. Non-finite activations are outside the contract.
+ *   Errors: TG_EINVAL (null or misaligned pointer, m out of range, a format other than BITCOS),
+ *   TG_EFORMAT / TG_ECORRUPT (descriptor), TG_ESHAPE (2 * m * k > 2^30), TG_EHIP.
+ */
+int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16_t *scales, const uint16_t *x16, float *y,
+                     int32_t m, void *stream);
+
+/*
  * Grouped launch: several GEMVs of one format and one activation-row count m (1 <= m <= 3; BITCOS
  * 1 <= m <= TG_MAX_M) run as
  * one persistent kernel. This is the batched form of the same operation (each GEMV is computed

@@ -260,3 +260,28 @@ def test_t5b_argument_errors_before_any_gpu_work():
     d2 = binding.TgDesc.from_buffer_copy(d)
     d2.group = 128
     assert L.ternary_gemv(ctypes.byref(d2), dummy, None, dummy, dummy, 1, None) == -4
+
+
+def test_f16_gemv_argument_errors_before_any_gpu_work():
+    L = binding.lib()
+    dummy = ctypes.c_void_p(256)
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = B.pack_bitcos(w).desc
+    # null or misaligned pointers, m out of range -> TG_EINVAL
+    assert L.ternary_gemv_f16(None, dummy, dummy, dummy, dummy, 1, None) == -1
+    for i in range(4):
+        args = [dummy] * 4
+        args[i] = None
+        assert L.ternary_gemv_f16(ctypes.byref(d), *args, 1, None) == -1
+    assert L.ternary_gemv_f16(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, None) == -1
+    assert L.ternary_gemv_f16(ctypes.byref(d), dummy, dummy, dummy, dummy, B.TG_MAX_M + 1, None) == -1
+    assert L.ternary_gemv_f16(ctypes.byref(d), dummy, dummy, ctypes.c_void_p(264), dummy, 1, None) == -1
+    assert L.ternary_gemv_f16(ctypes.byref(d), dummy, ctypes.c_void_p(257), dummy, dummy, 1, None) == -1
+    assert L.ternary_gemv_f16(ctypes.byref(d), dummy, dummy, dummy, ctypes.c_void_p(258), 1, None) == -1
+    # BITCOS only
+    for fmt in (B.FMT_5TRIT, B.FMT_2BIT):
+        d5 = B.pack(fmt, w).desc
+        assert L.ternary_gemv_f16(ctypes.byref(d5), dummy, dummy, dummy, dummy, 1, None) == -1
+    d2 = binding.TgDesc.from_buffer_copy(d)
+    d2.magic = 0
+    assert L.ternary_gemv_f16(ctypes.byref(d2), dummy, dummy, dummy, dummy, 1, None) == -4
