@@ -185,15 +185,26 @@ def activation_quant(torch, B, synth, ls, dev, steps, warmup):
     return out
 
 
-def fp16_activations(torch, B, synth, ls, dev):
-    """The BITCOS layer set against fp16 activations (ternary_gemv_f16; one launch per GEMV, replayed
-    from a graph that cycles through the 32 copies of each matrix): per-matrix time and the pass."""
-    st = torch.cuda.Stream()
-    st.wait_stream(torch.cuda.current_stream())
-    out, total_us = {}, 0.0
+def fp16_activations(torch, B, synth, ls, dev, steps, warmup):
+    """The BITCOS layer set against fp16 activations: the grouped step (tg_plan_init_f16, one launch for
+    the 224 GEMVs, one fp16 row per matrix role) and single calls (ternary_gemv_f16; one launch per
+    GEMV, replayed from a graph that cycles through the 32 copies of each matrix)."""
+    x16s = []
     for role, (name, n, k) in enumerate(LAYER):
         xf = synth.float_activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_XF))
-        x16 = torch.from_numpy(xf.astype(np.float16)).to(dev)
+        x16s.append(torch.from_numpy(xf.astype(np.float16)).to(dev))
+    mats = [(role, m) for row in ls.mats for role, m in enumerate(row)]
+    plan = B.Plan([m["w"] for _, m in mats], [x16s[r] for r, _ in mats], scales=[m["s"] for _, m in mats],
+                  ys=[m["y"] for _, m in mats], f16=True)
+    step_s = time_launches(torch, plan.run, steps, warmup) / steps
+    out = {"grouped_one_launch": {"gbs": round(ls.step_bytes / step_s / 1e9, 1),
+                                  "ms_per_step": round(step_s * 1e3, 4)}}
+    del plan
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    total_us = 0.0
+    for role, (name, n, k) in enumerate(LAYER):
+        x16 = x16s[role]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st):
             for row in ls.mats:
@@ -565,7 +576,7 @@ def main():
     out["activation_quant"] = activation_quant(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
 
     log("[bench] fp16 activations")
-    out["fp16_activations"] = fp16_activations(torch, B, synth, ls, dev)
+    out["fp16_activations"] = fp16_activations(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
 
     log("[bench] stream-read ceiling")
     ceil = stream_ceiling(torch, bd, dev)

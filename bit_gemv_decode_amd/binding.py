@@ -27,7 +27,7 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_pack_t5b", "tg_describe", "tg_validate", "tg_unpack",
            "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "ternary_gemv_f16",
            "tg_plan_table_bytes",
-           "tg_plan_init", "tg_plan_init_xs", "ternary_gemv_plan", "tg_stream_read", "tg_strerror", "tg_version"]
+           "tg_plan_init", "tg_plan_init_xs", "tg_plan_init_f16", "ternary_gemv_plan", "tg_stream_read", "tg_strerror", "tg_version"]
 
 
 class TgError(RuntimeError):
@@ -89,6 +89,9 @@ def lib():
         L.tg_plan_init_xs.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p,
                                       p, p, p, ctypes.c_int32]
         L.tg_plan_init_xs.restype = ctypes.c_int
+        L.tg_plan_init_f16.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p,
+                                       p, p, ctypes.c_int32]
+        L.tg_plan_init_f16.restype = ctypes.c_int
         L.tg_plan_table_bytes.argtypes = [ctypes.c_int32]
         L.tg_plan_table_bytes.restype = sz
         L.tg_plan_init.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p, p, p,
@@ -382,11 +385,12 @@ class Plan:
     weights: list of DeviceWeights; xs: int8 [m, k] device tensors; scales and ys (fp16 [n, k/128],
     float32 [m, n]) for fp32 outputs, or accs (int32 [m, n, k/128]) for accumulator outputs. With
     x_scales (float32 [m, k/128] per GEMV) the xs are quantised activations and every group term is
-    also multiplied by its activation group scale (tg_plan_init_xs). The plan keeps references to
-    every tensor it names, and its device table, for its lifetime.
+    also multiplied by its activation group scale (tg_plan_init_xs). With f16=True the xs are fp16
+    [m, k] activations of BITCOS GEMVs with fp32 outputs, m <= 2 (tg_plan_init_f16). The plan keeps
+    references to every tensor it names, and its device table, for its lifetime.
     """
 
-    def __init__(self, weights, xs, scales=None, ys=None, accs=None, x_scales=None):
+    def __init__(self, weights, xs, scales=None, ys=None, accs=None, x_scales=None, f16=False):
         import torch
 
         count = len(weights)
@@ -406,7 +410,7 @@ class Plan:
         m = xs[0].shape[0] if xs[0].dim() == 2 else 1
         for i, w in enumerate(weights):
             _require_cuda(w.tensor, torch.uint8, "weights")
-            _require_cuda(xs[i], torch.int8, "x")
+            _require_cuda(xs[i], torch.float16 if f16 else torch.int8, "x")
             if xs[i].shape[-1] != w.k or (xs[i].shape[0] if xs[i].dim() == 2 else 1) != m:
                 raise ValueError("every x must be [m, k] with the same m")
             if acc_mode:
@@ -433,7 +437,13 @@ class Plan:
         ptr = lambda ts: P(*[t.data_ptr() for t in ts]) if ts is not None else None
         self.plan = TgPlan()
         self._keep = (list(weights), list(xs), scales, ys, accs, x_scales)
-        if x_scales is not None:
+        if f16:
+            if acc_mode or x_scales is not None:
+                raise ValueError("fp16 plans write fp32 y only")
+            _check(L.tg_plan_init_f16(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count,
+                                      descs, ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(ys), m),
+                   "tg_plan_init_f16")
+        elif x_scales is not None:
             _check(L.tg_plan_init_xs(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count,
                                      descs, ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(x_scales),
                                      ptr(ys), m), "tg_plan_init_xs")

@@ -239,10 +239,20 @@ extern "C" size_t tg_plan_table_bytes(int32_t count) {
 
 namespace {
 
+// Plan paths (tg_plan::path).
+enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2 };
+
+// Waves of a launch on `path`.
+int path_waves(int fmt, int m, int path) {
+    return path == kPathF16 ? device_cus() * kF16Waves : plan_waves(fmt, m, path == kPathMfma);
+}
+
+// f16: the x are fp16 activations (BITCOS, fp32 outputs, m <= kF16MaxM, the fp16 kernel).
 int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                      const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
-                     const float *const *xs, float *const *y, int32_t *const *acc, int32_t m) {
+                     const float *const *xs, float *const *y, int32_t *const *acc, int32_t m, bool f16 = false) {
     if (!plan || !table || !descs || !W || !x || count < 1 || m < 1) return TG_EINVAL;
+    if (f16 && (descs[0].fmt != TG_FMT_BITCOS || acc || xs || m > kF16MaxM)) return TG_EINVAL;
     const bool acc_mode = acc != nullptr;
     const int fmt = descs[0].fmt;
     const bool t5b = fmt == TG_FMT_T5B;  // scale in the descriptor; no activation group scales
@@ -257,7 +267,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         int e = check_desc(d, 0);
         if (e) return e;
         if (d->fmt != fmt) return TG_EINVAL;
-        if (!fits_offsets(d, m)) return TG_ESHAPE;
+        if (!fits_offsets(d, m) || (f16 && (uint64_t)m * (uint64_t)d->k * 2 > (1ull << 30))) return TG_ESHAPE;
         if (!W[i] || !x[i] || ((uintptr_t)W[i] & 15) || ((uintptr_t)x[i] & 15)) return TG_EINVAL;
         if (acc_mode ? (!acc[i] || ((uintptr_t)acc[i] & 3))
                      : (!y[i] || ((uintptr_t)y[i] & 3) || (!t5b && (!scales[i] || ((uintptr_t)scales[i] & 1)))))
@@ -277,7 +287,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         w_all += wts;
         if (use_mfma(fmt, m, descs[i].k)) w_mfma += wts;
     }
-    const bool mfma = fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
+    const bool mfma =
+        !f16 && fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
+    const int path = f16 ? kPathF16 : mfma ? kPathMfma : kPathVector;
     for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma);
     {
         int64_t ub = 0;
@@ -286,7 +298,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
             ub += host[i].nunits;
         }
     }
-    if (want_fine(host, fmt, m, mfma, plan_waves(fmt, m, mfma)))
+    if (want_fine(host, fmt, m, mfma, path_waves(fmt, m, path)))
         for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, true);
     for (int32_t i = 0; i < count; ++i) rpu = std::max(rpu, (int)host[i].rpu);
     // Work order: GEMVs of one shape next to each other (by k, then n; the caller's order within a
@@ -308,7 +320,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         for (int64_t u = host[i].unit_begin; u < host[i].unit_begin + host[i].nunits; ++u)
             total_cost += unit_cost(host[i], fmt, mfma, u);
     // Contiguous unit ranges per wave, balanced by the cost model above.
-    const int nw = plan_waves(fmt, m, mfma);
+    const int nw = path_waves(fmt, m, path);
     std::vector<WaveRange> ranges((size_t)nw);
     {
         int32_t pi = 0;
@@ -344,7 +356,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     plan->rows_per_unit = rpu;
     plan->acc_mode = acc_mode ? kOutAcc : xs ? kOutYxs : kOutY;
     plan->waves = nw;
-    plan->path = mfma ? 1 : 0;
+    plan->path = path;
     plan->table = table;
     return TG_OK;
 }
@@ -364,21 +376,31 @@ extern "C" int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, i
     return plan_init_common(plan, table, table_bytes, count, descs, W, scales, xq, xs, y, nullptr, m);
 }
 
+extern "C" int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                                const void *const *W, const uint16_t *const *scales, const uint16_t *const *x16,
+                                float *const *y, int32_t m) {
+    return plan_init_common(plan, table, table_bytes, count, descs, W, scales,
+                            reinterpret_cast<const int8_t *const *>(x16), nullptr, y, nullptr, m, true);
+}
+
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
         plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs ||
-        plan->path < 0 || plan->path > 1 || (plan->path == 1 && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)))
+        plan->path < kPathVector || plan->path > kPathF16 ||
+        (plan->path == kPathMfma && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)) ||
+        (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
-    const bool mfma = plan->path == 1;
-    if (plan->waves != plan_waves(plan->fmt, plan->m, mfma)) return TG_EINVAL;  // built for another device
+    const bool mfma = plan->path == kPathMfma;
+    if (plan->waves != path_waves(plan->fmt, plan->m, plan->path)) return TG_EINVAL;  // built for another device
     g.ranges = (const WaveRange *)((const uint8_t *)plan->table + ranges_offset(plan->count));
     g.waves = plan->waves;
     g.count = plan->count;
     g.units = plan->units;
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
+    if (plan->path == kPathF16) return launch_bitcos_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     return launch(plan->fmt, g, plan->acc_mode, mfma, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
 }
 

@@ -238,7 +238,7 @@ typedef struct tg_plan {
     int32_t rows_per_unit;
     int32_t acc_mode;    /* 0: fp32 y; 1: int32 accumulator outputs; 2: fp32 y with activation group scales */
     int32_t waves;       /* waves of the launch the table's work split was made for */
-    int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS) */
+    int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2: fp16 activations */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 
@@ -252,6 +252,14 @@ int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, 
 int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                     const void *const *W, const uint16_t *const *scales, const int8_t *const *xq,
                     const float *const *xs, float *const *y, int32_t m);
+
+/* tg_plan_init for ternary_gemv_f16 outputs: every GEMV of the plan is BITCOS and takes fp16
+ * activations x16[i] (device binary16 [m][k], 16-byte aligned), 1 <= m <= 2; the launch runs the
+ * fp16 kernel (path 2) and each y is computed as ternary_gemv_f16 computes it. Errors as tg_plan_init,
+ * plus TG_EINVAL for another format or m > 2 and TG_ESHAPE for 2 * m * k > 2^30. */
+int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                     const void *const *W, const uint16_t *const *scales, const uint16_t *const *x16,
+                     float *const *y, int32_t m);
 int ternary_gemv_plan(const tg_plan *plan, void *stream);
 
 /*

@@ -285,3 +285,36 @@ def test_f16_gemv_argument_errors_before_any_gpu_work():
     d2 = binding.TgDesc.from_buffer_copy(d)
     d2.magic = 0
     assert L.ternary_gemv_f16(ctypes.byref(d2), dummy, dummy, dummy, dummy, 1, None) == -4
+
+
+def test_f16_plan_argument_errors_before_any_gpu_work():
+    L = binding.lib()
+    dummy = ctypes.c_void_p(256)
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = B.pack_bitcos(w).desc
+    descs = (binding.TgDesc * 1)(d)
+    P1 = ctypes.c_void_p * 1
+    ptrs = P1(256)
+    plan = binding.TgPlan()
+    nbytes = L.tg_plan_table_bytes(1)
+    # m outside [1, 2], null arrays or entries, misaligned activations
+    for m in (0, 3):
+        assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, m) == -1
+    assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, None, ptrs, 1) == -1
+    assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, P1(None), ptrs, 1) == -1
+    assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, P1(264), ptrs, 1) == -1
+    assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, None, ptrs, ptrs, 1) == -1
+    # BITCOS only
+    for fmt in (B.FMT_5TRIT, B.FMT_2BIT):
+        other = (binding.TgDesc * 1)(B.pack(fmt, w).desc)
+        assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, other, ptrs, ptrs, ptrs, ptrs, 1) == -1
+    # a plan claiming the fp16 path with another format, m or output mode is refused before launching
+    forged = binding.TgPlan(magic=0x4E4C5054, fmt=B.FMT_5TRIT, m=1, count=1, units=1, rows_per_unit=1,
+                            acc_mode=0, waves=8, path=2, table=256)
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
+    forged.fmt, forged.acc_mode = B.FMT_BITCOS, 1
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
+    forged.acc_mode, forged.m = 0, 3
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
+    forged.m, forged.path = 1, 3
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1

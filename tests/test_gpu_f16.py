@@ -160,3 +160,30 @@ def test_thin_batch_xs_after_f16_kernel():
         t = s.astype(np.float64)[None] * xs_ref.astype(np.float64)[:, None, :] * acc_ref.astype(np.float64)
         bound = 1e-5 * np.maximum(np.abs(y_ref.astype(np.float64)), np.abs(t).sum(-1) / np.sqrt(k // 128))
         assert np.all(np.abs(y.astype(np.float64) - y_ref.astype(np.float64)) <= bound)
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_f16_plan_matches_oracle(m):
+    # one grouped launch over GEMVs of mixed shapes (single-chunk, chunked, ragged), fp16 activations
+    dev = _dev()
+    shapes = [(96, 4096), (40, 5120), (33, 14336), (7, 2560), (130, 1024), (1, 128), (9, 25600), (300, 14336)]
+    _say(f"[gpu] f16 plan m={m}")
+    dws, ss, xs, ys, refs = [], [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.ternary(n, k, 0.4 + 0.01 * i, seed=700 + i)
+        s = synth.scales(n, k // 128, seed=700 + i)
+        x16 = synth.float_activations(m, k, seed=750 + i).astype(np.float16)
+        refs.append((w, s, x16, O.gemv_f16(w, s, x16)))
+        dws.append(B.DeviceWeights(B.pack_bitcos(w), dev))
+        ss.append(torch.from_numpy(s).to(dev))
+        xs.append(torch.from_numpy(x16).to(dev))
+        ys.append(torch.full((m, n), float("nan"), dtype=torch.float32, device=dev))
+    plan = B.Plan(dws, xs, scales=ss, ys=ys, f16=True)
+    assert plan.plan.path == 2
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (n, k) in enumerate(shapes):
+        w, s, x16, y_ref = refs[i]
+        y = ys[i].cpu().numpy()
+        err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+        assert np.all(err <= f16_bound(w, s, x16, y_ref)), f"f16 plan {n}x{k}"
