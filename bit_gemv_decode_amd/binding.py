@@ -386,7 +386,7 @@ class Plan:
     float32 [m, n]) for fp32 outputs, or accs (int32 [m, n, k/128]) for accumulator outputs. With
     x_scales (float32 [m, k/128] per GEMV) the xs are quantised activations and every group term is
     also multiplied by its activation group scale (tg_plan_init_xs). With f16=True the xs are fp16
-    [m, k] activations of BITCOS GEMVs with fp32 outputs, m <= 2 (tg_plan_init_f16). The plan keeps
+    [m, k] activations of BITCOS GEMVs with fp32 outputs, m <= 16 (tg_plan_init_f16). The plan keeps
     references to every tensor it names, and its device table, for its lifetime.
     """
 

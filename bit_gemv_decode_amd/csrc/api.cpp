@@ -179,6 +179,17 @@ extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16
     if (!fits_offsets(desc, m) || (uint64_t)m * (uint64_t)desc->k * 2 > (1ull << 30)) return TG_ESHAPE;
     hipStream_t s = (hipStream_t)stream;
     const int64_t n = desc->n, k = desc->k;
+    if (m >= kF16MfmaMinM) {  // all rows in one launch on matrix cores
+        GroupArgs g{};
+        g.one = make_problem(desc, W, scales, reinterpret_cast<const int8_t *>(x16), y, nullptr);
+        g.count = 1;
+        g.m = m;
+        g.one.unit_begin = 0;
+        mfma_geometry(g.one);
+        g.rows_per_unit = g.one.rpu;
+        g.units = g.one.nunits;
+        return launch_bitcos_mfma_f16(g, s) == hipSuccess ? TG_OK : TG_EHIP;
+    }
     for (int32_t m0 = 0; m0 < m; m0 += kF16MaxM) {
         const int32_t mt = std::min<int32_t>(kF16MaxM, m - m0);
         GroupArgs g{};
@@ -240,19 +251,21 @@ extern "C" size_t tg_plan_table_bytes(int32_t count) {
 namespace {
 
 // Plan paths (tg_plan::path).
-enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2 };
+enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2, kPathF16Mfma = 3 };
 
 // Waves of a launch on `path`.
 int path_waves(int fmt, int m, int path) {
-    return path == kPathF16 ? device_cus() * kF16Waves : plan_waves(fmt, m, path == kPathMfma);
+    if (path == kPathF16) return device_cus() * kF16Waves;
+    return plan_waves(fmt, m, path == kPathMfma || path == kPathF16Mfma);
 }
 
-// f16: the x are fp16 activations (BITCOS, fp32 outputs, m <= kF16MaxM, the fp16 kernel).
+// f16: the x are fp16 activations (BITCOS, fp32 outputs; the fp16 vector kernel for m <= kF16MaxM,
+// the fp16 matrix-core kernel from kF16MfmaMinM rows).
 int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                      const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
                      const float *const *xs, float *const *y, int32_t *const *acc, int32_t m, bool f16 = false) {
     if (!plan || !table || !descs || !W || !x || count < 1 || m < 1) return TG_EINVAL;
-    if (f16 && (descs[0].fmt != TG_FMT_BITCOS || acc || xs || m > kF16MaxM)) return TG_EINVAL;
+    if (f16 && (descs[0].fmt != TG_FMT_BITCOS || acc || xs || m > TG_MAX_M)) return TG_EINVAL;
     const bool acc_mode = acc != nullptr;
     const int fmt = descs[0].fmt;
     const bool t5b = fmt == TG_FMT_T5B;  // scale in the descriptor; no activation group scales
@@ -287,9 +300,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         w_all += wts;
         if (use_mfma(fmt, m, descs[i].k)) w_mfma += wts;
     }
-    const bool mfma =
-        !f16 && fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
-    const int path = f16 ? kPathF16 : mfma ? kPathMfma : kPathVector;
+    const bool mfma = f16 ? m >= kF16MfmaMinM
+                          : fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
+    const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : kPathVector;
     for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma);
     {
         int64_t ub = 0;
@@ -386,9 +399,11 @@ extern "C" int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, 
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
         plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs ||
-        plan->path < kPathVector || plan->path > kPathF16 ||
+        plan->path < kPathVector || plan->path > kPathF16Mfma ||
         (plan->path == kPathMfma && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)) ||
-        (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)))
+        (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)) ||
+        (plan->path == kPathF16Mfma &&
+         (plan->fmt != TG_FMT_BITCOS || plan->m < kF16MfmaMinM || plan->acc_mode != kOutY)))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
@@ -401,6 +416,8 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
     if (plan->path == kPathF16) return launch_bitcos_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
+    if (plan->path == kPathF16Mfma)
+        return launch_bitcos_mfma_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     return launch(plan->fmt, g, plan->acc_mode, mfma, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
 }
 

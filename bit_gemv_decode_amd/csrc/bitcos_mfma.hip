@@ -30,6 +30,13 @@
 // The decode per bitmap byte is the lookup of the BITCOS tables (two LDS reads); its entries are
 // already the 8 int8 weights of the B operand.
 //
+// fp16 activations ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-B and II-D: weights
+// rebuilt as +-1 or 0 in fp16; the Xe2 kernel feeds fp16 weights and activations to its matrix
+// engine): the entries come from the fp16 table (binary16 high bytes of +-1), a byte-permute widens
+// each entry's 8 bytes into 8 fp16 weights, and v_mfma_f32_16x16x32_f16 takes one presence byte's
+// weights (k = 32q + 8j .. + 7 for entry j) per product, four products per group, in fp32; the
+// activation operand is the fp16 x at the same k.
+//
 // Pipeline, in half-steps h (one group step of all T tiles each): decode + products of step h - 4,
 // sign windows of step h - 3, activation operand of step h - 2; chunk c's data is rearranged at the
 // half-step where its first sign window is read, its bitmaps and scales were loaded six half-steps
@@ -46,6 +53,8 @@ namespace tg {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = kMfmaWavesPerCu;  // waves per block (one block per CU)
 constexpr int kBlock = 64 * kWaves;
@@ -99,7 +108,7 @@ __device__ __forceinline__ void gather4(uint32_t v, uint32_t (&out)[4]) {
 template <int T>
 __device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const uint32_t (&sw)[T][3],
                                             const uint32_t (&sh)[T], const char *lds, uint32_t laneoff,
-                                            i32x4 (&b0)[T], i32x4 (&b1)[T]) {
+                                            uint2 (&e)[T][4]) {
     uint2 info[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -108,7 +117,6 @@ __device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const uint
             const uint32_t ia = __builtin_amdgcn_perm(bmw[t], laneoff, 0x0C0C0000u | ((4u + i) << 8));
             info[t][i] = *reinterpret_cast<const uint2 *>(lds + ia);
         }
-    uint2 e[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const uint32_t lo = __builtin_amdgcn_alignbit(sw[t][1], sw[t][0], sh[t]);
@@ -121,10 +129,31 @@ __device__ __forceinline__ void decode_step(const uint32_t (&bmw)[T], const uint
             if (i < 3) c = __builtin_popcount(info[t][i].x) + c;
         }
     }
+}
+
+// One tile's products for one group: C[m][row] = sum over the group's 128 k of X[m][k] W[row][k]
+// (int32 exact; fp32 with F16). xo: the activation operand parts of the step (two of 16 int8, or four
+// of 8 fp16 per lane); e: the lane's four entries (presence bytes 0..3 of its bitmap dword).
+template <bool F16>
+__device__ __forceinline__ auto tile_products(const u32x4 (&xo)[F16 ? 4 : 2], const uint2 (&e)[4]) {
+    if constexpr (F16) {
+        f32x4 c = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        b0[t] = i32x4{(int)e[t][0].x, (int)e[t][0].y, (int)e[t][1].x, (int)e[t][1].y};
-        b1[t] = i32x4{(int)e[t][2].x, (int)e[t][2].y, (int)e[t][3].x, (int)e[t][3].y};
+        for (int j = 0; j < 4; ++j) {
+            // entry bytes to the high bytes of 8 binary16 weights (low bytes zero)
+            const u32x4 w{__builtin_amdgcn_perm(e[j].x, e[j].x, 0x050C040Cu),
+                          __builtin_amdgcn_perm(e[j].x, e[j].x, 0x070C060Cu),
+                          __builtin_amdgcn_perm(e[j].y, e[j].y, 0x050C040Cu),
+                          __builtin_amdgcn_perm(e[j].y, e[j].y, 0x070C060Cu)};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v, xo[j]), __builtin_bit_cast(h8v, w), c,
+                                                       0, 0, 0);
+        }
+        return c;
+    } else {
+        const i32x4 b0{(int)e[0].x, (int)e[0].y, (int)e[1].x, (int)e[1].y};
+        const i32x4 b1{(int)e[2].x, (int)e[2].y, (int)e[3].x, (int)e[3].y};
+        i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xo[0], b0, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xo[1], b1, c, 0, 0, 0);
     }
 }
 
@@ -142,9 +171,12 @@ __device__ __forceinline__ CPos next_chunk(CPos c, int nck) {
 // loads xs[lr][g] of two groups of the next chunk with its other chunk loads, the values go to a per-wave
 // LDS buffer [group][m] when the chunk's data is rearranged, and each step's sign-window stage reads
 // the four scales of its rows m = 4q .. 4q + 3 with one 16-byte LDS read.
-template <bool ACC, bool XS>
+template <bool ACC, bool XS, bool F16>
 __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int mrows, const char *lds,
                                          uint32_t *stg) {
+    static_assert(!(F16 && (ACC || XS)), "fp16 activations: fp32 outputs only");
+    constexpr uint32_t EB = F16 ? 2u : 1u;  // activation element bytes
+    constexpr int NP = F16 ? 4 : 2;         // activation operand parts (16 bytes each) per group
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15;  // weight row within a tile; activation row of the A operand
     const int q = lane >> 4;   // quarter of the group
@@ -161,7 +193,7 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     const __amdgpu_buffer_rsrc_t rsg = make_rsrc(reinterpret_cast<const uint8_t *>(p.signs) - 4, sg_bytes);
     const __amdgpu_buffer_rsrc_t rro = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.scales, ACC ? 0u : (uint32_t)p.n * (uint32_t)ng * 2u);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)mrows * (uint32_t)p.k);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)mrows * (uint32_t)p.k * EB);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, ACC ? 0u : (uint32_t)mrows * (uint32_t)p.n * 4u);
     const __amdgpu_buffer_rsrc_t racc =
         make_rsrc(p.acc, ACC ? (uint32_t)mrows * (uint32_t)p.n * (uint32_t)ng * 4u : 0u);
@@ -176,7 +208,7 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     }
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const uint32_t m_odd = (q & 1) ? ~0u : 0u, m_hi = (q >> 1) ? ~0u : 0u;
-    const uint32_t voff_x = lr < mrows ? (uint32_t)lr * (uint32_t)p.k + 32u * (uint32_t)q : kOffOff;
+    const uint32_t voff_x = lr < mrows ? ((uint32_t)lr * (uint32_t)p.k + 32u * (uint32_t)q) * EB : kOffOff;
     // this lane's row slot in the staging buffer, per tile
     uint32_t *stg_row[kT];
 #pragma unroll
@@ -199,7 +231,7 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     uint32_t bms[2][kT] = {}, sws[2][kT][3] = {}, shs[2][kT] = {}, scs[2][kT] = {};
     uint32_t rawx[2] = {};          // XS: xs[lr][g] of groups 2q, 2q + 1 of the next chunk as loaded
     u32x4 xss[2] = {};              // XS: step stage, xs[4q + i][g] of the step's group
-    u32x4 xa[4] = {}, xb[4] = {};
+    u32x4 xo[4][NP] = {};            // activation operand of the step, by step slot
     double facc[kT][4];
 #pragma unroll
     for (int t = 0; t < kT; ++t)
@@ -286,18 +318,15 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
                 const CPos c = j < 4 ? prev : cp;
                 const bool live = j < 4 ? live_prev : live_cur;
                 const int sl = j & 1;  // slot of step h - 4
-                i32x4 b0[kT], b1[kT], cc[kT];
-                decode_step<kT>(bms[sl], sws[sl], shs[sl], lds, laneoff, b0, b1);
+                uint2 e[kT][4];
+                decode_step<kT>(bms[sl], sws[sl], shs[sl], lds, laneoff, e);
+                decltype(tile_products<F16>(xo[0], e[0])) cc[kT];
 #pragma unroll
-                for (int t = 0; t < kT; ++t) {
-                    cc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xa[j & 3], b0[t], i32x4{0, 0, 0, 0}, 0, 0,
-                                                                  0);
-                    cc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)xb[j & 3], b1[t], cc[t], 0, 0, 0);
-                }
+                for (int t = 0; t < kT; ++t) cc[t] = tile_products<F16>(xo[j & 3], e[t]);
                 const int g = c.cu * kCG + pos;
 #pragma unroll
                 for (int t = 0; t < kT; ++t) {
-                    const i32x4 cv = cc[t];
+                    const auto cv = cc[t];
                     const int row = c.row + 16 * t + lr;
                     if constexpr (ACC) {
                         // acc[m][row][g]: the unit's first row and the group go in the scalar offset
@@ -350,9 +379,9 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
                 const int pos = (j - 2) & 7;
                 const CPos c = j < 2 ? prev : cp;
                 const bool live = j < 2 ? live_prev : live_cur;
-                const uint32_t soff = live_or_dead(live, (uint32_t)(c.cu * kCG + pos) * 128u);
-                xa[(j + 2) & 3] = ld4(rx, voff_x, soff);
-                xb[(j + 2) & 3] = ld4(rx, voff_x + 16u, soff);
+                const uint32_t soff = live_or_dead(live, (uint32_t)(c.cu * kCG + pos) * 128u * EB);
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) xo[(j + 2) & 3][pp] = ld4(rx, voff_x + 16u * pp, soff);
             }
             TG_SCHED_FENCE();
             if (j == 3) {
@@ -434,7 +463,7 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     }
 }
 
-template <bool ACC, bool XS>
+template <bool ACC, bool XS, bool F16 = false>
 __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
     constexpr uint32_t kWaveDwords = kStageDwords + (XS ? kXsDwords : 0u);
     __shared__ uint4 s_tab[kTabBytes / 16];
@@ -446,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
     wave_range<kWaves>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     const Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
-    load_bitcos_tables<kBlock>(s_tab);
+    load_bitcos_tables<kBlock, F16>(s_tab);
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     uint32_t *stg = s_stage + wave * kWaveDwords;
@@ -456,7 +485,7 @@ __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
         const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_mfma<ACC, XS>(p, u, u1, ga.m, lds, stg);
+        if (u < u1) run_mfma<ACC, XS, F16>(p, u, u1, ga.m, lds, stg);
         u = max(u, u1);
         ++pi;
     }
@@ -487,6 +516,14 @@ hipError_t launch_bitcos_mfma(const GroupArgs &g, int out, hipStream_t s) {
         hipLaunchKernelGGL((bitcos_mfma_kernel<false, true>), dim3(blocks), dim3(kBlock), 0, s, g);
     else
         hipLaunchKernelGGL((bitcos_mfma_kernel<false, false>), dim3(blocks), dim3(kBlock), 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_bitcos_mfma_f16(const GroupArgs &g, hipStream_t s) {
+    if (g.m < 1 || g.m > TG_MAX_M) return hipErrorInvalidValue;
+    const int blocks = grid_blocks<kWaves>(g);
+    if (blocks < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bitcos_mfma_kernel<false, false, true>), dim3(blocks), dim3(kBlock), 0, s, g);
     return hipGetLastError();
 }
 

@@ -122,6 +122,10 @@ hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s);
 constexpr int kF16MaxM = 2;
 constexpr int kF16Waves = 8;
 hipError_t launch_bitcos_f16(const GroupArgs &g, hipStream_t s);
+// ... and on matrix cores (the thin-batch kernel with fp16 operands, mfma_geometry, 1 <= m <= 16),
+// taken from kF16MfmaMinM activation rows.
+constexpr int kF16MfmaMinM = 3;
+hipError_t launch_bitcos_mfma_f16(const GroupArgs &g, hipStream_t s);
 
 // Per-group int8 quantisation of `groups` runs of 128 fp32 activations (one wave per group).
 hipError_t launch_quantize_x(const float *x, int64_t groups, int8_t *xq, float *xs, hipStream_t s);

@@ -190,11 +190,14 @@ int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, 
  * floating point and multiplied with the activations; Sec. II-D: lookup entries holding fp16
  * weights). x16: device binary16 [m][k] bit patterns (finite values), 16-byte aligned.
  *       y[m][n] = sum_g scale[n][g] * sum_{k in g} W[n][k] * x16[m][k]
- *   Each group sum is accumulated in fp32 (products exact, at most two roundings per pair of
- *   weights, so at most 128 roundings of partial sums no larger than sum_{k in g} |W x|), multiplied
- *   by the group scale in fp64 (exact), summed over groups in fp64 and stored as fp32:
+ *   Each group sum is accumulated in fp32 (products exact, at most 128 roundings of partial sums no
+ *   larger than sum_{k in g} |W x|), multiplied by the group scale in fp64 (exact), summed over
+ *   groups in fp64 and stored as fp32:
  *       |y - y_exact| <= 2^-23 |y_exact| + 2^-17 * sum_g |scale[n][g]| * sum_{k in g} |W x|.
- *   Launches of at most two activation rows. Non-finite activations are outside the contract.
+ *   1 <= m <= TG_MAX_M. Paths: m <= 2 runs the vector kernel (v_dot2_f32_f16, one launch per two
+ *   rows); from m = 3 one launch takes all rows on matrix cores (v_mfma_f32_16x16x32_f16, the decoded
+ *   fp16 weights as the B operand, X padded to 16 rows as A). Non-finite activations are outside the
+ *   contract.
  *   Errors: TG_EINVAL (null or misaligned pointer, m out of range, a format other than BITCOS),
  *   TG_EFORMAT / TG_ECORRUPT (descriptor), TG_ESHAPE (2 * m * k > 2^30), TG_EHIP.
  */
@@ -238,7 +241,8 @@ typedef struct tg_plan {
     int32_t rows_per_unit;
     int32_t acc_mode;    /* 0: fp32 y; 1: int32 accumulator outputs; 2: fp32 y with activation group scales */
     int32_t waves;       /* waves of the launch the table's work split was made for */
-    int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2: fp16 activations */
+    int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2 / 3: fp16
+                            activations on the vector / matrix-core kernel */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 
@@ -254,9 +258,10 @@ int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, int32_t coun
                     const float *const *xs, float *const *y, int32_t m);
 
 /* tg_plan_init for ternary_gemv_f16 outputs: every GEMV of the plan is BITCOS and takes fp16
- * activations x16[i] (device binary16 [m][k], 16-byte aligned), 1 <= m <= 2; the launch runs the
- * fp16 kernel (path 2) and each y is computed as ternary_gemv_f16 computes it. Errors as tg_plan_init,
- * plus TG_EINVAL for another format or m > 2 and TG_ESHAPE for 2 * m * k > 2^30. */
+ * activations x16[i] (device binary16 [m][k], 16-byte aligned), 1 <= m <= TG_MAX_M; the launch runs
+ * the fp16 vector kernel (path 2, m <= 2) or the fp16 matrix-core kernel (path 3, m >= 3), and each y
+ * is computed as ternary_gemv_f16 computes it. Errors as tg_plan_init, plus TG_EINVAL for another
+ * format and TG_ESHAPE for 2 * m * k > 2^30. */
 int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                      const void *const *W, const uint16_t *const *scales, const uint16_t *const *x16,
                      float *const *y, int32_t m);

@@ -297,8 +297,8 @@ def test_f16_plan_argument_errors_before_any_gpu_work():
     ptrs = P1(256)
     plan = binding.TgPlan()
     nbytes = L.tg_plan_table_bytes(1)
-    # m outside [1, 2], null arrays or entries, misaligned activations
-    for m in (0, 3):
+    # m outside [1, 16], null arrays or entries, misaligned activations
+    for m in (0, 17):
         assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, m) == -1
     assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, None, ptrs, 1) == -1
     assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, P1(None), ptrs, 1) == -1
@@ -316,5 +316,9 @@ def test_f16_plan_argument_errors_before_any_gpu_work():
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
     forged.acc_mode, forged.m = 0, 3
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
-    forged.m, forged.path = 1, 3
+    forged.m, forged.path = 2, 3  # the fp16 matrix-core path starts at m = 3
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
+    forged.m, forged.acc_mode = 4, 2
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
+    forged.acc_mode, forged.path = 0, 4
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1

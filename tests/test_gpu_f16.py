@@ -62,10 +62,13 @@ def run_f16(w, s, x16, label="", exact_check=True):
 
 # (n, k, zero density, m): single-chunk rows (k <= 8192, R = 64 / ng rows per step) with ragged row
 # counts, chunked rows (k > 8192: coarse 8-row units, fine 2-row units when the units are few), one
-# and two activation rows per launch, and m = 3 (launches of two rows and one).
+# and two activation rows per launch on the vector kernel; from m = 3 the matrix-core kernel (16-row
+# tiles, 8-group chunks: ragged tiles, a partial last chunk, m up to 16).
 SHAPES = [(1, 128, 0.42, 1), (3, 256, 0.0, 2), (5, 640, 1.0, 1), (37, 4096, 0.4, 1), (129, 5120, 0.47, 2),
           (17, 14336, 0.44, 1), (9, 25600, 0.47, 2), (64, 2560, 0.95, 1), (130, 1024, 0.515, 3),
-          (600, 14336, 0.4, 1), (301, 8320, 0.3, 2), (2051, 4096, 0.44, 1)]
+          (600, 14336, 0.4, 1), (301, 8320, 0.3, 2), (2051, 4096, 0.44, 1),
+          (1, 128, 0.4, 3), (33, 1152, 0.44, 4), (70, 4096, 0.0, 5), (97, 14336, 0.44, 8), (40, 2560, 1.0, 16),
+          (300, 4224, 0.47, 16), (15, 25600, 0.47, 7)]
 
 
 @pytest.mark.parametrize("n,k,z,m", SHAPES, ids=[f"{n}x{k}_z{z}_m{m}" for n, k, z, m in SHAPES])
@@ -93,6 +96,21 @@ def test_f16_integer_activations_match_the_int8_gemv():
     assert np.array_equal(y16, y8.cpu().numpy())
 
 
+def test_f16_integer_activations_match_the_int8_thin_batch():
+    # the same on the matrix-core kernels (m = 4): fp32 group sums of integers are exact, and both
+    # paths add the same fp64 terms in the same order
+    n, k = 77, 14336
+    w = synth.ternary(n, k, 0.44, seed=43)
+    s = synth.scales(n, k // 128, seed=43)
+    x8 = synth.activations(4, k, seed=43)
+    dev = _dev()
+    y16, y_ref = run_f16(w, s, x8.astype(np.float16), label="integer m=4")
+    dw = B.DeviceWeights(B.pack_bitcos(w), dev)
+    y8 = B.ternary_gemv(dw, torch.from_numpy(s).to(dev), torch.from_numpy(x8).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(y16, y8.cpu().numpy())
+
+
 def test_f16_whole_range_values():
     # fp16 activations drawn over every finite bit pattern (subnormals, the largest normal), with
     # weight rows of all-zero, all +1, all -1 and a single -1 at the last column
@@ -110,6 +128,9 @@ def test_f16_whole_range_values():
     w[3, k - 1] = -1
     s = synth.scales(n, k // 128, seed=12)
     y, y_ref = run_f16(w, s, x16, label="whole range")
+    assert np.all(y[:, 0] == 0.0)
+    x4 = np.concatenate([x16, -x16[::-1]])  # the matrix-core path
+    y, y_ref = run_f16(w, s, x4, label="whole range m=4")
     assert np.all(y[:, 0] == 0.0)
 
 
@@ -162,7 +183,7 @@ def test_thin_batch_xs_after_f16_kernel():
         assert np.all(np.abs(y.astype(np.float64) - y_ref.astype(np.float64)) <= bound)
 
 
-@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("m", [1, 2, 4])
 def test_f16_plan_matches_oracle(m):
     # one grouped launch over GEMVs of mixed shapes (single-chunk, chunked, ragged), fp16 activations
     dev = _dev()
@@ -179,7 +200,7 @@ def test_f16_plan_matches_oracle(m):
         xs.append(torch.from_numpy(x16).to(dev))
         ys.append(torch.full((m, n), float("nan"), dtype=torch.float32, device=dev))
     plan = B.Plan(dws, xs, scales=ss, ys=ys, f16=True)
-    assert plan.plan.path == 2
+    assert plan.plan.path == (2 if m <= 2 else 3)
     plan.run()
     torch.cuda.synchronize()
     for i, (n, k) in enumerate(shapes):
