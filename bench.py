@@ -278,14 +278,18 @@ def graph_call_us(torch, calls, reps=5):
     return round(secs / (reps * len(calls)) * 1e6, 3)
 
 
-def sustained(torch, B, dws, xs, ss, ys, launches=5):
-    """One grouped launch over all GEMVs: packed bytes per second and ms per launch."""
-    plan = B.Plan(dws, xs, scales=ss, ys=ys)
+PATHS = {0: "vector", 1: "matrix-core", 2: "fp16 vector", 3: "fp16 matrix-core"}
+
+
+def sustained(torch, B, dws, xs, ss, ys, launches=5, f16=False):
+    """One grouped launch over all GEMVs: packed bytes per second and ms per launch (f16: fp16
+    activations)."""
+    plan = B.Plan(dws, xs, scales=ss, ys=ys, f16=f16)
     settle(torch, plan.run)
     secs = time_launches(torch, plan.run, launches, 0)
     total = sum(packed_bytes(d) for d in dws)
     return {"gbs": round(total * launches / secs / 1e9, 1), "ms_per_launch": round(secs / launches * 1e3, 4),
-            "bytes_per_launch": total, "path": "matrix-core" if plan.plan.path == 1 else "vector"}
+            "bytes_per_launch": total, "path": PATHS[plan.plan.path]}
 
 
 def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label=""):
@@ -337,7 +341,8 @@ def suite_single(torch, B, synth, dev, n, k, z, reps, fmts, rounds=5, m=1, label
 
 
 def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
-    """gate 14336x4096 and down 4096x14336 at z = 0.44, BITCOS, activation rows m in `ms`."""
+    """gate 14336x4096 and down 4096x14336 at z = 0.44, BITCOS, activation rows m in `ms`: int8
+    activations (per-call and grouped) and fp16 activations (grouped)."""
     out = {}
     for name, n, k, role in (("gate", 14336, 4096, 4), ("down", 4096, 14336, 6)):
         w = synth.ternary(n, k, 0.44, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
@@ -350,10 +355,14 @@ def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
             calls = [(lambda d=dws[i % reps]: B.ternary_gemv(d, s, x, y)) for i in range(max(200, reps))]
             pc = per_call_us(torch, calls)
             pc["graph_us_per_call"] = graph_call_us(torch, calls)
+            x16 = torch.from_numpy(synth.float_activations(m, k, seed=m).astype(np.float16)).to(dev)
+            sh = sustained(torch, B, dws, [x16] * reps, [s] * reps, [y] * reps, f16=True)
             out[f"{name}_m{m}"] = {"n": n, "k": k, "m": m, "path": st["path"],
                                    "sustained_gbs": st["gbs"], "sustained_us_per_gemv": round(st["ms_per_launch"] * 1e3 / reps, 3),
                                    "per_call": pc, "packed_bytes": packed_bytes(dws[0]), "x_bytes": m * k,
-                                   "y_bytes": 4 * m * n}
+                                   "y_bytes": 4 * m * n,
+                                   "fp16": {"path": sh["path"], "sustained_gbs": sh["gbs"],
+                                            "sustained_us_per_gemv": round(sh["ms_per_launch"] * 1e3 / reps, 3)}}
         del dws
         torch.cuda.empty_cache()
     log("[suite] thin batch done")
