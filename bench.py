@@ -584,6 +584,13 @@ def main():
     log("[bench] float activations: quantiser and GEMV with activation group scales")
     out["activation_quant"] = activation_quant(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
 
+    log("[bench] BITCOS nibble-keyed decode")
+    pn = ls.plan(B).set_decode(B.DECODE_NIBBLE)
+    n_n = max(3, args.steps // 2)
+    sn = time_launches(torch, pn.run, n_n, args.warmup)
+    out["nibble_decode"] = {"gbs": round(ls.step_bytes * n_n / sn / 1e9, 1), "ms_per_step": round(sn / n_n * 1e3, 4)}
+    del pn
+
     log("[bench] fp16 activations")
     out["fp16_activations"] = fp16_activations(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
 

@@ -20,6 +20,7 @@ TG_HEADER_BYTES = 256
 FMT_BITCOS, FMT_5TRIT, FMT_2BIT, FMT_T5B = 1, 2, 3, 4
 FMT_NAMES = {FMT_BITCOS: "bitcos", FMT_5TRIT: "5trit", FMT_2BIT: "2bit", FMT_T5B: "t5b"}
 T5B_BLOCK = 160
+DECODE_BYTE, DECODE_NIBBLE = 0, 1
 ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4: "TG_EFORMAT",
           -5: "TG_ECORRUPT", -6: "TG_ENOSPACE", -7: "TG_EHIP"}
 
@@ -27,7 +28,7 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_pack_t5b", "tg_describe", "tg_validate", "tg_unpack",
            "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "ternary_gemv_f16",
            "tg_plan_table_bytes",
-           "tg_plan_init", "tg_plan_init_xs", "tg_plan_init_f16", "ternary_gemv_plan", "tg_stream_read", "tg_strerror", "tg_version"]
+           "tg_plan_init", "tg_plan_init_xs", "tg_plan_init_f16", "ternary_gemv_plan", "tg_plan_set_decode", "tg_stream_read", "tg_strerror", "tg_version"]
 
 
 class TgError(RuntimeError):
@@ -50,7 +51,7 @@ class TgPlan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("fmt", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("count", ctypes.c_int32), ("units", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
                 ("acc_mode", ctypes.c_int32), ("waves", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("table", ctypes.c_void_p)]
+                ("decode", ctypes.c_int32), ("table", ctypes.c_void_p)]
 
 
 _lib = None
@@ -92,6 +93,8 @@ def lib():
         L.tg_plan_init_f16.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p,
                                        p, p, ctypes.c_int32]
         L.tg_plan_init_f16.restype = ctypes.c_int
+        L.tg_plan_set_decode.argtypes = [ctypes.POINTER(TgPlan), ctypes.c_int32]
+        L.tg_plan_set_decode.restype = ctypes.c_int
         L.tg_plan_table_bytes.argtypes = [ctypes.c_int32]
         L.tg_plan_table_bytes.restype = sz
         L.tg_plan_init.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p, p, p,
@@ -451,6 +454,11 @@ class Plan:
             _check(L.tg_plan_init(ctypes.byref(self.plan), ctypes.c_void_p(self.table.data_ptr()), nbytes, count,
                                   descs, ptr([w.tensor for w in weights]), ptr(scales), ptr(xs), ptr(ys), ptr(accs),
                                   m), "tg_plan_init")
+
+    def set_decode(self, decode: int):
+        """BITCOS decode strategy: DECODE_BYTE (default) or DECODE_NIBBLE (tg_plan_set_decode)."""
+        _check(lib().tg_plan_set_decode(ctypes.byref(self.plan), decode), "tg_plan_set_decode")
+        return self
 
     def run(self, stream=None):
         _check(lib().ternary_gemv_plan(ctypes.byref(self.plan), _stream_handle(stream)), "ternary_gemv_plan")

@@ -396,6 +396,27 @@ extern "C" int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, 
                             reinterpret_cast<const int8_t *const *>(x16), nullptr, y, nullptr, m, true);
 }
 
+namespace {
+
+// Whether a plan may run the nibble-keyed decode.
+bool nibble_ok(const tg_plan *p) {
+    return p->fmt == TG_FMT_BITCOS && p->m == 1 && p->path == kPathVector &&
+           (p->acc_mode == kOutY || p->acc_mode == kOutAcc);
+}
+
+}  // namespace
+
+extern "C" int tg_plan_set_decode(tg_plan *plan, int32_t decode) {
+    if (!plan || plan->magic != TG_PLAN_MAGIC) return TG_EINVAL;
+    if (decode == TG_DECODE_BYTE) {
+        plan->decode = decode;
+        return TG_OK;
+    }
+    if (decode != TG_DECODE_NIBBLE || !nibble_ok(plan)) return TG_EINVAL;
+    plan->decode = decode;
+    return TG_OK;
+}
+
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
         plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs ||
@@ -403,7 +424,8 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
         (plan->path == kPathMfma && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)) ||
         (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)) ||
         (plan->path == kPathF16Mfma &&
-         (plan->fmt != TG_FMT_BITCOS || plan->m < kF16MfmaMinM || plan->acc_mode != kOutY)))
+         (plan->fmt != TG_FMT_BITCOS || plan->m < kF16MfmaMinM || plan->acc_mode != kOutY)) ||
+        (plan->decode != TG_DECODE_BYTE && (plan->decode != TG_DECODE_NIBBLE || !nibble_ok(plan))))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
@@ -415,6 +437,8 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     g.units = plan->units;
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
+    if (plan->decode == TG_DECODE_NIBBLE)
+        return launch_bitcos_nibble(g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->path == kPathF16) return launch_bitcos_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->path == kPathF16Mfma)
         return launch_bitcos_mfma_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;

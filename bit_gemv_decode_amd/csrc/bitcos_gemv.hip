@@ -31,6 +31,11 @@
 //     (exact in fp64) goes to an LDS tile; once per unit the tile's rows are summed (fp64, DPP) and
 //     stored as fp32. Chunked rows at m = 1 keep those terms in registers instead (one fp64 per row
 //     of the unit and lane) and reduce them over the wave at the unit's end.
+//   * alternative decode (NIB, Sec. II-D, Eq. 4): the Xe2 kernel's nibble-keyed lookup, a 256-entry
+//     table keyed by a presence nibble and the next four compact signs, each entry the nibble's 4 int8
+//     weights; one conflict-free 4-byte LDS read and one v_dot4_i32_i8 per nibble, with the sign
+//     cursor advanced by the nibble's popcount. Selected per grouped launch for comparison; it takes
+//     one LDS round trip per nibble but about twice the VALU work per weight of the byte-keyed decode.
 //   * fp16 activations (Sec. II-B: the weights rebuilt as +-1 or 0 in 16-bit floating point; Sec.
 //     II-D: lookup entries holding fp16 weights): the same lookups on a second table whose entry bytes
 //     are the binary16 high bytes of +1.0 and -1.0 (low bytes zero), so one byte-permute turns two
@@ -90,11 +95,32 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float acc) {
 // Two bitmap dwords (64 weights) of decode. lo*/hi* hold the sign-stream bits starting 3 bits before
 // each dword's first sign. All eight per-byte (mask, base) reads go out first, then all eight entry
 // reads, then the dot products: two LDS round trips for the 64 weights.
-// With F16, entries come from the fp16 table and xr holds fp16 activations (two per dword).
-template <int M, bool F16, int XW, typename A>
+// With F16, entries come from the fp16 table and xr holds fp16 activations (two per dword). With NIB
+// the lookups are nibble-keyed instead (int8 only).
+template <int M, bool F16, bool NIB, int XW, typename A>
 __device__ __forceinline__ void decode_pair(uint32_t bma, uint32_t bmb, uint32_t loa, uint32_t hia, uint32_t lob,
                                             uint32_t hib, const uint32_t (&xr)[M][XW], int d, const char *lds,
                                             uint32_t laneoff, A (&acc)[M]) {
+    if constexpr (NIB) {
+        static_assert(!F16, "nibble-keyed decode: int8 activations");
+        const uint32_t lane4 = laneoff >> 1;  // copy (lane % 32) of an entry
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t bm = h ? bmb : bma, lo = h ? lob : loa, hi = h ? hib : hia;
+            uint32_t c = 3;  // the dword's first sign sits at bit 3 of its window
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t nb = (bm >> (4 * j)) & 15u;
+                // c <= 3 + 28: the nibble's signs start inside the 64-bit window's low 35 bits
+                const uint32_t sg = __builtin_amdgcn_alignbit(hi, lo, c) & 15u;
+                const uint32_t ent = *reinterpret_cast<const uint32_t *>(lds + ((sg << 11) | (nb << 7) | lane4));
+                if (j < 7) c = __builtin_popcount(nb) + c;
+#pragma unroll
+                for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(ent, xr[mi][8 * d + 8 * h + j], acc[mi]);
+            }
+        }
+        return;
+    }
     uint2 info[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -143,7 +169,7 @@ __device__ __forceinline__ void decode_pair(uint32_t bma, uint32_t bmb, uint32_t
 }
 
 // Sums of the lane's 128 weights times x, per activation row (int32; fp32 with F16).
-template <int M, bool F16, int XW, typename A>
+template <int M, bool F16, bool NIB, int XW, typename A>
 __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const uint32_t (&xr)[M][XW],
                                        const char *lds, uint32_t laneoff, A (&acc)[M]) {
 #pragma unroll
@@ -159,7 +185,7 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
         const uint32_t pc = __builtin_popcount(q == 0 ? bm.x : bm.z);
         const uint64_t w01 = ((uint64_t)a1 << 32) | a0, w12 = ((uint64_t)a2 << 32) | a1;
         const uint32_t b0 = (uint32_t)(w01 >> pc), b1 = (uint32_t)(w12 >> pc);
-        decode_pair<M, F16>(q == 0 ? bm.x : bm.z, q == 0 ? bm.y : bm.w, a0, a1, b0, b1, xr, 2 * q, lds, laneoff, acc);
+        decode_pair<M, F16, NIB>(q == 0 ? bm.x : bm.z, q == 0 ? bm.y : bm.w, a0, a1, b0, b1, xr, 2 * q, lds, laneoff, acc);
     }
 }
 
@@ -175,7 +201,7 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
 // sign cursor runs on from step to step. Chunked GEMVs: a unit is NB rows; its steps go chunk by
 // chunk (NB steps per chunk pass), each row's cursor carried from its previous chunk. With NB > 4 the
 // body holds NB half-steps and the stage slots are taken modulo NB.
-template <int M, bool ACC, int NB, bool CHUNKED, bool XS, bool F16>
+template <int M, bool ACC, int NB, bool CHUNKED, bool XS, bool F16, bool NIB>
 __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     static_assert(!(F16 && (ACC || XS)), "fp16 activations: fp32 outputs only");
     // activation slice of a lane: 32 dwords of int8 or 64 dwords of fp16 (XB bytes)
@@ -274,7 +300,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                 const int s = h - 4;
                 const bool live = s >= 0 && s < T;
                 A acc[M];
-                decode<M, F16>(bm[jb], g[jb], xr, lds, laneoff, acc);
+                decode<M, F16, NIB>(bm[jb], g[jb], xr, lds, laneoff, acc);
                 const int slot = (j + U - 4) % NB;  // step h - 4 within its unit (pass)
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
@@ -391,23 +417,24 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     }
 }
 
-template <int M, bool ACC, int NB, bool XS, bool F16>
+template <int M, bool ACC, int NB, bool XS, bool F16, bool NIB>
 __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     if (p.nch == 1)
-        run_loop<M, ACC, NB, false, XS, F16>(p, u0, u1, lds, tile);
+        run_loop<M, ACC, NB, false, XS, F16, NIB>(p, u0, u1, lds, tile);
     else
         if constexpr (M == 1) {
             if (p.nbu == kChunkRows1Fine)
-                run_loop<1, ACC, kChunkRows1Fine, true, XS, F16>(p, u0, u1, lds, tile);
+                run_loop<1, ACC, kChunkRows1Fine, true, XS, F16, NIB>(p, u0, u1, lds, tile);
             else
-                run_loop<1, ACC, kChunkRows1, true, XS, F16>(p, u0, u1, lds, tile);
+                run_loop<1, ACC, kChunkRows1, true, XS, F16, NIB>(p, u0, u1, lds, tile);
         } else {
-            run_loop<M, ACC, NB, true, XS, F16>(p, u0, u1, lds, tile);
+            run_loop<M, ACC, NB, true, XS, F16, NIB>(p, u0, u1, lds, tile);
         }
 }
 
 // F16: fp16 activations, kF16Waves waves per CU (the 256-byte activation slices need the registers).
-template <int M, bool ACC, bool XS, bool F16 = false>
+// NIB: the nibble-keyed decode (its 32 KB table replaces the byte-keyed tables in LDS).
+template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false>
 __global__ __launch_bounds__((F16 ? 64 * kF16Waves : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
     GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
@@ -421,7 +448,10 @@ __global__ __launch_bounds__((F16 ? 64 * kF16Waves : Cfg<M, TG_FMT_BITCOS>::BLOC
     wave_range<WAVES>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
-    load_bitcos_tables<BLOCK, F16>(s_tab);
+    if constexpr (NIB)
+        load_nib_table<BLOCK>(s_tab);
+    else
+        load_bitcos_tables<BLOCK, F16>(s_tab);
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
@@ -431,7 +461,7 @@ __global__ __launch_bounds__((F16 ? 64 * kF16Waves : Cfg<M, TG_FMT_BITCOS>::BLOC
         const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_problem<M, ACC, NB, XS, F16>(p, u, u1, lds, tile);
+        if (u < u1) run_problem<M, ACC, NB, XS, F16, NIB>(p, u, u1, lds, tile);
         u = max(u, u1);
         ++pi;
     }
@@ -480,6 +510,18 @@ void gemv_geometry(Problem &p, int fmt, int m, bool fine) {
     p.gmagic = (65536u + (uint32_t)p.G - 1) / (uint32_t)p.G;
     p.rmagic = (65536u + (uint32_t)p.R - 1) / (uint32_t)p.R;
     p.nunits = (p.n + p.rpu - 1) / p.rpu;
+}
+
+hipError_t launch_bitcos_nibble(const GroupArgs &g, int out, hipStream_t s) {
+    using C = Cfg<1, TG_FMT_BITCOS>;
+    if (g.m != 1 || (out != kOutY && out != kOutAcc)) return hipErrorInvalidValue;
+    const int blocks = grid_blocks<C::WAVES>(g);
+    if (blocks < 1) return hipErrorInvalidValue;
+    if (out == kOutAcc)
+        hipLaunchKernelGGL((bitcos_gemv_kernel<1, true, false, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    else
+        hipLaunchKernelGGL((bitcos_gemv_kernel<1, false, false, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    return hipGetLastError();
 }
 
 hipError_t launch_bitcos_f16(const GroupArgs &g, hipStream_t s) {

@@ -111,5 +111,55 @@ __device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
     }
 }
 
+
+// Nibble-keyed lookup ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-D, Eq. 4): the key is
+// a presence nibble n (bits 0..3) and the next four compact sign bits s (bits 4..7); the entry holds
+// the nibble's 4 weights as int8, weight i = 0 where n_i = 0, else -1 or +1 by sign bit r_i of s, where
+// r_i counts the present weights before i. 256 entries of 4 bytes, kept in LDS in 32 copies: entry
+// key of copy c at byte (key << 7) | (c << 2), so lane l reading copy l % 32 never conflicts.
+constexpr uint32_t kNibCopies = 32;
+constexpr uint32_t kNibBytes = 256 * 4 * kNibCopies;
+
+struct NibTable {
+    uint32_t ent[256];
+};
+
+constexpr NibTable make_nib_table() {
+    NibTable t{};
+    for (uint32_t key = 0; key < 256; ++key) {
+        const uint32_t n = key & 15u, sg = key >> 4;
+        uint32_t v = 0, r = 0;
+        for (uint32_t i = 0; i < 4; ++i) {
+            if ((n >> i) & 1u) {
+                v |= (((sg >> r) & 1u) ? 0xFFu : 0x01u) << (8 * i);
+                ++r;
+            }
+        }
+        t.ent[key] = v;
+    }
+    return t;
+}
+
+__device__ const NibTable kNibTable = make_nib_table();
+
+// Copy the nibble table's 32 copies into LDS (s_tab: at least kNibBytes); the caller synchronises.
+template <int BLOCK>
+__device__ __forceinline__ void load_nib_table(uint4 *s_tab) {
+    constexpr int kWords = (int)(kNibBytes / 4);
+    constexpr int kPer = (kWords + BLOCK - 1) / BLOCK;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(s_tab);
+    uint32_t v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int w = (int)threadIdx.x + i * BLOCK;
+        v[i] = w < kWords ? kNibTable.ent[w / (int)kNibCopies] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int w = (int)threadIdx.x + i * BLOCK;
+        if (w < kWords) dst[w] = v[i];
+    }
+}
+
 }  // namespace
 }  // namespace tg

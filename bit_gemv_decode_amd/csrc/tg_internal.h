@@ -117,6 +117,9 @@ hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s);
 
+// BITCOS GEMV at m = 1 with the nibble-keyed decode (fp32 y or int32 accumulators; same geometry).
+hipError_t launch_bitcos_nibble(const GroupArgs &g, int out, hipStream_t s);
+
 // BITCOS GEMV against fp16 activations (Problem::x then points to fp16 [m][k]; fp32 y): launches of
 // at most kF16MaxM activation rows, kF16Waves waves per CU, vector-path geometry.
 constexpr int kF16MaxM = 2;

@@ -243,6 +243,7 @@ typedef struct tg_plan {
     int32_t waves;       /* waves of the launch the table's work split was made for */
     int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2 / 3: fp16
                             activations on the vector / matrix-core kernel */
+    int32_t decode;      /* TG_DECODE_BYTE (set by every tg_plan_init*) or TG_DECODE_NIBBLE */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 
@@ -266,6 +267,20 @@ int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
                      const void *const *W, const uint16_t *const *scales, const uint16_t *const *x16,
                      float *const *y, int32_t m);
 int ternary_gemv_plan(const tg_plan *plan, void *stream);
+
+/*
+ * BITCOS decode strategy of a plan. TG_DECODE_BYTE (the default): one lookup per presence byte in a
+ * byte-keyed table of 6561 entries. TG_DECODE_NIBBLE: the nibble-keyed lookup of "Breaking the
+ * 1.58-bit Barrier for Ternary LLMs", Sec. II-D, Eq. 4 (key: a presence nibble and the next four
+ * compact sign bits; entry: the nibble's 4 weights), one lookup per nibble in a 256-entry table.
+ * Both give the same exact int32 group sums and the same fp32 outputs; they differ in speed.
+ * tg_plan_set_decode: TG_DECODE_NIBBLE is accepted for initialised BITCOS plans with m = 1 on the
+ * vector path (path 0) writing fp32 y or int32 accumulators (tg_plan_init; not _xs); TG_EINVAL
+ * otherwise (the plan is then unchanged). Host only; takes effect at the next ternary_gemv_plan.
+ */
+#define TG_DECODE_BYTE 0
+#define TG_DECODE_NIBBLE 1
+int tg_plan_set_decode(tg_plan *plan, int32_t decode);
 
 /*
  * Bandwidth reference (not part of the GEMV): reads `bytes` bytes of device memory at buf

@@ -322,3 +322,28 @@ def test_f16_plan_argument_errors_before_any_gpu_work():
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
     forged.acc_mode, forged.path = 0, 4
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
+
+
+def test_plan_struct_layout_and_decode_selection_errors():
+    L = binding.lib()
+    # the C layout: ten 32-bit fields, then the table pointer
+    assert ctypes.sizeof(binding.TgPlan) == 48 and binding.TgPlan.table.offset == 40
+    assert binding.TgPlan.decode.offset == 36
+    assert L.tg_plan_set_decode(None, 1) == -1
+    assert L.tg_plan_set_decode(ctypes.byref(binding.TgPlan()), 1) == -1  # never initialised
+    ok = dict(magic=0x4E4C5054, fmt=B.FMT_BITCOS, m=1, count=1, units=1, rows_per_unit=1, acc_mode=0, waves=8,
+              path=0, table=256)
+    for bad in (dict(fmt=B.FMT_5TRIT), dict(m=2), dict(path=1), dict(path=2), dict(acc_mode=2)):
+        p = binding.TgPlan(**{**ok, **bad})
+        assert L.tg_plan_set_decode(ctypes.byref(p), 1) == -1 and p.decode == 0
+        assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0
+        p.decode = 1  # a forged plan claiming the nibble decode is refused before launching
+        assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+    p = binding.TgPlan(**ok)
+    assert L.tg_plan_set_decode(ctypes.byref(p), 2) == -1 and p.decode == 0
+    for acc_mode in (0, 1):
+        p.acc_mode = acc_mode
+        assert L.tg_plan_set_decode(ctypes.byref(p), 1) == 0 and p.decode == 1
+        assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0 and p.decode == 0
+    p.decode = 5
+    assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
