@@ -69,6 +69,14 @@ bool use_mfma(int fmt, int32_t m, int64_t k) {
            (m >= kMfmaAlwaysM || (m >= kMfmaMinM && k / TG_GROUP > kMfmaLongRowGroups));
 }
 
+// The same choice for fp16 activations: matrix cores from kF16MfmaMinM rows, and at two rows for
+// long rows (measured on MI355X, z = 0.44, 96 copies: 4096 x 14336 at m = 2 runs 1.27 TB/s on the
+// fp16 vector kernel, whose chunked rows reload 256-byte activation slices per pass, against
+// 2.34 TB/s for the matrix-core kernel at m = 4).
+bool use_mfma_f16(int32_t m, int64_t k) {
+    return m >= kF16MfmaMinM || (m == 2 && k / TG_GROUP > kMfmaLongRowGroups);
+}
+
 // Work geometry of one GEMV for a launch of m activation rows on the chosen path (fine: the smaller
 // units of chunked BITCOS rows at m = 1).
 void geometry(Problem &p, int fmt, int32_t m, bool mfma, bool fine = false) {
@@ -179,7 +187,7 @@ extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16
     if (!fits_offsets(desc, m) || (uint64_t)m * (uint64_t)desc->k * 2 > (1ull << 30)) return TG_ESHAPE;
     hipStream_t s = (hipStream_t)stream;
     const int64_t n = desc->n, k = desc->k;
-    if (m >= kF16MfmaMinM) {  // all rows in one launch on matrix cores
+    if (use_mfma_f16(m, k)) {  // all rows in one launch on matrix cores
         GroupArgs g{};
         g.one = make_problem(desc, W, scales, reinterpret_cast<const int8_t *>(x16), y, nullptr);
         g.count = 1;
@@ -298,9 +306,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     for (int32_t i = 0; i < count; ++i) {
         const double wts = (double)descs[i].n * (double)descs[i].k;
         w_all += wts;
-        if (use_mfma(fmt, m, descs[i].k)) w_mfma += wts;
+        if (f16 ? use_mfma_f16(m, descs[i].k) : use_mfma(fmt, m, descs[i].k)) w_mfma += wts;
     }
-    const bool mfma = f16 ? m >= kF16MfmaMinM
+    const bool mfma = f16 ? m >= kF16MfmaMinM || (m == 2 && 2 * w_mfma > w_all)
                           : fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
     const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : kPathVector;
     for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma);
@@ -424,7 +432,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
         (plan->path == kPathMfma && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)) ||
         (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)) ||
         (plan->path == kPathF16Mfma &&
-         (plan->fmt != TG_FMT_BITCOS || plan->m < kF16MfmaMinM || plan->acc_mode != kOutY)) ||
+         (plan->fmt != TG_FMT_BITCOS || plan->m < 2 || plan->acc_mode != kOutY)) ||
         (plan->decode != TG_DECODE_BYTE && (plan->decode != TG_DECODE_NIBBLE || !nibble_ok(plan))))
         return TG_EINVAL;
     GroupArgs g{};

@@ -126,7 +126,8 @@ constexpr int kF16MaxM = 2;
 constexpr int kF16Waves = 8;
 hipError_t launch_bitcos_f16(const GroupArgs &g, hipStream_t s);
 // ... and on matrix cores (the thin-batch kernel with fp16 operands, mfma_geometry, 1 <= m <= 16),
-// taken from kF16MfmaMinM activation rows.
+// taken from kF16MfmaMinM activation rows, and at two rows for rows of more than kMfmaLongRowGroups
+// groups.
 constexpr int kF16MfmaMinM = 3;
 hipError_t launch_bitcos_mfma_f16(const GroupArgs &g, hipStream_t s);
 

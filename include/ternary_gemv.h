@@ -194,9 +194,10 @@ int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, 
  *   larger than sum_{k in g} |W x|), multiplied by the group scale in fp64 (exact), summed over
  *   groups in fp64 and stored as fp32:
  *       |y - y_exact| <= 2^-23 |y_exact| + 2^-17 * sum_g |scale[n][g]| * sum_{k in g} |W x|.
- *   1 <= m <= TG_MAX_M. Paths: m <= 2 runs the vector kernel (v_dot2_f32_f16, one launch per two
- *   rows); from m = 3 one launch takes all rows on matrix cores (v_mfma_f32_16x16x32_f16, the decoded
- *   fp16 weights as the B operand, X padded to 16 rows as A). Non-finite activations are outside the
+ *   1 <= m <= TG_MAX_M. Paths: m = 1, and m = 2 with k <= 8192, run the vector kernel
+ *   (v_dot2_f32_f16); from m = 3, and at m = 2 with k > 8192, one launch takes all rows on matrix
+ *   cores (v_mfma_f32_16x16x32_f16, the decoded fp16 weights as the B operand, X padded to 16 rows
+ *   as A). Non-finite activations are outside the
  *   contract.
  *   Errors: TG_EINVAL (null or misaligned pointer, m out of range, a format other than BITCOS),
  *   TG_EFORMAT / TG_ECORRUPT (descriptor), TG_ESHAPE (2 * m * k > 2^30), TG_EHIP.
@@ -260,8 +261,9 @@ int tg_plan_init_xs(tg_plan *plan, void *table, size_t table_bytes, int32_t coun
 
 /* tg_plan_init for ternary_gemv_f16 outputs: every GEMV of the plan is BITCOS and takes fp16
  * activations x16[i] (device binary16 [m][k], 16-byte aligned), 1 <= m <= TG_MAX_M; the launch runs
- * the fp16 vector kernel (path 2, m <= 2) or the fp16 matrix-core kernel (path 3, m >= 3), and each y
- * is computed as ternary_gemv_f16 computes it. Errors as tg_plan_init, plus TG_EINVAL for another
+ * the fp16 vector kernel (path 2) or the fp16 matrix-core kernel (path 3: from m = 3, and at m = 2
+ * when GEMVs with k > 8192 hold most of the weights), and each y is computed as ternary_gemv_f16
+ * computes it. Errors as tg_plan_init, plus TG_EINVAL for another
  * format and TG_ESHAPE for 2 * m * k > 2^30. */
 int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                      const void *const *W, const uint16_t *const *scales, const uint16_t *const *x16,

@@ -316,7 +316,7 @@ def test_f16_plan_argument_errors_before_any_gpu_work():
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
     forged.acc_mode, forged.m = 0, 3
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
-    forged.m, forged.path = 2, 3  # the fp16 matrix-core path starts at m = 3
+    forged.m, forged.path = 1, 3  # the fp16 matrix-core path takes m >= 2
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
     forged.m, forged.acc_mode = 4, 2
     assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1

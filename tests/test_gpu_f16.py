@@ -68,7 +68,7 @@ SHAPES = [(1, 128, 0.42, 1), (3, 256, 0.0, 2), (5, 640, 1.0, 1), (37, 4096, 0.4,
           (17, 14336, 0.44, 1), (9, 25600, 0.47, 2), (64, 2560, 0.95, 1), (130, 1024, 0.515, 3),
           (600, 14336, 0.4, 1), (301, 8320, 0.3, 2), (2051, 4096, 0.44, 1),
           (1, 128, 0.4, 3), (33, 1152, 0.44, 4), (70, 4096, 0.0, 5), (97, 14336, 0.44, 8), (40, 2560, 1.0, 16),
-          (300, 4224, 0.47, 16), (15, 25600, 0.47, 7)]
+          (300, 4224, 0.47, 16), (15, 25600, 0.47, 7), (50, 14336, 0.44, 2), (33, 8320, 0.4, 2)]
 
 
 @pytest.mark.parametrize("n,k,z,m", SHAPES, ids=[f"{n}x{k}_z{z}_m{m}" for n, k, z, m in SHAPES])
@@ -185,6 +185,7 @@ def test_thin_batch_xs_after_f16_kernel():
 
 @pytest.mark.parametrize("m", [1, 2, 4])
 def test_f16_plan_matches_oracle(m):
+    # at m = 2 the long rows (k > 8192) hold most of the weights: the matrix-core path
     # one grouped launch over GEMVs of mixed shapes (single-chunk, chunked, ragged), fp16 activations
     dev = _dev()
     shapes = [(96, 4096), (40, 5120), (33, 14336), (7, 2560), (130, 1024), (1, 128), (9, 25600), (300, 14336)]
@@ -200,7 +201,7 @@ def test_f16_plan_matches_oracle(m):
         xs.append(torch.from_numpy(x16).to(dev))
         ys.append(torch.full((m, n), float("nan"), dtype=torch.float32, device=dev))
     plan = B.Plan(dws, xs, scales=ss, ys=ys, f16=True)
-    assert plan.plan.path == (2 if m <= 2 else 3)
+    assert plan.plan.path == (2 if m == 1 else 3)
     plan.run()
     torch.cuda.synchronize()
     for i, (n, k) in enumerate(shapes):
@@ -208,3 +209,30 @@ def test_f16_plan_matches_oracle(m):
         y = ys[i].cpu().numpy()
         err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
         assert np.all(err <= f16_bound(w, s, x16, y_ref)), f"f16 plan {n}x{k}"
+
+
+def test_f16_plan_m2_vector_path_with_chunked_rows():
+    # short rows hold most of the weights: the plan stays on the vector kernel, whose two-row chunked
+    # path then runs the long-row GEMV
+    dev = _dev()
+    m = 2
+    shapes = [(2000, 4096), (900, 2560), (60, 14336), (13, 8320)]
+    _say("[gpu] f16 plan m=2 vector")
+    dws, ss, xs, ys, refs = [], [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.ternary(n, k, 0.42, seed=800 + i)
+        s = synth.scales(n, k // 128, seed=800 + i)
+        x16 = synth.float_activations(m, k, seed=850 + i).astype(np.float16)
+        refs.append((w, s, x16, O.gemv_f16(w, s, x16)))
+        dws.append(B.DeviceWeights(B.pack_bitcos(w), dev))
+        ss.append(torch.from_numpy(s).to(dev))
+        xs.append(torch.from_numpy(x16).to(dev))
+        ys.append(torch.full((m, n), float("nan"), dtype=torch.float32, device=dev))
+    plan = B.Plan(dws, xs, scales=ss, ys=ys, f16=True)
+    assert plan.plan.path == 2
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (n, k) in enumerate(shapes):
+        w, s, x16, y_ref = refs[i]
+        err = np.abs(ys[i].cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+        assert np.all(err <= f16_bound(w, s, x16, y_ref)), f"f16 plan m=2 {n}x{k}"
