@@ -207,7 +207,7 @@ extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16
         g.m = mt;
         g.one.unit_begin = 0;
         gemv_geometry(g.one, TG_FMT_BITCOS, mt);
-        if (want_fine({g.one}, TG_FMT_BITCOS, mt, false, device_cus() * kF16Waves))
+        if (want_fine({g.one}, TG_FMT_BITCOS, mt, false, device_cus() * f16_waves(mt)))
             gemv_geometry(g.one, TG_FMT_BITCOS, mt, true);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
@@ -263,7 +263,7 @@ enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2, kPathF16Mfma = 3 }
 
 // Waves of a launch on `path`.
 int path_waves(int fmt, int m, int path) {
-    if (path == kPathF16) return device_cus() * kF16Waves;
+    if (path == kPathF16) return device_cus() * f16_waves(m);
     return plan_waves(fmt, m, path == kPathMfma || path == kPathF16Mfma);
 }
 

@@ -432,13 +432,13 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
         }
 }
 
-// F16: fp16 activations, kF16Waves waves per CU (the 256-byte activation slices need the registers).
+// F16: fp16 activations, f16_waves(M) waves per CU (the 256-byte activation slices need the registers).
 // NIB: the nibble-keyed decode (its 32 KB table replaces the byte-keyed tables in LDS).
 template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false>
-__global__ __launch_bounds__((F16 ? 64 * kF16Waves : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
+__global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
     GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
-    constexpr int NB = C::NB, WAVES = F16 ? kF16Waves : C::WAVES, BLOCK = 64 * WAVES;
+    constexpr int NB = C::NB, WAVES = F16 ? f16_waves(M) : C::WAVES, BLOCK = 64 * WAVES;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
@@ -483,9 +483,10 @@ hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
 
 template <int M>
 hipError_t launch_f16_m(const GroupArgs &g, hipStream_t s) {
-    const int blocks = grid_blocks<kF16Waves>(g);
+    constexpr int W = f16_waves(M);
+    const int blocks = grid_blocks<W>(g);
     if (blocks < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false, true>), dim3(blocks), dim3(64 * kF16Waves), 0, s, g);
+    hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false, true>), dim3(blocks), dim3(64 * W), 0, s, g);
     return hipGetLastError();
 }
 

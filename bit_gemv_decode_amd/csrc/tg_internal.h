@@ -121,9 +121,10 @@ hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_bitcos_nibble(const GroupArgs &g, int out, hipStream_t s);
 
 // BITCOS GEMV against fp16 activations (Problem::x then points to fp16 [m][k]; fp32 y): launches of
-// at most kF16MaxM activation rows, kF16Waves waves per CU, vector-path geometry.
+// at most kF16MaxM activation rows, f16_waves(m) waves per CU, vector-path geometry. At m = 1 the
+// kernel fits 168 registers and 12 waves share a CU; two rows need 253 registers (8 waves).
 constexpr int kF16MaxM = 2;
-constexpr int kF16Waves = 8;
+constexpr int f16_waves(int m) { return m == 1 ? 12 : 8; }
 hipError_t launch_bitcos_f16(const GroupArgs &g, hipStream_t s);
 // ... and on matrix cores (the thin-batch kernel with fp16 operands, mfma_geometry, 1 <= m <= 16),
 // taken from kF16MfmaMinM activation rows, and at two rows for rows of more than kMfmaLongRowGroups
