@@ -81,7 +81,7 @@ __device__ __forceinline__ uint32_t stage_signs(const Ctx &x, const u32x4 &bm, u
     g.s[0] = ld4(x.rsg, (b0 >> 5) << 2, sd);
     g.s[1] = ld4(x.rsg, (b2 >> 5) << 2, sd);
     g.sh = __builtin_amdgcn_perm(b2, b0, 0x0C0C0400u);  // byte 0: b0, byte 1: b2 (low 5 bits used)
-    g.scale = ACC ? (uint16_t)0 : ldh(x.rsc, voff_sc, live_or_dead(live, soff_sc));
+    g.scale = ACC ? (uint16_t)0 : ldhs(x.rsc, voff_sc, live_or_dead(live, soff_sc));
     return total;
 }
 
@@ -361,11 +361,11 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                 const bool live = s < T;
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
-                    bm[jb] = ld4(x.rbm, voff_bm, live_or_dead(live, (uint32_t)row0 * kb));
+                    bm[jb] = ld4s(x.rbm, voff_bm, live_or_dead(live, (uint32_t)row0 * kb));
                 } else {
                     const int slot = j % NB;
                     const int gc = cB == x.nch - 1 ? x.glast : 64;
-                    bm[jb] = ld4(x.rbm, lane < gc ? voff_bm : kOffOff,
+                    bm[jb] = ld4s(x.rbm, lane < gc ? voff_bm : kOffOff,
                                  live_or_dead(live, (uint32_t)(rB + slot) * kb + (uint32_t)cB * 1024u));
                     if (slot == 0) {
                         // the unit's row-index entries, for its first chunk pass
