@@ -79,11 +79,11 @@ bool use_mfma_f16(int32_t m, int64_t k) {
 
 // Work geometry of one GEMV for a launch of m activation rows on the chosen path (fine: the smaller
 // units of chunked BITCOS rows at m = 1).
-void geometry(Problem &p, int fmt, int32_t m, bool mfma, bool fine = false) {
+void geometry(Problem &p, int fmt, int32_t m, bool mfma, bool fine = false, bool f16 = false) {
     if (mfma)
         mfma_geometry(p);
     else
-        gemv_geometry(p, fmt, m, fine);
+        gemv_geometry(p, fmt, m, fine, f16);
 }
 
 // Whether a launch over these GEMVs (coarse geometry) should use fine units for chunked BITCOS rows
@@ -206,9 +206,9 @@ extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
-        gemv_geometry(g.one, TG_FMT_BITCOS, mt);
+        gemv_geometry(g.one, TG_FMT_BITCOS, mt, false, true);
         if (want_fine({g.one}, TG_FMT_BITCOS, mt, false, device_cus() * f16_waves(mt)))
-            gemv_geometry(g.one, TG_FMT_BITCOS, mt, true);
+            gemv_geometry(g.one, TG_FMT_BITCOS, mt, true, true);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
         if (launch_bitcos_f16(g, s) != hipSuccess) return TG_EHIP;
@@ -311,7 +311,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     const bool mfma = f16 ? m >= kF16MfmaMinM || (m == 2 && 2 * w_mfma > w_all)
                           : fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
     const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : kPathVector;
-    for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma);
+    for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, false, f16);
     {
         int64_t ub = 0;
         for (int32_t i = 0; i < count; ++i) {
@@ -320,7 +320,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         }
     }
     if (want_fine(host, fmt, m, mfma, path_waves(fmt, m, path)))
-        for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, true);
+        for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, true, f16);
     for (int32_t i = 0; i < count; ++i) rpu = std::max(rpu, (int)host[i].rpu);
     // Work order: GEMVs of one shape next to each other (by k, then n; the caller's order within a
     // shape). Each Problem carries its own pointers, so the order changes no result; on MI355X it

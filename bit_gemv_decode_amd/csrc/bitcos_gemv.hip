@@ -438,7 +438,8 @@ template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false>
 __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
     GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
-    constexpr int NB = C::NB, WAVES = F16 ? f16_waves(M) : C::WAVES, BLOCK = 64 * WAVES;
+    // the fp16 kernel keeps four-step units at m = 2 (its 8 waves gain nothing from shorter ones)
+    constexpr int NB = F16 ? 4 : C::NB, WAVES = F16 ? f16_waves(M) : C::WAVES, BLOCK = 64 * WAVES;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
@@ -492,8 +493,9 @@ hipError_t launch_f16_m(const GroupArgs &g, hipStream_t s) {
 
 }  // namespace
 
-void gemv_geometry(Problem &p, int fmt, int m, bool fine) {
-    const int nb = m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
+void gemv_geometry(Problem &p, int fmt, int m, bool fine, bool f16) {
+    const int nb = f16 ? 4 : m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB
+                           : m == 2 && fmt == TG_FMT_BITCOS ? Cfg<2, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
     p.ng = (int32_t)groups_per_row(fmt, p.k);
     p.nch = (p.ng + 63) / 64;
     if (p.nch == 1) {

@@ -19,7 +19,8 @@ namespace {
 
 template <int M, int FMT>
 struct Cfg {
-    static constexpr int NB = M == 3 ? 2 : 4;  // row bundles (steps per chunk pass) per unit
+    // row bundles (steps per chunk pass) per unit: 2 at m = 3, and for BITCOS at m = 2 (12 waves)
+    static constexpr int NB = M == 3 || (M == 2 && FMT == TG_FMT_BITCOS) ? 2 : 4;
     static constexpr int WAVES = gemv_waves(FMT, M);  // waves per block (= per CU)
     static constexpr int BLOCK = 64 * WAVES;
 };

@@ -71,8 +71,11 @@ struct GroupArgs {
 };
 
 // Waves per CU of a vector-path GEMV launch for m activation rows (one block per CU: the decode
-// tables fill most of the LDS): 16 at m = 1 (128 registers per lane), 8 at m = 2, 3.
-constexpr int gemv_waves(int fmt, int m) { return (void)fmt, m > 1 ? 8 : 16; }
+// tables fill most of the LDS): 16 at m = 1 (128 registers per lane), 8 at m = 2, 3, except BITCOS at
+// m = 2: 12 waves (163 registers) with units of two steps, whose LDS tile then fits beside the tables
+// (measured against 8 waves and 4-step units, 96 copies, identical outputs: 4096x4096 +7 %,
+// 1024x4096 +13 %, 2560x2560 +14 %, 1024x1024 +7 %, 14336x4096 +3 %).
+constexpr int gemv_waves(int fmt, int m) { return fmt == TG_FMT_BITCOS && m == 2 ? 12 : m > 1 ? 8 : 16; }
 constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
@@ -82,8 +85,9 @@ constexpr int kChunkRows1 = 8;
 constexpr int kChunkRows1Fine = 2;
 
 // Fill the work geometry of p (p.n, p.k set) for m activation rows on the vector path (the same for
-// every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 rows).
-void gemv_geometry(Problem &p, int fmt, int m, bool fine = false);
+// every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 rows and BITCOS
+// units at m = 2 are two steps long; f16: the fp16-activation kernel, four-step units).
+void gemv_geometry(Problem &p, int fmt, int m, bool fine = false, bool f16 = false);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
 // units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU. It is
