@@ -71,11 +71,13 @@ struct GroupArgs {
 };
 
 // Waves per CU of a vector-path GEMV launch for m activation rows (one block per CU: the decode
-// tables fill most of the LDS): 16 at m = 1 (128 registers per lane), 8 at m = 2, 3, except BITCOS at
-// m = 2: 12 waves (163 registers) with units of two steps, whose LDS tile then fits beside the tables
-// (measured against 8 waves and 4-step units, 96 copies, identical outputs: 4096x4096 +7 %,
-// 1024x4096 +13 %, 2560x2560 +14 %, 1024x1024 +7 %, 14336x4096 +3 %).
-constexpr int gemv_waves(int fmt, int m) { return fmt == TG_FMT_BITCOS && m == 2 ? 12 : m > 1 ? 8 : 16; }
+// tables fill most of the LDS): 16 at m = 1 (128 registers per lane), 8 at m = 3, and at m = 2 12 for
+// BITCOS, five-trit and 2-bit (163, 168 and 137 registers; BITCOS with units of two steps, whose LDS
+// tile then fits beside its tables), 8 for t5b (195 registers). Measured against 8 waves, 96 copies,
+// identical outputs: BITCOS 4096x4096 +7 %, 1024x4096 +13 %, 2560x2560 +14 %, 14336x4096 +3 %;
+// five-trit 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %; 2-bit +2 %, +3 %, +21 %; the
+// chunked 4096x14336 unchanged.
+constexpr int gemv_waves(int fmt, int m) { return fmt != TG_FMT_T5B && m == 2 ? 12 : m > 1 ? 8 : 16; }
 constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
