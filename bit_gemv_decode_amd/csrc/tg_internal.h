@@ -71,13 +71,15 @@ struct GroupArgs {
 };
 
 // Waves per CU of a vector-path GEMV launch for m activation rows (one block per CU: the decode
-// tables fill most of the LDS): 16 at m = 1 (128 registers per lane), 8 at m = 3, and at m = 2 12 for
-// BITCOS, five-trit and 2-bit (163, 168 and 137 registers; BITCOS with units of two steps, whose LDS
-// tile then fits beside its tables), 8 for t5b (195 registers). Measured against 8 waves, 96 copies,
-// identical outputs: BITCOS 4096x4096 +7 %, 1024x4096 +13 %, 2560x2560 +14 %, 14336x4096 +3 %;
-// five-trit 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %; 2-bit +2 %, +3 %, +21 %; the
-// chunked 4096x14336 unchanged.
-constexpr int gemv_waves(int fmt, int m) { return fmt != TG_FMT_T5B && m == 2 ? 12 : m > 1 ? 8 : 16; }
+// tables fill most of the LDS): 16 at m = 1 (128 registers per lane); 12 at m = 2 for BITCOS,
+// five-trit and 2-bit (163, 168 and 137 registers; BITCOS with units of two steps, whose LDS tile then
+// fits beside its tables) and at m = 3 for 2-bit (168); else 8 (t5b at m = 2: 195 registers). Measured
+// against 8 waves, 96 copies, identical outputs: BITCOS 4096x4096 +7 %, 1024x4096 +13 %,
+// 2560x2560 +14 %, 14336x4096 +3 %; five-trit 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %;
+// 2-bit +2 %, +3 %, +21 % at m = 2 and +8 %, +8 %, +22 % at m = 3; the chunked 4096x14336 within 1 %.
+constexpr int gemv_waves(int fmt, int m) {
+    return (fmt != TG_FMT_T5B && m == 2) || (fmt == TG_FMT_2BIT && m == 3) ? 12 : m > 1 ? 8 : 16;
+}
 constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
