@@ -347,3 +347,47 @@ def test_plan_struct_layout_and_decode_selection_errors():
         assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0 and p.decode == 0
     p.decode = 5
     assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+
+
+def _bitcos_desc(n, k, nnz):
+    """A consistent BITCOS descriptor of an n x k matrix with nnz non-zeros (the packer's layout),
+    for shapes too large to pack here."""
+    d = binding.TgDesc.from_buffer_copy(B.pack_bitcos(np.zeros((1, 128), np.int8)).desc)
+    up = lambda v, a=256: (v + a - 1) // a * a
+    sign_bytes = (nnz + 7) // 8
+    d.n, d.k, d.nnz = n, k, nnz
+    d.bytes_codes = n * k // 8
+    d.off_signs = up(d.off_codes + d.bytes_codes)
+    d.bytes_signs = up(sign_bytes + 16, 8)
+    d.off_index = up(d.off_signs + d.bytes_signs)
+    d.bytes_index = 4 * (n + 1)
+    d.bytes_total = up(d.off_index + d.bytes_index)
+    d.bytes_payload = d.bytes_codes + sign_bytes + d.bytes_index
+    return d
+
+
+def test_offset_limits_refused_before_any_gpu_work():
+    # The kernels address each section with 32-bit offsets (switched-off accesses use offsets from
+    # 2^31): bitmaps, scales and outputs must stay below 1 GiB, sign windows below 512 MiB, and fp16
+    # activation rows (2 m k bytes) at most 1 GiB. Descriptors past a limit are TG_ESHAPE.
+    L = binding.lib()
+    dummy = ctypes.c_void_p(256)
+    at_bitmap_limit = _bitcos_desc(65536, 131072, 1 << 20)   # bitmap exactly 1 GiB
+    at_sign_limit = _bitcos_desc(65535, 131072, (1 << 32) - 1)  # 512 MiB of signs
+    big_out = _bitcos_desc(65535, 131072, 1 << 20)          # n * k/128 * 4 * m > 1 GiB from m = 5
+    long_rows = _bitcos_desc(1, 1 << 28, 1 << 20)            # 2 m k > 2^30 at m = 3
+    for d in (at_bitmap_limit, at_sign_limit):
+        assert L.ternary_gemv(ctypes.byref(d), dummy, dummy, dummy, dummy, 1, None) == -3
+        assert L.ternary_gemv_acc(ctypes.byref(d), dummy, dummy, dummy, 1, None) == -3
+        assert L.ternary_gemv_f16(ctypes.byref(d), dummy, dummy, dummy, dummy, 1, None) == -3
+    assert L.ternary_gemv_acc(ctypes.byref(big_out), dummy, dummy, dummy, 5, None) == -3
+    assert L.ternary_gemv(ctypes.byref(big_out), dummy, dummy, dummy, dummy, 5, None) == -3
+    assert L.ternary_gemv_f16(ctypes.byref(long_rows), dummy, dummy, dummy, dummy, 3, None) == -3
+    descs = (binding.TgDesc * 1)(at_bitmap_limit)
+    P1 = ctypes.c_void_p * 1
+    ptrs = P1(256)
+    plan = binding.TgPlan()
+    nbytes = L.tg_plan_table_bytes(1)
+    assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -3
+    assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, (binding.TgDesc * 1)(long_rows), ptrs, ptrs,
+                              ptrs, ptrs, 3) == -3
