@@ -494,8 +494,8 @@ hipError_t launch_f16_m(const GroupArgs &g, hipStream_t s) {
 }  // namespace
 
 void gemv_geometry(Problem &p, int fmt, int m, bool fine, bool f16) {
-    const int nb = f16 ? 4 : m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB
-                           : m == 2 && fmt == TG_FMT_BITCOS ? Cfg<2, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
+    const int nb = f16 || fmt != TG_FMT_BITCOS ? 4
+                   : m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : m == 2 ? Cfg<2, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
     p.ng = (int32_t)groups_per_row(fmt, p.k);
     p.nch = (p.ng + 63) / 64;
     if (p.nch == 1) {
