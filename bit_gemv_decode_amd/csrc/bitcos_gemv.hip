@@ -438,7 +438,7 @@ template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false>
 __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
     GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
-    // the fp16 kernel keeps four-step units at m = 2 (its 8 waves gain nothing from shorter ones)
+    // the fp16 kernel uses four-step units at m = 1, 2 (two-step ones were 3-4 % slower at m = 2)
     constexpr int NB = F16 ? 4 : C::NB, WAVES = F16 ? f16_waves(M) : C::WAVES, BLOCK = 64 * WAVES;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];

@@ -19,12 +19,12 @@ namespace {
 
 template <int M, int FMT>
 struct Cfg {
-    // row bundles (steps per chunk pass) per unit: 2 for BITCOS at m = 2 (12 waves) and m = 3 (its
-    // 118 KB of tables leave no room for a larger tile), else 4. The fixed-code formats' 4-row units
-    // at m = 3 were measured against 2-row ones (96 copies, identical outputs): chunked 4096x14336
-    // +64-67 % (the activation slices are reloaded once per pass for twice the rows), five-trit
-    // single-chunk shapes +9-11 %, 2-bit single-chunk shapes within 1 %.
-    static constexpr int NB = FMT == TG_FMT_BITCOS && (M == 2 || M == 3) ? 2 : 4;
+    // row bundles (steps per chunk pass) per unit: 2 for BITCOS at m = 3 (its 118 KB of tables leave
+    // no room for a larger tile), else 4. The fixed-code formats' 4-row units at m = 3 were measured
+    // against 2-row ones (96 copies, identical outputs): chunked 4096x14336 +64-67 % (the activation
+    // slices are reloaded once per pass for twice the rows), five-trit single-chunk shapes +9-11 %,
+    // 2-bit single-chunk shapes within 1 %.
+    static constexpr int NB = FMT == TG_FMT_BITCOS && M == 3 ? 2 : 4;
     static constexpr int WAVES = gemv_waves(FMT, M);  // waves per block (= per CU)
     static constexpr int BLOCK = 64 * WAVES;
 };

@@ -71,14 +71,17 @@ struct GroupArgs {
 };
 
 // Waves per CU of a vector-path GEMV launch for m activation rows (one block per CU: the decode
-// tables fill most of the LDS): 16 at m = 1 (128 registers per lane); 12 at m = 2 for BITCOS,
-// five-trit and 2-bit (163, 168 and 137 registers; BITCOS with units of two steps, whose LDS tile then
-// fits beside its tables) and at m = 3 for 2-bit (168); else 8 (t5b at m = 2: 195 registers). Measured
-// against 8 waves, 96 copies, identical outputs: BITCOS 4096x4096 +7 %, 1024x4096 +13 %,
-// 2560x2560 +14 %, 14336x4096 +3 %; five-trit 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %;
-// 2-bit +2 %, +3 %, +21 % at m = 2 and +8 %, +8 %, +22 % at m = 3; the chunked 4096x14336 within 1 %.
+// tables fill most of the LDS): 16 at m = 1 (128 registers per lane); 12 for five-trit and 2-bit at
+// m = 2 (168 and 137 registers) and 2-bit at m = 3 (168); else 8. Measured against 8 waves, 96 copies,
+// identical outputs: five-trit 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %; 2-bit +2 %, +3 %,
+// +21 % at m = 2 and +8 %, +8 %, +22 % at m = 3; the chunked 4096x14336 within 1 %. BITCOS at m = 2
+// fits 12 waves only with two-step units (its tables leave no room for a deeper tile): +3-14 % on
+// single-chunk shapes, but its chunked rows then reload the activation slices twice as often, and a
+// whole-layer plan at m = 2 (down on the vector path) ran 23 % slower, so BITCOS keeps 8 waves.
 constexpr int gemv_waves(int fmt, int m) {
-    return (fmt != TG_FMT_T5B && m == 2) || (fmt == TG_FMT_2BIT && m == 3) ? 12 : m > 1 ? 8 : 16;
+    return (fmt != TG_FMT_T5B && fmt != TG_FMT_BITCOS && m == 2) || (fmt == TG_FMT_2BIT && m == 3) ? 12
+           : m > 1                                                                                ? 8
+                                                                                                  : 16;
 }
 constexpr int kMaxWavesPerCu = 16;
 
@@ -90,7 +93,7 @@ constexpr int kChunkRows1Fine = 2;
 
 // Fill the work geometry of p (p.n, p.k set) for m activation rows on the vector path (the same for
 // every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 rows and BITCOS
-// units at m = 2 are two steps long; f16: the fp16-activation kernel, four-step units).
+// units at m = 3 are two steps long; f16: the fp16-activation kernel, four-step units).
 void gemv_geometry(Problem &p, int fmt, int m, bool fine = false, bool f16 = false);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
