@@ -71,17 +71,16 @@ struct GroupArgs {
 };
 
 // Waves per CU of a vector-path GEMV launch for m activation rows (one block per CU: the decode
-// tables fill most of the LDS): 16 at m = 1 (128 registers per lane); 12 for five-trit and 2-bit at
-// m = 2 (168 and 137 registers) and 2-bit at m = 3 (168); else 8. Measured against 8 waves, 96 copies,
-// identical outputs: five-trit 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %; 2-bit +2 %, +3 %,
-// +21 % at m = 2 and +8 %, +8 %, +22 % at m = 3; the chunked 4096x14336 within 1 %. BITCOS at m = 2
-// fits 12 waves only with two-step units (its tables leave no room for a deeper tile): +3-14 % on
-// single-chunk shapes, but its chunked rows then reload the activation slices twice as often, and a
-// whole-layer plan at m = 2 (down on the vector path) ran 23 % slower, so BITCOS keeps 8 waves.
+// tables fill most of the LDS): 16 at m = 1 (128 registers per lane); 12 for five-trit at m = 2 (168
+// registers) and 2-bit at m = 3 (168); else 8. Measured against 8 waves with identical outputs, on
+// single matrices (96 copies) and on the Llama3-8B layer set as one plan: five-trit at m = 2
+// 4096x4096 +12 %, 14336x4096 +8 %, 2560x2560 +22 %, layer set +0.1 % (its chunked down unchanged);
+// 2-bit at m = 3 +8 %, +8 %, +22 %, layer set +29 % (with 4-row units). 2-bit at m = 2 gained on
+// single matrices (+2 %, +3 %, +21 %) but lost 3.8 % on the layer set, and BITCOS at m = 2 fits 12
+// waves only with two-step units (its tables leave no room for a deeper tile), whose chunked rows
+// reload the activation slices twice as often: a layer-set plan at m = 2 ran 23 % slower. Both keep 8.
 constexpr int gemv_waves(int fmt, int m) {
-    return (fmt != TG_FMT_T5B && fmt != TG_FMT_BITCOS && m == 2) || (fmt == TG_FMT_2BIT && m == 3) ? 12
-           : m > 1                                                                                ? 8
-                                                                                                  : 16;
+    return (fmt == TG_FMT_5TRIT && m == 2) || (fmt == TG_FMT_2BIT && m == 3) ? 12 : m > 1 ? 8 : 16;
 }
 constexpr int kMaxWavesPerCu = 16;
 
