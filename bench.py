@@ -484,9 +484,9 @@ def main():
                     "configuration instead (several minutes) and write its JSON report to PATH")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the ternary GEMV shards across GPUs by rows (or by k with one "
-              "all-reduce of the output vector) in a deployment, but this build runs on a single MI355X. "
-              "Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the ternary GEMV would shard across GPUs by rows (or by k with one "
+              "all-reduce of the output vector), and the multi-GPU path is not implemented. Use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.suite:
