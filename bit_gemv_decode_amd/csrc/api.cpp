@@ -2,6 +2,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "tg_internal.h"
@@ -9,16 +10,21 @@
 namespace tg {
 
 int device_cus() {
-    static int cached = 0;
-    if (!cached) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-            cached = cus;
-        else
-            return 256;
+    // One entry per device ordinal: the compute-unit count is a fixed property of the device, so the
+    // cache is written at most once per entry with the same value, and concurrent first calls on
+    // several threads only race to store that value (relaxed atomics keep the accesses well defined).
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
-    return cached;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
+    if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, const int8_t *x, float *y,
@@ -133,12 +139,17 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
     hipStream_t s = (hipStream_t)stream;
     const int64_t n = desc->n, k = desc->k, ng = groups_per_row(desc->fmt, k);
     // Activation rows go in launches of at most three on the vector path (each launch reads the
-    // weights once); the matrix-core path takes all of them in one launch.
+    // weights once); the matrix-core path takes all of them in one launch. Every launch is set up and
+    // checked before the first one is enqueued, so an argument or geometry error enqueues nothing.
     const bool mfma = use_mfma(desc->fmt, m, desc->k);
     const int32_t step = mfma ? m : kVectorMaxM;
+    GroupArgs gs[(TG_MAX_M + kVectorMaxM - 1) / kVectorMaxM];
+    int nl = 0;
+    const int cus = device_cus();
     for (int32_t m0 = 0; m0 < m; m0 += step) {
         const int32_t mt = std::min<int32_t>(step, m - m0);
-        GroupArgs g{};
+        GroupArgs &g = gs[nl++];
+        g = GroupArgs{};
         g.one = make_problem(desc, W, scales, x + (size_t)m0 * k, acc_out ? nullptr : y + (size_t)m0 * n,
                              acc_out ? acc + (size_t)m0 * n * ng : nullptr,
                              out == kOutYxs ? xs + (size_t)m0 * ng : nullptr);
@@ -146,12 +157,14 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         g.m = mt;
         g.one.unit_begin = 0;
         geometry(g.one, desc->fmt, mt, mfma);
-        if (want_fine({g.one}, desc->fmt, mt, mfma, device_cus() * gemv_waves(desc->fmt, mt)))
+        if (want_fine({g.one}, desc->fmt, mt, mfma, cus * gemv_waves(desc->fmt, mt)))
             geometry(g.one, desc->fmt, mt, mfma, true);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
-        if (launch(desc->fmt, g, out, mfma, s) != hipSuccess) return TG_EHIP;
+        if (g.units < 1) return TG_ESHAPE;
     }
+    for (int i = 0; i < nl; ++i)
+        if (launch(desc->fmt, gs[i], out, mfma, s) != hipSuccess) return TG_EHIP;
     return TG_OK;
 }
 

@@ -38,15 +38,22 @@
  * Scales are IEEE binary16, row-major [n][k/128], and are passed separately from the packed weights.
  *
  * Conventions
- *   - Every buffer is owned by the caller. The library allocates no device memory and keeps no
- *     mutable global state; all functions are re-entrant.
- *   - Functions return TG_OK (0) or a negative TG_E* code; tg_strerror() names it. On error nothing
- *     is written to outputs and nothing is enqueued on the GPU.
+ *   - Every buffer is owned by the caller. The library allocates no device memory. Its only
+ *     global state is a per-device cache of the compute-unit count (written once per device with
+ *     the device's fixed value, atomically); all functions are re-entrant and thread-safe.
+ *   - Functions return TG_OK (0) or a negative TG_E* code; tg_strerror() names it. Argument,
+ *     descriptor and shape errors are detected before anything is enqueued, also for calls that
+ *     issue several launches (five-trit, 2-bit and t5b with m > 3 run up to six launches of at
+ *     most three activation rows: all of them are set up and checked before the first is
+ *     enqueued). Only a failure of the HIP runtime itself while enqueuing (TG_EHIP) can leave
+ *     earlier launches of such a call enqueued; their outputs are then partial.
  *   - Host functions (tg_pack_*, tg_describe, tg_validate, tg_unpack) take host pointers and are
  *     synchronous.
  *   - ternary_gemv / ternary_gemv_acc take a HOST copy of the packed buffer's descriptor and DEVICE
  *     pointers for everything else; they enqueue on `stream` (a hipStream_t passed as void*, NULL =
- *     the default stream) and return without synchronising.
+ *     the default stream) and return without synchronising. The format is not a separate argument:
+ *     it is desc->fmt, and the descriptor carries what a bare format code could not (shape, zero
+ *     count and section offsets within W), so a call cannot pair a format with the wrong layout.
  */
 #ifndef TERNARY_GEMV_H
 #define TERNARY_GEMV_H
@@ -193,7 +200,9 @@ int ternary_gemv_xs(const tg_desc *desc, const void *W, const uint16_t *scales, 
  *   Each group sum is accumulated in fp32 (products exact, at most 128 roundings of partial sums no
  *   larger than sum_{k in g} |W x|), multiplied by the group scale in fp64 (exact), summed over
  *   groups in fp64 and stored as fp32:
- *       |y - y_exact| <= 2^-23 |y_exact| + 2^-17 * sum_g |scale[n][g]| * sum_{k in g} |W x|.
+ *       |y - y_exact| <= 2^-24 |y_exact| + 2^-17 * sum_g |scale[n][g]| * sum_{k in g} |W x|,
+ *   and the parity checks accept |y - y_ref| <= 2^-22 |y_ref| + 2^-17 * sum_g |scale[n][g]| *
+ *   sum_{k in g} |W x| against the correctly rounded value y_ref (derived in oracle/bounds.py).
  *   1 <= m <= TG_MAX_M. Paths: m = 1, and m = 2 with k <= 8192, run the vector kernel
  *   (v_dot2_f32_f16); from m = 3, and at m = 2 with k > 8192, one launch takes all rows on matrix
  *   cores (v_mfma_f32_16x16x32_f16, the decoded fp16 weights as the B operand, X padded to 16 rows

@@ -391,3 +391,29 @@ def test_offset_limits_refused_before_any_gpu_work():
     assert L.tg_plan_init(ctypes.byref(plan), dummy, nbytes, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -3
     assert L.tg_plan_init_f16(ctypes.byref(plan), dummy, nbytes, 1, (binding.TgDesc * 1)(long_rows), ptrs, ptrs,
                               ptrs, ptrs, 3) == -3
+
+
+@pytest.mark.parametrize("fmt", [B.FMT_5TRIT, B.FMT_2BIT, B.FMT_T5B], ids=["5trit", "2bit", "t5b"])
+def test_multi_launch_calls_check_everything_before_enqueuing(fmt):
+    # Five-trit, 2-bit and t5b with m > 3 run several launches of at most three activation rows. All of
+    # them are set up and checked before the first is enqueued, so every bad argument comes back as its
+    # own code (on a machine without a GPU, reaching the HIP runtime would give TG_EHIP instead).
+    L = binding.lib()
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = (B.pack_t5b(w, 0.5) if fmt == B.FMT_T5B else B.pack(fmt, w)).desc
+    dummy = ctypes.c_void_p(256)
+    sc = None if fmt == B.FMT_T5B else dummy
+    for m in (4, 7, 16):
+        assert L.ternary_gemv(ctypes.byref(d), dummy, sc, dummy, ctypes.c_void_p(258), m, None) == -1  # y
+        assert L.ternary_gemv(ctypes.byref(d), dummy, sc, ctypes.c_void_p(264), dummy, m, None) == -1  # x
+        assert L.ternary_gemv(ctypes.byref(d), ctypes.c_void_p(264), sc, dummy, dummy, m, None) == -1  # W
+        assert L.ternary_gemv_acc(ctypes.byref(d), dummy, dummy, ctypes.c_void_p(258), m, None) == -1
+        if fmt != B.FMT_T5B:
+            assert L.ternary_gemv(ctypes.byref(d), dummy, ctypes.c_void_p(257), dummy, dummy, m, None) == -1
+        d2 = binding.TgDesc.from_buffer_copy(d)
+        d2.magic = 0
+        assert L.ternary_gemv(ctypes.byref(d2), dummy, sc, dummy, dummy, m, None) == -4
+        d2 = binding.TgDesc.from_buffer_copy(d)
+        d2.bytes_codes = 4
+        assert L.ternary_gemv_acc(ctypes.byref(d2), dummy, dummy, dummy, m, None) == -5
+    assert L.ternary_gemv(ctypes.byref(d), dummy, sc, dummy, dummy, 17, None) == -1

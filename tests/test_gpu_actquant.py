@@ -13,6 +13,7 @@ import pytest
 
 import bit_gemv_decode_amd as B
 import oracle as O
+from oracle import bounds
 from bit_gemv_decode_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -77,10 +78,7 @@ def test_quantize_special_groups_bit_exact():
 
 
 def y_xs_tolerance_ok(y, y_ref, acc, scales, xs):
-    t = scales.astype(np.float64)[None, :, :] * xs.astype(np.float64)[:, None, :] * acc.astype(np.float64)
-    bound = 1e-5 * np.maximum(np.abs(y_ref.astype(np.float64)), np.abs(t).sum(-1) / np.sqrt(acc.shape[-1]))
-    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
-    return bool(np.all(err <= bound)), int((y != y_ref).sum())
+    return bounds.int8_y_ok(y, y_ref, acc, scales, xs)
 
 
 def run_xs_case(w, xf, scales, fmts=FMTS, label="", exact=False):

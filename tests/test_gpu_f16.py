@@ -16,6 +16,7 @@ import pytest
 
 import bit_gemv_decode_amd as B
 import oracle as O
+from oracle import bounds
 from bit_gemv_decode_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -34,11 +35,7 @@ def _dev():
 
 
 def f16_bound(w, s, x16, y_ref):
-    n, k = w.shape
-    prod = np.abs(x16.astype(np.float64))[:, None, :] * np.abs(w.astype(np.float64))[None, :, :]  # m, n, k
-    sg = prod.reshape(x16.shape[0], n, k // 128, 128).sum(-1)
-    t = (np.abs(s.astype(np.float64))[None, :, :] * sg).sum(-1)
-    return 2.0**-22 * np.abs(y_ref.astype(np.float64)) + 2.0**-17 * t
+    return bounds.f16_bound(w, s, x16, y_ref)
 
 
 def run_f16(w, s, x16, label="", exact_check=True):
@@ -178,9 +175,7 @@ def test_thin_batch_xs_after_f16_kernel():
         torch.cuda.synchronize()
         y = y.cpu().numpy()
         assert np.all(np.isfinite(y))
-        t = s.astype(np.float64)[None] * xs_ref.astype(np.float64)[:, None, :] * acc_ref.astype(np.float64)
-        bound = 1e-5 * np.maximum(np.abs(y_ref.astype(np.float64)), np.abs(t).sum(-1) / np.sqrt(k // 128))
-        assert np.all(np.abs(y.astype(np.float64) - y_ref.astype(np.float64)) <= bound)
+        assert bounds.int8_y_ok(y, y_ref, acc_ref, s, xs_ref)[0]
 
 
 @pytest.mark.parametrize("m", [1, 2, 4])

@@ -12,6 +12,7 @@ import pytest
 
 import bit_gemv_decode_amd as B
 import oracle as O
+from oracle import bounds
 from bit_gemv_decode_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -30,9 +31,7 @@ def _dev():
 
 
 def y_ok(y, y_ref, acc, scales):
-    t = np.abs(scales.astype(np.float64)[None] * acc.astype(np.float64)).sum(-1) / np.sqrt(acc.shape[-1])
-    bound = 1e-5 * np.maximum(np.abs(y_ref.astype(np.float64)), t)
-    return bool(np.all(np.abs(y.astype(np.float64) - y_ref.astype(np.float64)) <= bound))
+    return bounds.int8_y_ok(y, y_ref, acc, scales)[0]
 
 
 # single-chunk rows of every step width (k = 128 .. 8192), ragged row counts, chunked rows (k > 8192)
