@@ -52,24 +52,33 @@ def kernel_source_hash() -> str:
 
 
 class LayerSet:
-    """The 7 matrices of one layer packed in `fmt`, stored `layers` times in device memory."""
+    """Matrices of one decoder layer packed in `fmt`, stored `layers` times in device memory.
 
-    def __init__(self, B, synth, torch, dev, fmt, layers=LAYERS):
+    shapes: (name, n, k) per matrix role; z: zero density; dead: row indices that are all zero in the
+    roles named in dead_roles (the same indices in each, as in the 70B-shaped stack)."""
+
+    def __init__(self, B, synth, torch, dev, fmt, layers=LAYERS, shapes=None, z=Z, dead=None,
+                 dead_roles=("gate", "up")):
         self.fmt = fmt
+        self.shapes = list(shapes) if shapes is not None else list(LAYER)
+        self.layers = layers
         self.mats = []      # per layer copy: list of dict(w=DeviceWeights, s, x, y)
         self.host = []      # one host copy per matrix role (for the CPU baseline)
         base = []
-        for role, (name, n, k) in enumerate(LAYER):
-            w = synth.ternary(n, k, Z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+        for role, (name, n, k) in enumerate(self.shapes):
+            w = synth.ternary(n, k, z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+            if dead is not None and name in dead_roles:
+                w[dead] = 0
             s = synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))
             x = synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))
             # t5b carries one scale per tensor instead of per-group scales
             p = B.pack_t5b(w, T5B_SCALE) if fmt == B.FMT_T5B else B.pack(fmt, w)
             self.host.append(dict(name=name, n=n, k=k, packed=p, s=s, x=x))
             base.append((B.DeviceWeights(p, dev), torch.from_numpy(s).to(dev), torch.from_numpy(x).to(dev)))
+            del w
         for layer in range(layers):
             row = []
-            for (dw, s, x), (name, n, k) in zip(base, LAYER):
+            for (dw, s, x), (name, n, k) in zip(base, self.shapes):
                 t = dw.tensor if layer == 0 else dw.tensor.clone()
                 row.append(dict(name=name, w=B.DeviceWeights.from_tensor(dw.desc, t), s=s if layer == 0 else s.clone(),
                                 x=x, y=torch.empty((1, n), dtype=torch.float32, device=dev)))
@@ -84,6 +93,22 @@ class LayerSet:
         mats = mats if mats is not None else self.flat()
         return B.Plan([m["w"] for m in mats], [m["x"] for m in mats],
                       scales=None if self.fmt == B.FMT_T5B else [m["s"] for m in mats], ys=[m["y"] for m in mats])
+
+
+# The 70B-shaped dense decoder: 64 layers, hidden 5120, FFN 25600, GQA k/v 1024 rows, z = 0.47, and
+# 4.76 % of FFN neurons (1219 of 25600) all-zero at the same indices in gate and up ("Sub-Two-Bit
+# Ternary Weight Storage with Table-Free Arithmetic Decoding", abstract: dead FFN neurons).
+STACK70B = [("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
+            ("gate", 25600, 5120), ("up", 25600, 5120), ("down", 5120, 25600)]
+STACK70B_LAYERS = 64
+STACK70B_Z = 0.47
+STACK70B_DEAD = 1219
+
+
+def stack70b(B, synth, torch, dev, layers=STACK70B_LAYERS):
+    """The 70B-shaped stack in BITCOS: one layer generated and stored `layers` times (6.08 GB for 64)."""
+    dead = synth.dead_rows(25600, STACK70B_DEAD, seed=0)
+    return LayerSet(B, synth, torch, dev, B.FMT_BITCOS, layers=layers, shapes=STACK70B, z=STACK70B_Z, dead=dead), dead
 
 
 def time_launches(torch, fn, steps, warmup):
@@ -369,39 +394,22 @@ def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
     return out
 
 
-def suite_70b(torch, B, synth, dev, layers=64, z=0.47):
+def suite_70b(torch, B, synth, dev, layers=STACK70B_LAYERS):
     """Llama-70B-shaped layer stack at batch 1 (q, o 5120x5120; k, v 1024x5120; gate, up 25600x5120;
     down 5120x25600), 1219 dead FFN rows per layer at the same indices in gate and up. One layer is
     generated and stored `layers` times (6.08 GB of BITCOS for 64), so every byte comes from HBM."""
-    shapes = [("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
-              ("gate", 25600, 5120), ("up", 25600, 5120), ("down", 5120, 25600)]
-    dead = synth.dead_rows(25600, 1219, seed=0)
-    base = []
-    for role, (name, n, k) in enumerate(shapes):
-        w = synth.ternary(n, k, z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
-        if name in ("gate", "up"):
-            w[dead] = 0
-        s = torch.from_numpy(synth.scales(n, k // 128, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_SCALE))).to(dev)
-        x = torch.from_numpy(synth.activations(1, k, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_X))).to(dev)
-        base.append((B.DeviceWeights(B.pack_bitcos(w), dev), s, x, n))
-        del w
-    dws, xs, ss, ys = [], [], [], []
-    for layer in range(layers):
-        for dw0, s, x, n in base:
-            dws.append(dw0 if layer == 0 else B.DeviceWeights.from_tensor(dw0.desc, dw0.tensor.clone()))
-            xs.append(x)
-            ss.append(s)
-            ys.append(torch.empty((1, n), dtype=torch.float32, device=dev))
+    st_set, dead = stack70b(B, synth, torch, dev, layers)
+    mats = st_set.flat()
+    dws, xs, ss, ys = [m["w"] for m in mats], [m["x"] for m in mats], [m["s"] for m in mats], [m["y"] for m in mats]
     st = sustained(torch, B, dws, xs, ss, ys, launches=5)
-    per_layer = [B.Plan(dws[7 * l:7 * l + 7], xs[7 * l:7 * l + 7], scales=ss[7 * l:7 * l + 7], ys=ys[7 * l:7 * l + 7])
-                 for l in range(layers)]
+    per_layer = [st_set.plan(B, row) for row in st_set.mats]
     settle(torch, lambda: [p.run() for p in per_layer])
     sl = time_launches(torch, lambda: [p.run() for p in per_layer], 3, 0)
-    out = {"layers": layers, "z": z, "dead_rows_per_layer": int(dead.size), "bytes_per_pass": st["bytes_per_launch"],
+    out = {"layers": layers, "z": STACK70B_Z, "dead_rows_per_layer": int(dead.size), "bytes_per_pass": st["bytes_per_launch"],
            "grouped_one_launch": {"gbs": st["gbs"], "us_per_pass": round(st["ms_per_launch"] * 1e3, 1)},
            "per_layer_launch": {"gbs": round(st["bytes_per_launch"] * 3 / sl / 1e9, 1),
                                 "us_per_pass": round(sl / 3 * 1e6, 1)}}
-    del dws, per_layer
+    del st_set, per_layer
     torch.cuda.empty_cache()
     log("[suite] 70B-shaped stack done")
     return out
