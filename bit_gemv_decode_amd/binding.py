@@ -44,14 +44,14 @@ class TgDesc(ctypes.Structure):
                 ("off_signs", ctypes.c_uint64), ("bytes_signs", ctypes.c_uint64),
                 ("off_index", ctypes.c_uint64), ("bytes_index", ctypes.c_uint64),
                 ("bytes_total", ctypes.c_uint64), ("bytes_payload", ctypes.c_uint64),
-                ("tensor_scale", ctypes.c_uint32), ("reserved32", ctypes.c_uint32), ("reserved", ctypes.c_uint64)]
+                ("tensor_scale", ctypes.c_uint32), ("empty_rows", ctypes.c_uint32), ("reserved", ctypes.c_uint64)]
 
 
 class TgPlan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("fmt", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("count", ctypes.c_int32), ("units", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
                 ("acc_mode", ctypes.c_int32), ("waves", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("decode", ctypes.c_int32), ("table", ctypes.c_void_p)]
+                ("decode", ctypes.c_int32), ("live_rows", ctypes.c_int32), ("table", ctypes.c_void_p)]
 
 
 _lib = None

@@ -46,6 +46,7 @@ Problem make_problem(const tg_desc *d, const void *W, const uint16_t *scales, co
     p.n = (int32_t)d->n;
     p.k = (int32_t)d->k;
     if (d->fmt == TG_FMT_T5B) memcpy(&p.tscale, &d->tensor_scale, 4);
+    if (d->fmt == TG_FMT_BITCOS) p.empty_rows = (int32_t)d->empty_rows;
     return p;
 }
 
@@ -161,6 +162,7 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
             geometry(g.one, desc->fmt, mt, mfma, true);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
+        g.live = desc->fmt == TG_FMT_BITCOS && desc->empty_rows > 0 && mt == 1 && !mfma && out != kOutAcc;
         if (g.units < 1) return TG_ESHAPE;
     }
     for (int i = 0; i < nl; ++i)
@@ -255,10 +257,16 @@ double pass_cost(int fmt, int rows_per_unit) { return (fmt == TG_FMT_BITCOS ? 2.
 // vector path costs about the same (one 128-weight group per lane, however many lanes are busy), so a
 // unit costs its step count, plus the activation reloads of chunked rows; a unit of the matrix-core
 // path costs its chunk count (all units of one plan take the same path).
-double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u) {
+double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u, bool live) {
     const int64_t row0 = (u - p.unit_begin) * (int64_t)p.rpu;
     const int64_t rows = std::min<int64_t>(p.rpu, (int64_t)p.n - row0);
     if (mfma) return (double)((p.ng + 7) / 8);
+    // A launch that walks only the rows with non-zeros skips the empty ones, but an empty row's step
+    // costs less than a full one on the plain walk too (every lane reads the same table entries) and
+    // the walk adds a little per step: counting an empty row as half a step balanced best on MI355X
+    // (the 70B-shaped stack, against no credit and a full one, identical outputs).
+    if (live && p.nch == 1 && p.R == 1 && p.empty_rows > 0)
+        return (double)rows * (1.0 - 0.5 * (double)p.empty_rows / (double)p.n);
     if (p.nch == 1) return (double)((rows + p.R - 1) / p.R);
     return (double)rows * ((double)p.nch + pass_cost(fmt, p.rpu));
 }
@@ -324,6 +332,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     const bool mfma = f16 ? m >= kF16MfmaMinM || (m == 2 && 2 * w_mfma > w_all)
                           : fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
     const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : kPathVector;
+    bool any_empty = false;
+    for (int32_t i = 0; i < count; ++i) any_empty = any_empty || host[i].empty_rows > 0;
+    const bool live = fmt == TG_FMT_BITCOS && m == 1 && path == kPathVector && !acc_mode && any_empty;
     for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, false, f16);
     {
         int64_t ub = 0;
@@ -352,7 +363,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     double total_cost = 0;
     for (int32_t i = 0; i < count; ++i)
         for (int64_t u = host[i].unit_begin; u < host[i].unit_begin + host[i].nunits; ++u)
-            total_cost += unit_cost(host[i], fmt, mfma, u);
+            total_cost += unit_cost(host[i], fmt, mfma, u, live);
     // Contiguous unit ranges per wave, balanced by the cost model above.
     const int nw = path_waves(fmt, m, path);
     std::vector<WaveRange> ranges((size_t)nw);
@@ -366,7 +377,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
             const double target = total_cost * (double)(w + 1) / (double)nw;
             while (u < units) {
                 while (pi + 1 < count && u >= host[pi + 1].unit_begin) ++pi;
-                const double cost = unit_cost(host[pi], fmt, mfma, u);
+                const double cost = unit_cost(host[pi], fmt, mfma, u, live);
                 if (done + 0.5 * cost > target && w + 1 < nw) break;
                 done += cost;
                 ++u;
@@ -391,6 +402,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     plan->acc_mode = acc_mode ? kOutAcc : xs ? kOutYxs : kOutY;
     plan->waves = nw;
     plan->path = path;
+    plan->live_rows = live ? 1 : 0;
     plan->table = table;
     return TG_OK;
 }
@@ -446,7 +458,9 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
         (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)) ||
         (plan->path == kPathF16Mfma &&
          (plan->fmt != TG_FMT_BITCOS || plan->m < 2 || plan->acc_mode != kOutY)) ||
-        (plan->decode != TG_DECODE_BYTE && (plan->decode != TG_DECODE_NIBBLE || !nibble_ok(plan))))
+        (plan->decode != TG_DECODE_BYTE && (plan->decode != TG_DECODE_NIBBLE || !nibble_ok(plan))) ||
+        (plan->live_rows != 0 && (plan->live_rows != 1 || plan->fmt != TG_FMT_BITCOS || plan->m != 1 ||
+                                  plan->path != kPathVector || plan->acc_mode == kOutAcc)))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;
@@ -458,6 +472,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     g.units = plan->units;
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
+    g.live = plan->live_rows;
     if (plan->decode == TG_DECODE_NIBBLE)
         return launch_bitcos_nibble(g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->path == kPathF16) return launch_bitcos_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;

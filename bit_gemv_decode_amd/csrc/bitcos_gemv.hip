@@ -417,11 +417,170 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     }
 }
 
-template <int M, bool ACC, int NB, bool XS, bool F16, bool NIB>
+// Row sums of a finished tile of four one-row steps whose output rows are r0..r3 (wave-uniform; a
+// negative row stores nothing): the lane holding tile row i's sum picks ri with selects on scalar
+// operands and stores it.
+__device__ __forceinline__ void reduce_store_rows(const Ctx &x, const Red &r, const double *tile, int r0, int r1,
+                                                  int r2, int r3) {
+    __builtin_amdgcn_wave_barrier();
+    double t = 0.0;
+    for (int e = 0; e < r.epl; ++e)
+        if (e < r.cnt) t += tile[r.base + e];
+    const uint32_t yv = __builtin_bit_cast(uint32_t, (float)seg_sum_f64(t, r.lpr));
+    __builtin_amdgcn_wave_barrier();
+    const int lo = (r.rho & 1) ? r1 : r0, hi = (r.rho & 1) ? r3 : r2;
+    const int row = (r.rho & 2) ? hi : lo;
+    st1(yv, x.ry, r.own && row >= 0 ? (uint32_t)row * 4u : kOffOff, 0u);
+}
+
+// Single-chunk GEMVs with one row per step (32 < k/128 <= 64) at m = 1 with fp32 outputs, when the
+// descriptor reports rows without non-zero weights (the dead FFN neurons of "Sub-Two-Bit Ternary
+// Weight Storage with Table-Free Arithmetic Decoding", abstract: all-zero rows at the same indices in
+// gate and up). A row is empty exactly when its index entries are equal, rowoff[r + 1] == rowoff[r]
+// (every non-zero weight has one sign), so the index alone finds them: the steps walk the non-empty
+// rows only, and each empty row's output is stored as 0 without reading its bitmap or scales. An
+// empty row holds no signs, so the sign cursor of the next row is unchanged.
+//
+// Rows [row_begin, row_end), at most kLiveSegRows of them. First, 64-row windows of the index are
+// read (eight windows' loads in flight at a time); a ballot of rowoff[r + 1] != rowoff[r] gives each
+// window's mask of non-empty rows, which lane w keeps for window w (two registers), and the empty
+// rows' outputs are stored. The step count is then exact, and each step of the pipeline of run_loop
+// (bitmap at step h, signs at h - 2, decode at h - 4) takes its row from the lowest set bit of the
+// current window's mask; each step's row rides along in a four-slot ring, and the tile's rows go to
+// their output rows by scalar selects.
+constexpr int kLiveSegRows = 64 * 64;
+
+template <bool XS>
+__device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, int row_end, const char *lds,
+                                              double *tile) {
+    constexpr int M = 1, NB = 4, U = 4, LAG = 2, XW = 32;
+    constexpr uint32_t XB = 4u * XW;
+    const int lane = threadIdx.x & 63;
+    Ctx x;
+    x.n = p.n;
+    x.k = p.k;
+    x.ng = p.ng;
+    x.nch = p.nch;
+    x.G = p.G;
+    x.R = p.R;
+    x.glast = p.glast;
+    x.rbm = make_rsrc(p.codes, p.codes_bytes);
+    x.rsg = make_rsrc(reinterpret_cast<const uint8_t *>(p.signs) - 4, p.sign_bytes + 4u);
+    x.rsc = make_rsrc(p.scales, (uint32_t)p.n * (uint32_t)p.ng * 2u);
+    x.rro = make_rsrc(p.rowoff, (uint32_t)(p.n + 1) * 4u);
+    x.rx = make_rsrc(p.x, (uint32_t)p.k);
+    x.ry = make_rsrc(p.y, (uint32_t)p.n * 4u);
+    x.racc = make_rsrc(p.acc, 0u);
+    x.rxs = make_rsrc(p.xs, XS ? (uint32_t)p.ng * 4u : 0u);
+    const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
+    const uint32_t kb = (uint32_t)(p.k >> 3);
+    const bool act = lane < x.G;
+    const uint32_t voff_bm = act ? (uint32_t)lane * 16u : kOffOff;
+    const uint32_t voff_sc = act ? (uint32_t)lane * 2u : kOffOff;
+    const uint32_t voff_x = act ? (uint32_t)lane * XB : kOffOff;
+    const Red red = make_red(NB, 1, x.G, p.rmagic);
+
+    uint32_t xr[M][XW];
+    float xsv[M];
+    load_x<M, XW>(x, voff_x, xr);
+    load_xs<M, XS>(x, voff_x, xsv);
+    uint32_t cur = uniform_u32(buf_u32(x.rro, (uint32_t)row_begin * 4u));
+    // masks of the non-empty rows: lane w holds window w (rows row_begin + 64 w .. + 63)
+    const int nw = (row_end - row_begin + 63) >> 6;
+    uint32_t mlo = 0, mhi = 0;
+    int T = 0;
+    for (int w0 = 0; w0 < nw; w0 += 8) {
+        u32x2 pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = row_begin + 64 * (w0 + i) + lane;
+            pr[i] = __builtin_amdgcn_raw_buffer_load_b64(x.rro, w0 + i < nw ? (uint32_t)r * 4u : kOffOff, 0u, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = row_begin + 64 * (w0 + i) + lane;
+            const bool in = w0 + i < nw && r < row_end;
+            const bool live = in && pr[i].y != pr[i].x;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(live);
+            T += __builtin_popcountll(m);
+            mlo = lane == w0 + i ? (uint32_t)m : mlo;
+            mhi = lane == w0 + i ? (uint32_t)(m >> 32) : mhi;
+            st1(0u, x.ry, in && !live ? (uint32_t)r * 4u : kOffOff, 0u);
+        }
+    }
+    wait_x<M, XW>(xr);
+    wait_xs<M, XS>(xsv);
+    // windows holding non-empty rows (bit w: window w), so that the next one is found without a loop
+    const uint64_t nz = __builtin_amdgcn_ballot_w64(lane < nw && (mlo | mhi) != 0u);
+
+    u32x4 bm[4] = {};
+    SgBuf g[4] = {};
+    int rq[4] = {-1, -1, -1, -1};      // row of the step in each pipeline slot (-1: none)
+    int trow[NB] = {-1, -1, -1, -1};   // rows of the tile being filled
+    int cw = 0;                        // window of the next row
+    uint64_t cm = 0;                   // its non-empty rows not taken yet
+    uint64_t ahead = nz;               // windows after cw holding non-empty rows (all of nz at first)
+
+    for (int it = 0; U * it - 4 < T; ++it) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int h = U * it + j;
+            const int jb = j & 3;
+            // ---- decode step h - 4 ----
+            {
+                int acc[M];
+                decode<M, false, false>(bm[jb], g[jb], xr, lds, laneoff, acc);
+                trow[j] = rq[jb];
+                emit<M, false, NB, XS>(x, acc, (double)half_bits_to_float(g[jb].scale), xsv, tile, j, false, kOffOff, 0u);
+                if (j == NB - 1) reduce_store_rows(x, red, tile, trow[0], trow[1], trow[2], trow[3]);
+            }
+            TG_SCHED_FENCE();
+            // ---- row of step h (the next non-empty row), then its bitmap ----
+            {
+                // when the current window is used up, move to the next window with non-empty rows
+                // (selects only: every step runs the same instructions); past the last row, row = -1
+                const bool adv = cm == 0 && ahead != 0;
+                const int nwin = (int)__builtin_ctzll(ahead | (1ull << 63));
+                cw = adv ? nwin : cw;
+                ahead = adv ? ahead & (ahead - 1) : ahead;
+                const uint64_t fresh = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, cw) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane((int)mlo, cw);
+                cm = adv ? fresh : cm;
+                const int row = h < T ? row_begin + 64 * cw + (int)__builtin_ctzll(cm | (1ull << 63)) : -1;
+                cm &= cm - 1;
+                rq[jb] = row;
+                bm[jb] = ld4s(x.rbm, voff_bm, row >= 0 ? (uint32_t)row * kb : kDeadS);
+            }
+            TG_SCHED_FENCE();
+            // ---- signs of step h - LAG ----
+            {
+                const int row = rq[(j + 4 - LAG) & 3];
+                const bool live = row >= 0;
+                const uint32_t total = stage_signs<false>(x, bm[(j + 4 - LAG) & 3], cur, live, voff_sc,
+                                                          (uint32_t)(live ? row : 0) * (uint32_t)x.ng * 2u,
+                                                          g[(j + 4 - LAG) & 3]);
+                cur += live ? total : 0u;
+            }
+            TG_SCHED_FENCE();
+        }
+    }
+}
+
+template <int M, bool ACC, int NB, bool XS, bool F16, bool NIB, bool LIVE>
 __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, const char *lds, double *tile) {
-    if (p.nch == 1)
+    if (p.nch == 1) {
+        if constexpr (LIVE) {
+            static_assert(M == 1 && !ACC && !F16 && !NIB, "the live-row walk: m = 1, fp32 outputs");
+            if (p.R == 1 && p.empty_rows > 0) {
+                const int row_begin = (u0 - p.unit_begin) * p.rpu;
+                const int row_end = min(p.n, (u1 - p.unit_begin) * p.rpu);
+                for (int r = row_begin; r < row_end; r += kLiveSegRows)
+                    run_loop_live<XS>(p, r, min(row_end, r + kLiveSegRows), lds, tile);
+                return;
+            }
+        }
         run_loop<M, ACC, NB, false, XS, F16, NIB>(p, u0, u1, lds, tile);
-    else
+    } else
         if constexpr (M == 1) {
             if (p.nbu == kChunkRows1Fine)
                 run_loop<1, ACC, kChunkRows1Fine, true, XS, F16, NIB>(p, u0, u1, lds, tile);
@@ -434,7 +593,9 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
 
 // F16: fp16 activations, f16_waves(M) waves per CU (the 256-byte activation slices need the registers).
 // NIB: the nibble-keyed decode (its 32 KB table replaces the byte-keyed tables in LDS).
-template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false>
+// LIVE: single-chunk one-row-per-step GEMVs that report rows without non-zeros walk the other rows
+// only (m = 1, fp32 outputs); a separate build, so that the kernel without it keeps its registers.
+template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false, bool LIVE = false>
 __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
     GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
@@ -462,7 +623,7 @@ __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::B
         const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_problem<M, ACC, NB, XS, F16, NIB>(p, u, u1, lds, tile);
+        if (u < u1) run_problem<M, ACC, NB, XS, F16, NIB, LIVE>(p, u, u1, lds, tile);
         u = max(u, u1);
         ++pi;
     }
@@ -473,10 +634,17 @@ hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
     using C = Cfg<M, TG_FMT_BITCOS>;
     const int blocks = grid_blocks<C::WAVES>(g);
     if (blocks < 1) return hipErrorInvalidValue;
+    const bool live = M == 1 && g.live;
     if (out == kOutAcc)
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, true, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    else if (out == kOutYxs && live)
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, true, false, false, M == 1>), dim3(blocks), dim3(C::BLOCK), 0,
+                           s, g);
     else if (out == kOutYxs)
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
+    else if (live)
+        hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false, false, false, M == 1>), dim3(blocks), dim3(C::BLOCK),
+                           0, s, g);
     else
         hipLaunchKernelGGL((bitcos_gemv_kernel<M, false, false>), dim3(blocks), dim3(C::BLOCK), 0, s, g);
     return hipGetLastError();

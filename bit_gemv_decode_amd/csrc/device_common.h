@@ -149,6 +149,7 @@ __device__ __forceinline__ Problem uniform_problem(const Problem &q) {
     p.gmagic = uniform_u32(q.gmagic);
     p.rmagic = uniform_u32(q.rmagic);
     p.tscale = __builtin_bit_cast(float, uniform_u32(__builtin_bit_cast(uint32_t, q.tscale)));
+    p.empty_rows = uniform_i32(q.empty_rows);
     return p;
 }
 

@@ -147,7 +147,9 @@ int check_desc(const tg_desc *d, uint64_t limit) {
         if (!section_ok(d->off_index, d->bytes_index, d->off_signs + d->bytes_signs)) return TG_ECORRUPT;
         if (d->bytes_payload != d->bytes_codes + sign_bytes + d->bytes_index) return TG_ECORRUPT;
         if ((d->bytes_signs / 4) > 0xFFFFFFFFull) return TG_ECORRUPT;
+        if (d->empty_rows > n) return TG_ECORRUPT;
     } else {
+        if (d->empty_rows) return TG_ECORRUPT;
         uint64_t want = d->fmt == TG_FMT_5TRIT ? n * (k / TG_GROUP) * 26
                         : d->fmt == TG_FMT_T5B ? n * t5b_blocks(k) * 32
                                                : n * k / 4;
@@ -171,6 +173,7 @@ extern "C" int tg_pack_bitcos(const int8_t *w, int64_t n, int64_t k, void *out, 
     if (nnz > 0xFFFFFFFFull) return TG_ESHAPE;
     tg_desc d;
     fill_header(&d, TG_FMT_BITCOS, n, k, nnz);
+    d.empty_rows = (uint32_t)std::count(row_nnz.begin(), row_nnz.end(), 0u);
     uint64_t sign_bytes = (nnz + 7) / 8;
     d.off_codes = TG_HEADER_BYTES;
     d.bytes_codes = (uint64_t)n * k / 8;
@@ -372,14 +375,19 @@ int validate_contents(const uint8_t *base, const tg_desc &d) {
         const uint64_t *bm = (const uint64_t *)codes;
         const uint32_t *rowoff = (const uint32_t *)(base + d.off_index);
         if (rowoff[0] != 0 || rowoff[n] != d.nnz) return TG_ECORRUPT;
+        std::atomic<uint64_t> empty{0};
         parallel_rows(n, n * k / 8, [&](int64_t lo, int64_t hi) {
+            uint64_t e = 0;
             for (int64_t r = lo; r < hi; r++) {
                 uint64_t c = 0;
                 for (int64_t j = 0; j < k / 64; j++) c += (uint64_t)__builtin_popcountll(bm[r * (k / 64) + j]);
                 if (rowoff[r + 1] < rowoff[r] || rowoff[r + 1] - rowoff[r] != c) err = TG_ECORRUPT;
+                e += c == 0;
             }
+            empty += e;
         });
-        return err;
+        if (err) return err;
+        return empty.load() == d.empty_rows ? TG_OK : TG_ECORRUPT;
     }
     parallel_rows(n, n * k / 4, [&](int64_t lo, int64_t hi) {
         uint64_t local = 0;

@@ -49,6 +49,7 @@ struct Problem {
     uint32_t gmagic;          // ceil(65536 / G): lane / G as (lane * gmagic) >> 16 for lane < 64
     uint32_t rmagic;          // ceil(65536 / R): likewise for R
     float tscale;             // t5b: the per-tensor scale (other formats: unused)
+    int32_t empty_rows;       // BITCOS: rows without non-zeros the descriptor reports (a hint)
 };
 
 // Work units a wave processes: [begin, end), starting in GEMV `problem` of the table.
@@ -66,7 +67,8 @@ struct GroupArgs {
     int32_t m;                // activation rows (1 .. 3 on the vector path)
     int32_t rows_per_unit;    // unused (each GEMV's rows per unit are in Problem::rpu)
     int32_t waves;            // waves the launch must have (table mode: ranges has this many entries)
-    int32_t reserved;
+    int32_t live;             // BITCOS, m = 1, fp32 outputs: some GEMV reports rows without non-zeros,
+                              // and the launch walks only the other rows of such GEMVs
     Problem one;
 };
 

@@ -108,7 +108,10 @@ typedef struct tg_desc {
     uint64_t bytes_total; /* whole buffer, header included */
     uint64_t bytes_payload; /* algorithmic bytes: codes + ceil(nnz/8) sign bytes + index (no padding, no header) */
     uint32_t tensor_scale;  /* TG_FMT_T5B: the per-tensor scale, IEEE binary32 bits; 0 otherwise */
-    uint32_t reserved32;
+    uint32_t empty_rows;    /* TG_FMT_BITCOS: rows without a non-zero weight (rowoff[r + 1] == rowoff[r]),
+                               written by tg_pack_bitcos; 0 for the other formats. A hint only: the
+                               m = 1 kernel walks only the other rows of a GEMV that reports some (and
+                               stores 0 for these), and any value up to n gives the same results. */
     uint64_t reserved;
 } tg_desc;
 
@@ -254,6 +257,10 @@ typedef struct tg_plan {
     int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2 / 3: fp16
                             activations on the vector / matrix-core kernel */
     int32_t decode;      /* TG_DECODE_BYTE (set by every tg_plan_init*) or TG_DECODE_NIBBLE */
+    int32_t live_rows;   /* 1: some GEMV reports rows without non-zeros (tg_desc.empty_rows), and the
+                            launch (BITCOS, m = 1, vector path, fp32 outputs, byte-keyed decode) walks
+                            only the other rows of the GEMVs with one row per step, storing 0 for
+                            the empty ones; 0 otherwise */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 

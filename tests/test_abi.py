@@ -326,9 +326,9 @@ def test_f16_plan_argument_errors_before_any_gpu_work():
 
 def test_plan_struct_layout_and_decode_selection_errors():
     L = binding.lib()
-    # the C layout: ten 32-bit fields, then the table pointer
-    assert ctypes.sizeof(binding.TgPlan) == 48 and binding.TgPlan.table.offset == 40
-    assert binding.TgPlan.decode.offset == 36
+    # the C layout: eleven 32-bit fields, then the table pointer
+    assert ctypes.sizeof(binding.TgPlan) == 56 and binding.TgPlan.table.offset == 48
+    assert binding.TgPlan.decode.offset == 36 and binding.TgPlan.live_rows.offset == 40
     assert L.tg_plan_set_decode(None, 1) == -1
     assert L.tg_plan_set_decode(ctypes.byref(binding.TgPlan()), 1) == -1  # never initialised
     ok = dict(magic=0x4E4C5054, fmt=B.FMT_BITCOS, m=1, count=1, units=1, rows_per_unit=1, acc_mode=0, waves=8,
@@ -347,6 +347,32 @@ def test_plan_struct_layout_and_decode_selection_errors():
         assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0 and p.decode == 0
     p.decode = 5
     assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+    # a forged plan claiming the live-row walk where no kernel has it is refused before launching
+    for bad in (dict(live_rows=2), dict(live_rows=1, fmt=B.FMT_5TRIT), dict(live_rows=1, m=2),
+                dict(live_rows=1, acc_mode=1), dict(live_rows=1, path=1)):
+        p = binding.TgPlan(**{**ok, **bad})
+        assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+
+
+def test_empty_rows_field_checked():
+    # tg_desc.empty_rows: BITCOS rows without non-zeros (a hint for the kernel); at most n, zero for the
+    # other formats, and tg_validate compares it with the index.
+    w = synth.ternary(9, 256, 0.4, seed=4)
+    w[[1, 5, 6]] = 0
+    p = B.pack_bitcos(w)
+    assert p.desc.empty_rows == 3
+    B.validate(p.buf)
+    for value, code in ((10, -5), (2, -5), (4, -5)):
+        bad = _poke_desc(p.buf, "empty_rows", value)
+        with pytest.raises(B.TgError) as e:
+            B.validate(bad)
+        assert e.value.code == code
+    for fmt in (B.FMT_5TRIT, B.FMT_2BIT):
+        q = B.pack(fmt, w)
+        assert q.desc.empty_rows == 0
+        with pytest.raises(B.TgError) as e:
+            B.describe(_poke_desc(q.buf, "empty_rows", 1))
+        assert e.value.code == -5
 
 
 def _bitcos_desc(n, k, nnz):

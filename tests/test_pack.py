@@ -11,6 +11,8 @@ def _check_bitcos(w):
     p = B.pack_bitcos(w)
     o = O.bitcos_pack(w)
     assert p.nnz == o.nnz
+    # rows without non-zeros, as the oracle's index shows them (equal consecutive entries)
+    assert p.desc.empty_rows == int((np.diff(o.rowoff.astype(np.int64)) == 0).sum()) == int((~w.any(axis=1)).sum())
     assert np.array_equal(p.section("codes"), o.bitmap)
     assert np.array_equal(p.sign_bytes(), o.signs)
     assert np.array_equal(p.rowoff(), o.rowoff)
