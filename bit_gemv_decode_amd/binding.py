@@ -28,7 +28,9 @@ ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4
 EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_pack_t5b", "tg_describe", "tg_validate", "tg_unpack",
            "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "ternary_gemv_f16",
            "tg_plan_table_bytes",
-           "tg_plan_init", "tg_plan_init_xs", "tg_plan_init_f16", "ternary_gemv_plan", "tg_plan_set_decode", "tg_stream_read", "tg_strerror", "tg_version"]
+           "tg_plan_init", "tg_plan_init_xs", "tg_plan_init_f16", "ternary_gemv_plan", "tg_plan_init_noalloc",
+           "tg_plan_set_decode", "tg_stream_read", "tg_strerror", "tg_version"]
+NOALLOC_TABLE_BYTES = 256 * 1024
 
 
 class TgError(RuntimeError):
@@ -51,7 +53,8 @@ class TgPlan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("fmt", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("count", ctypes.c_int32), ("units", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
                 ("acc_mode", ctypes.c_int32), ("waves", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("decode", ctypes.c_int32), ("live_rows", ctypes.c_int32), ("table", ctypes.c_void_p)]
+                ("decode", ctypes.c_int32), ("live_rows", ctypes.c_int32), ("table_gen", ctypes.c_uint32),
+                ("table", ctypes.c_void_p)]
 
 
 _lib = None
@@ -100,6 +103,9 @@ def lib():
         L.tg_plan_init.argtypes = [ctypes.POINTER(TgPlan), p, sz, ctypes.c_int32, ctypes.POINTER(TgDesc), p, p, p, p,
                                    p, ctypes.c_int32]
         L.tg_plan_init.restype = ctypes.c_int
+        L.tg_plan_init_noalloc.argtypes = [ctypes.POINTER(TgPlan), ctypes.c_int32, ctypes.POINTER(TgDesc), p, p, p,
+                                           p, p, ctypes.c_int32]
+        L.tg_plan_init_noalloc.restype = ctypes.c_int
         L.ternary_gemv_plan.argtypes = [ctypes.POINTER(TgPlan), p]
         L.ternary_gemv_plan.restype = ctypes.c_int
         L.tg_stream_read.argtypes = [p, sz, p, ctypes.c_int32, ctypes.c_int32, p]
@@ -393,7 +399,7 @@ class Plan:
     references to every tensor it names, and its device table, for its lifetime.
     """
 
-    def __init__(self, weights, xs, scales=None, ys=None, accs=None, x_scales=None, f16=False):
+    def __init__(self, weights, xs, scales=None, ys=None, accs=None, x_scales=None, f16=False, noalloc=False):
         import torch
 
         count = len(weights)
@@ -433,13 +439,21 @@ class Plan:
                     if tuple(x_scales[i].reshape(m, -1).shape) != (m, w.k // TG_GROUP):
                         raise ValueError("x_scales has the wrong shape")
         L = lib()
-        nbytes = L.tg_plan_table_bytes(count)
-        self.table = torch.empty(nbytes, dtype=torch.uint8, device=xs[0].device)
         descs = (TgDesc * count)(*[w.desc for w in weights])
         P = ctypes.c_void_p * count
         ptr = lambda ts: P(*[t.data_ptr() for t in ts]) if ts is not None else None
         self.plan = TgPlan()
         self._keep = (list(weights), list(xs), scales, ys, accs, x_scales)
+        if noalloc:
+            # the table goes to the library's static device array (tg_plan_init_noalloc)
+            if f16 or x_scales is not None:
+                raise ValueError("tg_plan_init_noalloc takes int8 activations (fp32 y or int32 accumulators)")
+            self.table = None
+            _check(L.tg_plan_init_noalloc(ctypes.byref(self.plan), count, descs, ptr([w.tensor for w in weights]),
+                                          ptr(scales), ptr(xs), ptr(ys), ptr(accs), m), "tg_plan_init_noalloc")
+            return
+        nbytes = L.tg_plan_table_bytes(count)
+        self.table = torch.empty(nbytes, dtype=torch.uint8, device=xs[0].device)
         if f16:
             if acc_mode or x_scales is not None:
                 raise ValueError("fp16 plans write fp32 y only")

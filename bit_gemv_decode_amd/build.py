@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libternary_gemv.so")
-SOURCES = ["pack.cpp", "api.cpp", "bitcos_gemv.hip", "bitcos_mfma.hip", "fixed_gemv.hip", "actquant.hip", "stream_read.hip"]
+SOURCES = ["pack.cpp", "api.cpp", "bitcos_gemv.hip", "bitcos_mfma.hip", "fixed_gemv.hip", "actquant.hip", "stream_read.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -409,6 +409,16 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
 
 }  // namespace
 
+namespace tg {
+
+int plan_init_into(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                   const void *const *W, const uint16_t *const *scales, const int8_t *const *x, float *const *y,
+                   int32_t *const *acc, int32_t m) {
+    return plan_init_common(plan, table, table_bytes, count, descs, W, scales, x, nullptr, y, acc, m);
+}
+
+}  // namespace tg
+
 extern "C" int tg_plan_init(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
                             const void *const *W, const uint16_t *const *scales, const int8_t *const *x,
                             float *const *y, int32_t *const *acc, int32_t m) {
@@ -460,7 +470,8 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
          (plan->fmt != TG_FMT_BITCOS || plan->m < 2 || plan->acc_mode != kOutY)) ||
         (plan->decode != TG_DECODE_BYTE && (plan->decode != TG_DECODE_NIBBLE || !nibble_ok(plan))) ||
         (plan->live_rows != 0 && (plan->live_rows != 1 || plan->fmt != TG_FMT_BITCOS || plan->m != 1 ||
-                                  plan->path != kPathVector || plan->acc_mode == kOutAcc)))
+                                  plan->path != kPathVector || plan->acc_mode == kOutAcc)) ||
+        (plan->table_gen != 0 && !static_table_current(plan->table, plan->table_gen)))
         return TG_EINVAL;
     GroupArgs g{};
     g.table = (const Problem *)plan->table;

@@ -153,4 +153,13 @@ hipError_t launch_stream_read(const void *buf, uint32_t bytes, uint32_t *sink, i
 // Number of compute units of the current device (cached).
 int device_cus();
 
+// tg_plan_init writing its table into `table` (the body shared with tg_plan_init_noalloc).
+int plan_init_into(tg_plan *plan, void *table, size_t table_bytes, int32_t count, const tg_desc *descs,
+                   const void *const *W, const uint16_t *const *scales, const int8_t *const *x, float *const *y,
+                   int32_t *const *acc, int32_t m);
+
+// Whether `table` is the current device's static plan table and still holds generation `gen` (the
+// contents tg_plan_init_noalloc wrote for the plan that carries it).
+bool static_table_current(const void *table, uint32_t gen);
+
 }  // namespace tg

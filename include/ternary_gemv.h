@@ -261,6 +261,8 @@ typedef struct tg_plan {
                             launch (BITCOS, m = 1, vector path, fp32 outputs, byte-keyed decode) walks
                             only the other rows of the GEMVs with one row per step, storing 0 for
                             the empty ones; 0 otherwise */
+    uint32_t table_gen;  /* 0 for a caller-owned table; tg_plan_init_noalloc: the generation of the
+                            library's static table this plan was written into */
     void *table;         /* device table written by tg_plan_init */
 } tg_plan;
 
@@ -285,6 +287,29 @@ int tg_plan_init_f16(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
                      const void *const *W, const uint16_t *const *scales, const uint16_t *const *x16,
                      float *const *y, int32_t m);
 int ternary_gemv_plan(const tg_plan *plan, void *stream);
+
+/*
+ * tg_plan_init_noalloc: tg_plan_init for callers that cannot allocate device memory (code that runs
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * checks, work split and results as tg_plan_init, without the table argument: the table is written
+ * into the library's own static device array of TG_NOALLOC_TABLE_BYTES (one per GPU the library runs
+ * on, held until the process ends), with a synchronous hipMemcpy from host memory. It calls no
+ * hipMalloc or hipFree and no other allocating HIP or library routine. The plan is run with
+ * ternary_gemv_plan as usual.
+ * Limit: tg_plan_table_bytes(count) <= TG_NOALLOC_TABLE_BYTES (about 1400 GEMVs on a 256-CU GPU);
+ * larger counts return TG_ENOSPACE and leave the static table untouched.
+ * Sharing: every GPU has one static table, and it keeps what the last successful call wrote. Each
+ * call on a GPU whose count fits (successful or not) invalidates every plan made earlier by this
+ * function on that GPU: ternary_gemv_plan refuses them with TG_EINVAL. Calls and launches that
+ * overlap on one GPU race: a launch of an earlier static plan must have finished before the next
+ * call on that GPU, and two threads must not call it for one GPU at the same time.
+ * Errors: those of tg_plan_init, TG_ENOSPACE, and TG_EHIP when the static table's address cannot be
+ * obtained.
+ */
+#define TG_NOALLOC_TABLE_BYTES (256u * 1024u)
+int tg_plan_init_noalloc(tg_plan *plan, int32_t count, const tg_desc *descs, const void *const *W,
+                         const uint16_t *const *scales, const int8_t *const *x, float *const *y,
+                         int32_t *const *acc, int32_t m);
 
 /*
  * BITCOS decode strategy of a plan. TG_DECODE_BYTE (the default): one lookup per presence byte in a

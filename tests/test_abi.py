@@ -326,9 +326,10 @@ def test_f16_plan_argument_errors_before_any_gpu_work():
 
 def test_plan_struct_layout_and_decode_selection_errors():
     L = binding.lib()
-    # the C layout: eleven 32-bit fields, then the table pointer
+    # the C layout: twelve 32-bit fields, then the table pointer
     assert ctypes.sizeof(binding.TgPlan) == 56 and binding.TgPlan.table.offset == 48
     assert binding.TgPlan.decode.offset == 36 and binding.TgPlan.live_rows.offset == 40
+    assert binding.TgPlan.table_gen.offset == 44
     assert L.tg_plan_set_decode(None, 1) == -1
     assert L.tg_plan_set_decode(ctypes.byref(binding.TgPlan()), 1) == -1  # never initialised
     ok = dict(magic=0x4E4C5054, fmt=B.FMT_BITCOS, m=1, count=1, units=1, rows_per_unit=1, acc_mode=0, waves=8,
@@ -443,3 +444,25 @@ def test_multi_launch_calls_check_everything_before_enqueuing(fmt):
         d2.bytes_codes = 4
         assert L.ternary_gemv_acc(ctypes.byref(d2), dummy, dummy, dummy, m, None) == -5
     assert L.ternary_gemv(ctypes.byref(d), dummy, sc, dummy, dummy, 17, None) == -1
+
+
+def test_noalloc_plan_argument_errors_before_any_gpu_work():
+    # tg_plan_init_noalloc: the same checks as tg_plan_init; a count whose table exceeds the static
+    # array is TG_ENOSPACE before anything else happens
+    L = binding.lib()
+    w = synth.ternary(8, 256, 0.4, seed=1)
+    d = B.pack_bitcos(w).desc
+    descs = (binding.TgDesc * 1)(d)
+    P1 = ctypes.c_void_p * 1
+    ptrs = P1(256)
+    plan = binding.TgPlan()
+    assert L.tg_plan_init_noalloc(None, 1, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    assert L.tg_plan_init_noalloc(ctypes.byref(plan), 0, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -1
+    big = 1
+    while L.tg_plan_table_bytes(big) <= binding.NOALLOC_TABLE_BYTES:
+        big *= 2
+    assert L.tg_plan_init_noalloc(ctypes.byref(plan), big, descs, ptrs, ptrs, ptrs, ptrs, None, 1) == -6
+    # a plan claiming a static-table generation that is not the current one is refused
+    forged = binding.TgPlan(magic=0x4E4C5054, fmt=B.FMT_BITCOS, m=1, count=1, units=1, rows_per_unit=1, acc_mode=0,
+                            waves=8, path=0, table_gen=7, table=256)
+    assert L.ternary_gemv_plan(ctypes.byref(forged), None) == -1
