@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libternary_gemv.so")
+# TG_LIB_PATH selects another build of the library (e.g. one with sanitized host code)
+LIB_PATH = os.environ.get("TG_LIB_PATH") or os.path.join(PKG, "libternary_gemv.so")
 
 TG_GROUP = 128
 TG_MAX_M = 16

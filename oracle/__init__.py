@@ -36,9 +36,13 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build()
-        L = ctypes.CDLL(LIB)
+        # ORACLE_LIB selects another build of oracle.c (e.g. one with sanitizers); it is used as it is
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = LIB
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+        L = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
