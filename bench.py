@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 from bit_gemv_decode_amd.binding import FMT_T5B  # noqa: E402  (numpy and ctypes only)
 
 HBM_PEAK_GBS = 8000.0
-SETTLE_MS = 60.0  # GPU time of warm-up launches before a sustained-rate measurement (see --warmup)
+SETTLE_MS = 60.0  # GPU time of back-to-back launches before a sustained-rate measurement
 LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
 LAYERS = 32
@@ -158,23 +158,65 @@ def stream_ceiling(torch, bd, dev):
     return best
 
 
-def cpu_baseline(O, ls, budget_s=12.0):
-    """The oracle decoding BITCOS rows from packed bytes on the host cores, over one layer set."""
+def cpu_model():
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout.splitlines()
+        return [l.split(":", 1)[1].strip() for l in out if l.startswith("Model name")][0]
+    except Exception:
+        return "unknown"
+
+
+def cpu_baseline(O, ls, budget_s=12.0, one_core_budget_s=8.0):
+    """The oracle decoding BITCOS rows from packed bytes on the host cores, over one layer set: on
+    every core it may use (`value`, `cores`), and on one core."""
     total_bytes = sum(ls.layer_bytes)
-    times = []
-    t_all = time.time()
-    while True:
-        t0 = time.perf_counter()
-        for h in ls.host:
-            p = h["packed"]
-            O.gemv_packed(O.FMT_BITCOS, p.section("codes"), p.sign_bytes(), p.rowoff(), h["s"], h["n"], h["k"], h["x"])
-        times.append(time.perf_counter() - t0)
-        if time.time() - t_all > budget_s or len(times) >= 7:
-            break
-    t = float(np.median(times))
-    return dict(value=round(total_bytes / t / 1e9, 4), unit="GB/s", cores=int(O.threads()), kind="oracle",
+
+    def passes(budget, most):
+        times = []
+        t_all = time.time()
+        while True:
+            t0 = time.perf_counter()
+            for h in ls.host:
+                p = h["packed"]
+                O.gemv_packed(O.FMT_BITCOS, p.section("codes"), p.sign_bytes(), p.rowoff(), h["s"], h["n"], h["k"],
+                              h["x"])
+            times.append(time.perf_counter() - t0)
+            if time.time() - t_all > budget or len(times) >= most:
+                return float(np.median(times)), len(times)
+
+    cores = len(os.sched_getaffinity(0))
+    t, n = passes(budget_s, 7)
+    used = int(O.threads())
+    O.set_threads(1)
+    t1, n1 = passes(one_core_budget_s, 3)
+    O.set_threads(used)
+    return dict(value=round(total_bytes / t / 1e9, 4), unit="GB/s", cores=used, kind="oracle",
                 sample=f"one layer set (the 7 GEMVs, {total_bytes / 1e6:.1f} MB BITCOS, ~1/32 of a step), "
-                       f"median of {len(times)} passes, {t * 1e3:.1f} ms per pass")
+                       f"median of {n} passes, {t * 1e3:.1f} ms per pass",
+                one_core={"value": round(total_bytes / t1 / 1e9, 4), "unit": "GB/s",
+                          "ms_per_pass": round(t1 * 1e3, 1), "passes": n1},
+                cpu_model=cpu_model(), cores_available=cores)
+
+
+def cache_resident(torch, B, ls, copies=(1, 4), launches=200):
+    """Rate of one grouped launch over the first 1 and 4 layer copies (47 and 189 MB of BITCOS, inside
+    the 256 MB Infinity Cache once the first launch has read them), after SETTLE_MS of the same
+    launches. The marginal rate between the two cancels the fixed cost of a launch: the decode rate
+    with the weights served from the cache instead of HBM."""
+    res = {}
+    for L in copies:
+        p = ls.plan(B, [m for row in ls.mats[:L] for m in row])
+        settle(torch, p.run)
+        s = time_launches(torch, p.run, launches, 0) / launches
+        nbytes = L * sum(ls.layer_bytes)
+        res[f"layers_{L}"] = {"mb": round(nbytes / 1e6, 1), "us_per_launch": round(s * 1e6, 2),
+                              "gbs": round(nbytes / s / 1e9, 1)}
+        del p
+    a, b = res[f"layers_{copies[0]}"], res[f"layers_{copies[-1]}"]
+    res["marginal_gbs"] = round((b["mb"] - a["mb"]) * 1e6 / ((b["us_per_launch"] - a["us_per_launch"]) * 1e-6) / 1e9, 1)
+    res["fixed_us_per_launch"] = round(a["us_per_launch"] - a["mb"] * 1e6 / (res["marginal_gbs"] * 1e9) * 1e6, 2)
+    return res
 
 
 def activation_quant(torch, B, synth, ls, dev, steps, warmup):
@@ -417,14 +459,8 @@ def suite_70b(torch, B, synth, dev, layers=STACK70B_LAYERS):
 
 def suite_cpu(O, B, synth):
     """The oracle from packed BITCOS bytes on one core and on all cores (2560x2560 and 4096x4096)."""
-    import subprocess
-    try:
-        model = [l.split(":", 1)[1].strip() for l in subprocess.run(["lscpu"], capture_output=True, text=True).stdout.splitlines()
-                 if l.startswith("Model name")][0]
-    except Exception:
-        model = "unknown"
     cores = len(os.sched_getaffinity(0))
-    out = {"cpu_model": model, "cores_available": cores}
+    out = {"cpu_model": cpu_model(), "cores_available": cores}
     for n, k, z in ((2560, 2560, 0.42), (4096, 4096, 0.40)):
         w = synth.ternary(n, k, z, seed=0)
         p = B.pack_bitcos(w)
@@ -480,12 +516,13 @@ def run_suite(path):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # Back-to-back launches on MI355X run through a power transient: after a few fast launches the
-    # step time rises by up to ~50 % and decays back over 25-40 ms of load, 70-110 steps of this
-    # workload (per-launch kernel trace; isolated launches run at the settled rate). The default
-    # warm-up of 150 steps (~55 ms) covers it, so the timed steps are the sustained rate.
-    ap.add_argument("--warmup", type=int, default=150)
+    # Back-to-back launches of a decode-heavy kernel on MI355X run through a clock transient: the
+    # shader clock drops a few milliseconds into the load and recovers over some tens of
+    # milliseconds (`python -m bit_gemv_decode_amd.profiling transient` measures it). The timed
+    # region is what --steps/--warmup say, transient included; the `settled` field times the same
+    # launches again after SETTLE_MS of load.
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--quick", action="store_true", help="only the timed BITCOS step (for profiling runs)")
     ap.add_argument("--suite", metavar="PATH", help="run the measurement suite over every workload "
@@ -538,7 +575,6 @@ def main():
                    "zero_density": Z, "group": 128, "layers": LAYERS, "gemvs_per_step": LAYERS * len(LAYER),
                    "format": "bitcos", "m": 1},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "us_per_layer": round(step_s * 1e6 / LAYERS, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic["bytes_per_launch"] / ls.step_bytes, 4) if traffic else None),
@@ -550,6 +586,12 @@ def main():
         out["roofline"]["traffic_note"] = (f"HBM bytes per launch / algorithmic bytes, from rocprofv3 "
                                            f"FETCH_SIZE+WRITE_SIZE scaled by the stream-read calibration "
                                            f"({os.path.relpath(TRAFFIC_FILE, ROOT)})")
+    # the same launches again once the GPU has run them back to back for SETTLE_MS (an extra field:
+    # `value` above is the timed region of this command as given)
+    settle(torch, plan.run)
+    s_set = time_launches(torch, plan.run, args.steps, 0) / args.steps
+    out["settled"] = {"gbs": round(ls.step_bytes / s_set / 1e9, 1), "ms_per_step": round(s_set * 1e3, 4),
+                      "note": f"same step, timed after {SETTLE_MS:.0f} ms of back-to-back launches"}
     if args.quick:
         print(json.dumps(out), flush=True)
         return
@@ -568,7 +610,8 @@ def main():
     out["modes"] = {
         "grouped_one_launch": {"gbs": round(gbs, 1), "ms_per_step": round(step_s * 1e3, 3)},
         "per_layer_launch": {"gbs": round(ls.step_bytes * n_pl / s_layer / 1e9, 1),
-                             "ms_per_step": round(s_layer / n_pl * 1e3, 3), "launches_per_step": LAYERS},
+                             "ms_per_step": round(s_layer / n_pl * 1e3, 3), "launches_per_step": LAYERS,
+                             "us_per_launch": round(s_layer / n_pl / LAYERS * 1e6, 2)},
         "per_gemv_launch_graph": {"gbs": round(ls.step_bytes * n_pl / s_call / 1e9, 1),
                                   "ms_per_step": round(s_call / n_pl * 1e3, 3),
                                   "launches_per_step": LAYERS * len(LAYER)},
@@ -588,6 +631,8 @@ def main():
     out["per_matrix_single_call"] = per_mat
     del layer_plans, g
     torch.cuda.empty_cache()
+    log("[bench] cache-resident decode rate (1 and 4 layer copies)")
+    out["cache_resident"] = {"bitcos": cache_resident(torch, B, ls)}
 
     log("[bench] float activations: quantiser and GEMV with activation group scales")
     out["activation_quant"] = activation_quant(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
@@ -618,6 +663,8 @@ def main():
         n_f = max(3, args.steps // 2)
         formats[fname] = {"gbs": round(lf.step_bytes * n_f / sf / 1e9, 1), "ms_per_step": round(sf / n_f * 1e3, 3),
                           "step_bytes": lf.step_bytes}
+        if fname != "t5b":
+            out["cache_resident"][fname] = cache_resident(torch, B, lf)
         del pf, lf
         torch.cuda.empty_cache()
     out["formats"] = formats

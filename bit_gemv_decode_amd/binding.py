@@ -30,7 +30,7 @@ EXPORTS = ["tg_pack_bitcos", "tg_pack_5trit", "tg_pack_2bit", "tg_pack_t5b", "tg
            "ternary_gemv", "ternary_gemv_acc", "tg_quantize_x", "ternary_gemv_xs", "ternary_gemv_f16",
            "tg_plan_table_bytes",
            "tg_plan_init", "tg_plan_init_xs", "tg_plan_init_f16", "ternary_gemv_plan", "tg_plan_init_noalloc",
-           "tg_plan_set_decode", "tg_stream_read", "tg_strerror", "tg_version"]
+           "tg_plan_set_decode", "tg_stream_read", "tg_clock_probe", "tg_strerror", "tg_version"]
 NOALLOC_TABLE_BYTES = 256 * 1024
 
 
@@ -109,6 +109,8 @@ def lib():
         L.tg_plan_init_noalloc.restype = ctypes.c_int
         L.ternary_gemv_plan.argtypes = [ctypes.POINTER(TgPlan), p]
         L.ternary_gemv_plan.restype = ctypes.c_int
+        L.tg_clock_probe.argtypes = [p, ctypes.c_uint32, ctypes.c_uint32, p]
+        L.tg_clock_probe.restype = ctypes.c_int
         L.tg_stream_read.argtypes = [p, sz, p, ctypes.c_int32, ctypes.c_int32, p]
         L.tg_stream_read.restype = ctypes.c_int
         L.tg_strerror.argtypes = [ctypes.c_int]
@@ -489,3 +491,15 @@ def stream_read(buf, sink, blocks: int, unroll: int, stream=None):
         raise ValueError("sink needs blocks * 4 words")
     _check(lib().tg_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.c_void_p(sink.data_ptr()),
                                 blocks, unroll, _stream_handle(stream)), "tg_stream_read")
+
+
+def clock_probe(out, slot: int, spin_ticks: int = 100, stream=None):
+    """Counter samples into out[4 slot .. 4 slot + 3] (an int64 device tensor): constant 100 MHz counter
+    and shader-clock counter, at the start and after spin_ticks of the constant counter (tg_clock_probe)."""
+    import torch
+
+    _require_cuda(out, torch.int64, "out")
+    if out.numel() < 4 * (slot + 1):
+        raise ValueError("out needs 4 * (slot + 1) values")
+    _check(lib().tg_clock_probe(ctypes.c_void_p(out.data_ptr()), slot, spin_ticks, _stream_handle(stream)),
+           "tg_clock_probe")

@@ -492,6 +492,11 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     return launch(plan->fmt, g, plan->acc_mode, mfma, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
 }
 
+extern "C" int tg_clock_probe(uint64_t *out, uint32_t slot, uint32_t spin_ticks, void *stream) {
+    if (!out || ((uintptr_t)out & 7) || spin_ticks > 100000000u) return TG_EINVAL;
+    return launch_clock_probe(out, slot, spin_ticks, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
+}
+
 extern "C" int tg_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, int32_t unroll,
                               void *stream) {
     if (!buf || !sink || blocks < 1 || ((uintptr_t)buf & 15) || bytes == 0 || bytes > 0xFFFFFFFFull || bytes % 16)

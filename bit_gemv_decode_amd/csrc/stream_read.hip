@@ -31,7 +31,34 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *buf, ui
     if (lane == 0) sink[wave] = acc;
 }
 
+// One wave samples the shader-clock counter (s_memtime, which counts at the shader clock) and the
+// constant 100 MHz counter (s_memrealtime) at its start, spins until `spin` ticks of the constant
+// counter have passed, and samples both again: slot i of out gets the four values. Launched between
+// other launches on a stream, consecutive probes bracket them (their duration, from the constant
+// counter) and each probe gives the shader clock of its moment ((memtime delta) / (realtime delta) x
+// 100 MHz).
+__global__ void clock_probe_kernel(uint64_t *out, uint32_t slot, uint32_t spin) {
+    if (threadIdx.x == 0) {
+        const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+        const uint64_t c0 = __builtin_amdgcn_s_memtime();
+        uint64_t r1 = r0, c1 = c0;
+        while (r1 - r0 < spin) {
+            r1 = __builtin_amdgcn_s_memrealtime();
+            c1 = __builtin_amdgcn_s_memtime();
+        }
+        out[4 * (uint64_t)slot] = r0;
+        out[4 * (uint64_t)slot + 1] = c0;
+        out[4 * (uint64_t)slot + 2] = r1;
+        out[4 * (uint64_t)slot + 3] = c1;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_clock_probe(uint64_t *out, uint32_t slot, uint32_t spin, hipStream_t s) {
+    hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, s, out, slot, spin);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void *buf, uint32_t bytes, uint32_t *sink, int blocks, int unroll, hipStream_t s) {
     const uint8_t *b = (const uint8_t *)buf;

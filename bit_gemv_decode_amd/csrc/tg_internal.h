@@ -149,6 +149,8 @@ hipError_t launch_quantize_x(const float *x, int64_t groups, int8_t *xq, float *
 
 // Streaming-read reference kernel (bandwidth ceiling probe).
 hipError_t launch_stream_read(const void *buf, uint32_t bytes, uint32_t *sink, int blocks, int unroll, hipStream_t s);
+// Clock probe: one wave writes four counter samples to out[4 slot .. 4 slot + 3].
+hipError_t launch_clock_probe(uint64_t *out, uint32_t slot, uint32_t spin, hipStream_t s);
 
 // Number of compute units of the current device (cached).
 int device_cus();

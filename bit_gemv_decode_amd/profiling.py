@@ -10,6 +10,11 @@
   python -m bit_gemv_decode_amd.profiling traffic FETCH_CSV WRITE_CSV OUT.json "COMMANDS"
       From a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run of `drive`: calibrates both counters
       against the known-size kernels and converts the BITCOS dispatch's counts into HBM bytes.
+  python -m bit_gemv_decode_amd.profiling transient OUT.md [LAUNCHES]
+      Launch by launch from an idle GPU: the grouped BITCOS and five-trit steps over the Llama3-8B
+      layer set and a stream read of the same number of bytes, each after two idle seconds, with a
+      clock probe (tg_clock_probe) between consecutive launches: per time window, the launches'
+      average duration, their rate and the shader clock. Twice each, in rotated order.
 
 The counters report KiB summed over the dispatch; the calibration factor is what the counter reads
 for the known-size kernel divided by the bytes that kernel moves.
@@ -71,6 +76,78 @@ def drive():
     plan.run()
     torch.cuda.synchronize()
     print(json.dumps({"step_bytes": ls.step_bytes}), flush=True)
+
+
+def _curve(torch, bd, fn, launches, spin=100):
+    """Durations (µs) of `launches` back-to-back calls of fn() from an idle GPU, and the shader clock
+    (MHz) sampled before each of them and after the last."""
+    import time
+
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(4 * (launches + 1), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    for i in range(launches):
+        bd.clock_probe(buf, i, spin)
+        fn()
+    bd.clock_probe(buf, launches, spin)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy().reshape(-1, 4).astype("float64")
+    dur = (b[1:, 0] - b[:-1, 2]) / 100.0  # from the end of one probe to the start of the next
+    mhz = (b[:, 3] - b[:, 1]) / (b[:, 2] - b[:, 0]) * 100.0
+    return dur, mhz
+
+
+def transient(out_md, launches=300):
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import bench
+    import bit_gemv_decode_amd as B
+    from bit_gemv_decode_amd import binding as bd
+    from bit_gemv_decode_amd import synth
+
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lb = bench.LayerSet(B, synth, torch, dev, B.FMT_BITCOS)
+    lt = bench.LayerSet(B, synth, torch, dev, B.FMT_5TRIT)
+    pb, pt = lb.plan(B), lt.plan(B)
+    sbuf = torch.empty(lb.step_bytes // 256 * 256, dtype=torch.uint8, device=dev)
+    sbuf.fill_(1)
+    sink = torch.empty(cus * 4 * 4, dtype=torch.int32, device=dev)
+    work = {"BITCOS step": (pb.run, lb.step_bytes), "five-trit step": (pt.run, lt.step_bytes),
+            "stream read": (lambda: bd.stream_read(sbuf, sink, cus * 4, 1), sbuf.numel())}
+    windows = ((0, 1), (1, 3), (3, 6), (6, 10), (10, 15), (15, 20), (20, 30), (30, 40), (40, 60), (60, 80), (80, 120))
+    res = {k: [] for k in work}
+    names = list(work)
+    for rep in range(2):
+        for name in names[rep % 3:] + names[:rep % 3]:
+            fn, nbytes = work[name]
+            dur, mhz = _curve(torch, bd, fn, launches)
+            t = np.cumsum(dur) / 1e3
+            rows = []
+            for lo, hi in windows:
+                sel = (t > lo) & (t <= hi)
+                if sel.any():
+                    rows.append((f"{lo}-{hi}", int(sel.sum()), float(dur[sel].mean()), nbytes / float(dur[sel].mean()) / 1e3,
+                                 float(mhz[1:][sel].mean())))
+            res[name].append(rows)
+            print(json.dumps({"transient": name, "rep": rep, "rows": rows}), flush=True)
+    lines = [f"# Launch-by-launch rate and shader clock from an idle GPU: `{os.path.basename(out_md)}`", "",
+             "Command (from the repository root):", "",
+             f"    python3 -m bit_gemv_decode_amd.profiling transient {os.path.relpath(out_md, ROOT)} {launches}", "",
+             "Each workload starts after two idle seconds and runs back to back; a one-wave clock probe between "
+             "consecutive launches timestamps them and samples the shader clock (s_memtime against the 100 MHz "
+             "s_memrealtime). Windows are milliseconds since the first launch.", ""]
+    for name in names:
+        for rep, rows in enumerate(res[name]):
+            lines += [f"## {name}, run {rep + 1}", "", "| Window (ms) | Launches | µs per launch | GB/s | Shader clock (MHz) |",
+                      "|---|---|---|---|---|"]
+            lines += [f"| {w} | {n} | {d:.1f} | {g:.0f} | {c:.0f} |" for w, n, d, g, c in rows]
+            lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
 
 
 def _rows(path):
@@ -140,5 +217,7 @@ if __name__ == "__main__":
         stats(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6]), *(int(a) for a in sys.argv[6:7]))
     elif cmd == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif cmd == "transient":
+        transient(sys.argv[2], *(int(a) for a in sys.argv[3:4]))
     else:
         raise SystemExit(f"unknown command {cmd}")

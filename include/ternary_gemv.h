@@ -334,6 +334,16 @@ int tg_plan_set_decode(tg_plan *plan, int32_t decode);
  */
 int tg_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, int32_t unroll, void *stream);
 
+/*
+ * Clock reference (not part of the GEMV): one wave writes four 64-bit counter samples to
+ * out[4 slot .. 4 slot + 3] (device, 8-byte aligned, the caller sizes it): the constant 100 MHz
+ * counter and the shader-clock counter at its start, and both again once spin_ticks (at most 10^8) of
+ * the constant counter have passed. Enqueued between other launches on one stream, consecutive
+ * probes bracket those launches (durations in 10 ns ticks), and each probe's two deltas give the
+ * shader clock at that moment. Asynchronous. Errors: TG_EINVAL, TG_EHIP.
+ */
+int tg_clock_probe(uint64_t *out, uint32_t slot, uint32_t spin_ticks, void *stream);
+
 /* Static string for a TG_* code ("unknown error" for anything else). */
 const char *tg_strerror(int code);
 
