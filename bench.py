@@ -199,7 +199,7 @@ def cpu_baseline(O, ls, budget_s=12.0, one_core_budget_s=8.0):
                 cpu_model=cpu_model(), cores_available=cores)
 
 
-def cache_resident(torch, B, ls, copies=(1, 4), launches=200):
+def cache_resident(torch, B, ls, copies=(1, 4), launches=200, decode=None):
     """Rate of one grouped launch over the first 1 and 4 layer copies (47 and 189 MB of BITCOS, inside
     the 256 MB Infinity Cache once the first launch has read them), after SETTLE_MS of the same
     launches. The marginal rate between the two cancels the fixed cost of a launch: the decode rate
@@ -207,6 +207,8 @@ def cache_resident(torch, B, ls, copies=(1, 4), launches=200):
     res = {}
     for L in copies:
         p = ls.plan(B, [m for row in ls.mats[:L] for m in row])
+        if decode is not None:
+            p.set_decode(decode)
         settle(torch, p.run)
         s = time_launches(torch, p.run, launches, 0) / launches
         nbytes = L * sum(ls.layer_bytes)
@@ -665,6 +667,14 @@ def main():
                           "step_bytes": lf.step_bytes}
         if fname != "t5b":
             out["cache_resident"][fname] = cache_resident(torch, B, lf)
+        if fname in ("5trit", "t5b"):
+            # the table-free decode of the same codes (digits by multiply and shift, no LDS table)
+            pf.set_decode(B.DECODE_ARITH)
+            sa = time_launches(torch, pf.run, n_f, args.warmup)
+            formats[fname]["table_free"] = {"gbs": round(lf.step_bytes * n_f / sa / 1e9, 1),
+                                            "ms_per_step": round(sa / n_f * 1e3, 3)}
+            if fname == "5trit":
+                out["cache_resident"]["5trit_table_free"] = cache_resident(torch, B, lf, decode=B.DECODE_ARITH)
         del pf, lf
         torch.cuda.empty_cache()
     out["formats"] = formats

@@ -21,7 +21,7 @@ TG_HEADER_BYTES = 256
 FMT_BITCOS, FMT_5TRIT, FMT_2BIT, FMT_T5B = 1, 2, 3, 4
 FMT_NAMES = {FMT_BITCOS: "bitcos", FMT_5TRIT: "5trit", FMT_2BIT: "2bit", FMT_T5B: "t5b"}
 T5B_BLOCK = 160
-DECODE_BYTE, DECODE_NIBBLE = 0, 1
+DECODE_BYTE, DECODE_NIBBLE, DECODE_ARITH = 0, 1, 2
 ERRORS = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOTTERNARY", -3: "TG_ESHAPE", -4: "TG_EFORMAT",
           -5: "TG_ECORRUPT", -6: "TG_ENOSPACE", -7: "TG_EHIP"}
 
@@ -473,7 +473,8 @@ class Plan:
                                   m), "tg_plan_init")
 
     def set_decode(self, decode: int):
-        """BITCOS decode strategy: DECODE_BYTE (default) or DECODE_NIBBLE (tg_plan_set_decode)."""
+        """Decode strategy: DECODE_BYTE (default), DECODE_NIBBLE (BITCOS) or DECODE_ARITH (five-trit,
+        t5b) (tg_plan_set_decode)."""
         _check(lib().tg_plan_set_decode(ctypes.byref(self.plan), decode), "tg_plan_set_decode")
         return self
 

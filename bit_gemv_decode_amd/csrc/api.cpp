@@ -447,15 +447,21 @@ bool nibble_ok(const tg_plan *p) {
            (p->acc_mode == kOutY || p->acc_mode == kOutAcc);
 }
 
+// Whether a plan may run the table-free five-trit decode.
+bool arith_ok(const tg_plan *p) {
+    return (p->fmt == TG_FMT_5TRIT || p->fmt == TG_FMT_T5B) && p->m == 1 && p->path == kPathVector &&
+           (p->acc_mode == kOutY || p->acc_mode == kOutAcc);
+}
+
+bool decode_ok(const tg_plan *p, int32_t decode) {
+    return decode == TG_DECODE_BYTE || (decode == TG_DECODE_NIBBLE && nibble_ok(p)) ||
+           (decode == TG_DECODE_ARITH && arith_ok(p));
+}
+
 }  // namespace
 
 extern "C" int tg_plan_set_decode(tg_plan *plan, int32_t decode) {
-    if (!plan || plan->magic != TG_PLAN_MAGIC) return TG_EINVAL;
-    if (decode == TG_DECODE_BYTE) {
-        plan->decode = decode;
-        return TG_OK;
-    }
-    if (decode != TG_DECODE_NIBBLE || !nibble_ok(plan)) return TG_EINVAL;
+    if (!plan || plan->magic != TG_PLAN_MAGIC || !decode_ok(plan, decode)) return TG_EINVAL;
     plan->decode = decode;
     return TG_OK;
 }
@@ -468,7 +474,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
         (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)) ||
         (plan->path == kPathF16Mfma &&
          (plan->fmt != TG_FMT_BITCOS || plan->m < 2 || plan->acc_mode != kOutY)) ||
-        (plan->decode != TG_DECODE_BYTE && (plan->decode != TG_DECODE_NIBBLE || !nibble_ok(plan))) ||
+        !decode_ok(plan, plan->decode) ||
         (plan->live_rows != 0 && (plan->live_rows != 1 || plan->fmt != TG_FMT_BITCOS || plan->m != 1 ||
                                   plan->path != kPathVector || plan->acc_mode == kOutAcc)) ||
         (plan->table_gen != 0 && !static_table_current(plan->table, plan->table_gen)))
@@ -486,6 +492,9 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     g.live = plan->live_rows;
     if (plan->decode == TG_DECODE_NIBBLE)
         return launch_bitcos_nibble(g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
+    if (plan->decode == TG_DECODE_ARITH)
+        return launch_five_trit_arith(plan->fmt, g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK
+                                                                                                         : TG_EHIP;
     if (plan->path == kPathF16) return launch_bitcos_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->path == kPathF16Mfma)
         return launch_bitcos_mfma_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;

@@ -216,11 +216,94 @@ __device__ __forceinline__ void decode_fixed(const CodeBuf &b, const uint32_t (&
     }
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Table-free decode of the five-trit code ("Sub-Two-Bit Ternary Weight Storage with Table-Free
+// Arithmetic Decoding", abstract: the depth-one arithmetic decode). Digit i of a code byte c is
+// floor(c / 3^i) - 3 floor(c / 3^(i+1)); every floor comes straight from c with one multiply and one
+// shift (f = (c * M) >> s with M / 2^s just above 3^-i, exact for every c < 243; all products stay
+// below 2^16), so no digit waits for another. Two codes are decoded together, one in each 16-bit half
+// of cp (c in the half's low byte); d[i] holds digit i of both.
+__device__ __forceinline__ void t5_digit_pairs(uint32_t cp, u16x2 (&d)[5]) {
+    const u16x2 c = __builtin_bit_cast(u16x2, cp);
+    const u16x2 f1 = (c * (unsigned short)171) >> (unsigned short)9;   // floor(c / 3)
+    const u16x2 f2 = (c * (unsigned short)57) >> (unsigned short)9;    // floor(c / 9)
+    const u16x2 f3 = (c * (unsigned short)19) >> (unsigned short)9;    // floor(c / 27)
+    const u16x2 f4 = (c * (unsigned short)203) >> (unsigned short)14;  // floor(c / 81)
+    const unsigned short m3 = (unsigned short)0xFFFDu;                 // -3 modulo 2^16
+    d[0] = f1 * m3 + c;
+    d[1] = f2 * m3 + f1;
+    d[2] = f3 * m3 + f2;
+    d[3] = f4 * m3 + f3;
+    d[4] = f4;
+}
+
+// Sums of the lane's weights times x with the table-free decode: the digits (0, 1, 2) are contracted as
+// they are and sx, the sum of the group's activations, is taken off once, since weight = digit - 1.
+// Four code bytes give four words of digits 0..3 (one per code, against xa[j]) and one word of their
+// fifth digits (against xb[q]), as in the table path.
+template <int FMT, int M>
+__device__ __forceinline__ void decode_fixed_arith(const CodeBuf &b, const uint32_t (&xf)[M][Fmt<FMT>::kXWords],
+                                                   const int (&sx)[M], int (&acc)[M]) {
+    static_assert(FMT == TG_FMT_5TRIT || FMT == TG_FMT_T5B, "five-trit codes");
+    constexpr int kBytes = FMT == TG_FMT_T5B ? 32 : 26;
+    constexpr int kRuns = (kBytes + 3) / 4;
+    uint32_t w[8] = {b.c[0].x, b.c[0].y, b.c[0].z, b.c[0].w, b.c[1].x, b.c[1].y, b.c[1].z, b.c[1].w};
+    if constexpr (FMT == TG_FMT_5TRIT) {
+#pragma unroll
+        for (int d = 0; d < 7; ++d) w[d] = __builtin_amdgcn_alignbit(w[d + 1], w[d], b.sh);
+    }
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) acc[mi] = -sx[mi];
+#pragma unroll
+    for (int q = 0; q < kRuns; ++q) {
+        uint32_t fifth[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // codes 4q + 2h and 4q + 2h + 1 into the low bytes of the two halves
+            const uint32_t cp = __builtin_amdgcn_perm(w[q], w[q], h ? 0x0C030C02u : 0x0C010C00u);
+            u16x2 dg[5];
+            t5_digit_pairs(cp, dg);
+            const uint32_t e0 = __builtin_bit_cast(uint32_t, dg[0]), e1 = __builtin_bit_cast(uint32_t, dg[1]);
+            const uint32_t e2 = __builtin_bit_cast(uint32_t, dg[2]), e3 = __builtin_bit_cast(uint32_t, dg[3]);
+            const uint32_t t01 = __builtin_amdgcn_perm(e1, e0, 0x06040200u);  // d0 lo, d0 hi, d1 lo, d1 hi
+            const uint32_t t23 = __builtin_amdgcn_perm(e3, e2, 0x06040200u);  // d2 lo, d2 hi, d3 lo, d3 hi
+            fifth[h] = __builtin_bit_cast(uint32_t, dg[4]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int j = 4 * q + 2 * h + c;  // code byte
+                if (j < kBytes) {
+                    const uint32_t dw = __builtin_amdgcn_perm(t23, t01, c ? 0x07050301u : 0x06040200u);
+#pragma unroll
+                    for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(dw, xf[mi][j], acc[mi]);
+                }
+            }
+        }
+        // fifth digits of the run's four codes (a five-trit group's last run reaches two bytes of the
+        // next group, whose digits meet activation positions past 127, which are zero)
+        const uint32_t w4 = __builtin_amdgcn_perm(fifth[1], fifth[0], 0x06040200u);
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(w4, xf[mi][kBytes + q], acc[mi]);
+    }
+}
+
+// Sum of the activations of the lane's group (the words of xf hold each of them once).
+template <int FMT, int M>
+__device__ __forceinline__ void xf_sums(const uint32_t (&xf)[M][Fmt<FMT>::kXWords], int (&sx)[M]) {
+#pragma unroll
+    for (int mi = 0; mi < M; ++mi) {
+        int s = 0;
+#pragma unroll
+        for (int j = 0; j < Fmt<FMT>::kXWords; ++j) s = dot4(0x01010101u, xf[mi][j], s);
+        sx[mi] = s;
+    }
+}
+
 // Pipeline over the steps of units [u0, u1) of one GEMV: in half-step h, step h - 3 is decoded and
 // the codes of step h are loaded (four code buffers rotate with the four half-steps of the loop
 // body). Every stage runs on every half-step; dead steps use dead offsets and decode into tile slots
 // a live step overwrites first.
-template <int FMT, int M, bool ACC, int NB, bool CHUNKED, bool XS>
+template <int FMT, int M, bool ACC, int NB, bool CHUNKED, bool XS, bool ARITH>
 __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, const char *lds, double *tile) {
     constexpr uint32_t GB = Fmt<FMT>::kGroupBytes;
     constexpr int XW = Fmt<FMT>::kXWords;
@@ -282,6 +365,8 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     load_xs<M, XS>(x, voff_x, xsv);
     wait_xf<FMT, M>(xf);
     wait_xs<M, XS>(xsv);
+    int sx[M];  // table-free decode: the group's activation sum (recomputed when a pass reloads xf)
+    if constexpr (ARITH) xf_sums<FMT, M>(xf, sx);
 
     CodeBuf cb[4] = {};
     int cD = 0, rD = row_begin, cB = 0, rB = row_begin;
@@ -296,8 +381,15 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                 const bool live = s >= 0 && s < T;
                 const CodeBuf &b = cb[(j + 1) & 3];
                 int acc[M];
-                decode_fixed<FMT, M>(b, xf, lds, laneoff, acc);
                 const int slot = (j + 1) % NB;
+                if constexpr (ARITH) {
+                    if constexpr (CHUNKED) {
+                        if (slot == 0) xf_sums<FMT, M>(xf, sx);  // static: first step of a pass
+                    }
+                    decode_fixed_arith<FMT, M>(b, xf, sx, acc);
+                } else {
+                    decode_fixed<FMT, M>(b, xf, lds, laneoff, acc);
+                }
                 if constexpr (!CHUNKED) {
                     const int row0 = row_begin + s * x.R;
                     const bool va = live && act && row0 + (int)(((uint32_t)lane * p.gmagic) >> 16) < row_end;
@@ -367,11 +459,12 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     }
 }
 
-template <int FMT, int M, bool ACC, bool XS>
+// ARITH: the table-free five-trit decode (no LDS table, so no table fill either).
+template <int FMT, int M, bool ACC, bool XS, bool ARITH = false>
 __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupArgs ga) {
     using C = Cfg<M, FMT>;
     constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
-    __shared__ uint4 s_lut[kLutBytes / 16];
+    __shared__ uint4 s_lut[ARITH ? 1 : kLutBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
     // those two dependent scalar round trips overlap the fill instead of following it.
@@ -380,7 +473,7 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
     wave_range<WAVES>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     const Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
-    {
+    if constexpr (!ARITH) {
         // units of 64 bytes (16 copies of a 2-bit entry, 8 of a five-trit one), one load each, all
         // loads before any LDS write: the fill is one memory round trip
         constexpr int kUnits = kLutBytes / 64;
@@ -406,8 +499,8 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
                                                          : make_uint4(v[r].x, v[r].y, v[r].x, v[r].y);
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_lut);
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
     bool first = true;
@@ -418,9 +511,9 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
         const int u1 = min(u_end, p.unit_begin + p.nunits);
         if (u < u1) {
             if (p.nch == 1)
-                run_fixed<FMT, M, ACC, NB, false, XS>(p, u, u1, lds, tile);
+                run_fixed<FMT, M, ACC, NB, false, XS, ARITH>(p, u, u1, lds, tile);
             else
-                run_fixed<FMT, M, ACC, NB, true, XS>(p, u, u1, lds, tile);
+                run_fixed<FMT, M, ACC, NB, true, XS, ARITH>(p, u, u1, lds, tile);
         }
         u = max(u, u1);
         ++pi;
@@ -463,6 +556,33 @@ hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s) {
 
 hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s) {
     return launch_fixed<TG_FMT_2BIT>(g, out, s);
+}
+
+hipError_t launch_five_trit_arith(int fmt, const GroupArgs &g, int out, hipStream_t s) {
+    if (g.m != 1 || (out != kOutY && out != kOutAcc) || (fmt != TG_FMT_5TRIT && fmt != TG_FMT_T5B))
+        return hipErrorInvalidValue;
+    if (fmt == TG_FMT_5TRIT) {
+        using C = Cfg<1, TG_FMT_5TRIT>;
+        const int blocks = grid_blocks<C::WAVES>(g);
+        if (blocks < 1) return hipErrorInvalidValue;
+        if (out == kOutAcc)
+            hipLaunchKernelGGL((fixed_gemv_kernel<TG_FMT_5TRIT, 1, true, false, true>), dim3(blocks), dim3(C::BLOCK), 0,
+                               s, g);
+        else
+            hipLaunchKernelGGL((fixed_gemv_kernel<TG_FMT_5TRIT, 1, false, false, true>), dim3(blocks), dim3(C::BLOCK),
+                               0, s, g);
+    } else {
+        using C = Cfg<1, TG_FMT_T5B>;
+        const int blocks = grid_blocks<C::WAVES>(g);
+        if (blocks < 1) return hipErrorInvalidValue;
+        if (out == kOutAcc)
+            hipLaunchKernelGGL((fixed_gemv_kernel<TG_FMT_T5B, 1, true, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s,
+                               g);
+        else
+            hipLaunchKernelGGL((fixed_gemv_kernel<TG_FMT_T5B, 1, false, false, true>), dim3(blocks), dim3(C::BLOCK), 0,
+                               s, g);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s) {

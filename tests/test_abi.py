@@ -348,6 +348,23 @@ def test_plan_struct_layout_and_decode_selection_errors():
         assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0 and p.decode == 0
     p.decode = 5
     assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+    # the table-free decode: five-trit and t5b plans at m = 1 on the vector path, y or accumulators
+    for fmt in (B.FMT_5TRIT, B.FMT_T5B):
+        for acc_mode in (0, 1):
+            p = binding.TgPlan(**{**ok, "fmt": fmt, "acc_mode": acc_mode})
+            assert L.tg_plan_set_decode(ctypes.byref(p), 2) == 0 and p.decode == 2
+            assert L.tg_plan_set_decode(ctypes.byref(p), 1) == -1 and p.decode == 2  # nibble: BITCOS only
+            assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0 and p.decode == 0
+        for bad in (dict(m=2), dict(path=1), dict(acc_mode=2)):
+            p = binding.TgPlan(**{**ok, "fmt": fmt, **bad})
+            assert L.tg_plan_set_decode(ctypes.byref(p), 2) == -1 and p.decode == 0
+            p.decode = 2  # forged: refused before launching
+            assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+    for fmt in (B.FMT_BITCOS, B.FMT_2BIT):
+        p = binding.TgPlan(**{**ok, "fmt": fmt})
+        assert L.tg_plan_set_decode(ctypes.byref(p), 2) == -1 and p.decode == 0
+        p.decode = 2
+        assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
     # a forged plan claiming the live-row walk where no kernel has it is refused before launching
     for bad in (dict(live_rows=2), dict(live_rows=1, fmt=B.FMT_5TRIT), dict(live_rows=1, m=2),
                 dict(live_rows=1, acc_mode=1), dict(live_rows=1, path=1)):
