@@ -84,30 +84,49 @@ bool use_mfma_f16(int32_t m, int64_t k) {
     return m >= kF16MfmaMinM || (m == 2 && k / TG_GROUP > kMfmaLongRowGroups);
 }
 
-// Work geometry of one GEMV for a launch of m activation rows on the chosen path (fine: the smaller
-// units of chunked BITCOS rows at m = 1).
-void geometry(Problem &p, int fmt, int32_t m, bool mfma, bool fine = false, bool f16 = false) {
+// Work geometry of one GEMV for a launch of m activation rows on the chosen path (chunk: the unit
+// size of chunked BITCOS rows at m = 1).
+void geometry(Problem &p, int fmt, int32_t m, bool mfma, int chunk = kChunkCoarse, bool f16 = false) {
     if (mfma)
         mfma_geometry(p);
     else
-        gemv_geometry(p, fmt, m, fine, f16);
+        gemv_geometry(p, fmt, m, chunk, f16);
 }
 
-// Whether a launch over these GEMVs (coarse geometry) should use fine units for chunked BITCOS rows
-// at m = 1: when the coarse units are fewer than the launch's waves, some waves would get none and
-// the few holding chunked units (a whole 8-row unit each) set the launch time. Measured on MI355X:
-// a single 4096 x 14336 call 18.1 -> 14.7 us, a plan of 32 such GEMVs 24.0 -> 19.7 us per launch;
-// a one-layer Llama3-8B plan (more units than waves) runs 6 % slower with fine units, so it keeps
-// the coarse ones.
-bool want_fine(const std::vector<Problem> &ps, int fmt, int32_t m, bool mfma, int waves) {
-    if (mfma || fmt != TG_FMT_BITCOS || m != 1) return false;
+// Extra cost per row of a chunk pass of the vector path, in steps: the lanes reload their activation
+// slice once per pass of a unit, shared by its rows (measured on MI355X over the Llama3-8B layer set:
+// about two steps per pass for BITCOS, whose steps are longer, four for the fixed-size codes).
+double pass_cost(int fmt, int rows_per_unit) { return (fmt == TG_FMT_BITCOS ? 2.0 : 4.0) / rows_per_unit; }
+
+// Cost of a whole unit of p in steps (the last unit may be shorter), as unit_cost counts it without
+// empty-row credit.
+double full_unit_cost(const Problem &p, int fmt) {
+    if (p.nch == 1) return (double)p.nbu;
+    return (double)p.rpu * ((double)p.nch + pass_cost(fmt, p.rpu));
+}
+
+// Unit size of chunked BITCOS rows at m = 1 for a launch over these GEMVs (coarse geometry filled in).
+// Fine units when the coarse ones are fewer than the launch's waves: some waves would get none and
+// the few holding chunked units (a whole 8-row unit each) set the launch time (measured on MI355X: a
+// single 4096 x 14336 call 18.1 -> 14.7 us, a plan of 32 such GEMVs 24.0 -> 19.7 us per launch). Mid
+// units when there are enough units but a coarse chunked unit costs more than 1.5 times a wave's
+// share of the launch: a one-layer Llama3-8B plan (7 GEMVs, ~7 steps per wave) gives each 4096 x 14336
+// unit 18 steps, and the waves holding one finish ~10 us after the median wave (per-wave timestamps).
+int chunk_units(const std::vector<Problem> &ps, int fmt, int32_t m, bool mfma, int waves) {
+    if (mfma || fmt != TG_FMT_BITCOS || m != 1) return kChunkCoarse;
     int64_t units = 0;
     bool chunked = false;
+    double total = 0, longest = 0;
     for (const Problem &p : ps) {
         units += p.nunits;
         chunked = chunked || p.nch > 1;
+        const double c = full_unit_cost(p, fmt);
+        total += c * (double)p.nunits;
+        if (p.nch > 1) longest = std::max(longest, c);
     }
-    return chunked && units < waves;
+    if (!chunked) return kChunkCoarse;
+    if (units < waves) return kChunkFine;
+    return longest > 1.5 * total / (double)waves ? kChunkMid : kChunkCoarse;
 }
 
 hipError_t launch(int fmt, const GroupArgs &g, int out, bool mfma, hipStream_t s) {
@@ -158,8 +177,8 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         g.m = mt;
         g.one.unit_begin = 0;
         geometry(g.one, desc->fmt, mt, mfma);
-        if (want_fine({g.one}, desc->fmt, mt, mfma, cus * gemv_waves(desc->fmt, mt)))
-            geometry(g.one, desc->fmt, mt, mfma, true);
+        const int chunk = chunk_units({g.one}, desc->fmt, mt, mfma, cus * gemv_waves(desc->fmt, mt));
+        if (chunk != kChunkCoarse) geometry(g.one, desc->fmt, mt, mfma, chunk);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
         g.live = desc->fmt == TG_FMT_BITCOS && desc->empty_rows > 0 && mt == 1 && !mfma && out != kOutAcc;
@@ -221,9 +240,9 @@ extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
-        gemv_geometry(g.one, TG_FMT_BITCOS, mt, false, true);
-        if (want_fine({g.one}, TG_FMT_BITCOS, mt, false, device_cus() * f16_waves(mt)))
-            gemv_geometry(g.one, TG_FMT_BITCOS, mt, true, true);
+        gemv_geometry(g.one, TG_FMT_BITCOS, mt, kChunkCoarse, true);
+        const int chunk = chunk_units({g.one}, TG_FMT_BITCOS, mt, false, device_cus() * f16_waves(mt));
+        if (chunk != kChunkCoarse) gemv_geometry(g.one, TG_FMT_BITCOS, mt, chunk, true);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
         if (launch_bitcos_f16(g, s) != hipSuccess) return TG_EHIP;
@@ -247,11 +266,6 @@ int plan_waves_max() { return device_cus() * std::max(kMaxWavesPerCu, kMfmaWaves
 int plan_max_m(int fmt) { return fmt == TG_FMT_BITCOS ? TG_MAX_M : kVectorMaxM; }
 
 size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 255) / 256 * 256; }
-
-// Extra cost per row of a chunk pass of the vector path, in steps: the lanes reload their activation
-// slice once per pass of a unit, shared by its rows (measured on MI355X over the Llama3-8B layer set:
-// about two steps per pass for BITCOS, whose steps are longer, four for the fixed-size codes).
-double pass_cost(int fmt, int rows_per_unit) { return (fmt == TG_FMT_BITCOS ? 2.0 : 4.0) / rows_per_unit; }
 
 // Relative time of work unit u of p, for splitting a plan's units across waves. Every step of the
 // vector path costs about the same (one 128-weight group per lane, however many lanes are busy), so a
@@ -335,7 +349,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     bool any_empty = false;
     for (int32_t i = 0; i < count; ++i) any_empty = any_empty || host[i].empty_rows > 0;
     const bool live = fmt == TG_FMT_BITCOS && m == 1 && path == kPathVector && !acc_mode && any_empty;
-    for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, false, f16);
+    for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, kChunkCoarse, f16);
     {
         int64_t ub = 0;
         for (int32_t i = 0; i < count; ++i) {
@@ -343,8 +357,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
             ub += host[i].nunits;
         }
     }
-    if (want_fine(host, fmt, m, mfma, path_waves(fmt, m, path)))
-        for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, true, f16);
+    const int chunk = chunk_units(host, fmt, m, mfma, path_waves(fmt, m, path));
+    if (chunk != kChunkCoarse)
+        for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, chunk, f16);
     for (int32_t i = 0; i < count; ++i) rpu = std::max(rpu, (int)host[i].rpu);
     // Work order: GEMVs of one shape next to each other (by k, then n; the caller's order within a
     // shape). Each Problem carries its own pointers, so the order changes no result; on MI355X it

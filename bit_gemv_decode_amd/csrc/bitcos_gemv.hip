@@ -584,6 +584,8 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
         if constexpr (M == 1) {
             if (p.nbu == kChunkRows1Fine)
                 run_loop<1, ACC, kChunkRows1Fine, true, XS, F16, NIB>(p, u0, u1, lds, tile);
+            else if (p.nbu == kChunkRows1Mid)
+                run_loop<1, ACC, kChunkRows1Mid, true, XS, F16, NIB>(p, u0, u1, lds, tile);
             else
                 run_loop<1, ACC, kChunkRows1, true, XS, F16, NIB>(p, u0, u1, lds, tile);
         } else {
@@ -603,24 +605,26 @@ __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::B
     constexpr int NB = F16 ? 4 : C::NB, WAVES = F16 ? f16_waves(M) : C::WAVES, BLOCK = 64 * WAVES;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
-    // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
-    // those two dependent scalar round trips overlap the fill instead of following it.
+    // The table fill goes out first (straight into LDS); the wave's unit range and its first GEMV
+    // descriptor (two dependent scalar round trips) are read while it is in flight.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    int u, u_end, pi;
-    wave_range<WAVES>(ga, wave, u, u_end, pi);
-    const bool bad0 = ga.table && pi >= ga.count;
-    Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
     if constexpr (NIB)
         load_nib_table<BLOCK>(s_tab);
     else
         load_bitcos_tables<BLOCK, F16>(s_tab);
+    TG_SCHED_FENCE();
+    int u, u_end, pi;
+    wave_range<WAVES>(ga, wave, u, u_end, pi);
+    const bool bad0 = ga.table && pi >= ga.count;
+    Problem p0 = uniform_problem(launch_problem(ga, bad0 ? 0 : pi));
+    tables_landed();
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);
     bool first = true;
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
-        const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        const Problem p = first ? p0 : uniform_problem(launch_problem(ga, pi));
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
         if (u < u1) run_problem<M, ACC, NB, XS, F16, NIB, LIVE>(p, u, u1, lds, tile);
@@ -661,7 +665,7 @@ hipError_t launch_f16_m(const GroupArgs &g, hipStream_t s) {
 
 }  // namespace
 
-void gemv_geometry(Problem &p, int fmt, int m, bool fine, bool f16) {
+void gemv_geometry(Problem &p, int fmt, int m, int chunk, bool f16) {
     const int nb = f16 || fmt != TG_FMT_BITCOS ? 4
                    : m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : m == 2 ? Cfg<2, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
     p.ng = (int32_t)groups_per_row(fmt, p.k);
@@ -675,7 +679,10 @@ void gemv_geometry(Problem &p, int fmt, int m, bool fine, bool f16) {
         p.G = 64;
         p.R = 1;
         p.glast = p.ng - 64 * (p.nch - 1);
-        p.nbu = fmt == TG_FMT_BITCOS && m == 1 ? (fine ? kChunkRows1Fine : kChunkRows1) : nb;
+        p.nbu = fmt != TG_FMT_BITCOS || m != 1 ? nb
+                : chunk == kChunkFine          ? kChunkRows1Fine
+                : chunk == kChunkMid           ? kChunkRows1Mid
+                                               : kChunkRows1;
     }
     p.rpu = p.nbu * p.R;
     p.gmagic = (65536u + (uint32_t)p.G - 1) / (uint32_t)p.G;

@@ -468,21 +468,23 @@ __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
     constexpr uint32_t kWaveDwords = kStageDwords + (XS ? kXsDwords : 0u);
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ __attribute__((aligned(16))) uint32_t s_stage[kWaves * kWaveDwords];
-    // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
-    // those two dependent scalar round trips overlap the fill instead of following it.
+    // The table fill goes out first (straight into LDS); the wave's unit range and its first GEMV
+    // descriptor (two dependent scalar round trips) are read while it is in flight.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    load_bitcos_tables<kBlock, F16>(s_tab);
+    TG_SCHED_FENCE();
     int u, u_end, pi;
     wave_range<kWaves>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
-    const Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
-    load_bitcos_tables<kBlock, F16>(s_tab);
+    const Problem p0 = uniform_problem(launch_problem(ga, bad0 ? 0 : pi));
+    tables_landed();
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     uint32_t *stg = s_stage + wave * kWaveDwords;
     bool first = true;
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
-        const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        const Problem p = first ? p0 : uniform_problem(launch_problem(ga, pi));
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
         if (u < u1) run_mfma<ACC, XS, F16>(p, u, u1, ga.m, lds, stg);

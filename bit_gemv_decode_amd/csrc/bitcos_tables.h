@@ -27,7 +27,8 @@ constexpr uint32_t kTabBytes = (kEntOff + kEntBytes + 255) / 256 * 256;
 
 struct alignas(16) Tables {
     uint64_t ent[kEntries + 1];  // padded to an even count for 16-byte copies
-    uint32_t info[256][2];       // per presence byte: mask (popcount ones, shifted left 3), LDS base
+    uint32_t info[256][4];       // per presence byte: mask (popcount ones, shifted left 3), LDS base;
+                                 // twice, so that one 16-byte copy fills two bank copies
 };
 
 constexpr int popc8(uint32_t v) {
@@ -46,8 +47,8 @@ constexpr Tables make_tables(uint64_t pos = 0x01, uint64_t neg = 0xFF) {
     for (int c = 8; c >= 0; --c) {
         for (uint32_t pb = 0; pb < 256; ++pb) {
             if (popc8(pb) != c) continue;
-            t.info[pb][0] = ((1u << c) - 1u) << 3;
-            t.info[pb][1] = kEntOff + 8 * e;
+            t.info[pb][0] = t.info[pb][2] = ((1u << c) - 1u) << 3;
+            t.info[pb][1] = t.info[pb][3] = kEntOff + 8 * e;
             for (uint32_t sc = 0; sc < (1u << c); ++sc) {
                 uint64_t v = 0;
                 uint32_t rank = 0;
@@ -69,47 +70,38 @@ constexpr Tables make_tables(uint64_t pos = 0x01, uint64_t neg = 0xFF) {
 __device__ const Tables kTables = make_tables();
 __device__ const Tables kTablesF16 = make_tables(0x3C, 0xBC);
 
-// Copy both tables into LDS (s_tab: kTabBytes); the caller synchronises the block afterwards. Each
-// thread issues all of its loads before any LDS write (one 8-byte load serves 8 consecutive (mask,
-// base) copies of one presence byte), so the fill costs about one memory round trip (0.7-1 us per
-// launch on MI355X, measured with a kernel that stops after the fill).
+// Copy both tables into LDS (s_tab: kTabBytes); the caller waits (tables_landed) and synchronises the
+// block afterwards. The
+// copies go from global memory straight into LDS (global_load_lds_dwordx4: lane l of a wave writes
+// the 16 bytes it loads at the wave's LDS base + 16 l), 1 KB per wave instruction and no registers
+// in between: 64 instructions for the (mask, base) copies (one presence byte's 32 copies are 16
+// lanes' loads of the same doubled entry) and 52 for the entry table, spread over the block's waves,
+// all issued before the first completes, so the fill is about one memory round trip.
 template <int BLOCK, bool F16 = false>
 __device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
-    // (mask, base) copies in units of 8 consecutive copies of one presence byte (64 bytes)
-    constexpr int kUnits = 256 * 32 / 8;
-    constexpr int kUnitPer = (kUnits + BLOCK - 1) / BLOCK;
-    constexpr int kEntVec = (kEntries + 1) / 2;  // 16-byte vectors of the entry table
-    constexpr int kEntPer = (kEntVec + BLOCK - 1) / BLOCK;
-    const int t = threadIdx.x;
+    constexpr int kWaves = BLOCK / 64;
+    constexpr int kInfoChunks = (int)(kInfoBytes / 1024);  // 4 presence bytes per chunk
+    constexpr int kEntVec = (kEntries + 1) / 2;            // 16-byte vectors of the entry table
+    constexpr int kEntChunks = (kEntVec + 63) / 64;
+    static_assert(kInfoBytes % 1024 == 0 && kEntOff % 16 == 0, "whole chunks");
+    const int lane = (int)(threadIdx.x & 63);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const Tables &tab = F16 ? kTablesF16 : kTables;
-    const uint2 *inf = reinterpret_cast<const uint2 *>(tab.info);
-    const uint4 *src = reinterpret_cast<const uint4 *>(tab.ent);
-    uint2 iv[kUnitPer];
-    uint4 ev[kEntPer];
-#pragma unroll
-    for (int r = 0; r < kUnitPer; ++r) {
-        const int u = t + r * BLOCK;
-        iv[r] = u < kUnits ? inf[u >> 2] : make_uint2(0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < kEntPer; ++r) {
-        const int i = t + r * BLOCK;
-        ev[r] = i < kEntVec ? src[i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < kUnitPer; ++r) {
-        const int u = t + r * BLOCK;
-        if (u < kUnits) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) s_tab[u * 4 + c] = make_uint4(iv[r].x, iv[r].y, iv[r].x, iv[r].y);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < kEntPer; ++r) {
-        const int i = t + r * BLOCK;
-        if (i < kEntVec) s_tab[kEntOff / 16 + i] = ev[r];
+    const uint4 *inf = reinterpret_cast<const uint4 *>(tab.info);
+    const uint4 *ent = reinterpret_cast<const uint4 *>(tab.ent);
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    for (int c = wave; c < kInfoChunks; c += kWaves)
+        __builtin_amdgcn_global_load_lds(inf + 4 * c + (lane >> 4), (lds_ptr)(s_tab + 64 * c), 16, 0, 0);
+    for (int c = wave; c < kEntChunks; c += kWaves) {
+        // the last chunk is partial: its lanes past the table load nothing
+        if (64 * c + lane < kEntVec)
+            __builtin_amdgcn_global_load_lds(ent + 64 * c + lane, (lds_ptr)(s_tab + kEntOff / 16 + 64 * c), 16, 0, 0);
     }
 }
+
+// Wait until this wave's table copies have landed in LDS (they count as vector memory loads); the
+// block barrier that follows makes every wave's copies visible.
+__device__ __forceinline__ void tables_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 
 // Nibble-keyed lookup ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-D, Eq. 4): the key is

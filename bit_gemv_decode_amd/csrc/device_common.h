@@ -122,6 +122,22 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// GEMV description i of a launch: entry i of its table, or the one passed by value. Table entries are
+// read through the constant address space, so that the wave fetches them with scalar loads straight
+// into scalar registers (a generic pointer would take vector loads that the wave must wait for and
+// move to scalar registers before going on, e.g. before the table fill it should overlap).
+__device__ __forceinline__ Problem launch_problem(const GroupArgs &ga, int i) {
+    static_assert(sizeof(Problem) % 4 == 0, "whole words");
+    constexpr int kWords = (int)(sizeof(Problem) / 4);
+    if (!ga.table) return ga.one;
+    typedef const __attribute__((address_space(4))) uint32_t *ConstWords;
+    const ConstWords src = (ConstWords)ga.table + (size_t)i * kWords;
+    uint32_t w[kWords];
+#pragma unroll
+    for (int j = 0; j < kWords; ++j) w[j] = src[j];
+    return __builtin_bit_cast(Problem, w);
+}
+
 // A GEMV description (read from a table, or passed by value) as wave-uniform values.
 __device__ __forceinline__ Problem uniform_problem(const Problem &q) {
     Problem p;

@@ -472,7 +472,7 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
     int u, u_end, pi;
     wave_range<WAVES>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
-    const Problem p0 = uniform_problem(ga.table ? ga.table[bad0 ? 0 : pi] : ga.one);
+    const Problem p0 = uniform_problem(launch_problem(ga, bad0 ? 0 : pi));
     if constexpr (!ARITH) {
         // units of 64 bytes (16 copies of a 2-bit entry, 8 of a five-trit one), one load each, all
         // loads before any LDS write: the fill is one memory round trip
@@ -506,7 +506,7 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
     bool first = true;
     while (u < u_end) {
         if (ga.table && pi >= ga.count) break;  // ranges inconsistent with the table: stop
-        const Problem p = first ? p0 : uniform_problem(ga.table ? ga.table[pi] : ga.one);
+        const Problem p = first ? p0 : uniform_problem(launch_problem(ga, pi));
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
         if (u < u1) {

@@ -207,10 +207,15 @@ __device__ __forceinline__ void wave_range(const GroupArgs &ga, int wave, int &u
     const int nblk = gridDim.x;
     const int vblk = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
     if (ga.ranges) {
+        // through the constant address space: scalar loads, which do not wait for vector memory
+        // operations in flight (e.g. the table fill)
+        typedef const __attribute__((address_space(4))) int32_t *ConstWords;
         const int vw = vblk * WAVES + wave;
-        u = uniform_i32(ga.ranges[vw].begin);
-        u_end = uniform_i32(ga.ranges[vw].end);
-        pi = uniform_i32(ga.ranges[vw].problem);
+        static_assert(sizeof(WaveRange) == 16, "four words per range");
+        const ConstWords r = (ConstWords)ga.ranges + 4 * vw;
+        u = uniform_i32(r[0]);
+        u_end = uniform_i32(r[1]);
+        pi = uniform_i32(r[2]);
     } else {
         const int nw = nblk * WAVES;
         const int vw = wave * nblk + vblk;

@@ -88,14 +88,19 @@ constexpr int kMaxWavesPerCu = 16;
 
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
 constexpr int kChunkRows1 = 8;
-// ... or of kChunkRows1Fine rows when units of kChunkRows1 are too coarse to spread a launch's work
-// evenly over its waves (small plans, single calls).
+// ... or of kChunkRows1Fine rows when units of kChunkRows1 are fewer than a launch's waves (small
+// plans, single calls), or of kChunkRows1Mid rows when they are enough but each is so long against a
+// wave's share of the launch that the waves holding one set its time (one-layer plans).
 constexpr int kChunkRows1Fine = 2;
+constexpr int kChunkRows1Mid = 4;
+// Unit sizes of chunked BITCOS rows at m = 1 (gemv_geometry's `chunk` argument).
+enum ChunkUnits { kChunkCoarse = 0, kChunkMid = 1, kChunkFine = 2 };
 
 // Fill the work geometry of p (p.n, p.k set) for m activation rows on the vector path (the same for
-// every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 rows and BITCOS
+// every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 (or, by `chunk`,
+// kChunkRows1Mid or kChunkRows1Fine) rows and BITCOS
 // units at m = 3 are two steps long; f16: the fp16-activation kernel, four-step units).
-void gemv_geometry(Problem &p, int fmt, int m, bool fine = false, bool f16 = false);
+void gemv_geometry(Problem &p, int fmt, int m, int chunk = kChunkCoarse, bool f16 = false);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
 // units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU. It is
