@@ -267,7 +267,7 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
         voff_x = act ? (uint32_t)jl * XB : kOffOff;
         T = (u1 - u0) * NB;
         red = make_red(NB * x.R, x.R, x.G, p.rmagic);
-        cur = uniform_u32(buf_u32(x.rro, (uint32_t)row_begin * 4u));
+        cur = row_index_entry(p, row_begin);
     } else {
         voff_bm = (uint32_t)lane * 16u;
         voff_sc = (uint32_t)lane * 2u;
@@ -276,10 +276,16 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
         T = (u1 - u0) * NB * x.nch;
         red = make_red(NB, 1, 64, p.rmagic);
     }
+    // The activation slice is waited for only before the first decode: its loads go out with the
+    // first bitmaps, and waiting for those (the first sign stage) covers the slice too, since vector
+    // loads complete in order. One memory round trip less per range than waiting here.
+    // (Units of eight chunked rows decode in the first pass of the loop body already: they wait here.)
     load_x<M, XW>(x, voff_x, xr);
     load_xs<M, XS>(x, voff_x, xsv);
-    wait_x<M, XW>(xr);
-    wait_xs<M, XS>(xsv);
+    if constexpr (U != 4) {
+        wait_x<M, XW>(xr);
+        wait_xs<M, XS>(xsv);
+    }
 
     u32x4 bm[4] = {};
     SgBuf g[4] = {};
@@ -289,14 +295,18 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
     // Uniform branches cost each wave an instruction-fetch bubble, so the loop body has none: every
     // stage runs on every half-step, dead steps (pipeline fill and drain) decode whatever their
     // buffers hold into tile slots that a live step overwrites before use, and only their stores and
-    // loads are switched off (dead offsets). Scalar state advances with selects.
+    // loads are switched off (dead offsets). Scalar state advances with selects. The first pass of the
+    // body is a copy (FIRST) without the decodes of its first four half-steps, whose steps do not
+    // exist; the activation wait sits before its first decode.
     for (int it = 0; U * it - 4 < T; ++it) {
+        // with four half-steps per pass, the first pass holds no decode (its steps would be -4 .. -1)
+        const bool first = U == 4 && it == 0;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int h = U * it + j;
             const int jb = j & 3;  // stage buffer slot
             // ---- decode step h - 4 (buffers bm[jb], g[jb]) ----
-            {
+            if (!first) {
                 const int s = h - 4;
                 const bool live = s >= 0 && s < T;
                 A acc[M];
@@ -414,6 +424,10 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
             }
             TG_SCHED_FENCE();
         }
+        if (first) {
+            wait_x<M, XW>(xr);
+            wait_xs<M, XS>(xsv);
+        }
     }
 }
 
@@ -484,7 +498,7 @@ __device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, i
     float xsv[M];
     load_x<M, XW>(x, voff_x, xr);
     load_xs<M, XS>(x, voff_x, xsv);
-    uint32_t cur = uniform_u32(buf_u32(x.rro, (uint32_t)row_begin * 4u));
+    uint32_t cur = row_index_entry(p, row_begin);
     // masks of the non-empty rows: lane w holds window w (rows row_begin + 64 w .. + 63)
     const int nw = (row_end - row_begin + 63) >> 6;
     uint32_t mlo = 0, mhi = 0;
@@ -617,7 +631,7 @@ __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::B
     wave_range<WAVES>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     Problem p0 = uniform_problem(launch_problem(ga, bad0 ? 0 : pi));
-    tables_landed();
+    lds_copies_landed();
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     double *tile = s_tile + (ACC ? 0 : wave * M * NB * 64);

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
     wave_range<kWaves>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     const Problem p0 = uniform_problem(launch_problem(ga, bad0 ? 0 : pi));
-    tables_landed();
+    lds_copies_landed();
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(s_tab);
     uint32_t *stg = s_stage + wave * kWaveDwords;

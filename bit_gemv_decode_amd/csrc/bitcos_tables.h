@@ -70,7 +70,7 @@ constexpr Tables make_tables(uint64_t pos = 0x01, uint64_t neg = 0xFF) {
 __device__ const Tables kTables = make_tables();
 __device__ const Tables kTablesF16 = make_tables(0x3C, 0xBC);
 
-// Copy both tables into LDS (s_tab: kTabBytes); the caller waits (tables_landed) and synchronises the
+// Copy both tables into LDS (s_tab: kTabBytes); the caller waits (lds_copies_landed) and synchronises the
 // block afterwards. The
 // copies go from global memory straight into LDS (global_load_lds_dwordx4: lane l of a wave writes
 // the 16 bytes it loads at the wave's LDS base + 16 l), 1 KB per wave instruction and no registers
@@ -99,9 +99,6 @@ __device__ __forceinline__ void load_bitcos_tables(uint4 *s_tab) {
     }
 }
 
-// Wait until this wave's table copies have landed in LDS (they count as vector memory loads); the
-// block barrier that follows makes every wave's copies visible.
-__device__ __forceinline__ void tables_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 
 // Nibble-keyed lookup ("Breaking the 1.58-bit Barrier for Ternary LLMs", Sec. II-D, Eq. 4): the key is

@@ -138,6 +138,13 @@ __device__ __forceinline__ Problem launch_problem(const GroupArgs &ga, int i) {
     return __builtin_bit_cast(Problem, w);
 }
 
+// Entry r of a BITCOS GEMV's row index (the stream position of row r's first sign), read with a scalar
+// load through the constant address space: the wave waits for it only where the value is used.
+__device__ __forceinline__ uint32_t row_index_entry(const Problem &p, int r) {
+    typedef const __attribute__((address_space(4))) uint32_t *ConstWords;
+    return ((ConstWords)p.rowoff)[r];
+}
+
 // A GEMV description (read from a table, or passed by value) as wave-uniform values.
 __device__ __forceinline__ Problem uniform_problem(const Problem &q) {
     Problem p;

@@ -31,9 +31,11 @@ namespace {
 // copies, 256 bytes per entry value), five-trit entries 8 bytes (32 copies).
 constexpr uint32_t kLutBytes = 256 * 256;
 
+// Each entry is stored as the 16 bytes a lane copies into LDS: four copies of a 2-bit entry, two of a
+// five-trit one.
 struct alignas(16) FixedTables {
-    uint32_t b2[256];     // 2-bit: code byte -> 4 int8 weights
-    uint32_t t5[256][2];  // five-trit: code byte -> weights 0..3 as int8, weight 4 as int8 in word 1
+    uint32_t b2[256][4];  // 2-bit: code byte -> 4 int8 weights
+    uint32_t t5[256][4];  // five-trit: code byte -> weights 0..3 as int8, weight 4 as int8 in word 1
 };
 
 constexpr FixedTables make_fixed_tables() {
@@ -45,7 +47,7 @@ constexpr FixedTables make_fixed_tables() {
             const uint32_t w = c == 3 ? 0u : (c + 255u) & 0xFFu;  // c - 1 as int8
             v |= w << (8 * i);
         }
-        t.b2[b] = v;
+        t.b2[b][0] = t.b2[b][1] = t.b2[b][2] = t.b2[b][3] = v;
         uint32_t d = b < 243 ? b : 121;  // invalid bytes read as five zero weights
         uint32_t lo = 0, hi = 0;
         for (uint32_t i = 0; i < 5; ++i) {
@@ -56,8 +58,8 @@ constexpr FixedTables make_fixed_tables() {
             else
                 hi = w;
         }
-        t.t5[b][0] = lo;
-        t.t5[b][1] = hi;
+        t.t5[b][0] = t.t5[b][2] = lo;
+        t.t5[b][1] = t.t5[b][3] = hi;
     }
     return t;
 }
@@ -466,39 +468,27 @@ __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupA
     constexpr int NB = C::NB, WAVES = C::WAVES, BLOCK = C::BLOCK;
     __shared__ uint4 s_lut[ARITH ? 1 : kLutBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
-    // The wave's unit range and its first GEMV descriptor are read before the table fill, so that
-    // those two dependent scalar round trips overlap the fill instead of following it.
+    // The table fill goes out first, straight from global memory into LDS (global_load_lds_dwordx4:
+    // lane l of a wave writes its 16 bytes at the wave's LDS base + 16 l; 1 KB per instruction holds
+    // the copies of four code bytes); the wave's unit range and first GEMV descriptor (two dependent
+    // scalar round trips) are read while it is in flight.
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if constexpr (!ARITH) {
+        constexpr int kChunks = (int)(kLutBytes / 1024);
+        const int lane = (int)(threadIdx.x & 63);
+        const uint4 *src = reinterpret_cast<const uint4 *>(FMT == TG_FMT_2BIT ? &kFixedTables.b2[0][0]
+                                                                             : &kFixedTables.t5[0][0]);
+        typedef __attribute__((address_space(3))) void *lds_ptr;
+        for (int c = wave; c < kChunks; c += WAVES)
+            __builtin_amdgcn_global_load_lds(src + 4 * c + (lane >> 4), (lds_ptr)(s_lut + 64 * c), 16, 0, 0);
+    }
+    TG_SCHED_FENCE();
     int u, u_end, pi;
     wave_range<WAVES>(ga, wave, u, u_end, pi);
     const bool bad0 = ga.table && pi >= ga.count;
     const Problem p0 = uniform_problem(launch_problem(ga, bad0 ? 0 : pi));
     if constexpr (!ARITH) {
-        // units of 64 bytes (16 copies of a 2-bit entry, 8 of a five-trit one), one load each, all
-        // loads before any LDS write: the fill is one memory round trip
-        constexpr int kUnits = kLutBytes / 64;
-        constexpr int kUnitPer = (kUnits + BLOCK - 1) / BLOCK;
-        const int t = threadIdx.x;
-        uint2 v[kUnitPer];
-#pragma unroll
-        for (int r = 0; r < kUnitPer; ++r) {
-            const int u = t + r * BLOCK;
-            if constexpr (FMT == TG_FMT_2BIT)
-                v[r] = make_uint2(u < kUnits ? kFixedTables.b2[u >> 2] : 0u, 0u);
-            else
-                v[r] = u < kUnits ? make_uint2(kFixedTables.t5[u >> 2][0], kFixedTables.t5[u >> 2][1])
-                                  : make_uint2(0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < kUnitPer; ++r) {
-            const int u = t + r * BLOCK;
-            if (u < kUnits) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    s_lut[u * 4 + c] = FMT == TG_FMT_2BIT ? make_uint4(v[r].x, v[r].x, v[r].x, v[r].x)
-                                                         : make_uint4(v[r].x, v[r].y, v[r].x, v[r].y);
-            }
-        }
+        lds_copies_landed();
         __syncthreads();
     }
     const char *lds = reinterpret_cast<const char *>(s_lut);

@@ -33,6 +33,10 @@ struct Cfg {
 // pipeline stages in program order, so that each wait covers exactly the loads it needs.
 #define TG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Wait until this wave's copies from global memory into LDS (global_load_lds) have landed: they count
+// as vector memory loads. The block barrier that follows makes every wave's copies visible.
+__device__ __forceinline__ void lds_copies_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Buffer offsets. A lane with nothing to read gets kOffOff as its own (vector) offset; a pipeline
 // stage with nothing to do gets kDeadS as its wave-uniform (scalar) offset. Either way the sum lies
 // beyond every resource (bitmaps, scales and outputs are limited to less than 1 GiB, sign windows to
