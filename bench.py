@@ -580,7 +580,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic["bytes_per_launch"] / ls.step_bytes, 4) if traffic else None),
-                     "kernel": "bitcos_gemv_kernel<1,false,false,false> (grouped, one launch per step)",
+                     "kernel": "bitcos_gemv_kernel<1, false, false, false, false, false> (grouped, one launch per step)",
                      "algorithmic_bytes_per_launch": ls.step_bytes,
                      "avg_launch_us": round(step_s * 1e6, 2)},
     }

@@ -4,9 +4,10 @@
       Runs, in one process: the stream-read kernel over a 2 GiB buffer (known bytes read), a 1 GiB
       fill (known bytes written), then one warm-up and one timed grouped BITCOS step over the
       Llama3-8B-shaped layer set (the same workload bench.py times).
-  python -m bit_gemv_decode_amd.profiling stats STATS_CSV OUT.md "COMMAND" [TRACE_CSV LAST]
-      Writes a short markdown summary of a --kernel-trace --stats run (with TRACE_CSV and LAST, also
-      the average of the last LAST BITCOS dispatches: the timed region of a bench.py run).
+  python -m bit_gemv_decode_amd.profiling stats STATS_CSV OUT.md "COMMAND" [TRACE_CSV SKIP COUNT]
+      Writes a short markdown summary of a --kernel-trace --stats run (with TRACE_CSV, SKIP and COUNT,
+      also the average of BITCOS dispatches SKIP .. SKIP + COUNT - 1: the timed region of a bench.py
+      run is its dispatches WARMUP .. WARMUP + STEPS - 1).
   python -m bit_gemv_decode_amd.profiling traffic FETCH_CSV WRITE_CSV OUT.json "COMMANDS"
       From a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run of `drive`: calibrates both counters
       against the known-size kernels and converts the BITCOS dispatch's counts into HBM bytes.
@@ -155,7 +156,7 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def stats(stats_csv, out_md, command, trace_csv=None, last=0):
+def stats(stats_csv, out_md, command, trace_csv=None, skip=0, count=0):
     rows = _rows(stats_csv)
     lines = [f"# Kernel durations: `{os.path.basename(out_md)}`", "", "Command (from the repository root):", "",
              f"    {command}", "", "| Kernel | Calls | Average (µs) | Min (µs) | Max (µs) | Share of GPU time |",
@@ -166,14 +167,16 @@ def stats(stats_csv, out_md, command, trace_csv=None, last=0):
             name = name[:87] + "..."
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
-    if trace_csv and last:
-        # the timed region of bench.py: the last `last` dispatches of the BITCOS kernel
+    if trace_csv and count:
+        # the timed region of bench.py: BITCOS dispatches skip .. skip + count - 1
         tr = [r for r in _rows(trace_csv) if "bitcos_gemv_kernel" in r["Kernel_Name"]]
         tr.sort(key=lambda r: int(r["Start_Timestamp"]))
-        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-last:]]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[skip:skip + count]]
         if d:
-            lines += ["", f"Timed region (the last {len(d)} BITCOS dispatches, after the warm-up ones): "
-                          f"average {sum(d) / len(d):.2f} µs, min {min(d):.2f}, max {max(d):.2f}."]
+            lines += ["", f"Timed region (BITCOS dispatches {skip} .. {skip + len(d) - 1}, after {skip} warm-up ones): "
+                          f"average {sum(d) / len(d):.2f} µs, min {min(d):.2f}, max {max(d):.2f}; "
+                          f"all {len(tr)} BITCOS dispatches of the run (warm-up, timed, then the settled-rate "
+                          f"launches): average {sum((int(r['End_Timestamp']) - int(r['Start_Timestamp'])) / 1e3 for r in tr) / len(tr):.2f} µs."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -214,7 +217,7 @@ if __name__ == "__main__":
     if cmd == "drive":
         drive()
     elif cmd == "stats":
-        stats(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6]), *(int(a) for a in sys.argv[6:7]))
+        stats(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6]), *(int(a) for a in sys.argv[6:8]))
     elif cmd == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     elif cmd == "transient":
