@@ -85,3 +85,32 @@ def test_bench_fp16_step_every_output(layer_set):
         for layer in range(bench.LAYERS):
             y = ls.mats[layer][role]["y"].cpu().numpy()
             assert np.all(np.abs(y.astype(np.float64) - r["y16"].astype(np.float64)) <= bound), f"{name} copy {layer}"
+
+
+@pytest.mark.parametrize("mode", ["byte", "nibble", "fp16"])
+def test_per_layer_plans_every_output(layer_set, mode):
+    # the bench's per-layer mode: 32 launches of the 7 GEMVs of one layer each. A one-layer plan gives
+    # its chunked 4096 x 14336 rows 4-row units (8-row ones would each cost over 1.5 times a wave's
+    # share), and every range starts with the pass whose activation wait follows the first bitmaps.
+    bench, ls, refs, dev = layer_set
+    _say(f"[gpu] per-layer plans, {mode}")
+    if mode == "fp16":
+        x16 = [torch.from_numpy(r["x16"]).to(dev) for r in refs]
+        plans = [B.Plan([m["w"] for m in row], x16, scales=[m["s"] for m in row], ys=[m["y"] for m in row], f16=True)
+                 for row in ls.mats]
+    else:
+        plans = [ls.plan(B, row).set_decode(B.DECODE_NIBBLE if mode == "nibble" else B.DECODE_BYTE) for row in ls.mats]
+    _reset(ls)
+    for p in plans:
+        p.run()
+    torch.cuda.synchronize()
+    for role, (name, n, k) in enumerate(bench.LAYER):
+        r = refs[role]
+        bound = bounds.f16_bound(r["w"], r["s"], r["x16"], r["y16"]) if mode == "fp16" else None
+        for layer in range(bench.LAYERS):
+            y = ls.mats[layer][role]["y"].cpu().numpy()
+            if mode == "fp16":
+                err = np.abs(y.astype(np.float64) - r["y16"].astype(np.float64))
+                assert np.all(err <= bound), f"{name} copy {layer}"
+            else:
+                assert np.array_equal(y, r["y"]), f"{name} copy {layer}: not bit-identical"
