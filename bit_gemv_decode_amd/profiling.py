@@ -11,6 +11,10 @@
   python -m bit_gemv_decode_amd.profiling traffic FETCH_CSV WRITE_CSV OUT.json "COMMANDS"
       From a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run of `drive`: calibrates both counters
       against the known-size kernels and converts the BITCOS dispatch's counts into HBM bytes.
+  python -m bit_gemv_decode_amd.profiling counters OUT.md "COMMANDS" CSV [CSV ...]
+      From --pmc runs of `drive` (one counter set each): the timed BITCOS dispatch's counters, per
+      128-weight wave-group (one lane's group; 64 of them make a wave-step of 8192 weights) and as
+      shares of the waves' resident cycles.
   python -m bit_gemv_decode_amd.profiling transient OUT.md [LAUNCHES]
       Launch by launch from an idle GPU: the grouped BITCOS and five-trit steps over the Llama3-8B
       layer set and a stream read of the same number of bytes, each after two idle seconds, with a
@@ -181,6 +185,43 @@ def stats(stats_csv, out_md, command, trace_csv=None, skip=0, count=0):
         f.write("\n".join(lines) + "\n")
 
 
+def counters(out_md, command, csvs):
+    """Summary of the last BITCOS dispatch of `drive` (the timed step) over one or more --pmc runs."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    vals = {}
+    for path in csvs:
+        rows = _rows(path)
+        ds = sorted({int(r["Dispatch_Id"]) for r in rows if "bitcos_gemv_kernel" in r["Kernel_Name"]})
+        if not ds:
+            continue
+        last = ds[-1]
+        for r in rows:
+            if int(r["Dispatch_Id"]) == last:
+                vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    weights = bench.LAYERS * sum(n * k for _, n, k in bench.LAYER)
+    wave_steps = weights / 8192.0  # 64 lanes x 128 weights
+    lines = [f"# SQ counters of the grouped BITCOS step: `{os.path.basename(out_md)}`", "",
+             "Commands (from the repository root):", "", f"    {command}", "",
+             f"Timed dispatch of `drive` (the Llama3-8B-shaped layer set x{bench.LAYERS}, {weights / 1e9:.2f} G weights, "
+             f"{wave_steps:.0f} wave-steps of 8192 weights).", "", "| Counter | Total | Per wave-step |", "|---|---|---|"]
+    for name in sorted(vals):
+        lines.append(f"| `{name}` | {vals[name]:.4g} | {vals[name] / wave_steps:.2f} |")
+    wc = vals.get("SQ_WAVE_CYCLES")
+    if wc:
+        lines += ["", "Shares of the waves' resident cycles (`SQ_WAVE_CYCLES`):", ""]
+        for name in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS",
+                     "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY"):
+            if name in vals:
+                lines.append(f"- `{name}`: {100 * vals[name] / wc:.1f} %")
+    if vals.get("SQ_INSTS_LDS") and vals.get("SQ_LDS_BANK_CONFLICT"):
+        lines.append(f"- bank-conflict cycles per LDS instruction: "
+                     f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_INSTS_LDS']:.2f}")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def _per_dispatch(path, counter):
     agg = defaultdict(float)
     names = {}
@@ -220,6 +261,8 @@ if __name__ == "__main__":
         stats(sys.argv[2], sys.argv[3], sys.argv[4], *(sys.argv[5:6]), *(int(a) for a in sys.argv[6:8]))
     elif cmd == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif cmd == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4:])
     elif cmd == "transient":
         transient(sys.argv[2], *(int(a) for a in sys.argv[3:4]))
     else:
