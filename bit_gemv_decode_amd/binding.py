@@ -474,7 +474,7 @@ class Plan:
 
     def set_decode(self, decode: int):
         """Decode strategy: DECODE_BYTE (default), DECODE_NIBBLE (BITCOS) or DECODE_ARITH (five-trit,
-        t5b) (tg_plan_set_decode)."""
+        t5b, 2-bit) (tg_plan_set_decode)."""
         _check(lib().tg_plan_set_decode(ctypes.byref(self.plan), decode), "tg_plan_set_decode")
         return self
 

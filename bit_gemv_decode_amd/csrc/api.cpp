@@ -472,9 +472,10 @@ bool nibble_ok(const tg_plan *p) {
            (p->acc_mode == kOutY || p->acc_mode == kOutAcc);
 }
 
-// Whether a plan may run the table-free five-trit decode.
+// Whether a plan may run the table-free decode.
 bool arith_ok(const tg_plan *p) {
-    return (p->fmt == TG_FMT_5TRIT || p->fmt == TG_FMT_T5B) && p->m == 1 && p->path == kPathVector &&
+    return (p->fmt == TG_FMT_5TRIT || p->fmt == TG_FMT_T5B || p->fmt == TG_FMT_2BIT) && p->m == 1 &&
+           p->path == kPathVector &&
            (p->acc_mode == kOutY || p->acc_mode == kOutAcc);
 }
 

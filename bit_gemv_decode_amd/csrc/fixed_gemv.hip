@@ -96,8 +96,9 @@ struct CodeBuf {
 };
 
 // The lane's activation words for its group column: plain bytes for 2-bit, the permuted words for
-// five-trit (see the file comment).
-template <int FMT, int M>
+// five-trit (see the file comment). ARITH (2-bit): each 16-byte run transposed as a 4 x 4 byte matrix,
+// so that word 4d + i holds the activations of code i of the four code bytes of code dword d.
+template <int FMT, int M, bool ARITH = false>
 __device__ __forceinline__ void load_xf(const Ctx &x, uint32_t voff, uint32_t (&xf)[M][Fmt<FMT>::kXWords]) {
     if constexpr (FMT == TG_FMT_T5B) {
         // the block's 160 activation bytes (ten 16-byte loads; past k they meet padding weights of
@@ -132,7 +133,22 @@ __device__ __forceinline__ void load_xf(const Ctx &x, uint32_t voff, uint32_t (&
     }
     uint32_t xr[M][32];
     load_x<M>(x, voff, xr);
-    if constexpr (FMT == TG_FMT_2BIT) {
+    if constexpr (FMT == TG_FMT_2BIT && ARITH) {
+#pragma unroll
+        for (int mi = 0; mi < M; ++mi)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const uint32_t r0 = xr[mi][4 * d], r1 = xr[mi][4 * d + 1], r2 = xr[mi][4 * d + 2], r3 = xr[mi][4 * d + 3];
+                const uint32_t a = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+                const uint32_t b = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+                const uint32_t c = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+                const uint32_t e = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+                xf[mi][4 * d] = __builtin_amdgcn_perm(c, a, 0x05040100u);      // byte 0 of r0..r3
+                xf[mi][4 * d + 1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // byte 1
+                xf[mi][4 * d + 2] = __builtin_amdgcn_perm(e, b, 0x05040100u);  // byte 2
+                xf[mi][4 * d + 3] = __builtin_amdgcn_perm(e, b, 0x07060302u);  // byte 3
+            }
+    } else if constexpr (FMT == TG_FMT_2BIT) {
 #pragma unroll
         for (int mi = 0; mi < M; ++mi)
 #pragma unroll
@@ -240,52 +256,70 @@ __device__ __forceinline__ void t5_digit_pairs(uint32_t cp, u16x2 (&d)[5]) {
     d[4] = f4;
 }
 
-// Sums of the lane's weights times x with the table-free decode: the digits (0, 1, 2) are contracted as
-// they are and sx, the sum of the group's activations, is taken off once, since weight = digit - 1.
-// Four code bytes give four words of digits 0..3 (one per code, against xa[j]) and one word of their
-// fifth digits (against xb[q]), as in the table path.
+// Sums of the lane's weights times x with the table-free decode: the digits or codes (0, 1, 2) are
+// contracted as they are and sx, the sum of the group's activations, is taken off once, since
+// weight = digit - 1 = code - 1.
+// Five-trit: four code bytes give four words of digits 0..3 (one per code, against xa[j]) and one
+// word of their fifth digits (against xb[q]), as in the table path.
+// 2-bit (the shift, mask and subtract decode, without expanding a code to its weight): code i of the
+// four bytes of code dword d is (w >> 2i) & 0x03030303, contracted against the transposed activation
+// word 4d + i.
 template <int FMT, int M>
 __device__ __forceinline__ void decode_fixed_arith(const CodeBuf &b, const uint32_t (&xf)[M][Fmt<FMT>::kXWords],
                                                    const int (&sx)[M], int (&acc)[M]) {
-    static_assert(FMT == TG_FMT_5TRIT || FMT == TG_FMT_T5B, "five-trit codes");
-    constexpr int kBytes = FMT == TG_FMT_T5B ? 32 : 26;
-    constexpr int kRuns = (kBytes + 3) / 4;
-    uint32_t w[8] = {b.c[0].x, b.c[0].y, b.c[0].z, b.c[0].w, b.c[1].x, b.c[1].y, b.c[1].z, b.c[1].w};
-    if constexpr (FMT == TG_FMT_5TRIT) {
+    if constexpr (FMT == TG_FMT_2BIT) {
+        const uint32_t w[8] = {b.c[0].x, b.c[0].y, b.c[0].z, b.c[0].w, b.c[1].x, b.c[1].y, b.c[1].z, b.c[1].w};
 #pragma unroll
-        for (int d = 0; d < 7; ++d) w[d] = __builtin_amdgcn_alignbit(w[d + 1], w[d], b.sh);
-    }
+        for (int mi = 0; mi < M; ++mi) acc[mi] = -sx[mi];
 #pragma unroll
-    for (int mi = 0; mi < M; ++mi) acc[mi] = -sx[mi];
+        for (int d = 0; d < 8; ++d)
 #pragma unroll
-    for (int q = 0; q < kRuns; ++q) {
-        uint32_t fifth[2];
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c = (w[d] >> (2 * i)) & 0x03030303u;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // codes 4q + 2h and 4q + 2h + 1 into the low bytes of the two halves
-            const uint32_t cp = __builtin_amdgcn_perm(w[q], w[q], h ? 0x0C030C02u : 0x0C010C00u);
-            u16x2 dg[5];
-            t5_digit_pairs(cp, dg);
-            const uint32_t e0 = __builtin_bit_cast(uint32_t, dg[0]), e1 = __builtin_bit_cast(uint32_t, dg[1]);
-            const uint32_t e2 = __builtin_bit_cast(uint32_t, dg[2]), e3 = __builtin_bit_cast(uint32_t, dg[3]);
-            const uint32_t t01 = __builtin_amdgcn_perm(e1, e0, 0x06040200u);  // d0 lo, d0 hi, d1 lo, d1 hi
-            const uint32_t t23 = __builtin_amdgcn_perm(e3, e2, 0x06040200u);  // d2 lo, d2 hi, d3 lo, d3 hi
-            fifth[h] = __builtin_bit_cast(uint32_t, dg[4]);
+                for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(c, xf[mi][4 * d + i], acc[mi]);
+            }
+    } else {
+        static_assert(FMT == TG_FMT_5TRIT || FMT == TG_FMT_T5B, "five-trit codes");
+        constexpr int kBytes = FMT == TG_FMT_T5B ? 32 : 26;
+        constexpr int kRuns = (kBytes + 3) / 4;
+        uint32_t w[8] = {b.c[0].x, b.c[0].y, b.c[0].z, b.c[0].w, b.c[1].x, b.c[1].y, b.c[1].z, b.c[1].w};
+        if constexpr (FMT == TG_FMT_5TRIT) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int j = 4 * q + 2 * h + c;  // code byte
-                if (j < kBytes) {
-                    const uint32_t dw = __builtin_amdgcn_perm(t23, t01, c ? 0x07050301u : 0x06040200u);
+            for (int d = 0; d < 7; ++d) w[d] = __builtin_amdgcn_alignbit(w[d + 1], w[d], b.sh);
+        }
 #pragma unroll
-                    for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(dw, xf[mi][j], acc[mi]);
+        for (int mi = 0; mi < M; ++mi) acc[mi] = -sx[mi];
+#pragma unroll
+        for (int q = 0; q < kRuns; ++q) {
+            uint32_t fifth[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // codes 4q + 2h and 4q + 2h + 1 into the low bytes of the two halves
+                const uint32_t cp = __builtin_amdgcn_perm(w[q], w[q], h ? 0x0C030C02u : 0x0C010C00u);
+                u16x2 dg[5];
+                t5_digit_pairs(cp, dg);
+                const uint32_t e0 = __builtin_bit_cast(uint32_t, dg[0]), e1 = __builtin_bit_cast(uint32_t, dg[1]);
+                const uint32_t e2 = __builtin_bit_cast(uint32_t, dg[2]), e3 = __builtin_bit_cast(uint32_t, dg[3]);
+                const uint32_t t01 = __builtin_amdgcn_perm(e1, e0, 0x06040200u);  // d0 lo, d0 hi, d1 lo, d1 hi
+                const uint32_t t23 = __builtin_amdgcn_perm(e3, e2, 0x06040200u);  // d2 lo, d2 hi, d3 lo, d3 hi
+                fifth[h] = __builtin_bit_cast(uint32_t, dg[4]);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int j = 4 * q + 2 * h + c;  // code byte
+                    if (j < kBytes) {
+                        const uint32_t dw = __builtin_amdgcn_perm(t23, t01, c ? 0x07050301u : 0x06040200u);
+#pragma unroll
+                        for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(dw, xf[mi][j], acc[mi]);
+                    }
                 }
             }
-        }
-        // fifth digits of the run's four codes (a five-trit group's last run reaches two bytes of the
-        // next group, whose digits meet activation positions past 127, which are zero)
-        const uint32_t w4 = __builtin_amdgcn_perm(fifth[1], fifth[0], 0x06040200u);
+            // fifth digits of the run's four codes (a five-trit group's last run reaches two bytes of the
+            // next group, whose digits meet activation positions past 127, which are zero)
+            const uint32_t w4 = __builtin_amdgcn_perm(fifth[1], fifth[0], 0x06040200u);
 #pragma unroll
-        for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(w4, xf[mi][kBytes + q], acc[mi]);
+            for (int mi = 0; mi < M; ++mi) acc[mi] = dot4(w4, xf[mi][kBytes + q], acc[mi]);
+        }
     }
 }
 
@@ -363,7 +397,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
         T = (u1 - u0) * NB * x.nch;
         red = make_red(NB, 1, 64, p.rmagic);
     }
-    load_xf<FMT, M>(x, voff_x, xf);
+    load_xf<FMT, M, ARITH>(x, voff_x, xf);
     load_xs<M, XS>(x, voff_x, xsv);
     wait_xf<FMT, M>(xf);
     wait_xs<M, XS>(xsv);
@@ -415,7 +449,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
                         const int gcn = cD == x.nch - 1 ? x.glast : 64;
                         const uint32_t vx =
                             lane < gcn ? voff_x + (uint32_t)cD * (64u * Fmt<FMT>::kXBytes) : kOffOff;
-                        load_xf<FMT, M>(x, vx, xf);
+                        load_xf<FMT, M, ARITH>(x, vx, xf);
                         load_xs<M, XS>(x, vx, xsv);
                     }
                 }
@@ -461,7 +495,7 @@ __device__ __forceinline__ void run_fixed(const Problem &p, int u0, int u1, cons
     }
 }
 
-// ARITH: the table-free five-trit decode (no LDS table, so no table fill either).
+// ARITH: the table-free decode of the five-trit and 2-bit codes (no LDS table, so no table fill either).
 template <int FMT, int M, bool ACC, bool XS, bool ARITH = false>
 __global__ __launch_bounds__((Cfg<M, FMT>::BLOCK)) void fixed_gemv_kernel(GroupArgs ga) {
     using C = Cfg<M, FMT>;
@@ -549,9 +583,20 @@ hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s) {
 }
 
 hipError_t launch_five_trit_arith(int fmt, const GroupArgs &g, int out, hipStream_t s) {
-    if (g.m != 1 || (out != kOutY && out != kOutAcc) || (fmt != TG_FMT_5TRIT && fmt != TG_FMT_T5B))
+    if (g.m != 1 || (out != kOutY && out != kOutAcc) ||
+        (fmt != TG_FMT_5TRIT && fmt != TG_FMT_T5B && fmt != TG_FMT_2BIT))
         return hipErrorInvalidValue;
-    if (fmt == TG_FMT_5TRIT) {
+    if (fmt == TG_FMT_2BIT) {
+        using C = Cfg<1, TG_FMT_2BIT>;
+        const int blocks = grid_blocks<C::WAVES>(g);
+        if (blocks < 1) return hipErrorInvalidValue;
+        if (out == kOutAcc)
+            hipLaunchKernelGGL((fixed_gemv_kernel<TG_FMT_2BIT, 1, true, false, true>), dim3(blocks), dim3(C::BLOCK), 0, s,
+                               g);
+        else
+            hipLaunchKernelGGL((fixed_gemv_kernel<TG_FMT_2BIT, 1, false, false, true>), dim3(blocks), dim3(C::BLOCK), 0,
+                               s, g);
+    } else if (fmt == TG_FMT_5TRIT) {
         using C = Cfg<1, TG_FMT_5TRIT>;
         const int blocks = grid_blocks<C::WAVES>(g);
         if (blocks < 1) return hipErrorInvalidValue;

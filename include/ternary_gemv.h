@@ -317,13 +317,16 @@ int tg_plan_init_noalloc(tg_plan *plan, int32_t count, const tg_desc *descs, con
  * 243-entry table). TG_DECODE_NIBBLE (BITCOS): the nibble-keyed lookup of "Breaking the 1.58-bit
  * Barrier for Ternary LLMs", Sec. II-D, Eq. 4 (key: a presence nibble and the next four compact sign
  * bits; entry: the nibble's 4 weights), one lookup per nibble in a 256-entry table.
- * TG_DECODE_ARITH (five-trit and t5b): no table; each base-3 digit of a code byte is computed from the
- * byte directly by multiply and shift (the depth-one, table-free decode of "Sub-Two-Bit Ternary Weight
- * Storage with Table-Free Arithmetic Decoding", abstract). Every strategy gives the same exact int32
- * group sums and the same fp32 outputs; they differ in speed. Code bytes of 243 and above (invalid,
- * see tg_validate) decode to unspecified weights under TG_DECODE_ARITH, to zeros under the table.
+ * TG_DECODE_ARITH (five-trit, t5b, 2-bit): no table. Five-trit and t5b: each base-3 digit of a code
+ * byte is computed from the byte directly by multiply and shift (the depth-one, table-free decode of
+ * "Sub-Two-Bit Ternary Weight Storage with Table-Free Arithmetic Decoding", abstract); 2-bit: the codes
+ * are isolated by shift and mask and contracted as they are (the 2-bit expansion of "Breaking the
+ * 1.58-bit Barrier for Ternary LLMs", Sec. II-C). Either way the group's activation sum is subtracted
+ * once (weight = code - 1). Every strategy gives the same exact int32 group sums and the same fp32
+ * outputs; they differ in speed. Invalid codes (five-trit bytes of 243 and above, 2-bit code 3; see
+ * tg_validate) decode to unspecified weights under TG_DECODE_ARITH, to zeros under the table.
  * tg_plan_set_decode: TG_DECODE_NIBBLE is accepted for initialised BITCOS plans, TG_DECODE_ARITH for
- * five-trit and t5b plans, each with m = 1 on the vector path (path 0) writing fp32 y or int32
+ * five-trit, t5b and 2-bit plans, each with m = 1 on the vector path (path 0) writing fp32 y or int32
  * accumulators (tg_plan_init; not _xs); TG_EINVAL otherwise (the plan is then unchanged). Host only;
  * takes effect at the next ternary_gemv_plan.
  */

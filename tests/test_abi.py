@@ -348,8 +348,8 @@ def test_plan_struct_layout_and_decode_selection_errors():
         assert L.tg_plan_set_decode(ctypes.byref(p), 0) == 0 and p.decode == 0
     p.decode = 5
     assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
-    # the table-free decode: five-trit and t5b plans at m = 1 on the vector path, y or accumulators
-    for fmt in (B.FMT_5TRIT, B.FMT_T5B):
+    # the table-free decode: five-trit, t5b and 2-bit plans at m = 1 on the vector path, y or accumulators
+    for fmt in (B.FMT_5TRIT, B.FMT_T5B, B.FMT_2BIT):
         for acc_mode in (0, 1):
             p = binding.TgPlan(**{**ok, "fmt": fmt, "acc_mode": acc_mode})
             assert L.tg_plan_set_decode(ctypes.byref(p), 2) == 0 and p.decode == 2
@@ -360,7 +360,7 @@ def test_plan_struct_layout_and_decode_selection_errors():
             assert L.tg_plan_set_decode(ctypes.byref(p), 2) == -1 and p.decode == 0
             p.decode = 2  # forged: refused before launching
             assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
-    for fmt in (B.FMT_BITCOS, B.FMT_2BIT):
+    for fmt in (B.FMT_BITCOS,):
         p = binding.TgPlan(**{**ok, "fmt": fmt})
         assert L.tg_plan_set_decode(ctypes.byref(p), 2) == -1 and p.decode == 0
         p.decode = 2

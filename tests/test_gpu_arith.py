@@ -1,6 +1,8 @@
-"""GPU parity of the table-free five-trit decode (TG_DECODE_ARITH: each base-3 digit of a code byte by
-multiply and shift, the depth-one decode of "Sub-Two-Bit Ternary Weight Storage with Table-Free
-Arithmetic Decoding", abstract), for the five-trit code (26-byte groups) and t5b (32-byte blocks).
+"""GPU parity of the table-free decode (TG_DECODE_ARITH): for the five-trit code (26-byte groups) and t5b
+(32-byte blocks) each base-3 digit of a code byte by multiply and shift (the depth-one decode of
+"Sub-Two-Bit Ternary Weight Storage with Table-Free Arithmetic Decoding", abstract); for 2-bit the codes
+isolated by shift and mask and contracted as they are ("Breaking the 1.58-bit Barrier for Ternary LLMs",
+Sec. II-C: 2-bit expansion by shift, mask and subtract).
 
 The int32 group (block) sums must match the oracle bit for bit, and the fp32 outputs must be
 identical to the table decode's (both add the same exact fp64 terms in the same order) and within the
@@ -45,16 +47,16 @@ def _case(fmt, n, k, z, i):
         x[:] = -128
     elif i == 4:
         x[:] = 127
-    if fmt == B.FMT_5TRIT:
+    if fmt in (B.FMT_5TRIT, B.FMT_2BIT):
         s = synth.scales(n, k // 128, seed=1700 + i)
         acc_ref = O.gemv_acc(w, x)
-        return w, x, s, acc_ref, O.combine(acc_ref, s), B.pack_5trit(w)
+        return w, x, s, acc_ref, O.combine(acc_ref, s), B.pack_5trit(w) if fmt == B.FMT_5TRIT else B.pack_2bit(w)
     scale = 0.0213 + 0.001 * i
     acc_ref = O.gemv_acc_blocks(w, x)
     return w, x, scale, acc_ref, O.combine_tensor(acc_ref, scale), B.pack_t5b(w, scale)
 
 
-@pytest.mark.parametrize("fmt", [B.FMT_5TRIT, B.FMT_T5B], ids=["5trit", "t5b"])
+@pytest.mark.parametrize("fmt", [B.FMT_5TRIT, B.FMT_T5B, B.FMT_2BIT], ids=["5trit", "t5b", "2bit"])
 def test_arith_decode_matches_oracle_and_table_decode(fmt):
     dev = _dev()
     _say(f"[gpu] table-free decode plan, fmt={fmt}, {len(SHAPES)} GEMVs")
