@@ -11,8 +11,9 @@ sign index + fp16 scales), whole job.
 Also measured and reported beside it (same process): the same pass as 32 per-layer launches and as
 224 single-GEMV launches (captured in a HIP graph), each matrix's single-call time, the pass on
 float activations quantised per group (quantiser time per call, grouped GEMV with activation group
-scales), the five-trit and 2-bit formats on the same layer set, the stream-read ceiling of this GPU,
-and the CPU oracle.
+scales), the five-trit, 2-bit and t5b formats on the same layer set (each fixed code also with its
+table-free decode), the same launch with its weights in the Infinity Cache (the decode's own rate), the
+stream-read ceiling of this GPU, and the CPU oracle.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -199,27 +200,25 @@ def cpu_baseline(O, ls, budget_s=12.0, one_core_budget_s=8.0):
                 cpu_model=cpu_model(), cores_available=cores)
 
 
-def cache_resident(torch, B, ls, copies=(2, 4), launches=200, decode=None):
-    """Rate of one grouped launch over the first 2 and 4 layer copies (94 and 189 MB of BITCOS, inside
-    the 256 MB Infinity Cache once the first launch has read them), after SETTLE_MS of the same
-    launches. The marginal rate between the two cancels the fixed cost of a launch: the decode rate
-    with the weights served from the cache instead of HBM. (Both sizes give every wave several units
-    of the same kinds, so the fixed part is alike; a one-layer plan takes finer units and a shorter
-    start and would not cancel.)"""
-    res = {}
-    for L in copies:
-        p = ls.plan(B, [m for row in ls.mats[:L] for m in row])
-        if decode is not None:
-            p.set_decode(decode)
-        settle(torch, p.run)
-        s = time_launches(torch, p.run, launches, 0) / launches
-        nbytes = L * sum(ls.layer_bytes)
-        res[f"layers_{L}"] = {"mb": round(nbytes / 1e6, 1), "us_per_launch": round(s * 1e6, 2),
-                              "gbs": round(nbytes / s / 1e9, 1)}
-        del p
-    a, b = res[f"layers_{copies[0]}"], res[f"layers_{copies[-1]}"]
-    res["marginal_gbs"] = round((b["mb"] - a["mb"]) * 1e6 / ((b["us_per_launch"] - a["us_per_launch"]) * 1e-6) / 1e9, 1)
-    res["fixed_us_per_launch"] = round(a["us_per_launch"] - a["mb"] * 1e6 / (res["marginal_gbs"] * 1e9) * 1e6, 2)
+CACHE_FIT_BYTES = 200e6  # distinct weight bytes kept well inside the 256 MB Infinity Cache
+
+
+def cache_resident(torch, B, ls, launches=60, decode=None):
+    """The step's own launch (all LAYERS x 7 GEMVs, same plan shape) with its weights taken from the
+    first few layer copies only (as many as fit CACHE_FIT_BYTES: 4 of BITCOS, 189 MB), each referenced
+    in turn, so after SETTLE_MS of the same launches the weights come from the Infinity Cache instead
+    of HBM. The rate (algorithmic bytes of the 224 GEMVs per second) is the decode's own rate at the
+    step's launch shape. (Repeated GEMVs write the same outputs with the same values.)"""
+    distinct = max(1, min(4, int(CACHE_FIT_BYTES // sum(ls.layer_bytes))))
+    mats = [m for layer in range(ls.layers) for m in ls.mats[layer % distinct]]
+    p = ls.plan(B, mats)
+    if decode is not None:
+        p.set_decode(decode)
+    settle(torch, p.run)
+    s = time_launches(torch, p.run, launches, 0) / launches
+    res = {"copies": distinct, "distinct_mb": round(distinct * sum(ls.layer_bytes) / 1e6, 1), "us_per_launch": round(s * 1e6, 2),
+           "gbs": round(ls.step_bytes / s / 1e9, 1)}
+    del p
     return res
 
 
@@ -635,7 +634,7 @@ def main():
     out["per_matrix_single_call"] = per_mat
     del layer_plans, g
     torch.cuda.empty_cache()
-    log("[bench] cache-resident decode rate (2 and 4 layer copies)")
+    log("[bench] cache-resident decode rate (the step over 4 distinct layer copies)")
     out["cache_resident"] = {"bitcos": cache_resident(torch, B, ls)}
 
     log("[bench] float activations: quantiser and GEMV with activation group scales")
@@ -669,14 +668,14 @@ def main():
                           "step_bytes": lf.step_bytes}
         if fname != "t5b":
             out["cache_resident"][fname] = cache_resident(torch, B, lf)
-        if fname in ("5trit", "t5b"):
-            # the table-free decode of the same codes (digits by multiply and shift, no LDS table)
-            pf.set_decode(B.DECODE_ARITH)
-            sa = time_launches(torch, pf.run, n_f, args.warmup)
-            formats[fname]["table_free"] = {"gbs": round(lf.step_bytes * n_f / sa / 1e9, 1),
-                                            "ms_per_step": round(sa / n_f * 1e3, 3)}
-            if fname == "5trit":
-                out["cache_resident"]["5trit_table_free"] = cache_resident(torch, B, lf, decode=B.DECODE_ARITH)
+        # the table-free decode of the same codes (five-trit digits by multiply and shift, 2-bit codes by
+        # shift and mask; no LDS table)
+        pf.set_decode(B.DECODE_ARITH)
+        sa = time_launches(torch, pf.run, n_f, args.warmup)
+        formats[fname]["table_free"] = {"gbs": round(lf.step_bytes * n_f / sa / 1e9, 1),
+                                        "ms_per_step": round(sa / n_f * 1e3, 3)}
+        if fname != "t5b":
+            out["cache_resident"][f"{fname}_table_free"] = cache_resident(torch, B, lf, decode=B.DECODE_ARITH)
         del pf, lf
         torch.cuda.empty_cache()
     out["formats"] = formats
