@@ -218,6 +218,17 @@ def counters(out_md, command, csvs):
     if vals.get("SQ_INSTS_LDS") and vals.get("SQ_LDS_BANK_CONFLICT"):
         lines.append(f"- bank-conflict cycles per LDS instruction: "
                      f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_INSTS_LDS']:.2f}")
+    if wc and vals.get("SQ_ACTIVE_INST_VALU") and vals.get("SQ_WAVES"):
+        # 256 CUs x 4 SIMDs; the waves of the launch are resident together (one block per CU)
+        per_simd = vals["SQ_WAVES"] / (256 * 4)
+        lines += ["", "Reading: `SQ_WAVE_CYCLES` and `SQ_ACTIVE_INST_*` count quad-cycles summed over waves, and "
+                  "each VALU instruction holds its SIMD for one (`SQ_ACTIVE_INST_VALU` = `SQ_INSTS_VALU`: "
+                  f"{vals['SQ_ACTIVE_INST_VALU'] / wave_steps:.1f} against "
+                  f"{vals.get('SQ_INSTS_VALU', float('nan')) / wave_steps:.1f} per wave-step). With "
+                  f"{per_simd:.0f} waves per SIMD, the SIMD's VALU is busy about {per_simd:.0f} x "
+                  f"{100 * vals['SQ_ACTIVE_INST_VALU'] / wc:.1f} % = "
+                  f"{100 * per_simd * vals['SQ_ACTIVE_INST_VALU'] / wc:.0f} % of the dispatch: the step is bound by "
+                  "VALU issue, and one wave's waits are filled by the other waves of its SIMD."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
