@@ -327,17 +327,45 @@ __device__ __forceinline__ void run_loop(const Problem &p, int u0, int u1, const
                     const int gc = cD == x.nch - 1 ? x.glast : 64;
                     const bool va = live && lane < gc && row < row_end;
                     if constexpr (RACC && !ACC) {
-                        double term = (double)acc[0] * (double)half_bits_to_float(g[jb].scale);
-                        if constexpr (XS) term *= (double)xsv[0];
-                        facc[slot] = cD != 0 ? facc[slot] + term : term;
+                        // the first pass starts the row's term afresh (dead steps of the pipeline fill
+                        // leave garbage in it); acc * s is exact in fp64, so one fused multiply-add
+                        // rounds as the separate product and sum would
+                        const double s = (double)half_bits_to_float(g[jb].scale);
+                        const double b = cD != 0 ? facc[slot] : 0.0;
+                        if constexpr (XS)
+                            facc[slot] = b + (double)acc[0] * s * (double)xsv[0];
+                        else
+                            facc[slot] = __builtin_fma((double)acc[0], s, b);
                     } else {
                         emit<M, ACC, NB, XS>(x, acc, (double)half_bits_to_float(g[jb].scale), xsv, tile, slot,
                                              cD != 0, va ? voff_acc : kOffOff,
                                          live_or_dead(live, ((uint32_t)row * (uint32_t)x.ng + (uint32_t)cD * 64u) * 4u));
                     }
                     if (slot == NB - 1) {  // static: last step of a chunk pass
-                        if constexpr (RACC && !ACC) {
-                            // the unit's rows are complete after the last pass: lane r gets row r
+                        if constexpr (RACC && !ACC && NB % 4 == 0) {
+                            // the unit's rows are complete after the last pass. Four rows at a time go
+                            // through the tile (row q of the four at tile[64 q + lane]); lane l sums the
+                            // terms 4 (l % 16) .. 4 (l % 16) + 3 of row l / 16, then its 16-lane group
+                            // (every lane of the group receives the sum), and the group's first lane
+                            // stores the row.
+                            if (cD == x.nch - 1) {
+#pragma unroll
+                                for (int q0 = 0; q0 < NB; q0 += 4) {
+                                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) tile[64 * q + lane] = facc[q0 + q];
+                                    __builtin_amdgcn_wave_barrier();
+                                    const double *t = tile + 64 * (lane >> 4) + 4 * (lane & 15);
+                                    const double v = seg_sum_f64((t[0] + t[1]) + (t[2] + t[3]), 16);
+                                    const int row = rD + q0 + (lane >> 4);
+                                    const bool own = live && (lane & 15) == 0 && row < row_end;
+                                    st1(__builtin_bit_cast(uint32_t, (float)v), x.ry, own ? (uint32_t)row * 4u : kOffOff,
+                                        0u);
+                                }
+                                __builtin_amdgcn_wave_barrier();
+                            }
+                        } else if constexpr (RACC && !ACC) {
+                            // units of two rows: lane r gets row r from a reduction over the wave
                             double yl = 0.0;
                             if (cD == x.nch - 1) {
 #pragma unroll
