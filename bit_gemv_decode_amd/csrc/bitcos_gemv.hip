@@ -10,8 +10,9 @@
 // Mapping on CDNA4 (wave64, one persistent block per CU: 1024 threads at m = 1, 512 at m = 2, 3):
 //   * a lane owns one 128-weight group of one row per step: its four bitmap dwords arrive with one
 //     16-byte load, its scale with one 2-byte load. A row of k weights takes ng = k/128 lanes; when
-//     ng <= 64 a step holds R = 64/ng consecutive rows, otherwise a row is split into chunks of 64
-//     groups, one chunk per step. A lane's activation bytes (its group's 128 x values) stay in
+//     ng <= 64 a step holds R = 64/ng consecutive rows (at most 64/NB, so that a unit's NB steps hold
+//     no more rows than a wave has lanes: k = 128 and 256 leave lanes idle), otherwise a row is split
+//     into chunks of 64 groups, one chunk per step. A lane's activation bytes (its group's 128 x values) stay in
 //     registers for every row it sees, so x is read once per GEMV (or once per chunk pass).
 //   * sign positions: rows of a step are consecutive in the sign stream, so a lane's first sign sits
 //     at the step's cursor (from the row index, or carried from the row's previous chunk) plus the
@@ -714,7 +715,10 @@ void gemv_geometry(Problem &p, int fmt, int m, int chunk, bool f16) {
     p.nch = (p.ng + 63) / 64;
     if (p.nch == 1) {
         p.G = p.ng;
-        p.R = 64 / p.ng;
+        // The kernels run units of nb steps and reduce a unit's rows at its end, one lane or more per
+        // row, so a unit holds at most 64 rows: rows of one or two groups (k = 128, 256) take at most
+        // 64 / nb per step and leave the other lanes idle.
+        p.R = std::min(64 / p.ng, 64 / nb);
         p.glast = p.ng;
         p.nbu = std::max(1, std::min(nb, 64 / p.R));
     } else {
