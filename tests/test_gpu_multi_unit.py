@@ -68,3 +68,58 @@ def test_multi_unit_plans(fmt, m):
         assert ok, f"{label}: y outside the bound ({ndiff} differ)"
         ok, ndiff = bounds.int8_y_ok(yxs[j].cpu().numpy(), c["y_xs"], c["acc_q"], c["s"], c["xs_ref"])
         assert ok, f"{label}: y with activation scales outside the bound ({ndiff} differ)"
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 16])
+def test_multi_unit_f16_plans(m):
+    # fp16 activations (BITCOS): the vector kernel at m = 1, the matrix-core kernel above (the long rows
+    # hold most of these weights at m = 2), with the bound of the fp16 path
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    dev = torch.device("cuda:0")
+    _say(f"[gpu] multi-unit fp16 plans m={m}: {COPIES} x {len(SHAPES)} GEMVs")
+    cases = []
+    for i, (n, k) in enumerate(SHAPES):
+        seed = 9300 + 10 * i + m
+        w = synth.ternary(n, k, 0.42, seed=seed)
+        s = synth.scales(n, k // 128, seed=seed)
+        x16 = synth.float_activations(m, k, seed=seed).astype(np.float16)
+        y_ref = O.gemv_f16(w, s, x16)
+        cases.append(dict(n=n, bound=bounds.f16_bound(w, s, x16, y_ref), y=y_ref,
+                          dw=B.DeviceWeights(B.pack_bitcos(w), dev), st=torch.from_numpy(s).to(dev),
+                          x=torch.from_numpy(x16).to(dev)))
+        del w
+    order = [c for _ in range(COPIES) for c in cases]
+    ys = [torch.full((m, c["n"]), float("nan"), dtype=torch.float32, device=dev) for c in order]
+    B.Plan([c["dw"] for c in order], [c["x"] for c in order], scales=[c["st"] for c in order], ys=ys,
+           f16=True).run()
+    torch.cuda.synchronize()
+    for j, c in enumerate(order):
+        err = np.abs(ys[j].cpu().numpy().astype(np.float64) - c["y"].astype(np.float64))
+        assert np.all(err <= c["bound"]), f"GEMV {j} ({c['n']} rows): outside the fp16 bound"
+
+
+@pytest.mark.parametrize("m", [1, 2, 3])
+def test_multi_unit_t5b_plans(m):
+    # t5b: 32-byte blocks of 160 weights, one scale per tensor; the table and the table-free decode
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    dev = torch.device("cuda:0")
+    _say(f"[gpu] multi-unit t5b plans m={m}: {COPIES} x {len(SHAPES)} GEMVs")
+    cases = []
+    for i, (n, k) in enumerate(SHAPES):
+        seed = 9500 + 10 * i + m
+        scale = 0.031 + 0.002 * i
+        w = synth.ternary(n, k, 0.4, seed=seed)
+        x = synth.activations(m, k, seed=seed)
+        acc = O.gemv_acc_blocks(w, x)
+        cases.append(dict(n=n, acc=acc, scale=scale, y=O.combine_tensor(acc, scale),
+                          dw=B.DeviceWeights(B.pack_t5b(w, scale), dev), x=torch.from_numpy(x).to(dev)))
+        del w
+    order = [c for _ in range(COPIES) for c in cases]
+    decodes = [B.DECODE_BYTE] + ([B.DECODE_ARITH] if m == 1 else [])
+    for decode in decodes:
+        ys = [torch.full((m, c["n"]), float("nan"), dtype=torch.float32, device=dev) for c in order]
+        B.Plan([c["dw"] for c in order], [c["x"] for c in order], ys=ys).set_decode(decode).run()
+        torch.cuda.synchronize()
+        for j, c in enumerate(order):
+            ok, ndiff = bounds.tensor_y_ok(ys[j].cpu().numpy(), c["y"], c["acc"], c["scale"])
+            assert ok, f"GEMV {j} ({c['n']} rows), decode {decode}: outside the bound ({ndiff} differ)"
