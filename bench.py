@@ -12,8 +12,9 @@ Also measured and reported beside it (same process): the same pass as 32 per-lay
 224 single-GEMV launches (captured in a HIP graph), each matrix's single-call time, the pass on
 float activations quantised per group (quantiser time per call, grouped GEMV with activation group
 scales), the five-trit, 2-bit and t5b formats on the same layer set (each fixed code also with its
-table-free decode), the same launch with its weights in the Infinity Cache (the decode's own rate), the
-stream-read ceiling of this GPU, and the CPU oracle.
+table-free decode), the same launch with its weights in the Infinity Cache and a 2560x2560 matrix
+referenced 768 times from L2 (the decode's own rate), the stream-read ceiling of this GPU, and the CPU
+oracle.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -220,6 +221,37 @@ def cache_resident(torch, B, ls, launches=60, decode=None):
            "gbs": round(ls.step_bytes / s / 1e9, 1)}
     del p
     return res
+
+
+L2_SHAPE, L2_Z, L2_REFS = (2560, 2560), 0.42, 768
+
+
+def l2_resident(torch, B, synth, dev, launches=40):
+    """The decode rate with the matrix in L2: one 2560x2560 matrix (z = 0.42: 1.41 MB of BITCOS), referenced
+    768 times in one grouped launch with one output. Consecutive wave ranges share an XCD, so each XCD's
+    4 MB L2 holds the whole matrix after its first read and serves the other references; the rate is the
+    768 references' algorithmic bytes per second after SETTLE_MS of the same launches. BITCOS, five-trit and
+    2-bit (the fixed codes with their LDS table and table-free)."""
+    n, k = L2_SHAPE
+    w = synth.ternary(n, k, L2_Z, seed=0)
+    s = torch.from_numpy(synth.scales(n, k // 128, seed=0)).to(dev)
+    x = torch.from_numpy(synth.activations(1, k, seed=0)).to(dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+    out = {"shape": [n, k], "z": L2_Z, "references": L2_REFS}
+    for fname, fmt in (("bitcos", B.FMT_BITCOS), ("5trit", B.FMT_5TRIT), ("2bit", B.FMT_2BIT)):
+        dw = B.DeviceWeights(B.pack(fmt, w), dev)
+        for decode in ((None,) if fmt == B.FMT_BITCOS else (None, B.DECODE_ARITH)):
+            p = B.Plan([dw] * L2_REFS, [x] * L2_REFS, scales=[s] * L2_REFS, ys=[y] * L2_REFS)
+            if decode is not None:
+                p.set_decode(decode)
+            settle(torch, p.run)
+            secs = time_launches(torch, p.run, launches, 0) / launches
+            key = fname if decode is None else f"{fname}_table_free"
+            out[key] = {"mb": round(packed_bytes(dw) / 1e6, 3), "us_per_launch": round(secs * 1e6, 2),
+                        "gbs": round(L2_REFS * packed_bytes(dw) / secs / 1e9, 1)}
+            del p
+        del dw
+    return out
 
 
 def activation_quant(torch, B, synth, ls, dev, steps, warmup):
@@ -636,6 +668,8 @@ def main():
     torch.cuda.empty_cache()
     log("[bench] cache-resident decode rate (the step over 4 distinct layer copies)")
     out["cache_resident"] = {"bitcos": cache_resident(torch, B, ls)}
+    log("[bench] L2-resident decode rate (one 2560x2560 matrix, 768 references)")
+    out["l2_resident"] = l2_resident(torch, B, synth, dev)
 
     log("[bench] float activations: quantiser and GEMV with activation group scales")
     out["activation_quant"] = activation_quant(torch, B, synth, ls, dev, max(3, args.steps // 2), args.warmup)
