@@ -240,13 +240,13 @@ def l2_resident(torch, B, synth, dev, launches=40):
     out = {"shape": [n, k], "z": L2_Z, "references": L2_REFS}
     for fname, fmt in (("bitcos", B.FMT_BITCOS), ("5trit", B.FMT_5TRIT), ("2bit", B.FMT_2BIT)):
         dw = B.DeviceWeights(B.pack(fmt, w), dev)
-        for decode in ((None,) if fmt == B.FMT_BITCOS else (None, B.DECODE_ARITH)):
+        for decode in ((None,) if fmt == B.FMT_BITCOS else (B.DECODE_BYTE, B.DECODE_ARITH)):
             p = B.Plan([dw] * L2_REFS, [x] * L2_REFS, scales=[s] * L2_REFS, ys=[y] * L2_REFS)
             if decode is not None:
                 p.set_decode(decode)
             settle(torch, p.run)
             secs = time_launches(torch, p.run, launches, 0) / launches
-            key = fname if decode is None else f"{fname}_table_free"
+            key = f"{fname}_table_free" if decode == B.DECODE_ARITH else fname
             out[key] = {"mb": round(packed_bytes(dw) / 1e6, 3), "us_per_launch": round(secs * 1e6, 2),
                         "gbs": round(L2_REFS * packed_bytes(dw) / secs / 1e9, 1)}
             del p
@@ -696,19 +696,20 @@ def main():
         log(f"[bench] {fname} layer set")
         lf = LayerSet(B, synth, torch, dev, fmt)
         pf = lf.plan(B)
-        sf = time_launches(torch, pf.run, max(3, args.steps // 2), args.warmup)
+        default = pf.plan.decode  # the table-free decode for 2-bit, the LDS table for the others
         n_f = max(3, args.steps // 2)
-        formats[fname] = {"gbs": round(lf.step_bytes * n_f / sf / 1e9, 1), "ms_per_step": round(sf / n_f * 1e3, 3),
-                          "step_bytes": lf.step_bytes}
+        rates = {}
+        # the LDS-table decode and the table-free one (five-trit digits by multiply and shift, 2-bit codes
+        # by shift and mask; no LDS table), the plan's default decode reported at the top level
+        for decode in (B.DECODE_BYTE, B.DECODE_ARITH):
+            pf.set_decode(decode)
+            sf = time_launches(torch, pf.run, n_f, args.warmup)
+            rates[decode] = {"gbs": round(lf.step_bytes * n_f / sf / 1e9, 1), "ms_per_step": round(sf / n_f * 1e3, 3)}
+        formats[fname] = {**rates[default], "step_bytes": lf.step_bytes,
+                          "decode": "table_free" if default == B.DECODE_ARITH else "table",
+                          "table": rates[B.DECODE_BYTE], "table_free": rates[B.DECODE_ARITH]}
         if fname != "t5b":
-            out["cache_resident"][fname] = cache_resident(torch, B, lf)
-        # the table-free decode of the same codes (five-trit digits by multiply and shift, 2-bit codes by
-        # shift and mask; no LDS table)
-        pf.set_decode(B.DECODE_ARITH)
-        sa = time_launches(torch, pf.run, n_f, args.warmup)
-        formats[fname]["table_free"] = {"gbs": round(lf.step_bytes * n_f / sa / 1e9, 1),
-                                        "ms_per_step": round(sa / n_f * 1e3, 3)}
-        if fname != "t5b":
+            out["cache_resident"][fname] = cache_resident(torch, B, lf, decode=B.DECODE_BYTE)
             out["cache_resident"][f"{fname}_table_free"] = cache_resident(torch, B, lf, decode=B.DECODE_ARITH)
         del pf, lf
         torch.cuda.empty_cache()

@@ -473,8 +473,9 @@ class Plan:
                                   m), "tg_plan_init")
 
     def set_decode(self, decode: int):
-        """Decode strategy: DECODE_BYTE (default), DECODE_NIBBLE (BITCOS) or DECODE_ARITH (five-trit,
-        t5b, 2-bit) (tg_plan_set_decode)."""
+        """Decode strategy: DECODE_BYTE, DECODE_NIBBLE (BITCOS) or DECODE_ARITH (five-trit, t5b, 2-bit)
+        (tg_plan_set_decode). A new plan decodes by table (DECODE_BYTE), except 2-bit plans that may take
+        DECODE_ARITH, which start with it."""
         _check(lib().tg_plan_set_decode(ctypes.byref(self.plan), decode), "tg_plan_set_decode")
         return self
 

@@ -184,8 +184,13 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         g.live = desc->fmt == TG_FMT_BITCOS && desc->empty_rows > 0 && mt == 1 && !mfma && out != kOutAcc;
         if (g.units < 1) return TG_ESHAPE;
     }
+    // a 2-bit call of one activation row with fp32 or int32 outputs takes the table-free decode, as
+    // 2-bit plans do by default
+    const bool table_free = desc->fmt == TG_FMT_2BIT && m == 1 && !mfma && (out == kOutY || out == kOutAcc);
     for (int i = 0; i < nl; ++i)
-        if (launch(desc->fmt, gs[i], out, mfma, s) != hipSuccess) return TG_EHIP;
+        if ((table_free ? launch_table_free(desc->fmt, gs[i], out, s) : launch(desc->fmt, gs[i], out, mfma, s)) !=
+            hipSuccess)
+            return TG_EHIP;
     return TG_OK;
 }
 
@@ -301,6 +306,9 @@ int path_waves(int fmt, int m, int path) {
     if (path == kPathF16) return device_cus() * f16_waves(m);
     return plan_waves(fmt, m, path == kPathMfma || path == kPathF16Mfma);
 }
+
+// Whether a plan may run the table-free decode (defined with tg_plan_set_decode below).
+bool arith_ok(const tg_plan *p);
 
 // f16: the x are fp16 activations (BITCOS, fp32 outputs; the fp16 vector kernel for m <= kF16MaxM,
 // the fp16 matrix-core kernel from kF16MfmaMinM rows).
@@ -429,6 +437,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     plan->path = path;
     plan->live_rows = live ? 1 : 0;
     plan->table = table;
+    // 2-bit plans that the table-free decode serves take it by default: it reads no LDS table and
+    // issues two instructions per four codes (faster from HBM and from the caches, measured)
+    if (fmt == TG_FMT_2BIT && arith_ok(plan)) plan->decode = TG_DECODE_ARITH;
     return TG_OK;
 }
 
@@ -519,7 +530,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (plan->decode == TG_DECODE_NIBBLE)
         return launch_bitcos_nibble(g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->decode == TG_DECODE_ARITH)
-        return launch_five_trit_arith(plan->fmt, g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK
+        return launch_table_free(plan->fmt, g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK
                                                                                                          : TG_EHIP;
     if (plan->path == kPathF16) return launch_bitcos_f16(g, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->path == kPathF16Mfma)

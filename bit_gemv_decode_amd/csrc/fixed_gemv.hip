@@ -582,7 +582,7 @@ hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s) {
     return launch_fixed<TG_FMT_2BIT>(g, out, s);
 }
 
-hipError_t launch_five_trit_arith(int fmt, const GroupArgs &g, int out, hipStream_t s) {
+hipError_t launch_table_free(int fmt, const GroupArgs &g, int out, hipStream_t s) {
     if (g.m != 1 || (out != kOutY && out != kOutAcc) ||
         (fmt != TG_FMT_5TRIT && fmt != TG_FMT_T5B && fmt != TG_FMT_2BIT))
         return hipErrorInvalidValue;

@@ -134,7 +134,7 @@ hipError_t launch_t5(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_b2(const GroupArgs &g, int out, hipStream_t s);
 hipError_t launch_t5b(const GroupArgs &g, int out, hipStream_t s);
 // The table-free decode (five-trit, t5b or 2-bit; m = 1, fp32 y or int32 accumulators).
-hipError_t launch_five_trit_arith(int fmt, const GroupArgs &g, int out, hipStream_t s);
+hipError_t launch_table_free(int fmt, const GroupArgs &g, int out, hipStream_t s);
 
 // BITCOS GEMV at m = 1 with the nibble-keyed decode (fp32 y or int32 accumulators; same geometry).
 hipError_t launch_bitcos_nibble(const GroupArgs &g, int out, hipStream_t s);

@@ -256,7 +256,8 @@ typedef struct tg_plan {
     int32_t waves;       /* waves of the launch the table's work split was made for */
     int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2 / 3: fp16
                             activations on the vector / matrix-core kernel */
-    int32_t decode;      /* TG_DECODE_BYTE (set by every tg_plan_init*), _NIBBLE or _ARITH */
+    int32_t decode;      /* TG_DECODE_BYTE, _NIBBLE or _ARITH (tg_plan_init*: _ARITH for 2-bit plans
+                            that may take it, else _BYTE) */
     int32_t live_rows;   /* 1: some GEMV reports rows without non-zeros (tg_desc.empty_rows), and the
                             launch (BITCOS, m = 1, vector path, fp32 outputs, byte-keyed decode) walks
                             only the other rows of the GEMVs with one row per step, storing 0 for
@@ -312,9 +313,9 @@ int tg_plan_init_noalloc(tg_plan *plan, int32_t count, const tg_desc *descs, con
                          int32_t *const *acc, int32_t m);
 
 /*
- * Decode strategy of a plan. TG_DECODE_BYTE (the default): table lookups in LDS (BITCOS: one per
- * presence byte in a byte-keyed table of 6561 entries; five-trit and t5b: one per code byte in a
- * 243-entry table). TG_DECODE_NIBBLE (BITCOS): the nibble-keyed lookup of "Breaking the 1.58-bit
+ * Decode strategy of a plan. TG_DECODE_BYTE (the default, except for 2-bit plans below): table
+ * lookups in LDS (BITCOS: one per presence byte in a byte-keyed table of 6561 entries; five-trit and
+ * t5b: one per code byte in a 243-entry table; 2-bit: one per code byte in a 256-entry table). TG_DECODE_NIBBLE (BITCOS): the nibble-keyed lookup of "Breaking the 1.58-bit
  * Barrier for Ternary LLMs", Sec. II-D, Eq. 4 (key: a presence nibble and the next four compact sign
  * bits; entry: the nibble's 4 weights), one lookup per nibble in a 256-entry table.
  * TG_DECODE_ARITH (five-trit, t5b, 2-bit): no table. Five-trit and t5b: each base-3 digit of a code
@@ -325,6 +326,9 @@ int tg_plan_init_noalloc(tg_plan *plan, int32_t count, const tg_desc *descs, con
  * once (weight = code - 1). Every strategy gives the same exact int32 group sums and the same fp32
  * outputs; they differ in speed. Invalid codes (five-trit bytes of 243 and above, 2-bit code 3; see
  * tg_validate) decode to unspecified weights under TG_DECODE_ARITH, to zeros under the table.
+ * tg_plan_init* gives 2-bit plans that may take TG_DECODE_ARITH (below) that decode by default, and a
+ * ternary_gemv / ternary_gemv_acc call on 2-bit weights with m = 1 uses it too: measured faster from
+ * HBM and from the caches. tg_plan_set_decode(plan, TG_DECODE_BYTE) selects the table.
  * tg_plan_set_decode: TG_DECODE_NIBBLE is accepted for initialised BITCOS plans, TG_DECODE_ARITH for
  * five-trit, t5b and 2-bit plans, each with m = 1 on the vector path (path 0) writing fp32 y or int32
  * accumulators (tg_plan_init; not _xs); TG_EINVAL otherwise (the plan is then unchanged). Host only;

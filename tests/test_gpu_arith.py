@@ -107,3 +107,37 @@ def test_arith_decode_every_code_byte():
     B.Plan([dw], [torch.from_numpy(x).to(dev)], accs=[acc]).set_decode(B.DECODE_ARITH).run()
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+def test_2bit_plans_and_calls_default_to_the_table_free_decode():
+    # a new 2-bit plan that may take the table-free decode starts with it (m = 1, fp32 or int32 outputs);
+    # plans it cannot serve (m = 2, activation group scales) and the other formats start with the table;
+    # single calls give the same results as the plans
+    dev = _dev()
+    n, k = 300, 4224
+    w = synth.ternary(n, k, 0.4, seed=1901)
+    x = synth.activations(2, k, seed=1901)
+    s = synth.scales(n, k // 128, seed=1901)
+    acc_ref = O.gemv_acc(w, x[:1])
+    y_ref = O.combine(acc_ref, s)
+    dw = B.DeviceWeights(B.pack_2bit(w), dev)
+    xt, st = torch.from_numpy(x[:1].copy()).to(dev), torch.from_numpy(s).to(dev)
+    y = torch.full((1, n), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((1, n, k // 128), -7, dtype=torch.int32, device=dev)
+    py = B.Plan([dw], [xt], scales=[st], ys=[y])
+    pa = B.Plan([dw], [xt], accs=[acc])
+    assert py.plan.decode == B.DECODE_ARITH and pa.plan.decode == B.DECODE_ARITH
+    y2 = torch.empty((2, n), dtype=torch.float32, device=dev)
+    assert B.Plan([dw], [torch.from_numpy(x).to(dev)], scales=[st], ys=[y2]).plan.decode == B.DECODE_BYTE
+    xq, xs = B.quantize_x(torch.from_numpy(synth.float_activations(1, k, seed=1901)).to(dev))
+    assert B.Plan([dw], [xq], scales=[st], ys=[y], x_scales=[xs]).plan.decode == B.DECODE_BYTE
+    dw5 = B.DeviceWeights(B.pack_5trit(w), dev)
+    assert B.Plan([dw5], [xt], scales=[st], ys=[y]).plan.decode == B.DECODE_BYTE
+    py.run()
+    pa.run()
+    y_call = B.ternary_gemv(dw, st, xt)
+    acc_call = B.ternary_gemv_acc(dw, xt)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref) and np.array_equal(acc_call.cpu().numpy(), acc_ref)
+    assert bounds.int8_y_ok(y.cpu().numpy(), y_ref, acc_ref, s)[0]
+    assert np.array_equal(y_call.cpu().numpy(), y.cpu().numpy())
