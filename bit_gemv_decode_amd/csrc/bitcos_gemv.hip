@@ -16,9 +16,10 @@
 //     registers for every row it sees, so x is read once per GEMV (or once per chunk pass).
 //   * sign positions: rows of a step are consecutive in the sign stream, so a lane's first sign sits
 //     at the step's cursor (from the row index, or carried from the row's previous chunk) plus the
-//     exclusive prefix sum of the popcounts of the lanes before it (DPP scan). For each bitmap dword
-//     the lane loads the three sign-stream dwords holding bits [pos - 3, pos + 61) and funnel-shifts
-//     them (pos is that dword's first sign).
+//     exclusive prefix sum of the popcounts of the lanes before it (DPP scan). For each pair of bitmap
+//     dwords the lane loads the four sign-stream dwords holding bits [pos - 3, pos + 93) and
+//     funnel-shifts them (pos is the pair's first sign; the second dword's window follows by a 64-bit
+//     shift of the popcount of the first).
 //   * the deposit of Fig. 4 is a table lookup in LDS, keyed per presence byte (the nibble-keyed
 //     lookup of Sec. II-D, Eq. 4 and Fig. 9, widened to a byte): entry (pb, s) holds the 8 ternary
 //     int8 weights for presence byte pb followed by the popcount(pb) compact signs s; 3^8 = 6561
@@ -31,7 +32,8 @@
 //   * v_dot4_i32_i8 contracts 4 weights per instruction. Each group's int32 sum times its fp16 scale
 //     (exact in fp64) goes to an LDS tile; once per unit the tile's rows are summed (fp64, DPP) and
 //     stored as fp32. Chunked rows at m = 1 keep those terms in registers instead (one fp64 per row
-//     of the unit and lane) and reduce them over the wave at the unit's end.
+//     of the unit and lane, summed over the chunk passes) and, at the unit's end, pass them through
+//     the tile four rows at a time: each lane sums four terms of one row, then 16 lanes by DPP.
 //   * alternative decode (NIB, Sec. II-D, Eq. 4): the Xe2 kernel's nibble-keyed lookup, a 256-entry
 //     table keyed by a presence nibble and the next four compact signs, each entry the nibble's 4 int8
 //     weights; one conflict-free 4-byte LDS read and one v_dot4_i32_i8 per nibble, with the sign
@@ -43,9 +45,9 @@
 //     entry bytes into two fp16 weights and v_dot2_f32_f16 contracts them with two activations into
 //     an fp32 group sum. Each lane holds its group's 128 activations (256 bytes) in registers.
 //   * loads are software-pipelined: a step's bitmap four half-steps before its decode, its sign
-//     windows two, with the loop unrolled so that no register with a load in flight is ever copied. Every load goes
-//     through a buffer resource and is issued unconditionally; lanes with nothing to read use an
-//     out-of-range offset, which returns zero without a memory request.
+//     windows two, with the loop unrolled so that no register with a load in flight is ever copied.
+//     Every load goes through a buffer resource and is issued unconditionally; lanes with nothing to
+//     read use an out-of-range offset, which returns zero without a memory request.
 #include <algorithm>
 #include <type_traits>
 

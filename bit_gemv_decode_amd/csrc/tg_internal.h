@@ -9,7 +9,12 @@
 namespace tg {
 
 constexpr uint64_t kAlign = 256;      // section alignment inside a packed buffer
-constexpr uint64_t kSignPad = 16;     // zero bytes after the sign stream (room for 2-dword windows)
+// Zero bytes after the sign stream (and after the fixed codes). The kernels read these sections
+// through buffer resources that end with the section (the thin-batch kernel's sign stretches: with the
+// row index after it), so a window or stretch that runs past the stream's end reads zeros whatever its
+// length (the vector kernels' 4-dword windows, the thin-batch kernel's 36-dword stretches); the pad
+// keeps a 16-byte read that starts in the stream inside the packed buffer for plain loads too.
+constexpr uint64_t kSignPad = 16;
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
