@@ -612,15 +612,20 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": (round(traffic["bytes_per_launch"] / ls.step_bytes, 4) if traffic else None),
+                     # HBM bytes per launch over the same launch time as `achieved` (GB/s)
+                     "traffic": (round(traffic["bytes_per_launch"] / step_s / 1e9, 2) if traffic else None),
+                     "traffic_ratio": (round(traffic["bytes_per_launch"] / ls.step_bytes, 4) if traffic else None),
+                     "hbm_bytes_per_launch": traffic["bytes_per_launch"] if traffic else None,
                      "kernel": "bitcos_gemv_kernel<1, false, false, false, false, false> (grouped, one launch per step)",
                      "algorithmic_bytes_per_launch": ls.step_bytes,
                      "avg_launch_us": round(step_s * 1e6, 2)},
     }
     if traffic:
-        out["roofline"]["traffic_note"] = (f"HBM bytes per launch / algorithmic bytes, from rocprofv3 "
-                                           f"FETCH_SIZE+WRITE_SIZE scaled by the stream-read calibration "
-                                           f"({os.path.relpath(TRAFFIC_FILE, ROOT)})")
+        out["roofline"]["traffic_note"] = (f"traffic: HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                           f"scaled by the counters' readings for a stream read and a fill of "
+                                           f"known size; {os.path.relpath(TRAFFIC_FILE, ROOT)}) over the "
+                                           f"launch time of `achieved`; traffic_ratio: the same bytes over "
+                                           f"the algorithmic bytes")
     # the same launches again once the GPU has run them back to back for SETTLE_MS (an extra field:
     # `value` above is the timed region of this command as given)
     settle(torch, plan.run)
