@@ -181,7 +181,8 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         if (chunk != kChunkCoarse) geometry(g.one, desc->fmt, mt, mfma, chunk);
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
-        g.live = desc->fmt == TG_FMT_BITCOS && desc->empty_rows > 0 && mt == 1 && !mfma && out != kOutAcc;
+        g.live = desc->fmt == TG_FMT_BITCOS && (desc->empty_rows > 0 || desc->k == kWideLaneK) && mt == 1 && !mfma &&
+                 out != kOutAcc;
         if (g.units < 1) return TG_ESHAPE;
     }
     // a 2-bit call of one activation row with fp32 or int32 outputs takes the table-free decode, as
@@ -284,6 +285,8 @@ double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u, bool live) {
     // costs less than a full one on the plain walk too (every lane reads the same table entries) and
     // the walk adds a little per step: counting an empty row as half a step balanced best on MI355X
     // (the 70B-shaped stack, against no credit and a full one, identical outputs).
+    if (live && p.nch == 1 && p.k == kWideLaneK)
+        return (double)rows * kWideLaneStepCost * (1.0 - 0.5 * (double)p.empty_rows / (double)p.n);
     if (live && p.nch == 1 && p.R == 1 && p.empty_rows > 0)
         return (double)rows * (1.0 - 0.5 * (double)p.empty_rows / (double)p.n);
     if (p.nch == 1) return (double)((rows + p.R - 1) / p.R);
@@ -355,7 +358,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
                           : fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
     const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : kPathVector;
     bool any_empty = false;
-    for (int32_t i = 0; i < count; ++i) any_empty = any_empty || host[i].empty_rows > 0;
+    for (int32_t i = 0; i < count; ++i) any_empty = any_empty || host[i].empty_rows > 0 || host[i].k == kWideLaneK;
     const bool live = fmt == TG_FMT_BITCOS && m == 1 && path == kPathVector && !acc_mode && any_empty;
     for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, kChunkCoarse, f16);
     {

@@ -192,6 +192,95 @@ __device__ __forceinline__ void decode(const u32x4 &bm, const SgBuf &g, const ui
     }
 }
 
+// Rows of 5120 weights (40 groups) at m = 1 with fp32 outputs. With a lane per 128-weight group,
+// a step of such a row keeps 24 of the 64 lanes idle. Instead each lane takes 80 consecutive weights
+// (ten presence bytes), so a row fills the wave: lane l holds weights [80 l, 80 l + 80), which lie in
+// one group or straddle two, the boundary falling on an even presence byte. The lane keeps its int32
+// sum up to the boundary apart and scales the two parts with their own group scales.
+constexpr int kW80Groups = (int)(kWideLaneK / TG_GROUP);
+
+// Sign stage of one step of a wide-lane row: one four-dword window of the sign stream holding bits
+// [pos - 3, pos + 93) (pos = the lane's first sign; its at most 80 signs end before pos + 80), the
+// funnel-shift amount into it, the scales of the lane's first and last group.
+struct SgBufW {
+    u32x4 s;
+    uint32_t sh;
+    uint16_t sc1, sc2;
+};
+
+// The lane's ten bitmap bytes start `bsh` bits (0 or 16) into its 16-byte load: they are moved to the
+// bottom of bm (bm.z keeps bytes 8 and 9 in its low half). Then the row's popcount scan and the sign
+// and scale loads, as stage_signs does for group lanes.
+__device__ __forceinline__ uint32_t stage_signs_w80(const Ctx &x, u32x4 &bm, uint32_t bsh, uint32_t cur, bool live,
+                                                    uint32_t voff_sc1, uint32_t voff_sc2, uint32_t soff_sc,
+                                                    SgBufW &g) {
+    const uint32_t d0 = __builtin_amdgcn_alignbit(bm.y, bm.x, bsh);
+    const uint32_t d1 = __builtin_amdgcn_alignbit(bm.z, bm.y, bsh);
+    const uint32_t d2 = __builtin_amdgcn_alignbit(bm.w, bm.z, bsh) & 0xFFFFu;
+    bm.x = d0;
+    bm.y = d1;
+    bm.z = d2;
+    const uint32_t pc = __builtin_popcount(d0) + __builtin_popcount(d1) + __builtin_popcount(d2);
+    const uint32_t incl = wave_incl_scan(pc);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    // window start = first sign - 3, biased by +32 (the sign resource starts one dword early)
+    const uint32_t b0 = cur + 29u + incl - pc;
+    g.s = ld4(x.rsg, (b0 >> 5) << 2, live_or_dead(live, 0u));
+    g.sh = b0;  // alignbit uses the low 5 bits
+    const uint32_t so = live_or_dead(live, soff_sc);
+    g.sc1 = ldhs(x.rsc, voff_sc1, so);
+    g.sc2 = ldhs(x.rsc, voff_sc2, so);
+    return total;
+}
+
+// Ten presence bytes of a wide lane: bytes 0..3 in d.x, 4..7 in d.y, 8 and 9 in d.z. The (mask, base)
+// and entry reads are those of decode_pair, for the pair plus the two bytes after it, whose window
+// starts popcount(d.x) + popcount(d.y) signs in. acc1 is the sum over the bytes before `sb` (the byte
+// where the lane's second group starts; 10 when it has one group), acc2 over the rest.
+__device__ __forceinline__ void decode_w80(const u32x4 &d, const SgBufW &g, const uint32_t (&xr)[1][20],
+                                           const char *lds, uint32_t laneoff, int sb, int &acc1, int &acc2) {
+    const uint32_t a0 = __builtin_amdgcn_alignbit(g.s.y, g.s.x, g.sh);
+    const uint32_t a1 = __builtin_amdgcn_alignbit(g.s.z, g.s.y, g.sh);
+    const uint32_t a2 = __builtin_amdgcn_alignbit(g.s.w, g.s.z, g.sh);
+    const uint32_t p0 = __builtin_popcount(d.x);
+    const uint32_t pp = __builtin_popcount(d.y) + p0;  // 0 .. 64
+    const uint64_t w01 = ((uint64_t)a1 << 32) | a0, w12 = ((uint64_t)a2 << 32) | a1;
+    const uint32_t b0 = (uint32_t)(w01 >> p0), b1 = (uint32_t)(w12 >> p0);
+    const uint32_t we = pp < 32u ? (uint32_t)(w01 >> pp) : (uint32_t)(w12 >> (pp - 32u));
+    uint2 info[10];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t src = i < 4 ? d.x : i < 8 ? d.y : d.z;
+        const uint32_t ia = __builtin_amdgcn_perm(src, laneoff, 0x0C0C0000u | ((4u + (i & 3)) << 8));
+        info[i] = *reinterpret_cast<const uint2 *>(lds + ia);
+    }
+    uint2 e[10];
+    uint32_t ca = 0, cb = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wa = i == 0 ? a0 : __builtin_amdgcn_alignbit(a1, a0, ca);
+        const uint32_t wb = i == 0 ? b0 : __builtin_amdgcn_alignbit(b1, b0, cb);
+        e[i] = *reinterpret_cast<const uint2 *>(lds + ((wa & info[i].x) | info[i].y));
+        e[4 + i] = *reinterpret_cast<const uint2 *>(lds + ((wb & info[4 + i].x) | info[4 + i].y));
+        if (i < 3) {
+            ca = __builtin_popcount(info[i].x) + ca;
+            cb = __builtin_popcount(info[4 + i].x) + cb;
+        }
+    }
+    e[8] = *reinterpret_cast<const uint2 *>(lds + ((we & info[8].x) | info[8].y));
+    const uint32_t w9 = we >> __builtin_popcount(info[8].x);
+    e[9] = *reinterpret_cast<const uint2 *>(lds + ((w9 & info[9].x) | info[9].y));
+    int acc = 0, snap = 0;
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        acc = dot4(e[i].x, xr[0][2 * i], acc);
+        acc = dot4(e[i].y, xr[0][2 * i + 1], acc);
+        if (i == 1 || i == 3 || i == 5 || i == 7) snap = sb == i + 1 ? acc : snap;
+    }
+    acc1 = sb < 10 ? snap : acc;
+    acc2 = acc - acc1;
+}
+
 // Pipeline over the steps of units [u0, u1) of one GEMV. In half-step h, step h - 4 is decoded, the
 // bitmap of step h is loaded, and the signs of step h - LAG (LAG = 2 for units of four or more steps,
 // else 1) are located and loaded: a bitmap has LAG half-steps to arrive, a sign window 4 - LAG (the
@@ -495,12 +584,18 @@ __device__ __forceinline__ void reduce_store_rows(const Ctx &x, const Red &r, co
 // their output rows by scalar selects.
 constexpr int kLiveSegRows = 64 * 64;
 
-template <bool XS>
+//
+// W80: rows of kW80Groups groups with wide lanes (above) take the same walk, whether or not they have
+// empty rows (without any, every row is taken).
+template <bool XS, bool W80>
 __device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, int row_end, const char *lds,
                                               double *tile) {
-    constexpr int M = 1, NB = 4, U = 4, LAG = 2, XW = 32;
+    constexpr int M = 1, NB = 4, U = 4, LAG = 2, XW = W80 ? 20 : 32;
     constexpr uint32_t XB = 4u * XW;
-    const int lane = threadIdx.x & 63;
+    // the empty asm keeps the lane constants below inside this walk: hoisted to the kernel's entry they
+    // would stay live across every other loop of the kernel and spill there
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     Ctx x;
     x.n = p.n;
     x.k = p.k;
@@ -519,16 +614,28 @@ __device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, i
     x.rxs = make_rsrc(p.xs, XS ? (uint32_t)p.ng * 4u : 0u);
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const uint32_t kb = (uint32_t)(p.k >> 3);
-    const bool act = lane < x.G;
-    const uint32_t voff_bm = act ? (uint32_t)lane * 16u : kOffOff;
-    const uint32_t voff_sc = act ? (uint32_t)lane * 2u : kOffOff;
-    const uint32_t voff_x = act ? (uint32_t)lane * XB : kOffOff;
-    const Red red = make_red(NB, 1, x.G, p.rmagic);
+    // group lanes: lane < G takes group `lane`; wide lanes: every lane takes ten presence bytes, in
+    // the 16-byte load at the 4-byte boundary below byte 10 l (groups g1 <= g2 of its first and last
+    // weight, second group from byte sb)
+    const bool act = W80 || lane < x.G;
+    const uint32_t voff_bm = !act ? kOffOff : W80 ? (uint32_t)(10 * lane - 2 * (lane & 1)) : (uint32_t)lane * 16u;
+    const uint32_t bsh = (uint32_t)(lane & 1) * 16u;
+    const int g1 = (80 * lane) >> 7, g2 = (80 * lane + 79) >> 7;
+    const int sb = g2 > g1 ? (128 * g2 - 80 * lane) >> 3 : 10;
+    const uint32_t voff_sc = !act ? kOffOff : W80 ? (uint32_t)g1 * 2u : (uint32_t)lane * 2u;
+    const uint32_t voff_sc2 = (uint32_t)g2 * 2u;
+    const uint32_t voff_x = !act ? kOffOff : W80 ? (uint32_t)lane * 80u : (uint32_t)lane * XB;
+    const Red red = make_red(NB, 1, W80 ? 64 : x.G, p.rmagic);
 
     uint32_t xr[M][XW];
-    float xsv[M];
+    float xsv[M], xsv2[M];
     load_x<M, XW>(x, voff_x, xr);
-    load_xs<M, XS>(x, voff_x, xsv);
+    if constexpr (W80) {
+        load_xs<M, XS>(x, (uint32_t)g1 * 128u, xsv);
+        load_xs<M, XS>(x, (uint32_t)g2 * 128u, xsv2);
+    } else {
+        load_xs<M, XS>(x, voff_x, xsv);
+    }
     uint32_t cur = row_index_entry(p, row_begin);
     // masks of the non-empty rows: lane w holds window w (rows row_begin + 64 w .. + 63)
     const int nw = (row_end - row_begin + 63) >> 6;
@@ -555,11 +662,12 @@ __device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, i
     }
     wait_x<M, XW>(xr);
     wait_xs<M, XS>(xsv);
+    if constexpr (W80) wait_xs<M, XS>(xsv2);
     // windows holding non-empty rows (bit w: window w), so that the next one is found without a loop
     const uint64_t nz = __builtin_amdgcn_ballot_w64(lane < nw && (mlo | mhi) != 0u);
 
     u32x4 bm[4] = {};
-    SgBuf g[4] = {};
+    typename std::conditional<W80, SgBufW, SgBuf>::type g[4] = {};
     int rq[4] = {-1, -1, -1, -1};      // row of the step in each pipeline slot (-1: none)
     int trow[NB] = {-1, -1, -1, -1};   // rows of the tile being filled
     int cw = 0;                        // window of the next row
@@ -573,10 +681,24 @@ __device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, i
             const int jb = j & 3;
             // ---- decode step h - 4 ----
             {
-                int acc[M];
-                decode<M, false, false>(bm[jb], g[jb], xr, lds, laneoff, acc);
                 trow[j] = rq[jb];
-                emit<M, false, NB, XS>(x, acc, (double)half_bits_to_float(g[jb].scale), xsv, tile, j, false, kOffOff, 0u);
+                if constexpr (W80) {
+                    int acc1, acc2;
+                    decode_w80(bm[jb], g[jb], xr, lds, laneoff, sb, acc1, acc2);
+                    // each part times its group scale (and activation group scale), exact in fp64
+                    double t1 = (double)acc1 * (double)half_bits_to_float(g[jb].sc1);
+                    double t2 = (double)acc2 * (double)half_bits_to_float(g[jb].sc2);
+                    if constexpr (XS) {
+                        t1 *= (double)xsv[0];
+                        t2 *= (double)xsv2[0];
+                    }
+                    tile[j * 64 + lane] = t1 + t2;
+                } else {
+                    int acc[M];
+                    decode<M, false, false>(bm[jb], g[jb], xr, lds, laneoff, acc);
+                    emit<M, false, NB, XS>(x, acc, (double)half_bits_to_float(g[jb].scale), xsv, tile, j, false, kOffOff,
+                                           0u);
+                }
                 if (j == NB - 1) reduce_store_rows(x, red, tile, trow[0], trow[1], trow[2], trow[3]);
             }
             TG_SCHED_FENCE();
@@ -601,9 +723,13 @@ __device__ __forceinline__ void run_loop_live(const Problem &p, int row_begin, i
             {
                 const int row = rq[(j + 4 - LAG) & 3];
                 const bool live = row >= 0;
-                const uint32_t total = stage_signs<false>(x, bm[(j + 4 - LAG) & 3], cur, live, voff_sc,
-                                                          (uint32_t)(live ? row : 0) * (uint32_t)x.ng * 2u,
-                                                          g[(j + 4 - LAG) & 3]);
+                const uint32_t soff = (uint32_t)(live ? row : 0) * (uint32_t)x.ng * 2u;
+                uint32_t total;
+                if constexpr (W80)
+                    total = stage_signs_w80(x, bm[(j + 4 - LAG) & 3], bsh, cur, live, voff_sc, voff_sc2, soff,
+                                            g[(j + 4 - LAG) & 3]);
+                else
+                    total = stage_signs<false>(x, bm[(j + 4 - LAG) & 3], cur, live, voff_sc, soff, g[(j + 4 - LAG) & 3]);
                 cur += live ? total : 0u;
             }
             TG_SCHED_FENCE();
@@ -616,11 +742,16 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
     if (p.nch == 1) {
         if constexpr (LIVE) {
             static_assert(M == 1 && !ACC && !F16 && !NIB, "the live-row walk: m = 1, fp32 outputs");
-            if (p.R == 1 && p.empty_rows > 0) {
+            const bool wide = p.ng == kW80Groups;
+            if (wide || (p.R == 1 && p.empty_rows > 0)) {
                 const int row_begin = (u0 - p.unit_begin) * p.rpu;
                 const int row_end = min(p.n, (u1 - p.unit_begin) * p.rpu);
-                for (int r = row_begin; r < row_end; r += kLiveSegRows)
-                    run_loop_live<XS>(p, r, min(row_end, r + kLiveSegRows), lds, tile);
+                for (int r = row_begin; r < row_end; r += kLiveSegRows) {
+                    if (wide)
+                        run_loop_live<XS, true>(p, r, min(row_end, r + kLiveSegRows), lds, tile);
+                    else
+                        run_loop_live<XS, false>(p, r, min(row_end, r + kLiveSegRows), lds, tile);
+                }
                 return;
             }
         }

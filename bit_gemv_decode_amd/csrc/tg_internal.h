@@ -91,6 +91,13 @@ constexpr int gemv_waves(int fmt, int m) {
 }
 constexpr int kMaxWavesPerCu = 16;
 
+// BITCOS rows of this many weights (40 groups) at m = 1 with fp32 outputs run on the row-walk build
+// of the kernel with a lane per 80 weights, so that a row fills the wave instead of 40 of its 64
+// lanes; a step of such a row costs about kWideLaneStepCost of a step of group lanes (ten presence
+// bytes per lane instead of sixteen) in the planner's balance.
+constexpr int64_t kWideLaneK = 5120;
+constexpr double kWideLaneStepCost = 0.8;
+
 // Rows per unit of chunked BITCOS GEMVs at m = 1 (their row sums live in registers, not the tile).
 constexpr int kChunkRows1 = 8;
 // ... or of kChunkRows1Fine rows when units of kChunkRows1 are fewer than a launch's waves (small
