@@ -57,7 +57,7 @@ class LayerSet:
     """Matrices of one decoder layer packed in `fmt`, stored `layers` times in device memory.
 
     shapes: (name, n, k) per matrix role; z: zero density; dead: row indices that are all zero in the
-    roles named in dead_roles (the same indices in each, as in the 70B-shaped stack)."""
+    roles named in dead_roles (the same indices in each, as in the 32B-shaped stack)."""
 
     def __init__(self, B, synth, torch, dev, fmt, layers=LAYERS, shapes=None, z=Z, dead=None,
                  dead_roles=("gate", "up")):
@@ -97,20 +97,20 @@ class LayerSet:
                       scales=None if self.fmt == B.FMT_T5B else [m["s"] for m in mats], ys=[m["y"] for m in mats])
 
 
-# The 70B-shaped dense decoder: 64 layers, hidden 5120, FFN 25600, GQA k/v 1024 rows, z = 0.47, and
+# The 32B-shaped dense decoder: 64 layers, hidden 5120, FFN 25600, GQA k/v 1024 rows, z = 0.47, and
 # 4.76 % of FFN neurons (1219 of 25600) all-zero at the same indices in gate and up ("Sub-Two-Bit
 # Ternary Weight Storage with Table-Free Arithmetic Decoding", abstract: dead FFN neurons).
-STACK70B = [("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
+STACK32B = [("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
             ("gate", 25600, 5120), ("up", 25600, 5120), ("down", 5120, 25600)]
-STACK70B_LAYERS = 64
-STACK70B_Z = 0.47
-STACK70B_DEAD = 1219
+STACK32B_LAYERS = 64
+STACK32B_Z = 0.47
+STACK32B_DEAD = 1219
 
 
-def stack70b(B, synth, torch, dev, layers=STACK70B_LAYERS):
-    """The 70B-shaped stack in BITCOS: one layer generated and stored `layers` times (6.08 GB for 64)."""
-    dead = synth.dead_rows(25600, STACK70B_DEAD, seed=0)
-    return LayerSet(B, synth, torch, dev, B.FMT_BITCOS, layers=layers, shapes=STACK70B, z=STACK70B_Z, dead=dead), dead
+def stack32b(B, synth, torch, dev, layers=STACK32B_LAYERS):
+    """The 32B-shaped stack in BITCOS: one layer generated and stored `layers` times (6.08 GB for 64)."""
+    dead = synth.dead_rows(25600, STACK32B_DEAD, seed=0)
+    return LayerSet(B, synth, torch, dev, B.FMT_BITCOS, layers=layers, shapes=STACK32B, z=STACK32B_Z, dead=dead), dead
 
 
 def time_launches(torch, fn, steps, warmup):
@@ -471,24 +471,24 @@ def suite_thin(torch, B, synth, dev, reps=96, ms=(1, 2, 4, 8, 16)):
     return out
 
 
-def suite_70b(torch, B, synth, dev, layers=STACK70B_LAYERS):
-    """Llama-70B-shaped layer stack at batch 1 (q, o 5120x5120; k, v 1024x5120; gate, up 25600x5120;
+def suite_32b(torch, B, synth, dev, layers=STACK32B_LAYERS):
+    """32B-shaped layer stack at batch 1 (q, o 5120x5120; k, v 1024x5120; gate, up 25600x5120;
     down 5120x25600), 1219 dead FFN rows per layer at the same indices in gate and up. One layer is
     generated and stored `layers` times (6.08 GB of BITCOS for 64), so every byte comes from HBM."""
-    st_set, dead = stack70b(B, synth, torch, dev, layers)
+    st_set, dead = stack32b(B, synth, torch, dev, layers)
     mats = st_set.flat()
     dws, xs, ss, ys = [m["w"] for m in mats], [m["x"] for m in mats], [m["s"] for m in mats], [m["y"] for m in mats]
     st = sustained(torch, B, dws, xs, ss, ys, launches=5)
     per_layer = [st_set.plan(B, row) for row in st_set.mats]
     settle(torch, lambda: [p.run() for p in per_layer])
     sl = time_launches(torch, lambda: [p.run() for p in per_layer], 3, 0)
-    out = {"layers": layers, "z": STACK70B_Z, "dead_rows_per_layer": int(dead.size), "bytes_per_pass": st["bytes_per_launch"],
+    out = {"layers": layers, "z": STACK32B_Z, "dead_rows_per_layer": int(dead.size), "bytes_per_pass": st["bytes_per_launch"],
            "grouped_one_launch": {"gbs": st["gbs"], "us_per_pass": round(st["ms_per_launch"] * 1e3, 1)},
            "per_layer_launch": {"gbs": round(st["bytes_per_launch"] * 3 / sl / 1e9, 1),
                                 "us_per_pass": round(sl / 3 * 1e6, 1)}}
     del st_set, per_layer
     torch.cuda.empty_cache()
-    log("[suite] 70B-shaped stack done")
+    log("[suite] 32B-shaped stack done")
     return out
 
 
@@ -538,7 +538,7 @@ def run_suite(path):
     res["zero_density_8192"] = {str(z): suite_single(torch, B, synth, dev, 8192, 8192, z, 96, F, label=f"8192 z={z}")
                                 for z in (0.30, 0.375, 0.42, 0.47, 0.515)}
     res["thin_batch"] = suite_thin(torch, B, synth, dev)
-    res["llama70b_stack"] = suite_70b(torch, B, synth, dev)
+    res["stack32b"] = suite_32b(torch, B, synth, dev)
     import oracle as O
     log("[suite] CPU oracle")
     res["cpu_oracle"] = suite_cpu(O, B, synth)

@@ -284,7 +284,7 @@ double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u, bool live) {
     // A launch that walks only the rows with non-zeros skips the empty ones, but an empty row's step
     // costs less than a full one on the plain walk too (every lane reads the same table entries) and
     // the walk adds a little per step: counting an empty row as half a step balanced best on MI355X
-    // (the 70B-shaped stack, against no credit and a full one, identical outputs).
+    // (the 32B-shaped stack, against no credit and a full one, identical outputs).
     if (live && p.nch == 1 && p.k == kWideLaneK)
         return (double)rows * kWideLaneStepCost * (1.0 - 0.5 * (double)p.empty_rows / (double)p.n);
     if (live && p.nch == 1 && p.R == 1 && p.empty_rows > 0)

@@ -1,4 +1,4 @@
-"""Full-size parity of the 70B-shaped stack: 64 layers of q, o 5120x5120; k, v 1024x5120; gate, up
+"""Full-size parity of the 32B-shaped stack: 64 layers of q, o 5120x5120; k, v 1024x5120; gate, up
 25600x5120 with 1219 all-zero rows at the same indices in both; down 5120x25600; z = 0.47 (6.08 GB of
 BITCOS). The stack is the one the measurement suite times: one layer generated and stored 64 times,
 so the oracle computes the 7 distinct GEMVs and every output of every copy is checked against them,
@@ -33,18 +33,18 @@ def stack():
 
     assert torch.cuda.is_available(), "GPU tests need a visible GPU"
     dev = torch.device("cuda:0")
-    _say("[gpu] 70B-shaped stack: packing and storing 64 copies")
-    ls, dead = bench.stack70b(B, synth, torch, dev)
+    _say("[gpu] 32B-shaped stack: packing and storing 64 copies")
+    ls, dead = bench.stack32b(B, synth, torch, dev)
     refs = []
-    for role, (name, n, k) in enumerate(bench.STACK70B):
-        w = synth.ternary(n, k, bench.STACK70B_Z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
+    for role, (name, n, k) in enumerate(bench.STACK32B):
+        w = synth.ternary(n, k, bench.STACK32B_Z, seed=0, tid=synth.tensor_id(0, role, synth.STREAM_W))
         if name in ("gate", "up"):
             w[dead] = 0
         h = ls.host[role]
         acc = O.gemv_acc(w, h["x"])
         refs.append(dict(name=name, s=h["s"], acc=acc, y=O.combine(acc, h["s"])))
         del w
-    _say("[gpu] 70B-shaped stack: oracle done")
+    _say("[gpu] 32B-shaped stack: oracle done")
     yield bench, ls, refs, dead
     del ls
     torch.cuda.empty_cache()
@@ -67,11 +67,11 @@ def _check_all(bench, ls, refs, dead, label):
                 assert np.all(y[:, dead] == 0), f"{label}: {r['name']} copy {layer}: dead rows not zero"
 
 
-def test_stack70b_one_launch_every_output(stack):
+def test_stack32b_one_launch_every_output(stack):
     bench, ls, refs, dead = stack
-    _say("[gpu] 70B-shaped stack, one grouped launch over 448 GEMVs")
+    _say("[gpu] 32B-shaped stack, one grouped launch over 448 GEMVs")
     plan = ls.plan(B)
-    assert plan.plan.count == 7 * bench.STACK70B_LAYERS and plan.plan.path == 0
+    assert plan.plan.count == 7 * bench.STACK32B_LAYERS and plan.plan.path == 0
     for rep in range(2):  # twice: the second launch must not depend on what the first left behind
         _reset(ls)
         plan.run()
@@ -79,9 +79,9 @@ def test_stack70b_one_launch_every_output(stack):
         _check_all(bench, ls, refs, dead, f"one launch, run {rep}")
 
 
-def test_stack70b_per_layer_launches_every_output(stack):
+def test_stack32b_per_layer_launches_every_output(stack):
     bench, ls, refs, dead = stack
-    _say("[gpu] 70B-shaped stack, 64 per-layer launches of 7 GEMVs")
+    _say("[gpu] 32B-shaped stack, 64 per-layer launches of 7 GEMVs")
     plans = [ls.plan(B, row) for row in ls.mats]
     _reset(ls)
     for p in plans:
@@ -90,9 +90,9 @@ def test_stack70b_per_layer_launches_every_output(stack):
     _check_all(bench, ls, refs, dead, "per-layer launches")
 
 
-def test_stack70b_single_calls(stack):
+def test_stack32b_single_calls(stack):
     bench, ls, refs, dead = stack
-    _say("[gpu] 70B-shaped stack, single calls of every matrix (layer copies 0 and 63)")
+    _say("[gpu] 32B-shaped stack, single calls of every matrix (layer copies 0 and 63)")
     for layer in (0, len(ls.mats) - 1):
         for role, m in enumerate(ls.mats[layer]):
             m["y"].fill_(float("nan"))
