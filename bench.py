@@ -492,6 +492,43 @@ def suite_32b(torch, B, synth, dev, layers=STACK32B_LAYERS):
     return out
 
 
+# One GPU's share of an 8-way tensor-parallel split, laid out as the column-split dataflow of the
+# untitled page on a NUMA-aware decode engine for ternary models (Sec. 5): q, k, v, gate and up split
+# by output rows, o and down by the reduction dimension (group-aligned), so each GPU runs these shapes
+# and the partial outputs of o and down meet in one all-reduce per matrix (not part of one GPU's step).
+TP = 8
+SHARD_32B = [("q", 5120 // TP, 5120), ("k", 1024 // TP, 5120), ("v", 1024 // TP, 5120), ("o", 5120, 5120 // TP),
+             ("gate", 25600 // TP, 5120), ("up", 25600 // TP, 5120), ("down", 5120, 25600 // TP)]
+SHARD_8B = [("q", 4096 // TP, 4096), ("k", 1024 // TP, 4096), ("v", 1024 // TP, 4096), ("o", 4096, 4096 // TP),
+            ("gate", 14336 // TP, 4096), ("up", 14336 // TP, 4096), ("down", 4096, 14336 // TP)]
+
+
+def suite_shards(torch, B, synth, dev):
+    """The first GPU's shard of an 8-way split of the 32B-shaped stack (64 layers; its gate and up rows
+    keep the dead rows that fall in the first 3200) and of the Llama3-8B layer set (32 layers, 189 MB:
+    the share fits the 256 MB cache), one grouped launch per pass and per-layer launches, settled."""
+    out = {"tp": TP}
+    dead = synth.dead_rows(25600, STACK32B_DEAD, seed=0)
+    for key, shapes, layers, z, dd in (("stack32b", SHARD_32B, STACK32B_LAYERS, STACK32B_Z, dead[dead < 25600 // TP]),
+                                       ("llama3_8b", SHARD_8B, LAYERS, Z, None)):
+        ls = LayerSet(B, synth, torch, dev, B.FMT_BITCOS, layers=layers, shapes=shapes, z=z, dead=dd)
+        mats = ls.flat()
+        st = sustained(torch, B, [m["w"] for m in mats], [m["x"] for m in mats], [m["s"] for m in mats],
+                       [m["y"] for m in mats], launches=10)
+        per_layer = [ls.plan(B, row) for row in ls.mats]
+        settle(torch, lambda: [p.run() for p in per_layer])
+        sl = time_launches(torch, lambda: [p.run() for p in per_layer], 3, 0)
+        out[key] = {"shapes": [list(x) for x in shapes], "layers": layers, "z": z,
+                    "dead_rows_per_layer": 0 if dd is None else int(dd.size), "bytes_per_pass": st["bytes_per_launch"],
+                    "grouped_one_launch": {"gbs": st["gbs"], "us_per_pass": round(st["ms_per_launch"] * 1e3, 1)},
+                    "per_layer_launch": {"gbs": round(st["bytes_per_launch"] * 3 / sl / 1e9, 1),
+                                         "us_per_layer": round(sl / 3 / layers * 1e6, 2)}}
+        del ls, per_layer, mats
+        torch.cuda.empty_cache()
+    log("[suite] tensor-parallel shards done")
+    return out
+
+
 def suite_cpu(O, B, synth):
     """The oracle from packed BITCOS bytes on one core and on all cores (2560x2560 and 4096x4096)."""
     cores = len(os.sched_getaffinity(0))
@@ -539,6 +576,7 @@ def run_suite(path):
                                 for z in (0.30, 0.375, 0.42, 0.47, 0.515)}
     res["thin_batch"] = suite_thin(torch, B, synth, dev)
     res["stack32b"] = suite_32b(torch, B, synth, dev)
+    res["tp8_shards"] = suite_shards(torch, B, synth, dev)
     import oracle as O
     log("[suite] CPU oracle")
     res["cpu_oracle"] = suite_cpu(O, B, synth)
