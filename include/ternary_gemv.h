@@ -258,10 +258,12 @@ typedef struct tg_plan {
                             activations on the vector / matrix-core kernel */
     int32_t decode;      /* TG_DECODE_BYTE, _NIBBLE or _ARITH (tg_plan_init*: _ARITH for 2-bit plans
                             that may take it, else _BYTE) */
-    int32_t live_rows;   /* 1: some GEMV reports rows without non-zeros (tg_desc.empty_rows), and the
-                            launch (BITCOS, m = 1, vector path, fp32 outputs, byte-keyed decode) walks
-                            only the other rows of the GEMVs with one row per step, storing 0 for
-                            the empty ones; 0 otherwise */
+    int32_t live_rows;   /* 1: the launch (BITCOS, m = 1, vector path, fp32 outputs, byte-keyed
+                            decode) takes the row-walk kernel, because some GEMV reports rows without
+                            non-zeros (tg_desc.empty_rows) or has rows of 5120 weights: it walks only
+                            the non-empty rows of the GEMVs with one row per step, storing 0 for the
+                            empty ones, and runs 5120-weight rows with a lane per 80 weights; 0
+                            otherwise */
     uint32_t table_gen;  /* 0 for a caller-owned table; tg_plan_init_noalloc: the generation of the
                             library's static table this plan was written into */
     void *table;         /* device table written by tg_plan_init */
