@@ -380,7 +380,7 @@ def graph_call_us(torch, calls, reps=5):
     return round(secs / (reps * len(calls)) * 1e6, 3)
 
 
-PATHS = {0: "vector", 1: "matrix-core", 2: "fp16 vector", 3: "fp16 matrix-core"}
+PATHS = {0: "vector", 1: "matrix-core", 2: "fp16 vector", 3: "fp16 matrix-core", 4: "vector, 12 waves"}
 
 
 def sustained(torch, B, dws, xs, ss, ys, launches=5, f16=False):

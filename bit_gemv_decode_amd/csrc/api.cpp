@@ -86,11 +86,21 @@ bool use_mfma_f16(int32_t m, int64_t k) {
 
 // Work geometry of one GEMV for a launch of m activation rows on the chosen path (chunk: the unit
 // size of chunked BITCOS rows at m = 1).
-void geometry(Problem &p, int fmt, int32_t m, bool mfma, int chunk = kChunkCoarse, bool f16 = false) {
+void geometry(Problem &p, int fmt, int32_t m, bool mfma, int chunk = kChunkCoarse, bool f16 = false,
+              bool short_units = false) {
     if (mfma)
         mfma_geometry(p);
     else
-        gemv_geometry(p, fmt, m, chunk, f16);
+        gemv_geometry(p, fmt, m, chunk, f16, short_units);
+}
+
+// A BITCOS launch of two activation rows on the vector path runs 12 waves per CU with two-step units
+// when none of its GEMVs has chunked rows (more than 64 groups per row): with two-step units chunked
+// rows would reload their activation slices twice as often (measured on MI355X: a Llama3-8B layer plan
+// at m = 2 23 % slower), while single-chunk shapes gained 3-14 % (4096x4096 +7-9 %, 1024x4096 +13 %,
+// 2560x2560 +14 %) over 8 waves with four-step units.
+bool short_units_ok(int fmt, int32_t m, int64_t max_groups_per_row) {
+    return fmt == TG_FMT_BITCOS && m == 2 && max_groups_per_row <= 64;
 }
 
 // Extra cost per row of a chunk pass of the vector path, in steps: the lanes reload their activation
@@ -176,7 +186,8 @@ int gemv_common(const tg_desc *desc, const void *W, const uint16_t *scales, cons
         g.count = 1;
         g.m = mt;
         g.one.unit_begin = 0;
-        geometry(g.one, desc->fmt, mt, mfma);
+        g.short_units = !mfma && short_units_ok(desc->fmt, mt, ng) ? 1 : 0;
+        geometry(g.one, desc->fmt, mt, mfma, kChunkCoarse, false, g.short_units != 0);
         const int chunk = chunk_units({g.one}, desc->fmt, mt, mfma, cus * gemv_waves(desc->fmt, mt));
         if (chunk != kChunkCoarse) geometry(g.one, desc->fmt, mt, mfma, chunk);
         g.rows_per_unit = g.one.rpu;
@@ -302,11 +313,12 @@ extern "C" size_t tg_plan_table_bytes(int32_t count) {
 namespace {
 
 // Plan paths (tg_plan::path).
-enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2, kPathF16Mfma = 3 };
+enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2, kPathF16Mfma = 3, kPathVectorShort = 4 };
 
 // Waves of a launch on `path`.
 int path_waves(int fmt, int m, int path) {
     if (path == kPathF16) return device_cus() * f16_waves(m);
+    if (path == kPathVectorShort) return device_cus() * kBitcosM2ShortWaves;
     return plan_waves(fmt, m, path == kPathMfma || path == kPathF16Mfma);
 }
 
@@ -356,11 +368,14 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     }
     const bool mfma = f16 ? m >= kF16MfmaMinM || (m == 2 && 2 * w_mfma > w_all)
                           : fmt == TG_FMT_BITCOS && m >= kMfmaMinM && (m >= kMfmaAlwaysM || 2 * w_mfma > w_all);
-    const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : kPathVector;
+    int64_t max_groups = 0;
+    for (int32_t i = 0; i < count; ++i) max_groups = std::max<int64_t>(max_groups, groups_per_row(fmt, descs[i].k));
+    const bool short_units = !f16 && !mfma && short_units_ok(fmt, m, max_groups);
+    const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : short_units ? kPathVectorShort : kPathVector;
     bool any_empty = false;
     for (int32_t i = 0; i < count; ++i) any_empty = any_empty || host[i].empty_rows > 0 || host[i].k == kWideLaneK;
     const bool live = fmt == TG_FMT_BITCOS && m == 1 && path == kPathVector && !acc_mode && any_empty;
-    for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, kChunkCoarse, f16);
+    for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, kChunkCoarse, f16, short_units);
     {
         int64_t ub = 0;
         for (int32_t i = 0; i < count; ++i) {
@@ -370,7 +385,7 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     }
     const int chunk = chunk_units(host, fmt, m, mfma, path_waves(fmt, m, path));
     if (chunk != kChunkCoarse)
-        for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, chunk, f16);
+        for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, chunk, f16, short_units);
     for (int32_t i = 0; i < count; ++i) rpu = std::max(rpu, (int)host[i].rpu);
     // Work order: GEMVs of one shape next to each other (by k, then n; the caller's order within a
     // shape). Each Problem carries its own pointers, so the order changes no result; on MI355X it
@@ -509,7 +524,8 @@ extern "C" int tg_plan_set_decode(tg_plan *plan, int32_t decode) {
 extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     if (!plan || plan->magic != TG_PLAN_MAGIC || !plan->table || plan->count < 1 || plan->m < 1 ||
         plan->m > plan_max_m(plan->fmt) || plan->acc_mode < kOutY || plan->acc_mode > kOutYxs ||
-        plan->path < kPathVector || plan->path > kPathF16Mfma ||
+        plan->path < kPathVector || plan->path > kPathVectorShort ||
+        (plan->path == kPathVectorShort && (plan->fmt != TG_FMT_BITCOS || plan->m != 2)) ||
         (plan->path == kPathMfma && (plan->fmt != TG_FMT_BITCOS || plan->m < kMfmaMinM)) ||
         (plan->path == kPathF16 && (plan->fmt != TG_FMT_BITCOS || plan->m > kF16MaxM || plan->acc_mode != kOutY)) ||
         (plan->path == kPathF16Mfma &&
@@ -530,6 +546,7 @@ extern "C" int ternary_gemv_plan(const tg_plan *plan, void *stream) {
     g.m = plan->m;
     g.rows_per_unit = plan->rows_per_unit;
     g.live = plan->live_rows;
+    g.short_units = plan->path == kPathVectorShort ? 1 : 0;
     if (plan->decode == TG_DECODE_NIBBLE)
         return launch_bitcos_nibble(g, plan->acc_mode, (hipStream_t)stream) == hipSuccess ? TG_OK : TG_EHIP;
     if (plan->decode == TG_DECODE_ARITH)

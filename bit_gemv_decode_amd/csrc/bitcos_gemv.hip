@@ -773,12 +773,17 @@ __device__ __forceinline__ void run_problem(const Problem &p, int u0, int u1, co
 // NIB: the nibble-keyed decode (its 32 KB table replaces the byte-keyed tables in LDS).
 // LIVE: single-chunk one-row-per-step GEMVs that report rows without non-zeros walk the other rows
 // only (m = 1, fp32 outputs); a separate build, so that the kernel without it keeps its registers.
-template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false, bool LIVE = false>
-__global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(
-    GroupArgs ga) {
+// SHORT: m = 2 launches without chunked rows: 12 waves per CU with two-step units (the tile of
+// four-step units for 12 waves would not fit the LDS beside the tables).
+template <int M, bool ACC, bool XS, bool F16 = false, bool NIB = false, bool LIVE = false, bool SHORT = false>
+__global__ __launch_bounds__((F16 ? 64 * f16_waves(M)
+                              : SHORT ? 64 * kBitcosM2ShortWaves
+                                      : Cfg<M, TG_FMT_BITCOS>::BLOCK)) void bitcos_gemv_kernel(GroupArgs ga) {
     using C = Cfg<M, TG_FMT_BITCOS>;
+    static_assert(!SHORT || (M == 2 && !F16 && !NIB && !LIVE), "the 12-wave build: m = 2, int8 activations");
     // the fp16 kernel uses four-step units at m = 1, 2 (two-step ones were 3-4 % slower at m = 2)
-    constexpr int NB = F16 ? 4 : C::NB, WAVES = F16 ? f16_waves(M) : C::WAVES, BLOCK = 64 * WAVES;
+    constexpr int NB = F16 ? 4 : SHORT ? 2 : C::NB;
+    constexpr int WAVES = F16 ? f16_waves(M) : SHORT ? kBitcosM2ShortWaves : C::WAVES, BLOCK = 64 * WAVES;
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ double s_tile[ACC ? 1 : WAVES * M * NB * 64];
     // The table fill goes out first (straight into LDS); the wave's unit range and its first GEMV
@@ -812,6 +817,23 @@ __global__ __launch_bounds__((F16 ? 64 * f16_waves(M) : Cfg<M, TG_FMT_BITCOS>::B
 template <int M>
 hipError_t launch_m(const GroupArgs &g, int out, hipStream_t s) {
     using C = Cfg<M, TG_FMT_BITCOS>;
+    if constexpr (M == 2) {
+        if (g.short_units) {
+            constexpr int W = kBitcosM2ShortWaves;
+            const int blocks = grid_blocks<W>(g);
+            if (blocks < 1) return hipErrorInvalidValue;
+            if (out == kOutAcc)
+                hipLaunchKernelGGL((bitcos_gemv_kernel<2, true, false, false, false, false, true>), dim3(blocks),
+                                   dim3(64 * W), 0, s, g);
+            else if (out == kOutYxs)
+                hipLaunchKernelGGL((bitcos_gemv_kernel<2, false, true, false, false, false, true>), dim3(blocks),
+                                   dim3(64 * W), 0, s, g);
+            else
+                hipLaunchKernelGGL((bitcos_gemv_kernel<2, false, false, false, false, false, true>), dim3(blocks),
+                                   dim3(64 * W), 0, s, g);
+            return hipGetLastError();
+        }
+    }
     const int blocks = grid_blocks<C::WAVES>(g);
     if (blocks < 1) return hipErrorInvalidValue;
     const bool live = M == 1 && g.live;
@@ -841,8 +863,9 @@ hipError_t launch_f16_m(const GroupArgs &g, hipStream_t s) {
 
 }  // namespace
 
-void gemv_geometry(Problem &p, int fmt, int m, int chunk, bool f16) {
+void gemv_geometry(Problem &p, int fmt, int m, int chunk, bool f16, bool short_units) {
     const int nb = f16 || fmt != TG_FMT_BITCOS ? 4
+                   : short_units ? 2
                    : m == 3 ? Cfg<3, TG_FMT_BITCOS>::NB : m == 2 ? Cfg<2, TG_FMT_BITCOS>::NB : Cfg<1, TG_FMT_BITCOS>::NB;
     p.ng = (int32_t)groups_per_row(fmt, p.k);
     p.nch = (p.ng + 63) / 64;

@@ -74,6 +74,7 @@ struct GroupArgs {
     int32_t waves;            // waves the launch must have (table mode: ranges has this many entries)
     int32_t live;             // BITCOS, m = 1, fp32 outputs: some GEMV reports rows without non-zeros,
                               // and the launch walks only the other rows of such GEMVs
+    int32_t short_units;      // BITCOS, m = 2, no chunked rows: the 12-wave build with two-step units
     Problem one;
 };
 
@@ -85,10 +86,13 @@ struct GroupArgs {
 // 2-bit at m = 3 +8 %, +8 %, +22 %, layer set +29 % (with 4-row units). 2-bit at m = 2 gained on
 // single matrices (+2 %, +3 %, +21 %) but lost 3.8 % on the layer set, and BITCOS at m = 2 fits 12
 // waves only with two-step units (its tables leave no room for a deeper tile), whose chunked rows
-// reload the activation slices twice as often: a layer-set plan at m = 2 ran 23 % slower. Both keep 8.
+// reload the activation slices twice as often: a layer-set plan at m = 2 ran 23 % slower. Both keep 8,
+// except that a BITCOS launch at m = 2 with no chunked rows takes the 12-wave build with two-step
+// units (kBitcosM2ShortWaves; single-chunk shapes +3-14 % in that measurement).
 constexpr int gemv_waves(int fmt, int m) {
     return (fmt == TG_FMT_5TRIT && m == 2) || (fmt == TG_FMT_2BIT && m == 3) ? 12 : m > 1 ? 8 : 16;
 }
+constexpr int kBitcosM2ShortWaves = 12;
 constexpr int kMaxWavesPerCu = 16;
 
 // BITCOS rows of this many weights (40 groups) at m = 1 with fp32 outputs run on the row-walk build
@@ -112,7 +116,8 @@ enum ChunkUnits { kChunkCoarse = 0, kChunkMid = 1, kChunkFine = 2 };
 // every format, except that chunked BITCOS rows at m = 1 go in units of kChunkRows1 (or, by `chunk`,
 // kChunkRows1Mid or kChunkRows1Fine) rows and BITCOS
 // units at m = 3 are two steps long; f16: the fp16-activation kernel, four-step units).
-void gemv_geometry(Problem &p, int fmt, int m, int chunk = kChunkCoarse, bool f16 = false);
+// short_units: two-step units of the 12-wave BITCOS build at m = 2 (single-chunk rows only).
+void gemv_geometry(Problem &p, int fmt, int m, int chunk = kChunkCoarse, bool f16 = false, bool short_units = false);
 
 // Thin-batch BITCOS path on matrix cores: m in [kMfmaMinM, TG_MAX_M] activation rows in one launch,
 // units of kMfmaTiles tiles of 16 rows each over the whole row, kMfmaWavesPerCu waves per CU. It is

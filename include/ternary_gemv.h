@@ -255,7 +255,9 @@ typedef struct tg_plan {
     int32_t acc_mode;    /* 0: fp32 y; 1: int32 accumulator outputs; 2: fp32 y with activation group scales */
     int32_t waves;       /* waves of the launch the table's work split was made for */
     int32_t path;        /* 0: vector kernels; 1: thin-batch matrix-core kernel (BITCOS); 2 / 3: fp16
-                            activations on the vector / matrix-core kernel */
+                            activations on the vector / matrix-core kernel; 4: the vector kernel at 12
+                            waves per CU with two-step units (BITCOS, m = 2, no GEMV with more than 64
+                            groups per row) */
     int32_t decode;      /* TG_DECODE_BYTE, _NIBBLE or _ARITH (tg_plan_init*: _ARITH for 2-bit plans
                             that may take it, else _BYTE) */
     int32_t live_rows;   /* 1: the launch (BITCOS, m = 1, vector path, fp32 outputs, byte-keyed

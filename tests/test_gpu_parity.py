@@ -255,9 +255,12 @@ def test_graph_replays_match_eager(fmt):
 
 
 # Plans of long rows only (k > 8192) at m = 2 take the thin-batch matrix-core path; mixed with shorter
-# rows that hold most of the weights they stay on the vector kernels. Both must match the oracle.
+# rows that hold most of the weights they stay on the vector kernels; without chunked rows they take
+# the 12-wave vector build with two-step units. All must match the oracle.
 @pytest.mark.parametrize("shapes,path", [([(33, 14336), (9, 25600), (20, 16384)], 1),
-                                          ([(33, 14336), (300, 4096)], 0)], ids=["long-rows", "mixed"])
+                                          ([(33, 14336), (300, 4096)], 0),
+                                          ([(300, 4096), (77, 2560), (130, 8192), (5, 128), (64, 1024)], 4)],
+                         ids=["long-rows", "mixed", "single-chunk"])
 def test_plan_m2_path_choice(shapes, path):
     dev = _dev()
     m = 2
