@@ -89,7 +89,7 @@ bool use_mfma_f16(int32_t m, int64_t k) {
 void geometry(Problem &p, int fmt, int32_t m, bool mfma, int chunk = kChunkCoarse, bool f16 = false,
               bool short_units = false) {
     if (mfma)
-        mfma_geometry(p);
+        mfma_geometry(p, mfma_tiles(m, f16));
     else
         gemv_geometry(p, fmt, m, chunk, f16, short_units);
 }
@@ -244,7 +244,7 @@ extern "C" int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16
         g.count = 1;
         g.m = m;
         g.one.unit_begin = 0;
-        mfma_geometry(g.one);
+        mfma_geometry(g.one, mfma_tiles(m, true));
         g.rows_per_unit = g.one.rpu;
         g.units = g.one.nunits;
         return launch_bitcos_mfma_f16(g, s) == hipSuccess ? TG_OK : TG_EHIP;
@@ -276,7 +276,10 @@ namespace {
 
 // Waves of a persistent launch on this device for m activation rows; a plan's per-wave ranges are
 // sized for it (the table has room for the largest count).
-int plan_waves(int fmt, int m, bool mfma) { return device_cus() * (mfma ? kMfmaWavesPerCu : gemv_waves(fmt, m)); }
+// Waves of a vector-path (f16 = false) or matrix-core launch of m activation rows.
+int plan_waves(int fmt, int m, bool mfma, bool f16 = false) {
+    return device_cus() * (mfma ? mfma_waves(mfma_tiles(m, f16)) : gemv_waves(fmt, m));
+}
 int plan_waves_max() { return device_cus() * std::max(kMaxWavesPerCu, kMfmaWavesPerCu); }
 
 // Largest m a plan of this format takes (one launch per plan).
@@ -319,7 +322,7 @@ enum PlanPath { kPathVector = 0, kPathMfma = 1, kPathF16 = 2, kPathF16Mfma = 3, 
 int path_waves(int fmt, int m, int path) {
     if (path == kPathF16) return device_cus() * f16_waves(m);
     if (path == kPathVectorShort) return device_cus() * kBitcosM2ShortWaves;
-    return plan_waves(fmt, m, path == kPathMfma || path == kPathF16Mfma);
+    return plan_waves(fmt, m, path == kPathMfma || path == kPathF16Mfma, path == kPathF16Mfma);
 }
 
 // Whether a plan may run the table-free decode (defined with tg_plan_set_decode below).

@@ -56,13 +56,12 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = kMfmaWavesPerCu;  // waves per block (one block per CU)
-constexpr int kBlock = 64 * kWaves;
-constexpr int kT = kMfmaTiles;           // 16-row tiles per unit
+// T: 16-row tiles per unit (kMfmaTiles, or kMfmaTilesWide from kMfmaWideM rows), mfma_waves(T) waves
+// per block (one block per CU).
 constexpr int kCG = 8;                   // groups per chunk
 constexpr int kSW = 36;                  // staged sign-stream dwords per row and chunk
 constexpr int kSWL = kSW / 4;            // ... loaded by each lane of the row
-constexpr uint32_t kStageDwords = kT * 16 * kSW;  // per wave
+constexpr uint32_t stage_dwords(int T) { return (uint32_t)T * 16u * kSW; }  // per wave
 constexpr uint32_t kXsDwords = kCG * 16;          // per wave: a chunk's activation scales, [group][m]
 
 // (a, b) -> (a', b'): lane rows 1 and 3 of a take rows 0 and 2 of b, and rows 0 and 2 of b take rows 1
@@ -162,18 +161,20 @@ struct CPos {
     int row, cu;
 };
 
+template <int T>
 __device__ __forceinline__ CPos next_chunk(CPos c, int nck) {
     const bool wrap = c.cu == nck - 1;
-    return CPos{wrap ? c.row + 16 * kT : c.row, wrap ? 0 : c.cu + 1};
+    return CPos{wrap ? c.row + 16 * T : c.row, wrap ? 0 : c.cu + 1};
 }
 
 // With XS each group's term is also multiplied by its activation group scales xs[m][g]: lane (lr, q)
 // loads xs[lr][g] of two groups of the next chunk with its other chunk loads, the values go to a per-wave
 // LDS buffer [group][m] when the chunk's data is rearranged, and each step's sign-window stage reads
 // the four scales of its rows m = 4q .. 4q + 3 with one 16-byte LDS read.
-template <bool ACC, bool XS, bool F16>
+template <int kT, bool ACC, bool XS, bool F16>
 __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int mrows, const char *lds,
                                          uint32_t *stg) {
+    constexpr uint32_t kStageDwords = stage_dwords(kT);
     static_assert(!(F16 && (ACC || XS)), "fp16 activations: fp32 outputs only");
     constexpr uint32_t EB = F16 ? 2u : 1u;  // activation element bytes
     constexpr int NP = F16 ? 4 : 2;         // activation operand parts (16 bytes each) per group
@@ -301,14 +302,14 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
         for (int t = 0; t < kT; ++t) cbn[t] = ro_nxt[t];  // waits for the row index of chunk 0
         load_signs(live0);
         load_chunk(c0, live0);
-        load_ro(next_chunk(c0, nck), NC > 1);
+        load_ro(next_chunk<kT>(c0, nck), NC > 1);
 #pragma unroll
         for (int t = 0; t < kT; ++t) ro_cur[t] = ro_nxt[t];
     }
 
     CPos prev = c0, cp = c0;  // chunks ci - 1 and ci (prev is dead at ci = 0)
     for (int ci = 0; ci <= NC; ++ci) {
-        const CPos nx = next_chunk(cp, nck), nn = next_chunk(nx, nck);
+        const CPos nx = next_chunk<kT>(cp, nck), nn = next_chunk<kT>(nx, nck);
         const bool live_prev = ci >= 1, live_cur = ci < NC;
 #pragma unroll
         for (int j = 0; j < kCG; ++j) {
@@ -463,9 +464,10 @@ __device__ __forceinline__ void run_mfma(const Problem &p, int u0, int u1, int m
     }
 }
 
-template <bool ACC, bool XS, bool F16 = false>
-__global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
-    constexpr uint32_t kWaveDwords = kStageDwords + (XS ? kXsDwords : 0u);
+template <int T, bool ACC, bool XS, bool F16 = false>
+__global__ __launch_bounds__(64 * mfma_waves(T)) void bitcos_mfma_kernel(GroupArgs ga) {
+    constexpr int kWaves = mfma_waves(T), kBlock = 64 * kWaves;
+    constexpr uint32_t kWaveDwords = stage_dwords(T) + (XS ? kXsDwords : 0u);
     __shared__ uint4 s_tab[kTabBytes / 16];
     __shared__ __attribute__((aligned(16))) uint32_t s_stage[kWaves * kWaveDwords];
     // The table fill goes out first (straight into LDS); the wave's unit range and its first GEMV
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
         const Problem p = first ? p0 : uniform_problem(launch_problem(ga, pi));
         first = false;
         const int u1 = min(u_end, p.unit_begin + p.nunits);
-        if (u < u1) run_mfma<ACC, XS, F16>(p, u, u1, ga.m, lds, stg);
+        if (u < u1) run_mfma<T, ACC, XS, F16>(p, u, u1, ga.m, lds, stg);
         u = max(u, u1);
         ++pi;
     }
@@ -495,37 +497,47 @@ __global__ __launch_bounds__(kBlock) void bitcos_mfma_kernel(GroupArgs ga) {
 
 }  // namespace
 
-void mfma_geometry(Problem &p) {
+void mfma_geometry(Problem &p, int tiles) {
     p.ng = p.k / 128;
     p.nch = 1;
     p.G = p.ng;
     p.R = 1;
     p.glast = p.ng;
-    p.nbu = kT;
-    p.rpu = 16 * kT;
+    p.nbu = tiles;
+    p.rpu = 16 * tiles;
     p.gmagic = 0;
     p.rmagic = 0;
     p.nunits = (p.n + p.rpu - 1) / p.rpu;
 }
 
-hipError_t launch_bitcos_mfma(const GroupArgs &g, int out, hipStream_t s) {
-    if (g.m < kMfmaMinM || g.m > TG_MAX_M) return hipErrorInvalidValue;
-    const int blocks = grid_blocks<kWaves>(g);
+namespace {
+template <int T>
+hipError_t launch_mfma_t(const GroupArgs &g, int out, hipStream_t s) {
+    constexpr int W = mfma_waves(T);
+    const int blocks = grid_blocks<W>(g);
     if (blocks < 1) return hipErrorInvalidValue;
     if (out == kOutAcc)
-        hipLaunchKernelGGL((bitcos_mfma_kernel<true, false>), dim3(blocks), dim3(kBlock), 0, s, g);
+        hipLaunchKernelGGL((bitcos_mfma_kernel<T, true, false>), dim3(blocks), dim3(64 * W), 0, s, g);
     else if (out == kOutYxs)
-        hipLaunchKernelGGL((bitcos_mfma_kernel<false, true>), dim3(blocks), dim3(kBlock), 0, s, g);
+        hipLaunchKernelGGL((bitcos_mfma_kernel<T, false, true>), dim3(blocks), dim3(64 * W), 0, s, g);
     else
-        hipLaunchKernelGGL((bitcos_mfma_kernel<false, false>), dim3(blocks), dim3(kBlock), 0, s, g);
+        hipLaunchKernelGGL((bitcos_mfma_kernel<T, false, false>), dim3(blocks), dim3(64 * W), 0, s, g);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_bitcos_mfma(const GroupArgs &g, int out, hipStream_t s) {
+    if (g.m < kMfmaMinM || g.m > TG_MAX_M) return hipErrorInvalidValue;
+    return mfma_tiles(g.m, false) == kMfmaTilesWide ? launch_mfma_t<kMfmaTilesWide>(g, out, s)
+                                                     : launch_mfma_t<kMfmaTiles>(g, out, s);
 }
 
 hipError_t launch_bitcos_mfma_f16(const GroupArgs &g, hipStream_t s) {
     if (g.m < 1 || g.m > TG_MAX_M) return hipErrorInvalidValue;
-    const int blocks = grid_blocks<kWaves>(g);
+    constexpr int W = mfma_waves(kMfmaTiles);
+    const int blocks = grid_blocks<W>(g);
     if (blocks < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bitcos_mfma_kernel<false, false, true>), dim3(blocks), dim3(kBlock), 0, s, g);
+    hipLaunchKernelGGL((bitcos_mfma_kernel<kMfmaTiles, false, false, true>), dim3(blocks), dim3(64 * W), 0, s, g);
     return hipGetLastError();
 }
 

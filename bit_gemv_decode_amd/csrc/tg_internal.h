@@ -129,7 +129,17 @@ constexpr int kMfmaAlwaysM = 3;  // from this m every BITCOS GEMV takes the matr
 constexpr int kMfmaLongRowGroups = 64;  // at m = 2, rows of more groups than this take it
 constexpr int kMfmaTiles = 2;
 constexpr int kMfmaWavesPerCu = 8;
-void mfma_geometry(Problem &p);
+// From kMfmaWideM activation rows (int8 activations) the units take kMfmaTilesWide tiles at
+// kMfmaWavesWide waves per CU (the LDS holds no more stages): each activation operand load then
+// serves 48 weight rows instead of 32. Measured on MI355X (gate 14336x4096 and down 4096x14336, 96
+// copies, alternating builds, identical outputs): at m = 16 gate 2228 -> 2385 GB/s and down 2177 ->
+// 2260; at m = 14 within 1 %; at m = 10, 12 3-10 % slower, at m = 4, 8 13-17 % slower.
+constexpr int kMfmaWideM = 16;
+constexpr int kMfmaTilesWide = 3;
+constexpr int kMfmaWavesWide = 6;
+constexpr int mfma_tiles(int m, bool f16) { return !f16 && m >= kMfmaWideM ? kMfmaTilesWide : kMfmaTiles; }
+constexpr int mfma_waves(int tiles) { return tiles == kMfmaTilesWide ? kMfmaWavesWide : kMfmaWavesPerCu; }
+void mfma_geometry(Problem &p, int tiles);
 hipError_t launch_bitcos_mfma(const GroupArgs &g, int out, hipStream_t s);
 
 // Host-side checks of a descriptor; `limit` is the buffer length when known (0 = trust bytes_total).
