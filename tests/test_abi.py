@@ -367,9 +367,15 @@ def test_plan_struct_layout_and_decode_selection_errors():
         assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
     # a forged plan claiming the live-row walk where no kernel has it is refused before launching
     for bad in (dict(live_rows=2), dict(live_rows=1, fmt=B.FMT_5TRIT), dict(live_rows=1, m=2),
-                dict(live_rows=1, acc_mode=1), dict(live_rows=1, path=1)):
+                dict(live_rows=1, acc_mode=1), dict(live_rows=1, path=1), dict(live_rows=1, m=2, path=4)):
         p = binding.TgPlan(**{**ok, **bad})
         assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+    # path 4 (the 12-wave build with two-step units) exists for BITCOS at m = 2 only; no path 5
+    for bad in (dict(path=4), dict(path=4, m=3), dict(path=4, m=2, fmt=B.FMT_5TRIT), dict(path=4, m=2, fmt=B.FMT_2BIT),
+                dict(path=5, m=2)):
+        p = binding.TgPlan(**{**ok, **bad})
+        assert L.ternary_gemv_plan(ctypes.byref(p), None) == -1
+        assert L.tg_plan_set_decode(ctypes.byref(p), 1) == -1
 
 
 def test_empty_rows_field_checked():
