@@ -7,13 +7,16 @@
 // negative) pair into w = p - 2n (Eq. 2), contracts against int8 activations in int32 and applies
 // the group scale once per 128-element group.
 //
-// Mapping on CDNA4 (wave64, one persistent block per CU: 1024 threads at m = 1, 512 at m = 2, 3):
+// Mapping on CDNA4 (wave64, one persistent block per CU: 1024 threads at m = 1, 512 at m = 2, 3; 768 at
+// m = 2 for launches without chunked rows, with two-step units):
 //   * a lane owns one 128-weight group of one row per step: its four bitmap dwords arrive with one
 //     16-byte load, its scale with one 2-byte load. A row of k weights takes ng = k/128 lanes; when
 //     ng <= 64 a step holds R = 64/ng consecutive rows (at most 64/NB, so that a unit's NB steps hold
 //     no more rows than a wave has lanes: k = 128 and 256 leave lanes idle), otherwise a row is split
 //     into chunks of 64 groups, one chunk per step. A lane's activation bytes (its group's 128 x values) stay in
-//     registers for every row it sees, so x is read once per GEMV (or once per chunk pass).
+//     registers for every row it sees, so x is read once per GEMV (or once per chunk pass). Rows of
+//     40 groups (k = 5120) at m = 1 with fp32 outputs take wide lanes instead: 80 weights per lane, so
+//     one row fills the wave (see kW80Groups).
 //   * sign positions: rows of a step are consecutive in the sign stream, so a lane's first sign sits
 //     at the step's cursor (from the row index, or carried from the row's previous chunk) plus the
 //     exclusive prefix sum of the popcounts of the lanes before it (DPP scan). For each pair of bitmap
