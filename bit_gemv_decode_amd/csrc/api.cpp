@@ -375,9 +375,10 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     for (int32_t i = 0; i < count; ++i) max_groups = std::max<int64_t>(max_groups, groups_per_row(fmt, descs[i].k));
     const bool short_units = !f16 && !mfma && short_units_ok(fmt, m, max_groups);
     const int path = f16 ? (mfma ? kPathF16Mfma : kPathF16) : mfma ? kPathMfma : short_units ? kPathVectorShort : kPathVector;
-    bool any_empty = false;
-    for (int32_t i = 0; i < count; ++i) any_empty = any_empty || host[i].empty_rows > 0 || host[i].k == kWideLaneK;
-    const bool live = fmt == TG_FMT_BITCOS && m == 1 && path == kPathVector && !acc_mode && any_empty;
+    // the row-walk build: some GEMV has empty rows to skip or rows of kWideLaneK weights (wide lanes)
+    bool walk = false;
+    for (int32_t i = 0; i < count; ++i) walk = walk || host[i].empty_rows > 0 || host[i].k == kWideLaneK;
+    const bool live = fmt == TG_FMT_BITCOS && m == 1 && path == kPathVector && !acc_mode && walk;
     for (int32_t i = 0; i < count; ++i) geometry(host[i], fmt, m, mfma, kChunkCoarse, f16, short_units);
     {
         int64_t ub = 0;
