@@ -228,7 +228,8 @@ int ternary_gemv_f16(const tg_desc *desc, const void *W, const uint16_t *scales,
  * tg_plan_table_bytes(count): bytes of device memory the table of `count` GEMVs needs.
  * tg_plan_init: checks every descriptor and pointer (the same rules as ternary_gemv; all formats
  *   equal), chooses one path for the launch (BITCOS: the thin-batch kernel from m = 3, and at m = 2
- *   when GEMVs with k > 8192 hold most of the weights; else the vector kernels), then writes the
+ *   when GEMVs with k > 8192 hold most of the weights; at m = 2 with no such GEMV the vector kernel's
+ *   12-wave build; else the vector kernels; plan->path records it), then writes the
  *   table into `table` (caller-owned DEVICE memory of at least tg_plan_table_bytes(count) bytes,
  *   16-byte aligned) with a synchronous host-to-device copy, and
  *   fills the host struct *plan. descs, W, scales, x, y, acc are host arrays of `count` entries;
