@@ -83,6 +83,26 @@ def drive():
     print(json.dumps({"step_bytes": ls.step_bytes}), flush=True)
 
 
+def drive32b(warmup=3, launches=10):
+    """The 32B-shaped stack (64 layers, hidden 5120, 6.0 GB of BITCOS) as one grouped launch: `warmup`
+    launches, then `launches` more, for rocprofv3 kernel traces and counters of the row-walk build
+    (wide lanes for its 5120-weight rows, the dead-row skip)."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import bench
+    import bit_gemv_decode_amd as B
+    from bit_gemv_decode_amd import synth
+
+    dev = torch.device("cuda:0")
+    st, _ = bench.stack32b(B, synth, torch, dev)
+    plan = st.plan(B)
+    for _ in range(warmup + launches):
+        plan.run()
+    torch.cuda.synchronize()
+    print(json.dumps({"step_bytes": st.step_bytes, "live_rows": plan.plan.live_rows}), flush=True)
+
+
 def _curve(torch, bd, fn, launches, spin=100):
     """Durations (µs) of `launches` back-to-back calls of fn() from an idle GPU, and the shader clock
     (MHz) sampled before each of them and after the last."""
@@ -185,8 +205,9 @@ def stats(stats_csv, out_md, command, trace_csv=None, skip=0, count=0):
         f.write("\n".join(lines) + "\n")
 
 
-def counters(out_md, command, csvs):
-    """Summary of the last BITCOS dispatch of `drive` (the timed step) over one or more --pmc runs."""
+def counters(out_md, command, csvs, workload="layerset"):
+    """Summary of the last BITCOS dispatch of `drive` (the timed step; workload "layerset") or of
+    `drive32b` (workload "stack32b") over one or more --pmc runs."""
     sys.path.insert(0, ROOT)
     import bench
 
@@ -200,11 +221,16 @@ def counters(out_md, command, csvs):
         for r in rows:
             if int(r["Dispatch_Id"]) == last:
                 vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    weights = bench.LAYERS * sum(n * k for _, n, k in bench.LAYER)
+    if workload == "stack32b":
+        weights = bench.STACK32B_LAYERS * sum(n * k for _, n, k in bench.STACK32B)
+        what = f"`drive32b` (the 32B-shaped stack x{bench.STACK32B_LAYERS}"
+    else:
+        weights = bench.LAYERS * sum(n * k for _, n, k in bench.LAYER)
+        what = f"`drive` (the Llama3-8B-shaped layer set x{bench.LAYERS}"
     wave_steps = weights / 8192.0  # 64 lanes x 128 weights
     lines = [f"# SQ counters of the grouped BITCOS step: `{os.path.basename(out_md)}`", "",
              "Commands (from the repository root):", "", f"    {command}", "",
-             f"Timed dispatch of `drive` (the Llama3-8B-shaped layer set x{bench.LAYERS}, {weights / 1e9:.2f} G weights, "
+             f"Timed dispatch of {what}, {weights / 1e9:.2f} G weights, "
              f"{wave_steps:.0f} wave-steps of 8192 weights).", "", "| Counter | Total | Per wave-step |", "|---|---|---|"]
     for name in sorted(vals):
         lines.append(f"| `{name}` | {vals[name]:.4g} | {vals[name] / wave_steps:.2f} |")
@@ -274,6 +300,10 @@ if __name__ == "__main__":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     elif cmd == "counters":
         counters(sys.argv[2], sys.argv[3], sys.argv[4:])
+    elif cmd == "counters32b":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4:], workload="stack32b")
+    elif cmd == "drive32b":
+        drive32b()
     elif cmd == "transient":
         transient(sys.argv[2], *(int(a) for a in sys.argv[3:4]))
     else:
