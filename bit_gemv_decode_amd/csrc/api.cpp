@@ -291,6 +291,9 @@ size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 
 // vector path costs about the same (one 128-weight group per lane, however many lanes are busy), so a
 // unit costs its step count, plus the activation reloads of chunked rows; a unit of the matrix-core
 // path costs its chunk count (all units of one plan take the same path).
+// Steps per wave from which a launch takes the strong age-class shares (below).
+constexpr double kLongRangeSteps = 64.0;
+
 double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u, bool live) {
     const int64_t row0 = (u - p.unit_begin) * (int64_t)p.rpu;
     const int64_t rows = std::min<int64_t>(p.rpu, (int64_t)p.n - row0);
@@ -413,14 +416,20 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     // the SIMDs: with 16 waves per CU, wave w of a block runs on SIMD w % 4, and a SIMD issues for its
     // oldest ready wave first, so of equal shares the block's waves 0-3 finish first and 12-15 last
     // (per-wave timestamps of the Llama3-8B layer-set step: 225, 252, 289 and 332 us, every CU alike).
-    // Shares 1.12 : 1.04 : 0.96 : 0.88 by wave w / 4 narrowed that and ran the step 3 % faster after
-    // the clock has settled (no change in the first milliseconds of load, where the clock decides).
+    // Shares by wave w / 4 narrow that. Launches of many steps per wave take 1.30 : 1.10 : 0.90 : 0.70
+    // (measured on MI355X against 1.12 : 1.04 : 0.96 : 0.88, alternating builds, three runs: the
+    // Llama3-8B step +2.1-2.3 % in the first launches from idle and +1.9-2.8 % settled; 1.40 : ... : 0.60
+    // no better), launches of few steps per wave the milder ones (one-layer plans, ~7 steps per wave,
+    // ran 1.8-2.6 % slower with the strong shares), and so do launches of the row-walk build (the
+    // 32B-shaped stack: +1.6 % in the first launches but -0.4 to -1.4 % settled with the strong ones).
     const int nw = path_waves(fmt, m, path);
     std::vector<WaveRange> ranges((size_t)nw);
     {
         const int wpb = path == kPathF16 ? f16_waves(m) : path == kPathVector ? gemv_waves(fmt, m) : 0;
         const bool by_age = wpb == 16 && nw % 16 == 0;
-        const double age_share[4] = {1.12, 1.04, 0.96, 0.88};
+        const bool long_ranges = !live && total_cost >= kLongRangeSteps * (double)nw;
+        const double age_share_long[4] = {1.30, 1.10, 0.90, 0.70}, age_share_short[4] = {1.12, 1.04, 0.96, 0.88};
+        const double *age_share = long_ranges ? age_share_long : age_share_short;
         std::vector<double> cum((size_t)nw + 1, 0.0);
         for (int w = 0; w < nw; ++w) cum[w + 1] = cum[w] + (by_age ? age_share[(w % 16) / 4] : 1.0);
         int32_t pi = 0;
