@@ -421,13 +421,16 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     // Llama3-8B step +2.1-2.3 % in the first launches from idle and +1.9-2.8 % settled; 1.40 : ... : 0.60
     // no better), launches of few steps per wave the milder ones (one-layer plans, ~7 steps per wave,
     // ran 1.8-2.6 % slower with the strong shares), and so do launches of the row-walk build (the
-    // 32B-shaped stack: +1.6 % in the first launches but -0.4 to -1.4 % settled with the strong ones).
+    // 32B-shaped stack: +1.6 % in the first launches but -0.4 to -1.4 % settled with the strong ones)
+    // and 2-bit plans (the layer set with the LDS table: -6.1 % in the first launches and -4.0 %
+    // settled with the strong shares; table-free +0.3 / +0.4 %; five-trit gains +0.7 / +2.7 %, t5b
+    // +3.9 / +2.9 %).
     const int nw = path_waves(fmt, m, path);
     std::vector<WaveRange> ranges((size_t)nw);
     {
         const int wpb = path == kPathF16 ? f16_waves(m) : path == kPathVector ? gemv_waves(fmt, m) : 0;
         const bool by_age = wpb == 16 && nw % 16 == 0;
-        const bool long_ranges = !live && total_cost >= kLongRangeSteps * (double)nw;
+        const bool long_ranges = !live && fmt != TG_FMT_2BIT && total_cost >= kLongRangeSteps * (double)nw;
         const double age_share_long[4] = {1.30, 1.10, 0.90, 0.70}, age_share_short[4] = {1.12, 1.04, 0.96, 0.88};
         const double *age_share = long_ranges ? age_share_long : age_share_short;
         std::vector<double> cum((size_t)nw + 1, 0.0);
