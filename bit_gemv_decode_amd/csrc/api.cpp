@@ -424,17 +424,29 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     // 32B-shaped stack: +1.6 % in the first launches but -0.4 to -1.4 % settled with the strong ones)
     // and 2-bit plans (the layer set with the LDS table: -6.1 % in the first launches and -4.0 %
     // settled with the strong shares; table-free +0.3 / +0.4 %; five-trit gains +0.7 / +2.7 %, t5b
-    // +3.9 / +2.9 %).
+    // +3.9 / +2.9 %). The same order holds with 12 waves per CU (three per SIMD: m = 2 with two-step
+    // units) and 8 (two per SIMD: the thin-batch matrix-core launches of two-tile units); for their
+    // long launches, measured on 96-copy plans of 14336 x 4096 and 4096 x 14336 (settled, alternating
+    // builds, two runs): 12 waves with 1.30 : 1.00 : 0.70 +3.6-3.7 % against equal shares (1.20 : 1.00
+    // : 0.80 +1.2-3.6 %); 8 waves with 1.15 : 0.85 +0.3-2.7 % for 4096 x 14336 at m = 2, 4, 8 and -1.0
+    // to +0.7 % for 14336 x 4096 (1.20 : 0.80: -3 to -6 %). Their short launches keep milder or equal
+    // shares. Six-wave launches (three-tile units) leave two SIMDs with one wave: equal shares.
     const int nw = path_waves(fmt, m, path);
     std::vector<WaveRange> ranges((size_t)nw);
     {
-        const int wpb = path == kPathF16 ? f16_waves(m) : path == kPathVector ? gemv_waves(fmt, m) : 0;
-        const bool by_age = wpb == 16 && nw % 16 == 0;
-        const bool long_ranges = !live && fmt != TG_FMT_2BIT && total_cost >= kLongRangeSteps * (double)nw;
-        const double age_share_long[4] = {1.30, 1.10, 0.90, 0.70}, age_share_short[4] = {1.12, 1.04, 0.96, 0.88};
-        const double *age_share = long_ranges ? age_share_long : age_share_short;
+        const int wpb = path == kPathF16 ? f16_waves(m) : path == kPathVector ? gemv_waves(fmt, m)
+                        : path == kPathVectorShort ? kBitcosM2ShortWaves
+                        : path == kPathMfma ? mfma_waves(mfma_tiles(m, false)) : 0;
+        const bool by_age = (wpb == 16 || wpb == 12 || wpb == 8) && nw % wpb == 0;
+        const bool long_ranges = !live && total_cost >= kLongRangeSteps * (double)nw;
+        const double age16_long[4] = {1.30, 1.10, 0.90, 0.70}, age16_short[4] = {1.12, 1.04, 0.96, 0.88};
+        const double age12_long[3] = {1.30, 1.00, 0.70}, age12_short[3] = {1.10, 1.00, 0.90};
+        const double age8_long[2] = {1.15, 0.85}, age8_short[2] = {1.0, 1.0};
+        const double *age_share = wpb == 16 ? (long_ranges && fmt != TG_FMT_2BIT ? age16_long : age16_short)
+                                  : wpb == 12 ? (long_ranges ? age12_long : age12_short)
+                                  : (long_ranges ? age8_long : age8_short);
         std::vector<double> cum((size_t)nw + 1, 0.0);
-        for (int w = 0; w < nw; ++w) cum[w + 1] = cum[w] + (by_age ? age_share[(w % 16) / 4] : 1.0);
+        for (int w = 0; w < nw; ++w) cum[w + 1] = cum[w] + (by_age ? age_share[(w % wpb) / 4] : 1.0);
         int32_t pi = 0;
         int64_t u = 0;
         double done = 0;
