@@ -294,6 +294,12 @@ size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 
 // Steps per wave from which a launch takes the strong age-class shares (below).
 constexpr double kLongRangeSteps = 64.0;
 
+// Whether a launch's wave ranges are long (at least kLongRangeSteps of cost per wave) and not a
+// row-walk build: such launches take the stronger issue-order shares.
+bool long_ranges_of(double total_cost, int nw, bool live) {
+    return !live && total_cost >= kLongRangeSteps * (double)nw;
+}
+
 double unit_cost(const Problem &p, int fmt, bool mfma, int64_t u, bool live) {
     const int64_t row0 = (u - p.unit_begin) * (int64_t)p.rpu;
     const int64_t rows = std::min<int64_t>(p.rpu, (int64_t)p.n - row0);
@@ -430,7 +436,11 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     // builds, two runs): 12 waves with 1.30 : 1.00 : 0.70 +3.6-3.7 % against equal shares (1.20 : 1.00
     // : 0.80 +1.2-3.6 %); 8 waves with 1.15 : 0.85 +0.3-2.7 % for 4096 x 14336 at m = 2, 4, 8 and -1.0
     // to +0.7 % for 14336 x 4096 (1.20 : 0.80: -3 to -6 %). Their short launches keep milder or equal
-    // shares. Six-wave launches (three-tile units) leave two SIMDs with one wave: equal shares.
+    // shares. Six-wave launches (three-tile units, m >= 16) leave SIMDs 2 and 3 with one wave each,
+    // which runs ahead of the two pairs: their long launches take per-wave shares 1.05, 1.05, 1.15,
+    // 1.15, 0.80, 0.80 (4096 x 14336 and 14336 x 4096 at m = 16: +5.1 and +5.9 % against equal
+    // shares; 1.05 / 1.20 / 0.75 +4.8 and +3.4 %, 1.10 / 1.20 / 0.70 +4.1 and +3.3 %, 1.10 / 1.40 /
+    // 0.50 -4 and -6 %).
     const int nw = path_waves(fmt, m, path);
     std::vector<WaveRange> ranges((size_t)nw);
     {
@@ -438,7 +448,10 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
                         : path == kPathVectorShort ? kBitcosM2ShortWaves
                         : path == kPathMfma ? mfma_waves(mfma_tiles(m, false)) : 0;
         const bool by_age = (wpb == 16 || wpb == 12 || wpb == 8) && nw % wpb == 0;
-        const bool long_ranges = !live && total_cost >= kLongRangeSteps * (double)nw;
+        // six waves: SIMDs 0 and 1 hold waves 0, 4 and 1, 5; SIMDs 2 and 3 hold waves 2 and 3 alone
+        const bool by_wave6 = path == kPathMfma && wpb == 6 && nw % 6 == 0 && long_ranges_of(total_cost, nw, live);
+        const double wave6_share[6] = {1.05, 1.05, 1.15, 1.15, 0.80, 0.80};
+        const bool long_ranges = long_ranges_of(total_cost, nw, live);
         const double age16_long[4] = {1.30, 1.10, 0.90, 0.70}, age16_short[4] = {1.12, 1.04, 0.96, 0.88};
         const double age12_long[3] = {1.30, 1.00, 0.70}, age12_short[3] = {1.10, 1.00, 0.90};
         const double age8_long[2] = {1.15, 0.85}, age8_short[2] = {1.0, 1.0};
@@ -446,7 +459,8 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
                                   : wpb == 12 ? (long_ranges ? age12_long : age12_short)
                                   : (long_ranges ? age8_long : age8_short);
         std::vector<double> cum((size_t)nw + 1, 0.0);
-        for (int w = 0; w < nw; ++w) cum[w + 1] = cum[w] + (by_age ? age_share[(w % wpb) / 4] : 1.0);
+        for (int w = 0; w < nw; ++w)
+            cum[w + 1] = cum[w] + (by_age ? age_share[(w % wpb) / 4] : by_wave6 ? wave6_share[w % 6] : 1.0);
         int32_t pi = 0;
         int64_t u = 0;
         double done = 0;
