@@ -435,8 +435,14 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     // long launches, measured on 96-copy plans of 14336 x 4096 and 4096 x 14336 (settled, alternating
     // builds, two runs): 12 waves with 1.30 : 1.00 : 0.70 +3.6-3.7 % against equal shares (1.20 : 1.00
     // : 0.80 +1.2-3.6 %); 8 waves with 1.15 : 0.85 +0.3-2.7 % for 4096 x 14336 at m = 2, 4, 8 and -1.0
-    // to +0.7 % for 14336 x 4096 (1.20 : 0.80: -3 to -6 %). Their short launches keep milder or equal
-    // shares. Six-wave launches (three-tile units, m >= 16) leave SIMDs 2 and 3 with one wave each,
+    // to +0.7 % for 14336 x 4096 (1.20 : 0.80: -3 to -6 %); the fp16 matrix-core launches (8 waves)
+    // with 1.15 : 0.85 +3.2-3.5 % at m = 4, +1.4-2.0 % at m = 8, -0.5-0 % at m = 16 (both shapes).
+    // The other 12- and 8-wave launches against equal shares (same plans): fp16 activations at m = 1
+    // (12 waves) +4.9 / +2.6 % (14336 x 4096 / 4096 x 14336) and m = 2 +4.9 / +5.1 %, five-trit
+    // m = 2 (12) +7.0 / +3.0 % and m = 3 (8) +5.4 / +2.4 %; but 2-bit m = 2 (8) -8.4 / +2.4 % and
+    // m = 3 (12) -14.3 / +1.8 %, so 2-bit plans keep equal shares there.
+    // Their short launches keep milder or equal shares. Six-wave launches (three-tile units,
+    // m >= 16) leave SIMDs 2 and 3 with one wave each,
     // which runs ahead of the two pairs: their long launches take per-wave shares 1.05, 1.05, 1.15,
     // 1.15, 0.80, 0.80 (4096 x 14336 and 14336 x 4096 at m = 16: +5.1 and +5.9 % against equal
     // shares; 1.05 / 1.20 / 0.75 +4.8 and +3.4 %, 1.10 / 1.20 / 0.70 +4.1 and +3.3 %, 1.10 / 1.40 /
@@ -446,8 +452,9 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
     {
         const int wpb = path == kPathF16 ? f16_waves(m) : path == kPathVector ? gemv_waves(fmt, m)
                         : path == kPathVectorShort ? kBitcosM2ShortWaves
-                        : path == kPathMfma ? mfma_waves(mfma_tiles(m, false)) : 0;
-        const bool by_age = (wpb == 16 || wpb == 12 || wpb == 8) && nw % wpb == 0;
+                        : path == kPathMfma ? mfma_waves(mfma_tiles(m, false))
+                        : path == kPathF16Mfma ? mfma_waves(mfma_tiles(m, true)) : 0;
+        const bool by_age = (wpb == 16 || ((wpb == 12 || wpb == 8) && fmt != TG_FMT_2BIT)) && nw % wpb == 0;
         // six waves: SIMDs 0 and 1 hold waves 0, 4 and 1, 5; SIMDs 2 and 3 hold waves 2 and 3 alone
         const bool by_wave6 = path == kPathMfma && wpb == 6 && nw % 6 == 0 && long_ranges_of(total_cost, nw, live);
         const double wave6_share[6] = {1.05, 1.05, 1.15, 1.15, 0.80, 0.80};
