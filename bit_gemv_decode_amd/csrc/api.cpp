@@ -291,8 +291,11 @@ size_t ranges_offset(int32_t count) { return ((size_t)count * sizeof(Problem) + 
 // vector path costs about the same (one 128-weight group per lane, however many lanes are busy), so a
 // unit costs its step count, plus the activation reloads of chunked rows; a unit of the matrix-core
 // path costs its chunk count (all units of one plan take the same path).
-// Steps per wave from which a launch takes the strong age-class shares (below).
-constexpr double kLongRangeSteps = 64.0;
+// Steps per wave from which a launch takes the strong age-class shares (below). One-layer plans of
+// the Llama3-8B-shaped layer (~7 steps per wave) run slower with them; one GPU's 8-way shard of the
+// 32-layer set (~26 steps per wave) runs faster (+3.3 % in the first launches from idle, +2.6 %
+// settled, against a threshold of 64), as do the longer launches.
+constexpr double kLongRangeSteps = 16.0;
 
 // Whether a launch's wave ranges are long (at least kLongRangeSteps of cost per wave) and not a
 // row-walk build: such launches take the stronger issue-order shares.
