@@ -462,7 +462,12 @@ int plan_init_common(tg_plan *plan, void *table, size_t table_bytes, int32_t cou
         const bool by_wave6 = path == kPathMfma && wpb == 6 && nw % 6 == 0 && long_ranges_of(total_cost, nw, live);
         const double wave6_share[6] = {1.05, 1.05, 1.15, 1.15, 0.80, 0.80};
         const bool long_ranges = long_ranges_of(total_cost, nw, live);
-        const double age16_long[4] = {1.30, 1.10, 0.90, 0.70}, age16_short[4] = {1.12, 1.04, 0.96, 0.88};
+        const double age16_long[4] = {1.30, 1.10, 0.90, 0.70}, age16_mild[4] = {1.12, 1.04, 0.96, 0.88};
+        // 2-bit launches of few steps per wave (one-layer plans, table-free decode: 16.91 -> 16.09 us
+        // per launch against the mild shares; BITCOS and five-trit within 1 %)
+        const double age16_2bit_short[4] = {1.08, 1.03, 0.97, 0.92};
+        const double *age16_short = fmt == TG_FMT_2BIT && !live && total_cost < kLongRangeSteps * (double)nw
+                                        ? age16_2bit_short : age16_mild;
         const double age12_long[3] = {1.30, 1.00, 0.70}, age12_short[3] = {1.10, 1.00, 0.90};
         const double age8_long[2] = {1.15, 0.85}, age8_short[2] = {1.0, 1.0};
         const double *age_share = wpb == 16 ? (long_ranges && fmt != TG_FMT_2BIT ? age16_long : age16_short)
